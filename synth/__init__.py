@@ -1,0 +1,128 @@
+"""Seeded synthetic inputs for the W4A16 / ternary small-M linear layer.
+
+This module only draws random inputs and packs them into the canonical storage
+format; it holds none of the layer's arithmetic (no dequantization, no
+products).  Both the CPU oracle and the GPU path consume exactly the arrays it
+returns, so the two sides see the same bits.
+
+Canonical format (the library's boundary input):
+  qweight int32 [N][K/8]   nibble i of word (n, j) holds q[k=8j+i][n]
+  scales  uint16 [K/g][N]  IEEE binary16 bit patterns
+  zeros   int32 [K/g][N/8] nibble i of word (gi, j) holds z[gi][8j+i]
+  codes   int32 [N][K/16]  2-bit field i of word (n, j) holds c[k=16j+i][n], c in {0,1,2}
+  x       uint16 [M][K]    binary16 or bfloat16 bit patterns
+
+Distributions (the layer shapes are the 27B-class projections the Z100 vLLM
+article, section 四/五, and the ternary tuning page, section 六, time; the
+pages give no value distributions, so these are stated choices):
+  x       standard normal drawn in float64, rounded to nearest-even into fp16
+          (bf16: float64 -> float32 -> bfloat16, each step nearest-even);
+          optional outliers: round(frac*M*K) distinct positions set to
+          +-magnitude with a fair random sign.
+  q, z    iid uniform on 0..15 (uniform random 32-bit words).
+  s       uniform on [lo, hi] in float64, rounded to nearest-even fp16.
+  c       iid with P(c=0)=1/4, P(c=1)=1/2, P(c=2)=1/4, i.e. the sum of two fair
+          bits, so weight = c - 1 is -1/0/+1 with probability 1/4, 1/2, 1/4.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BASE_SEED = 20261202
+
+
+def rng_for(*key: int) -> np.random.Generator:
+    """A PCG64 stream keyed by (BASE_SEED, *key); distinct keys give
+    independent streams."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([BASE_SEED, *[int(k) for k in key]])))
+
+
+def f64_to_f16_bits(a: np.ndarray) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def f32_to_bf16_bits(a32: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16, nearest-even, returning the 16-bit patterns
+    (inputs here are finite)."""
+    b = np.asarray(a32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def f64_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    return f32_to_bf16_bits(np.asarray(a, dtype=np.float64).astype(np.float32))
+
+
+def random_words(rng: np.random.Generator, count: int) -> np.ndarray:
+    """`count` uniform 32-bit words as int32."""
+    return rng.integers(0, 2**32, size=count, dtype=np.uint32).view(np.int32)
+
+
+def gen_x(key, M: int, K: int, dtype: str = "f16", outlier_frac: float = 0.0,
+          outlier_mag: float = 20.0) -> np.ndarray:
+    """Activations as uint16 bit patterns [M][K]."""
+    rng = rng_for(*key, 1)
+    v = rng.standard_normal((M, K))
+    n_out = int(round(outlier_frac * M * K))
+    if n_out:
+        pos = rng.choice(M * K, size=n_out, replace=False)
+        sign = np.where(rng.integers(0, 2, size=n_out) == 1, 1.0, -1.0)
+        v.reshape(-1)[pos] = sign * outlier_mag
+    if dtype == "f16":
+        return f64_to_f16_bits(v)
+    if dtype == "bf16":
+        return f64_to_bf16_bits(v)
+    raise ValueError(dtype)
+
+
+def gen_w4(key, N: int, K: int, group: int, s_lo: float = 0.002, s_hi: float = 0.02):
+    """Canonical 4-bit weights: dict(qweight [N][K/8] int32, scales [G][N]
+    uint16, zeros [G][N/8] int32)."""
+    if K % group or K % 8 or N % 8:
+        raise ValueError("need K % group == 0, K % 8 == 0, N % 8 == 0")
+    G = K // group
+    rq = rng_for(*key, 2)
+    rs = rng_for(*key, 3)
+    rz = rng_for(*key, 4)
+    qweight = random_words(rq, N * (K // 8)).reshape(N, K // 8)
+    scales = f64_to_f16_bits(rs.uniform(s_lo, s_hi, size=(G, N)))
+    zeros = random_words(rz, G * (N // 8)).reshape(G, N // 8)
+    return {"qweight": qweight, "scales": scales, "zeros": zeros}
+
+
+def pack_codes(c: np.ndarray) -> np.ndarray:
+    """Pack 2-bit codes c[N][K] (values 0..3) into int32 [N][K/16], field i of
+    word j holding c[16j+i]."""
+    N, K = c.shape
+    c = c.astype(np.uint32).reshape(N, K // 16, 16)
+    words = np.zeros((N, K // 16), dtype=np.uint32)
+    for i in range(16):
+        words |= c[:, :, i] << np.uint32(2 * i)
+    return words.view(np.int32)
+
+
+def gen_w2t(key, N: int, K: int, group: int, s_lo: float = 0.01, s_hi: float = 0.05):
+    """Canonical ternary weights: dict(codes [N][K/16] int32, scales [G][N] uint16)."""
+    if K % group or K % 16:
+        raise ValueError("need K % group == 0 and K % 16 == 0")
+    G = K // group
+    rc = rng_for(*key, 5)
+    rs = rng_for(*key, 6)
+    # Two independent uniform bits per weight, taken from two random words per
+    # 16-weight word: field i = bit i of A + bit i of B.
+    a = rc.integers(0, 2**32, size=(N, K // 16), dtype=np.uint32)
+    b = rc.integers(0, 2**32, size=(N, K // 16), dtype=np.uint32)
+    words = np.zeros((N, K // 16), dtype=np.uint32)
+    for i in range(16):
+        c = ((a >> np.uint32(i)) & np.uint32(1)) + ((b >> np.uint32(i)) & np.uint32(1))
+        words |= c << np.uint32(2 * i)
+    scales = f64_to_f16_bits(rs.uniform(s_lo, s_hi, size=(G, N)))
+    return {"codes": words.view(np.int32), "scales": scales}
+
+
+# Layer shapes of the 27B-class decoder (K, N): fused QKV, o_proj, fused
+# gate_up, down.  64 layers of these four matrices make one decode token's
+# weight sweep.
+LAYER_SHAPES = (("qkv", 5120, 7168), ("o_proj", 5120, 5120),
+                ("gate_up", 5120, 34816), ("down", 17408, 5120))
+N_LAYERS = 64
