@@ -1,0 +1,349 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 small-M linear layer on one MI355X.
+
+One step = one decode token's weight sweep of a 64-layer 27B-class decoder:
+64 layers x (fused QKV 5120->7168, o_proj 5120->5120, fused gate_up
+5120->34816, down 17408->5120), 256 distinct packed weight buffers (11.00 GB),
+M = 1, fp16 x, group 128, fp32 y, all 256 w4a16_gemv calls captured in one
+HIP graph and replayed.  `value` is the effective bandwidth of that sweep
+(algorithmic bytes / time; bytes = packed weights + fp16 scales + 4-bit zeros
++ x + y), with inputs resident in HBM.
+
+Also reported: the same sweep at M = 4 (bf16 x with 1% outliers of magnitude
+20), per-shape microseconds per call, the read-only bandwidth probe, a roofline
+object for the GEMV kernel and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+GROUP = 128
+SHAPES = (("qkv", 5120, 7168), ("o_proj", 5120, 5120), ("gate_up", 5120, 34816),
+          ("down", 17408, 5120))
+N_LAYERS = 64
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4_gemv_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "bit_weight_only_03_amd", "csrc", "w4_gemv.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def alg_bytes(M, N, K, g, x_bytes=2, y_bytes=4):
+    """Algorithmic bytes of one call: packed q + fp16 scales + 4-bit zeros + x + y."""
+    G = K // g
+    return N * K // 2 + G * N * 2 + G * N // 2 + M * K * x_bytes + M * N * y_bytes
+
+
+def gbps(nbytes, seconds):
+    return nbytes / seconds / 1e9
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """Per-dispatch HBM bytes of the GEMV kernel from committed rocprofv3 PMC
+    summaries, if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_dispatch")
+
+
+class Sweep:
+    """256 packed matrices plus per-call x and y buffers for one M."""
+
+    def __init__(self, L, torch, synth, M, x_dtype, outliers, mats=None):
+        self.L, self.torch = L, torch
+        self.M, self.x_dtype = M, x_dtype
+        self.mats = mats if mats is not None else self._make_mats(synth)
+        self.xs, self.ys = [], []
+        for i, (layer, name, K, N, _) in enumerate(self.mats_meta):
+            self.xs.append(synth.gen_x_torch((2, M, layer, i), M, K, x_dtype,
+                                             outlier_frac=0.01 if outliers else 0.0))
+            self.ys.append(torch.empty((M, N), dtype=torch.float32, device="cuda"))
+        self.bytes = sum(alg_bytes(M, N, K, GROUP) for (_, _, K, N, _) in self.mats_meta)
+
+    @property
+    def mats_meta(self):
+        return self.mats
+
+    def _make_mats(self, synth):
+        torch, L = self.torch, self.L
+        mats = []
+        for layer in range(N_LAYERS):
+            for mi, (name, K, N) in enumerate(SHAPES):
+                w = synth.gen_w4_torch((1, layer, mi), N, K, GROUP)
+                qb, sb, zb = L.w4a16_packed_sizes(N, K, GROUP)
+                q = torch.empty(qb, dtype=torch.uint8, device="cuda")
+                s = torch.empty(sb, dtype=torch.uint8, device="cuda")
+                z = torch.empty(zb, dtype=torch.uint8, device="cuda")
+                L.w4a16_pack(w["qweight"], w["scales"], w["zeros"], q, s, z, N, K, GROUP)
+                mats.append((layer, name, K, N, (q, s, z)))
+                del w
+            if layer % 16 == 15:
+                torch.cuda.synchronize()
+                log(f"packed {layer + 1}/{N_LAYERS} layers")
+        return mats
+
+    def launch(self, i, stream):
+        layer, name, K, N, (q, s, z) = self.mats[i]
+        self.L.w4a16_gemv(self.xs[i], self.x_dtype, q, s, z, self.ys[i], "f32", self.M, N, K,
+                          GROUP, None, 0, stream)
+
+    def run_all(self, stream):
+        for i in range(len(self.mats)):
+            self.launch(i, stream)
+
+    def capture(self, stream):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            self.run_all(stream)
+        return g
+
+    def time_graph(self, graph, stream, steps, warmup):
+        torch = self.torch
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / steps
+
+    def time_launches(self, stream, reps=3):
+        """Per-launch kernel time with HIP events bracketing each launch on
+        its stream (eager).  Returns seconds per call, median of reps, in
+        call order."""
+        torch = self.torch
+        n = len(self.mats)
+        out = np.zeros((reps, n))
+        with torch.cuda.stream(stream):
+            for r in range(reps):
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(n)]
+                torch.cuda.synchronize()
+                for i in range(n):
+                    ev[i][0].record(stream)
+                    self.launch(i, stream)
+                    ev[i][1].record(stream)
+                torch.cuda.synchronize()
+                out[r] = [a.elapsed_time(b) / 1e3 for a, b in ev]
+        return np.median(out, axis=0)
+
+    def time_eager(self, stream, steps):
+        torch = self.torch
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                self.run_all(stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / steps
+
+
+def parity_guard(L, torch, synth, oracle_mod, sweep):
+    """Sampled columns of a few calls against the oracle, so a timing is never
+    reported for wrong results."""
+    rng = np.random.default_rng(0)
+    worst = 0.0
+    for i in (0, 1, 2, 3, len(sweep.mats) - 1):
+        layer, name, K, N, _ = sweep.mats[i]
+        mi = i % 4
+        w = synth.gen_w4_torch((1, layer, mi), N, K, GROUP)
+        wq = w["qweight"].cpu().numpy()
+        ws = w["scales"].cpu().numpy().view(np.uint16)
+        wz = w["zeros"].cpu().numpy()
+        x = sweep.xs[i].cpu().numpy().view(np.uint16)
+        cols = np.sort(rng.choice(N, size=64, replace=False)).astype(np.int64)
+        ref = oracle_mod.w4_gemv(x, sweep.x_dtype, wq, ws, wz, sweep.M, N, K, GROUP, cols=cols)
+        got = sweep.ys[i].cpu().numpy().astype(np.float64)[:, cols]
+        rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        mx = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+        if rel > 1e-3 or mx > 4e-3:
+            raise SystemExit(f"parity guard failed on call {i} ({name}): rel={rel:.2e} max={mx:.2e}")
+        worst = max(worst, rel)
+    return worst
+
+
+def cpu_baseline(torch, synth, oracle_mod, budget_s=20.0):
+    """The fp64 oracle on the host cores, on a bounded sample: full layers of
+    the sweep (4 matrices, M = 1) until about budget_s seconds have passed."""
+    t_total, nbytes, layers = 0.0, 0, 0
+    while t_total < budget_s and layers < 4:
+        for mi, (name, K, N) in enumerate(SHAPES):
+            w = synth.gen_w4_torch((1, layers, mi), N, K, GROUP)
+            wq = w["qweight"].cpu().numpy()
+            ws = w["scales"].cpu().numpy().view(np.uint16)
+            wz = w["zeros"].cpu().numpy()
+            x = synth.gen_x_torch((2, 1, layers, 4 * layers + mi), 1, K, "f16").cpu().numpy().view(np.uint16)
+            t0 = time.perf_counter()
+            oracle_mod.w4_gemv(x, "f16", wq, ws, wz, 1, N, K, GROUP)
+            t_total += time.perf_counter() - t0
+            nbytes += alg_bytes(1, N, K, GROUP)
+        layers += 1
+        log(f"cpu oracle: {layers} layer(s), {t_total:.1f} s")
+    return {"value": round(gbps(nbytes, t_total), 4), "unit": "GB/s",
+            "cores": oracle_mod.num_threads(), "kind": "oracle",
+            "sample": f"{layers} full decoder layer(s) of the M=1 sweep (qkv, o_proj, gate_up, "
+                      f"down; {nbytes / 1e9:.3f} GB algorithmic), fp64 oracle, "
+                      f"{t_total:.1f} s; GB/s over that sample"}
+
+
+def bw_probe(L, torch, nbytes=4 << 30, reps=5):
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(L.w4a16_bw_probe_sink_floats(), dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    L.w4a16_bw_probe(buf, nbytes, sink, s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        L.w4a16_bw_probe(buf, nbytes, sink, s)
+    e1.record(s)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / reps
+    del buf
+    return gbps(nbytes, t)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-m4", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this library has no multi-GPU path "
+              f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_weight_only_03_amd as L
+    import synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev_name = torch.cuda.get_device_name(0)
+    log(f"device: {dev_name}")
+    stream = torch.cuda.Stream()
+
+    log("building the M=1 sweep (64 layers x 4 matrices, packed on device)")
+    s1 = Sweep(L, torch, synth, 1, "f16", outliers=False)
+    torch.cuda.synchronize()
+    s1.run_all(stream)
+    torch.cuda.synchronize()
+    log("variant (last call): " + L.w4a16_last_variant())
+
+    import oracle as oracle_mod
+    worst = parity_guard(L, torch, synth, oracle_mod, s1)
+    log(f"parity guard ok (worst sampled rel Frobenius {worst:.2e})")
+
+    g1 = s1.capture(stream)
+    t1 = s1.time_graph(g1, stream, args.steps, args.warmup)
+    log(f"M=1 sweep: {t1 * 1e3:.4f} ms/token, {gbps(s1.bytes, t1):.1f} GB/s")
+    te1 = s1.time_eager(stream, max(2, args.steps // 4))
+    per_call = s1.time_launches(stream)
+    per_shape = {}
+    for mi, (name, K, N) in enumerate(SHAPES):
+        us = float(np.median(per_call[mi::4]) * 1e6)
+        per_shape[name] = {"us": round(us, 3),
+                           "GBps": round(alg_bytes(1, N, K, GROUP) / (us * 1e-6) / 1e9, 1)}
+    mean_launch = float(np.mean(per_call))
+    mean_bytes = s1.bytes / len(s1.mats)
+    achieved = gbps(mean_bytes, mean_launch)
+    traffic = load_traffic()
+
+    extra = {"device": dev_name, "sweep_bytes": s1.bytes, "pct_of_peak": round(100 * gbps(s1.bytes, t1) / PEAK_GBPS, 2),
+             "m1_eager_ms": round(te1 * 1e3, 4), "m1_per_shape": per_shape,
+             "variant": L.w4a16_last_variant()}
+
+    if not args.no_m4:
+        log("M=4 sweep (bf16 x, 1% outliers), same weights")
+        s4 = Sweep(L, torch, synth, 4, "bf16", outliers=True, mats=s1.mats)
+        s4.run_all(stream)
+        torch.cuda.synchronize()
+        w4 = parity_guard(L, torch, synth, oracle_mod, s4)
+        g4 = s4.capture(stream)
+        t4 = s4.time_graph(g4, stream, args.steps, args.warmup)
+        pc4 = s4.time_launches(stream, reps=1)
+        extra["m4_sweep"] = {"ms_per_token": round(t4 * 1e3, 4), "GBps": round(gbps(s4.bytes, t4), 1),
+                             "pct_of_peak": round(100 * gbps(s4.bytes, t4) / PEAK_GBPS, 2),
+                             "bytes": s4.bytes, "parity_worst_rel": w4,
+                             "per_shape_us": {name: round(float(np.median(pc4[mi::4]) * 1e6), 3)
+                                              for mi, (name, K, N) in enumerate(SHAPES)}}
+        log(f"M=4 sweep: {t4 * 1e3:.4f} ms/token, {gbps(s4.bytes, t4):.1f} GB/s")
+        del g4, s4
+
+    probe = bw_probe(L, torch)
+    extra["bw_probe_GBps"] = round(probe, 1)
+    extra["value_pct_of_probe"] = round(100 * gbps(s1.bytes, t1) / probe, 2)
+    log(f"bw_probe read ceiling: {probe:.1f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(torch, synth, oracle_mod)
+
+    result = {
+        "metric": "W4A16 GEMV effective HBM GB/s (% of peak) + µs/call at M=1,4; ms/token sweep",
+        "value": round(gbps(s1.bytes, t1), 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t1 * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "27B-class decoder weight sweep: 64 layers x (qkv K5120 N7168, "
+                               "o_proj K5120 N5120, gate_up K5120 N34816, down K17408 N5120), "
+                               "M=1, group 128, 256 distinct packed buffers, hipGraph replay",
+                   "M": 1, "group": GROUP, "layers": N_LAYERS, "x": "f16", "y": "f32"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "w4_gemv_kernel<f16, group 128, depth 8>",
+                     "per_launch_alg_bytes": round(mean_bytes), "per_launch_us": round(mean_launch * 1e6, 3)},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

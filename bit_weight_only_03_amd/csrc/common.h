@@ -1,0 +1,119 @@
+// common.h -- shared definitions of the gfx950 W4A16 / ternary library:
+// device-layout geometry, bit-cast helpers and host-side argument checks.
+//
+// Device layout of the 4-bit weights ("w4").  Columns are grouped in tiles of
+// 16, k in units of 128.  One unit of one tile is 1 KiB: 64 lanes x 16 bytes,
+// exactly one 16-byte load per lane of a wave64, so a wave streams a tile with
+// fully coalesced dwordx4 loads and every lane dequantizes in registers.
+//   qweight_dev uint32 [Np/16][Kp/128][64 lanes][4 dwords]
+//   lane l: column n = 16*t + (l & 15), k-block kc = l >> 4
+//   dword j of lane l in unit u holds the 8 weights k = 128u + 32j + 8kc + e,
+//   e = 0..7, which are exactly the 8 nibbles of canonical word
+//   qweight[n][16u + 4j + kc].  Inside the dword, nibble position p
+//   (bits 4p..4p+3) holds element e = kNibbleElem[p] = {0,2,4,6,1,3,5,7}[p], so
+//   masks 0x000F000F / 0x00F000F0 applied to the word and to the word >> 8 give
+//   the element pairs (0,1), (2,3), (4,5), (6,7) in the two 16-bit halves.
+//   scales_dev uint16 [Np/16][Gp][16]     (fp16 scale of group g, column c)
+//   zeros_dev  uint32 [Np/16][Gp][2]      (nibble c of the 8 bytes = zero of column c)
+// with Np = N rounded up to 16, Kp = K rounded up to 128, Gp = Kp / group.
+// Padding holds q = 0, z = 0, s = +0, so padded weights are exactly zero.
+//
+// Device layout of the ternary weights ("w2t"): the same tiles with 256-k units.
+//   qweight_dev uint32 [Np/16][Kp/256][64][4]; dword d of lane l in unit u holds
+//   16 codes: k = 256u + 32(2d + h) + 8kc + e for h = 0, 1 and e = 0..7, i.e. the
+//   16 fields of canonical word codes[n][16u + 4d + 2h... ] -- see w2t.hip.
+//   scales_dev uint16 [Np/16][Gp][16], Kp = K rounded up to 256, Gp = Kp / group.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/w4a16.h"
+
+namespace w4k {
+
+constexpr int kTileN = 16;       // columns per tile
+constexpr int kUnitK = 128;      // k per 4-bit unit (one 16-byte load per lane)
+constexpr int kUnitK2 = 256;     // k per ternary unit
+constexpr int kLanes = 64;
+
+__host__ __device__ inline int pad_n(int N) { return (N + 15) & ~15; }
+__host__ __device__ inline int pad_k(int K) { return (K + kUnitK - 1) / kUnitK * kUnitK; }
+__host__ __device__ inline int pad_k2(int K) { return (K + kUnitK2 - 1) / kUnitK2 * kUnitK2; }
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From& v) {
+    static_assert(sizeof(To) == sizeof(From), "size mismatch");
+    return __builtin_bit_cast(To, v);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+    return (float)bitcast<_Float16>(h);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN kept quiet).
+__host__ __device__ inline uint16_t f32_to_bf16_bits(float f) {
+    uint32_t b = __builtin_bit_cast(uint32_t, f);
+    if ((b & 0x7f800000u) == 0x7f800000u && (b & 0x7fffffu)) return (uint16_t)((b >> 16) | 0x40);
+    b += 0x7fffu + ((b >> 16) & 1u);
+    return (uint16_t)(b >> 16);
+}
+
+// Streamed, read-once loads: non-temporal so the weights do not evict x and
+// the scales from the caches.
+__device__ __forceinline__ u32x4_t load_nt(const u32x4_t* p) {
+    return __builtin_nontemporal_load(p);
+}
+
+// Raw buffer resources: a wave-uniform 128-bit descriptor (base, byte size)
+// lets every load take its lane offset from one VGPR and its unit offset from
+// an SGPR, with no per-load 64-bit address arithmetic.  Lanes whose
+// VGPR + immediate offset falls outside the byte size read zeros.
+constexpr int kRsrcFlags = 0x00020000;   // raw (untyped) 32-bit data, gfx9 family
+constexpr int kAuxNT = 2;                // non-temporal cache policy
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kRsrcFlags);
+}
+
+}  // namespace w4k
+
+// ---------------------------------------------------------------- host side
+
+namespace w4h {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline bool group_ok(int group) {
+    return group == 32 || group == 64 || group == 128 || group == 256;
+}
+
+// Shape contract of the 4-bit functions (see w4a16.h).
+inline int check_w4_shape(int N, int K, int group) {
+    if (N < 1 || K < 1 || !group_ok(group)) return W4A16_ERR_SHAPE;
+    if (N % 8 || K % 8 || K % group) return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+inline int check_w2_shape(int N, int K, int group) {
+    if (N < 1 || K < 1 || !group_ok(group)) return W4A16_ERR_SHAPE;
+    if (K % 16 || K % group) return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+inline int launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+void set_last_variant(const char* fmt, ...);
+
+}  // namespace w4h

@@ -1,0 +1,82 @@
+// misc.hip -- status strings, the dispatch probe string and the read-only
+// HBM bandwidth probe.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "common.h"
+
+using namespace w4k;
+
+namespace {
+
+constexpr int kProbeBlocks = 4096;
+constexpr int kProbeThreads = 256;
+
+thread_local char g_last_variant[160] = "none";
+
+// Streams `n16` 16-byte words with non-temporal loads, grid-stride, eight
+// loads in flight per thread, and folds them with XOR so nothing is elided.
+__global__ __launch_bounds__(kProbeThreads) void bw_probe_kernel(const u32x4_t* __restrict__ buf,
+                                                                 size_t n16, float* __restrict__ sink) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        u32x4_t v[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) v[r] = load_nt(buf + i + r * stride);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc ^= v[r][0] ^ v[r][1] ^ v[r][2] ^ v[r][3];
+    }
+    for (; i < n16; i += stride) {
+        const u32x4_t v = load_nt(buf + i);
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    __shared__ uint32_t red[kProbeThreads];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t a = 0;
+        for (int t = 0; t < kProbeThreads; ++t) a ^= red[t];
+        sink[blockIdx.x] = (float)(a & 0xffffu);
+    }
+}
+
+}  // namespace
+
+namespace w4h {
+void set_last_variant(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_variant, sizeof g_last_variant, fmt, ap);
+    va_end(ap);
+}
+}  // namespace w4h
+
+extern "C" const char* w4a16_last_variant(void) { return g_last_variant; }
+
+extern "C" const char* w4a16_status_string(int status) {
+    switch (status) {
+        case W4A16_OK: return "ok";
+        case W4A16_ERR_NULL: return "a required pointer is NULL";
+        case W4A16_ERR_SHAPE: return "M, N, K or group outside the supported contract";
+        case W4A16_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+        case W4A16_ERR_DTYPE: return "unknown or disallowed dtype";
+        case W4A16_ERR_WORKSPACE: return "workspace smaller than the size query reports";
+        case W4A16_ERR_UNSUPPORTED: return "valid request not implemented by this build";
+        case W4A16_ERR_HIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int w4a16_bw_probe_sink_floats(void) { return kProbeBlocks; }
+
+extern "C" int w4a16_bw_probe(const void* buf, size_t bytes, float* sink, w4a16_stream_t stream) {
+    if (!buf || !sink) return W4A16_ERR_NULL;
+    if (bytes == 0 || bytes % 16) return W4A16_ERR_SHAPE;
+    if (!w4h::aligned16(buf) || !w4h::aligned16(sink)) return W4A16_ERR_ALIGN;
+    hipLaunchKernelGGL(bw_probe_kernel, dim3(kProbeBlocks), dim3(kProbeThreads), 0,
+                       (hipStream_t)stream, (const u32x4_t*)buf, bytes / 16, sink);
+    w4h::set_last_variant("bw_probe blocks=%d threads=%d", kProbeBlocks, kProbeThreads);
+    return w4h::launch_status();
+}

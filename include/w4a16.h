@@ -1,0 +1,163 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) small-M W4A16 / ternary linear layer.
+ *
+ * The operation.  One decode step's linear layer, y[M,N] = x[M,K] . W[K,N],
+ * where M is 1 for a single generated token or a few rows when draft tokens
+ * are verified together, so every call re-reads all of W once
+ * (Ninfer V100 article, haowenji.com, section 三: decode speed is bounded by
+ * memory bandwidth over the bytes read per token, and verifying several
+ * draft tokens costs one weight read; Z100 vLLM port article,
+ * forum.sourcefind.cn, section 五: stream the weights once for all M rows).
+ * W is stored group-wise as 4-bit integers: for the group of `group`
+ * consecutive k of column n, w = (q - z) * s with an fp16 scale s and a 4-bit
+ * zero point z (Ninfer V100 article, section 十一, "groupwise-int"; Z100
+ * article, section 四, unpack INT4, read scale and zero point, restore,
+ * multiply-add).  The ternary variant stores w in {-1, 0, +1} times a per-group
+ * scale ("NINFER 三元引擎性能调优", sections 五 and 六).  Accumulation is fp32.
+ *
+ * Canonical storage (the format callers hand in; all little-endian):
+ *   qweight_canon int32 [N][K/8]   nibble i (bits 4i..4i+3) of word (n, j) = q[8j+i][n]
+ *   scales_canon  fp16  [K/group][N]
+ *   zeros_canon   int32 [K/group][N/8]  nibble i of word (g, j) = z[g][8j+i]
+ *   codes_canon   int32 [N][K/16]  2-bit field i of word (n, j) = c[16j+i][n],
+ *                                  ternary weight = c - 1, c in {0, 1, 2}
+ *   x             fp16 or bf16 [M][K], row-major, contiguous (leading dim K)
+ *   y             fp32, fp16 or bf16 [M][N], row-major, contiguous (leading dim N)
+ *
+ * Device layout.  *_pack converts canonical arrays into the library's own
+ * interleaved layout once, at load time, before any graph capture (Z100
+ * article, section 四: the repacked weights and the output-major scales and
+ * zero points must be built after loading, not lazily inside a captured
+ * graph).  Its sizes come from *_packed_sizes; its contents are opaque and
+ * *_unpack restores the canonical arrays bit for bit.  The device arrays hold
+ * exactly the canonical information (4-bit q and z, fp16 s), padded up to
+ * whole 16-column by 128-k tiles (256-k for ternary).
+ *
+ * Conventions for every function:
+ *   - Pointers are device pointers unless stated otherwise.  All buffers are
+ *     owned by the caller; the library never allocates or frees memory and
+ *     keeps no per-call state.
+ *   - Device pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously; no function synchronizes, so every call can be captured
+ *     into a hipGraph.
+ *   - Arguments are checked on the host before anything is launched; a
+ *     negative w4a16_status is returned and nothing is enqueued.  There is
+ *     never a silent fallback: a valid but unsupported request returns
+ *     W4A16_ERR_UNSUPPORTED.  A launch failure returns W4A16_ERR_HIP.
+ *   - Size-query functions (*_packed_sizes, *_workspace_bytes) do no GPU work.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;                       /* hipStream_t is struct ihipStream_t* */
+typedef struct ihipStream_t* w4a16_stream_t;
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_NULL = -1,         /* a required pointer is NULL */
+    W4A16_ERR_SHAPE = -2,        /* M, N, K or group outside the contract */
+    W4A16_ERR_ALIGN = -3,        /* a device pointer is not 16-byte aligned */
+    W4A16_ERR_DTYPE = -4,        /* unknown or disallowed dtype */
+    W4A16_ERR_WORKSPACE = -5,    /* workspace smaller than *_workspace_bytes */
+    W4A16_ERR_UNSUPPORTED = -6,  /* valid request this build does not implement */
+    W4A16_ERR_HIP = -7           /* the HIP runtime reported an error at launch */
+} w4a16_status;
+
+typedef enum { W4A16_F16 = 0, W4A16_BF16 = 1, W4A16_F32 = 2 } w4a16_dtype;
+
+/* Shape contract shared by the 4-bit functions:
+ *   1 <= N, 1 <= K, N % 8 == 0, K % group == 0, K % 8 == 0,
+ *   group in {32, 64, 128, 256}; for the GEMV also 1 <= M <= 16. */
+
+/* Bytes of the device layout for an N x K matrix with the given group.  Host
+ * only.  Returns W4A16_OK or W4A16_ERR_SHAPE / W4A16_ERR_NULL. */
+int w4a16_packed_sizes(int N, int K, int group, size_t* q_bytes, size_t* s_bytes,
+                       size_t* z_bytes);
+
+/* Canonical -> device layout (a pure bit permutation plus zero padding).
+ * Reads qweight_canon [N][K/8], scales_canon [K/group][N], zeros_canon
+ * [K/group][N/8]; writes the three device arrays of w4a16_packed_sizes bytes
+ * (every byte, padding included).  Canonical and device buffers must not
+ * overlap. */
+int w4a16_pack(const int32_t* qweight_canon, const uint16_t* scales_canon,
+               const int32_t* zeros_canon, void* qweight, void* scales, void* zeros, int N,
+               int K, int group, w4a16_stream_t stream);
+
+/* Device layout -> canonical, the exact inverse of w4a16_pack. */
+int w4a16_unpack(const void* qweight, const void* scales, const void* zeros,
+                 int32_t* qweight_canon, uint16_t* scales_canon, int32_t* zeros_canon, int N,
+                 int K, int group, w4a16_stream_t stream);
+
+/* Fp32 workspace bytes w4a16_gemv needs for this shape (0 when the shape runs
+ * without a K split).  Host only; the answer is fixed for the life of the
+ * process, so a workspace sized once may be reused inside a captured graph
+ * (NINFER tuning page, section 五: declare workspace capacity up front). */
+int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* bytes);
+
+/* y[M,N] = x[M,K] . ((q - z) * s)[K,N] from the packed device layout.
+ * x_dtype: W4A16_F16 or W4A16_BF16.  y_dtype: W4A16_F32, W4A16_F16 or
+ * W4A16_BF16 (rounded to nearest even from the fp32 result).  Products and
+ * sums are fp32; the result is deterministic: the same inputs give the same
+ * bits on every call and every graph replay.  workspace may be NULL when
+ * w4a16_workspace_bytes reports 0; otherwise it must hold that many bytes and
+ * is scratch owned by the call while it runs (no zeroing needed).  x and y
+ * must not overlap the weights or each other. */
+int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const void* scales,
+               const void* zeros, void* y, int y_dtype, int M, int N, int K, int group,
+               void* workspace, size_t workspace_bytes, w4a16_stream_t stream);
+
+/* Debug / parity: the dequantized matrix w[K][N] = (q - z) * s as fp32 from the
+ * packed layout.  Exact, since |q - z| <= 15 times an fp16 scale fits in fp32. */
+int w4a16_dequant(const void* qweight, const void* scales, const void* zeros, float* w, int N,
+                  int K, int group, w4a16_stream_t stream);
+
+/* ---- ternary 2-bit variant: w = (c - 1) * s, one fp16 scale per group ----
+ * Shape contract: 1 <= N, 1 <= K, K % group == 0, K % 16 == 0,
+ * group in {32, 64, 128, 256}; for the GEMV also 1 <= M <= 16.
+ * A code of 3 is invalid input: the output for such weights is unspecified
+ * (no error is reported; the GPU path does not scan for it). */
+int w2t_packed_sizes(int N, int K, int group, size_t* q_bytes, size_t* s_bytes);
+int w2t_pack(const int32_t* codes_canon, const uint16_t* scales_canon, void* qweight,
+             void* scales, int N, int K, int group, w4a16_stream_t stream);
+int w2t_unpack(const void* qweight, const void* scales, int32_t* codes_canon,
+               uint16_t* scales_canon, int N, int K, int group, w4a16_stream_t stream);
+int w2t_workspace_bytes(int M, int N, int K, int group, size_t* bytes);
+int w2t_gemv(const void* x, int x_dtype, const void* qweight, const void* scales, void* y,
+             int y_dtype, int M, int N, int K, int group, void* workspace,
+             size_t workspace_bytes, w4a16_stream_t stream);
+int w2t_dequant(const void* qweight, const void* scales, float* w, int N, int K, int group,
+                w4a16_stream_t stream);
+
+/* ---- measurement and diagnostics ---- */
+
+/* Read-only HBM streaming probe: reads `bytes` (a multiple of 16) from buf
+ * with 16-byte loads and writes one fp32 per workgroup into sink so the reads
+ * cannot be elided; sink must hold w4a16_bw_probe_sink_floats() floats.  The
+ * achievable read bandwidth it measures is the ceiling the GEMV is judged
+ * against beside the published peak (the pages each measure their own card's
+ * ceiling first: Ninfer V100 article, section 十九; Z100 article, section 四). */
+int w4a16_bw_probe(const void* buf, size_t bytes, float* sink, w4a16_stream_t stream);
+int w4a16_bw_probe_sink_floats(void);
+
+/* Static text for a status code. */
+const char* w4a16_status_string(int status);
+
+/* Name of the kernel variant the most recent gemv call on this host thread
+ * chose, with its launch shape, e.g. "w4_mfma16 f16 tiles=320 waves=8 split=1"
+ * (every dispatch branch reports itself: NINFER tuning page, section 二).
+ * Host string owned by the library, valid until the next call on the thread. */
+const char* w4a16_last_variant(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

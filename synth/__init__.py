@@ -126,3 +126,72 @@ def gen_w2t(key, N: int, K: int, group: int, s_lo: float = 0.01, s_hi: float = 0
 LAYER_SHAPES = (("qkv", 5120, 7168), ("o_proj", 5120, 5120),
                 ("gate_up", 5120, 34816), ("down", 17408, 5120))
 N_LAYERS = 64
+
+
+# ---------------------------------------------------------------------------
+# Device-side generators for large benchmark inputs (an 11 GB weight sweep is
+# slow to draw on the host).  Same distributions as above, drawn with torch's
+# seeded Philox generator on the given device; anything that needs the values
+# on the host copies them back.  Imported lazily so the module stays usable
+# without torch.
+
+def _torch_gen(key, device):
+    import torch
+    seed = int(np.random.SeedSequence([BASE_SEED, *[int(k) for k in key]]).generate_state(1, np.uint64)[0])
+    g = torch.Generator(device=device)
+    g.manual_seed(seed & ((1 << 63) - 1))
+    return g
+
+
+def gen_w4_torch(key, N: int, K: int, group: int, device="cuda", s_lo: float = 0.002,
+                 s_hi: float = 0.02):
+    """Canonical 4-bit weights as device tensors (int32 qweight [N][K/8],
+    int16 scale bits [G][N], int32 zeros [G][N/8])."""
+    import torch
+    if K % group or K % 8 or N % 8:
+        raise ValueError("need K % group == 0, K % 8 == 0, N % 8 == 0")
+    G = K // group
+    g = _torch_gen(key, device)
+    q = torch.randint(-2**31, 2**31, (N, K // 8), dtype=torch.int32, device=device, generator=g)
+    z = torch.randint(-2**31, 2**31, (G, N // 8), dtype=torch.int32, device=device, generator=g)
+    u = torch.rand((G, N), dtype=torch.float64, device=device, generator=g)
+    s = (s_lo + (s_hi - s_lo) * u).to(torch.float16).view(torch.int16)
+    return {"qweight": q, "scales": s, "zeros": z}
+
+
+def gen_x_torch(key, M: int, K: int, dtype: str = "f16", outlier_frac: float = 0.0,
+                outlier_mag: float = 20.0, device="cuda"):
+    """Activations as an int16 device tensor of fp16/bf16 bit patterns [M][K]."""
+    import torch
+    g = _torch_gen(key, device)
+    v = torch.randn((M, K), dtype=torch.float64, device=device, generator=g)
+    n_out = int(round(outlier_frac * M * K))
+    if n_out:
+        pos = torch.randperm(M * K, device=device, generator=g)[:n_out]
+        sign = torch.randint(0, 2, (n_out,), device=device, generator=g).to(torch.float64) * 2 - 1
+        v.view(-1)[pos] = sign * outlier_mag
+    if dtype == "f16":
+        return v.to(torch.float16).view(torch.int16)
+    if dtype == "bf16":
+        return v.to(torch.float32).to(torch.bfloat16).view(torch.int16)
+    raise ValueError(dtype)
+
+
+def gen_w2t_torch(key, N: int, K: int, group: int, device="cuda", s_lo: float = 0.01,
+                  s_hi: float = 0.05):
+    """Canonical ternary codes as device tensors (int32 codes [N][K/16], int16
+    scale bits [G][N]); each code is the sum of two fair random bits."""
+    import torch
+    if K % group or K % 16:
+        raise ValueError("need K % group == 0 and K % 16 == 0")
+    G = K // group
+    g = _torch_gen(key, device)
+    a = torch.randint(-2**31, 2**31, (N, K // 16), dtype=torch.int32, device=device, generator=g)
+    b = torch.randint(-2**31, 2**31, (N, K // 16), dtype=torch.int32, device=device, generator=g)
+    words = torch.zeros((N, K // 16), dtype=torch.int32, device=device)
+    for i in range(16):
+        c = ((a >> i) & 1) + ((b >> i) & 1)
+        words |= c << (2 * i)
+    u = torch.rand((G, N), dtype=torch.float64, device=device, generator=g)
+    s = (s_lo + (s_hi - s_lo) * u).to(torch.float16).view(torch.int16)
+    return {"codes": words, "scales": s}

@@ -1,0 +1,92 @@
+"""Helpers for the GPU tests: device buffers, packing through the C ABI and
+the parity bar against the oracle.  Every GPU computation goes through the
+library's entry points; torch only allocates memory and provides the stream."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import bit_weight_only_03_amd as L
+
+DEV = "cuda"
+
+# Parity bar for floating-point results (relative Frobenius and max-abs
+# relative to the largest oracle magnitude).
+REL_FROB = 1e-3
+MAX_ABS = 4e-3
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).to(DEV)
+
+
+def host_bits(t: torch.Tensor, dtype) -> np.ndarray:
+    return t.cpu().numpy().view(dtype)
+
+
+def empty_bytes(n: int) -> torch.Tensor:
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=DEV)
+
+
+class PackedW4:
+    """A 4-bit matrix packed on the device with w4a16_pack."""
+
+    def __init__(self, w: dict, N: int, K: int, group: int):
+        self.N, self.K, self.group = N, K, group
+        qb, sb, zb = L.w4a16_packed_sizes(N, K, group)
+        self.q, self.s, self.z = empty_bytes(qb), empty_bytes(sb), empty_bytes(zb)
+        self.canon = (dev(w["qweight"]), dev(w["scales"]), dev(w["zeros"]))
+        L.w4a16_pack(*self.canon, self.q, self.s, self.z, N, K, group)
+
+    def gemv(self, x: torch.Tensor, x_dtype: str, M: int, y_dtype: str = "f32",
+             workspace=None) -> torch.Tensor:
+        ydt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[y_dtype]
+        y = torch.empty((M, self.N), dtype=ydt, device=DEV)
+        ws_bytes = L.w4a16_workspace_bytes(M, self.N, self.K, self.group)
+        if ws_bytes and workspace is None:
+            workspace = empty_bytes(ws_bytes)
+        L.w4a16_gemv(x, x_dtype, self.q, self.s, self.z, y, y_dtype, M, self.N, self.K,
+                     self.group, workspace, workspace.numel() if workspace is not None else 0)
+        return y
+
+
+class PackedW2T:
+    """A ternary matrix packed on the device with w2t_pack."""
+
+    def __init__(self, w: dict, N: int, K: int, group: int):
+        self.N, self.K, self.group = N, K, group
+        qb, sb = L.w2t_packed_sizes(N, K, group)
+        self.q, self.s = empty_bytes(qb), empty_bytes(sb)
+        self.canon = (dev(w["codes"]), dev(w["scales"]))
+        L.w2t_pack(*self.canon, self.q, self.s, N, K, group)
+
+    def gemv(self, x: torch.Tensor, x_dtype: str, M: int, y_dtype: str = "f32") -> torch.Tensor:
+        ydt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[y_dtype]
+        y = torch.empty((M, self.N), dtype=ydt, device=DEV)
+        ws_bytes = L.w2t_workspace_bytes(M, self.N, self.K, self.group)
+        ws = empty_bytes(ws_bytes) if ws_bytes else None
+        L.w2t_gemv(x, x_dtype, self.q, self.s, y, y_dtype, M, self.N, self.K, self.group, ws,
+                   ws_bytes)
+        return y
+
+
+def to_f64(y: torch.Tensor) -> np.ndarray:
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def assert_parity(y_gpu: np.ndarray, y_ref: np.ndarray, what: str = "", extra_rel: float = 0.0):
+    """Relative Frobenius error <= 1e-3 and max abs error <= 4e-3 * max|y_ref|
+    (plus, for rounded outputs, the rounding of the output type itself)."""
+    diff = y_gpu - y_ref
+    ref_norm = np.linalg.norm(y_ref)
+    scale = np.max(np.abs(y_ref))
+    rel = np.linalg.norm(diff) / ref_norm if ref_norm > 0 else np.linalg.norm(diff)
+    mx = np.max(np.abs(diff)) if diff.size else 0.0
+    assert rel <= REL_FROB + extra_rel, f"{what}: relative Frobenius error {rel:.3e}"
+    assert mx <= (MAX_ABS + extra_rel) * scale + 1e-30, f"{what}: max abs error {mx:.3e} vs {scale:.3e}"
+    return rel, mx

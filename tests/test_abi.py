@@ -1,0 +1,110 @@
+"""CPU checks of the C ABI: the library loads, exports every function the
+header declares, and its host-side logic (size queries, argument checks,
+dispatch sizing) behaves as documented.  Nothing here launches a kernel: every
+call below returns before any HIP work is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+import bit_weight_only_03_amd as lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(w(?:4a16|2t)_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("w4a16_pack", "w4a16_unpack", "w4a16_gemv", "w4a16_dequant", "w4a16_packed_sizes",
+              "w4a16_workspace_bytes", "w2t_pack", "w2t_unpack", "w2t_gemv", "w2t_dequant",
+              "w2t_packed_sizes", "w2t_workspace_bytes", "w4a16_bw_probe", "w4a16_status_string",
+              "w4a16_last_variant"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    so = ctypes.CDLL(lib.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(so, n), n
+    assert set(declared_functions()) == set(lib.EXPORTED)
+
+
+def test_packed_sizes():
+    # 4096 x 4096, g128: 8 MiB of nibbles, 32 x 4096 fp16 scales, 32 x 4096 nibble zeros
+    assert lib.w4a16_packed_sizes(4096, 4096, 128) == (8388608, 262144, 65536)
+    # ragged: N = 24 pads to 32 columns, K = 96 (g = 32) pads to 128
+    assert lib.w4a16_packed_sizes(24, 96, 32) == (32 * 128 // 2, 32 * 4 * 2, 32 * 4 // 2)
+    assert lib.w2t_packed_sizes(5120, 17408, 128) == (5120 * 17408 // 4, 5120 * 136 * 2)
+    # ternary: N needs no multiple of 8; 7 columns pad to 16, K = 32 pads to 256
+    assert lib.w2t_packed_sizes(7, 32, 32) == (16 * 256 // 4, 16 * 8 * 2)
+
+
+@pytest.mark.parametrize("N,K,g", [(0, 128, 128), (12, 128, 128), (16, 100, 128), (16, 128, 96),
+                                   (16, 192, 128), (16, -128, 128)])
+def test_packed_sizes_rejects_bad_shapes(N, K, g):
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.w4a16_packed_sizes(N, K, g)
+    assert e.value.status == -2
+
+
+def test_gemv_argument_checks_return_before_launch():
+    good = 1 << 20  # aligned fake pointers: the call must fail before touching them
+    args = dict(x=good, x_dtype=0, qweight=good, scales=good, zeros=good, y=good, y_dtype=2,
+                M=1, N=4096, K=4096, group=128, stream=0)
+
+    def rc(**over):
+        a = dict(args, **over)
+        try:
+            lib.w4a16_gemv(a["x"], a["x_dtype"], a["qweight"], a["scales"], a["zeros"], a["y"],
+                           a["y_dtype"], a["M"], a["N"], a["K"], a["group"], stream=a["stream"])
+        except lib.W4A16Error as e:
+            return e.status
+        return 0
+
+    assert rc(x=0) == -1
+    assert rc(zeros=0) == -1
+    assert rc(x_dtype=2) == -4          # x must be f16 or bf16
+    assert rc(y_dtype=7) == -4
+    assert rc(M=0) == -2 and rc(M=17) == -2
+    assert rc(N=0) == -2 and rc(N=4100) == -2
+    assert rc(K=4100) == -2 and rc(group=100) == -2
+    assert rc(x=good + 8) == -3 and rc(y=good + 4) == -3
+
+
+def test_workspace_query_and_check():
+    # 4096 columns fill the GPU with tiles: no K split, no workspace.
+    assert lib.w4a16_workspace_bytes(1, 4096, 4096, 128) == 0
+    # A narrow column shard (one GPU's share of down, N = 512) splits K.
+    ws = lib.w4a16_workspace_bytes(4, 512, 17408, 128)
+    assert ws > 0 and ws % (4 * 512 * 4) == 0
+    good = 1 << 20
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.w4a16_gemv(good, 0, good, good, good, good, 2, 4, 512, 17408, 128, workspace=good,
+                       workspace_bytes=ws - 4, stream=0)
+    assert e.value.status == -5
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.w4a16_gemv(good, 0, good, good, good, good, 2, 4, 512, 17408, 128, stream=0)
+    assert e.value.status == -1
+
+
+def test_status_strings():
+    for s in range(-7, 1):
+        assert lib.w4a16_status_string(s) != "unknown status"
+    assert lib.w4a16_status_string(-99) == "unknown status"
+
+
+def test_ternary_argument_checks():
+    good = 1 << 20
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.w2t_gemv(good, 0, good, good, good, 2, 1, 5120, 5120 + 8, 128, stream=0)
+    assert e.value.status == -2
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.w2t_pack(good, good, 0, good, 16, 256, 128, stream=0)
+    assert e.value.status == -1

@@ -1,0 +1,338 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+on the same seeded inputs.
+
+Bar: the repacking round trip and the dequantized weights are bit-exact;
+GEMV outputs are within relative Frobenius 1e-3 and max abs 4e-3 * max|y|;
+identities of w = (q - z) * s (q = z, s -> 2s, one-hot x, ternary +-1 counts)
+hold bitwise.  Sizes span several tiles with ragged tails; the full 27B-class
+shapes run in the benchmark's launch configuration with sampled columns.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import bit_weight_only_03_amd as L  # noqa: E402
+from gpu_util import (PackedW2T, PackedW4, assert_parity, dev, empty_bytes, host_bits,  # noqa: E402
+                      to_f64)
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------ pack / unpack ---
+
+W4_SHAPES = [(8, 128, 128), (24, 96, 32), (40, 384, 64), (136, 1152, 128), (16, 512, 256),
+             (4104, 640, 64), (7168, 5120, 128)]
+
+
+@pytest.mark.parametrize("N,K,g", W4_SHAPES)
+def test_w4_pack_unpack_roundtrip_bitexact(N, K, g):
+    say(f"w4 roundtrip N={N} K={K} g={g}")
+    w = synth.gen_w4((101, N, K, g), N, K, g)
+    P = PackedW4(w, N, K, g)
+    qc = torch.empty((N, K // 8), dtype=torch.int32, device="cuda")
+    sc = torch.empty((K // g, N), dtype=torch.int16, device="cuda")
+    zc = torch.empty((K // g, N // 8), dtype=torch.int32, device="cuda")
+    L.w4a16_unpack(P.q, P.s, P.z, qc, sc, zc, N, K, g)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(qc, np.int32), w["qweight"])
+    assert np.array_equal(host_bits(sc, np.uint16), w["scales"])
+    assert np.array_equal(host_bits(zc, np.int32), w["zeros"])
+
+
+W2_SHAPES = [(7, 32, 32), (40, 768, 128), (136, 1280, 64), (5120, 512, 256)]
+
+
+@pytest.mark.parametrize("N,K,g", W2_SHAPES)
+def test_w2t_pack_unpack_roundtrip_bitexact(N, K, g):
+    say(f"w2t roundtrip N={N} K={K} g={g}")
+    w = synth.gen_w2t((102, N, K, g), N, K, g)
+    P = PackedW2T(w, N, K, g)
+    cc = torch.empty((N, K // 16), dtype=torch.int32, device="cuda")
+    sc = torch.empty((K // g, N), dtype=torch.int16, device="cuda")
+    L.w2t_unpack(P.q, P.s, cc, sc, N, K, g)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(cc, np.int32), w["codes"])
+    assert np.array_equal(host_bits(sc, np.uint16), w["scales"])
+
+
+# ------------------------------------------------------------ dequant exact ---
+
+@pytest.mark.parametrize("N,K,g", W4_SHAPES + [(5120, 17408, 128)])
+def test_w4_dequant_bitexact(N, K, g):
+    say(f"w4 dequant N={N} K={K} g={g}")
+    w = synth.gen_w4((103, N, K, g), N, K, g)
+    P = PackedW4(w, N, K, g)
+    out = torch.empty((K, N), dtype=torch.float32, device="cuda")
+    L.w4a16_dequant(P.q, P.s, P.z, out, N, K, g)
+    ref = oracle.w4_dequant(w["qweight"], w["scales"], w["zeros"], N, K, g)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("N,K,g", W2_SHAPES + [(7168, 5120, 128)])
+def test_w2t_dequant_bitexact(N, K, g):
+    say(f"w2t dequant N={N} K={K} g={g}")
+    w = synth.gen_w2t((104, N, K, g), N, K, g)
+    P = PackedW2T(w, N, K, g)
+    out = torch.empty((K, N), dtype=torch.float32, device="cuda")
+    L.w2t_dequant(P.q, P.s, out, N, K, g)
+    ref = oracle.w2t_dequant(w["codes"], w["scales"], N, K, g)
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+
+
+# -------------------------------------------------------- GEMV, whole output ---
+
+GEMV_CASES = [
+    # (M, N, K, group, x dtype)
+    (1, 8, 128, 128, "f16"),
+    (1, 24, 96, 32, "f16"),
+    (3, 40, 384, 64, "bf16"),
+    (1, 136, 1152, 128, "f16"),
+    (2, 136, 1152, 128, "bf16"),
+    (4, 264, 2176, 128, "f16"),
+    (5, 264, 2176, 64, "bf16"),
+    (8, 520, 4096, 128, "f16"),
+    (6, 1032, 1536, 256, "bf16"),
+    (16, 264, 896, 32, "f16"),
+    (7, 4104, 640, 64, "f16"),
+    (1, 4096, 4096, 128, "f16"),
+    (4, 5120, 5120, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,g,xdt", GEMV_CASES)
+def test_w4_gemv_matches_oracle(M, N, K, g, xdt):
+    say(f"w4 gemv M={M} N={N} K={K} g={g} x={xdt}")
+    key = (105, M, N, K, g)
+    w = synth.gen_w4(key, N, K, g)
+    x = synth.gen_x(key, M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    P = PackedW4(w, N, K, g)
+    xd = dev(x)
+    y = P.gemv(xd, xdt, M, "f32")
+    torch.cuda.synchronize()
+    say("  variant: " + L.w4a16_last_variant())
+    ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g)
+    assert_parity(to_f64(y), ref, f"M={M} N={N} K={K} g={g} {xdt}")
+    # fp16 and bf16 outputs: the same result rounded once more.
+    y16 = P.gemv(xd, xdt, M, "f16")
+    assert_parity(to_f64(y16), ref, "f16 out", extra_rel=2.0 ** -11)
+    yb = P.gemv(xd, xdt, M, "bf16")
+    assert_parity(to_f64(yb), ref, "bf16 out", extra_rel=2.0 ** -8)
+
+
+W2_GEMV_CASES = [
+    (1, 7, 32, 32, "f16"),
+    (4, 40, 768, 128, "f16"),
+    (8, 136, 1280, 64, "bf16"),
+    (3, 264, 2304, 256, "f16"),
+    (16, 520, 512, 32, "bf16"),
+    (1, 7168, 5120, 128, "f16"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,g,xdt", W2_GEMV_CASES)
+def test_w2t_gemv_matches_oracle(M, N, K, g, xdt):
+    say(f"w2t gemv M={M} N={N} K={K} g={g} x={xdt}")
+    key = (106, M, N, K, g)
+    w = synth.gen_w2t(key, N, K, g)
+    x = synth.gen_x(key, M, K, xdt)
+    P = PackedW2T(w, N, K, g)
+    y = P.gemv(dev(x), xdt, M)
+    torch.cuda.synchronize()
+    say("  variant: " + L.w4a16_last_variant())
+    ref = oracle.w2t_gemv(x, xdt, w["codes"], w["scales"], M, N, K, g)
+    assert_parity(to_f64(y), ref, f"w2t M={M} N={N} K={K}")
+
+
+# ----------------------------------------------------------- bitwise identities ---
+
+def test_w4_zero_point_identity_gives_exact_zero():
+    say("w4 q = z identity")
+    M, N, K, g = 4, 264, 1024, 128
+    rng = np.random.default_rng(7)
+    G = K // g
+    z = rng.integers(0, 16, size=(G, N))
+    q = np.repeat(z, g, axis=0)  # [K][N]
+    qweight = np.zeros((N, K // 8), dtype=np.uint32)
+    for i in range(8):
+        qweight |= (q[i::8].T.astype(np.uint32) << np.uint32(4 * i))
+    zeros = np.zeros((G, N // 8), dtype=np.uint32)
+    for i in range(8):
+        zeros |= (z[:, i::8].astype(np.uint32) << np.uint32(4 * i))
+    w = {"qweight": qweight.view(np.int32), "zeros": zeros.view(np.int32),
+         "scales": synth.f64_to_f16_bits(rng.uniform(0.002, 0.02, size=(G, N)))}
+    assert np.all(oracle.w4_gemv(synth.gen_x((1,), M, K), "f16", w["qweight"], w["scales"],
+                                 w["zeros"], M, N, K, g) == 0)
+    P = PackedW4(w, N, K, g)
+    for xdt in ("f16", "bf16"):
+        y = P.gemv(dev(synth.gen_x((1,), M, K, xdt)), xdt, M)
+        assert torch.count_nonzero(y).item() == 0
+
+
+def test_w4_scale_doubling_is_bitwise():
+    say("w4 s -> 2s")
+    M, N, K, g = 4, 520, 2048, 128
+    w = synth.gen_w4((107,), N, K, g)
+    w2 = dict(w, scales=(w["scales"].view(np.float16) * np.float16(2)).view(np.uint16))
+    x = dev(synth.gen_x((107,), M, K))
+    y1 = PackedW4(w, N, K, g).gemv(x, "f16", M)
+    y2 = PackedW4(w2, N, K, g).gemv(x, "f16", M)
+    assert torch.equal(y2, 2 * y1)
+
+
+def test_w4_one_hot_rows_are_exact():
+    say("w4 one-hot rows")
+    N, K, g = 136, 512, 64
+    w = synth.gen_w4((108,), N, K, g)
+    P = PackedW4(w, N, K, g)
+    Wref = oracle.w4_dequant(w["qweight"], w["scales"], w["zeros"], N, K, g)
+    ks = [0, 1, 7, 8, 31, 32, 63, 64, 65, 127, 128, 200, 255, 256, 383, 448, 511]
+    for start in range(0, len(ks), 16):
+        chunk = ks[start:start + 16]
+        x = np.zeros((len(chunk), K), dtype=np.uint16)
+        for r, k in enumerate(chunk):
+            x[r, k] = 0x3C00
+        y = to_f64(P.gemv(dev(x), "f16", len(chunk)))
+        for r, k in enumerate(chunk):
+            assert np.array_equal(y[r], Wref[k]), f"k={k}"
+
+
+def test_w2t_all_ones_counts_exact():
+    say("w2t +-1 counts")
+    N, K, g = 264, 2048, 128
+    w = synth.gen_w2t((109,), N, K, g)
+    w["scales"] = np.full_like(w["scales"], 0x3C00)
+    P = PackedW2T(w, N, K, g)
+    x = np.full((1, K), 0x3C00, dtype=np.uint16)
+    y = to_f64(P.gemv(dev(x), "f16", 1))
+    codes = w["codes"].view(np.uint32)
+    c = np.stack([(codes >> np.uint32(2 * i)) & 3 for i in range(16)], axis=-1).reshape(N, K)
+    expect = (c == 2).sum(axis=1) - (c == 0).sum(axis=1)
+    assert np.array_equal(y[0], expect.astype(np.float64))
+
+
+# ------------------------------------------------------- determinism and graphs ---
+
+def test_repeat_calls_and_graph_replay_are_bitwise_identical():
+    say("determinism + graph replay")
+    M, N, K, g = 4, 5120, 17408, 128
+    w = synth.gen_w4((110,), N, K, g)
+    P = PackedW4(w, N, K, g)
+    x = dev(synth.gen_x((110,), M, K, "bf16", outlier_frac=0.01))
+    y0 = P.gemv(x, "bf16", M).clone()
+    for _ in range(20):
+        assert torch.equal(P.gemv(x, "bf16", M), y0)
+    y = torch.empty_like(y0)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        L.w4a16_gemv(x, "bf16", P.q, P.s, P.z, y, "f32", M, N, K, g, stream=s)  # warm up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        L.w4a16_gemv(x, "bf16", P.q, P.s, P.z, y, "f32", M, N, K, g, stream=s)
+    for r in range(5):
+        y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0), f"replay {r}"
+        assert torch.equal(P.gemv(x, "bf16", M), y0)   # eager work between replays
+
+
+def test_split_k_narrow_shard_parity_and_poisoned_workspace():
+    # One GPU's column share of down (N = 5120/8 = 640) splits K across
+    # workgroups and merges fp32 partials from the workspace.
+    M, N, K, g = 4, 640, 17408, 128
+    say(f"split-K M={M} N={N} K={K}")
+    ws = L.w4a16_workspace_bytes(M, N, K, g)
+    assert ws > 0
+    w = synth.gen_w4((111,), N, K, g)
+    x = synth.gen_x((111,), M, K, "bf16", outlier_frac=0.01)
+    P = PackedW4(w, N, K, g)
+    work = empty_bytes(ws)
+    work.view(torch.float32)[:] = float("nan")
+    y = P.gemv(dev(x), "bf16", M, workspace=work)
+    torch.cuda.synchronize()
+    variant = L.w4a16_last_variant()
+    say("  variant: " + variant)
+    assert "split=1 " not in variant
+    ref = oracle.w4_gemv(x, "bf16", w["qweight"], w["scales"], w["zeros"], M, N, K, g)
+    assert_parity(to_f64(y), ref, "split-K")
+    work.view(torch.float32)[:] = float("inf")
+    assert torch.equal(P.gemv(dev(x), "bf16", M, workspace=work), y)
+
+
+# ----------------------------------------------- full 27B-class shapes, sampled ---
+
+FULL = [("qkv", 5120, 7168), ("o_proj", 5120, 5120), ("gate_up", 5120, 34816),
+        ("down", 17408, 5120), ("lm_head", 5120, 152064)]
+
+
+def sample_cols(N, rng, n=192):
+    cols = set(rng.choice(N, size=min(n, N), replace=False).tolist())
+    cols |= {0, 15, 16, N // 2, N - 17, N - 16, N - 1}
+    return np.array(sorted(cols), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name,K,N", FULL)
+@pytest.mark.parametrize("M,xdt", [(1, "f16"), (4, "bf16"), (8, "f16")])
+def test_full_size_sampled_columns(name, K, N, M, xdt):
+    say(f"full {name} K={K} N={N} M={M} x={xdt}")
+    g = 128
+    key = (112, K, N, M)
+    w = synth.gen_w4(key, N, K, g)
+    x = synth.gen_x(key, M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    P = PackedW4(w, N, K, g)
+    y = to_f64(P.gemv(dev(x), xdt, M))
+    cols = sample_cols(N, np.random.default_rng(N + M))
+    ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g, cols=cols)
+    assert_parity(y[:, cols], ref, name)
+
+
+@pytest.mark.parametrize("K,N", [(5120, 7168), (5120, 34816), (17408, 5120)])
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_w2t_full_size_sampled_columns(K, N, M):
+    say(f"w2t full K={K} N={N} M={M}")
+    g = 128
+    key = (113, K, N, M)
+    w = synth.gen_w2t(key, N, K, g)
+    x = synth.gen_x(key, M, K, "f16")
+    P = PackedW2T(w, N, K, g)
+    y = to_f64(P.gemv(dev(x), "f16", M))
+    cols = sample_cols(N, np.random.default_rng(N + M))
+    ref = oracle.w2t_gemv(x, "f16", w["codes"], w["scales"], M, N, K, g, cols=cols)
+    assert_parity(y[:, cols], ref, "w2t full")
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 6, 8])
+@pytest.mark.parametrize("g", [64, 128])
+@pytest.mark.parametrize("KN", [4096, 5120, 8192])
+def test_skinny_sweep_sampled(M, g, KN):
+    say(f"sweep M={M} g={g} K=N={KN}")
+    key = (114, M, g, KN)
+    w = synth.gen_w4(key, KN, KN, g)
+    x = synth.gen_x(key, M, KN, "f16")
+    P = PackedW4(w, KN, KN, g)
+    y = to_f64(P.gemv(dev(x), "f16", M))
+    cols = sample_cols(KN, np.random.default_rng(KN + M + g), n=96)
+    ref = oracle.w4_gemv(x, "f16", w["qweight"], w["scales"], w["zeros"], M, KN, KN, g, cols=cols)
+    assert_parity(y[:, cols], ref, "sweep")
+
+
+def test_gpu_rejects_bad_arguments_without_launching():
+    good = empty_bytes(1 << 16)
+    with pytest.raises(L.W4A16Error) as e:
+        L.w4a16_gemv(good, "f16", good, good, good, good, "f32", 0, 16, 128, 128)
+    assert e.value.status == -2
+    with pytest.raises(L.W4A16Error) as e:
+        L.w4a16_gemv(good.data_ptr() + 2, "f16", good, good, good, good, "f32", 1, 16, 128, 128)
+    assert e.value.status == -3
