@@ -109,11 +109,20 @@ inline int check_w2_shape(int N, int K, int group) {
     return W4A16_OK;
 }
 
+void set_last_variant(const char* fmt, ...);
+void set_last_error(const char* what);
+
+// Launch checking.  begin_launches() clears an error another component may
+// have left in HIP's per-thread "last error" slot (it belongs to an earlier
+// call, not to this one); launch_status() then reports only what the launches
+// of this call raised, and records the HIP error name for w4a16_last_error().
+inline void begin_launches() { (void)hipGetLastError(); }
+
 inline int launch_status() {
     hipError_t e = hipGetLastError();
-    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+    if (e == hipSuccess) return W4A16_OK;
+    set_last_error(hipGetErrorName(e));
+    return W4A16_ERR_HIP;
 }
-
-void set_last_variant(const char* fmt, ...);
 
 }  // namespace w4h

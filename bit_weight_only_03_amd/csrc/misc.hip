@@ -13,6 +13,7 @@ constexpr int kProbeBlocks = 4096;
 constexpr int kProbeThreads = 256;
 
 thread_local char g_last_variant[160] = "none";
+thread_local char g_last_error[96] = "none";
 
 // Streams `n16` 16-byte words with non-temporal loads, grid-stride, eight
 // loads in flight per thread, and folds them with XOR so nothing is elided.
@@ -51,9 +52,12 @@ void set_last_variant(const char* fmt, ...) {
     vsnprintf(g_last_variant, sizeof g_last_variant, fmt, ap);
     va_end(ap);
 }
+void set_last_error(const char* what) { snprintf(g_last_error, sizeof g_last_error, "%s", what); }
 }  // namespace w4h
 
 extern "C" const char* w4a16_last_variant(void) { return g_last_variant; }
+
+extern "C" const char* w4a16_last_error(void) { return g_last_error; }
 
 extern "C" const char* w4a16_status_string(int status) {
     switch (status) {
@@ -75,6 +79,7 @@ extern "C" int w4a16_bw_probe(const void* buf, size_t bytes, float* sink, w4a16_
     if (!buf || !sink) return W4A16_ERR_NULL;
     if (bytes == 0 || bytes % 16) return W4A16_ERR_SHAPE;
     if (!w4h::aligned16(buf) || !w4h::aligned16(sink)) return W4A16_ERR_ALIGN;
+    w4h::begin_launches();
     hipLaunchKernelGGL(bw_probe_kernel, dim3(kProbeBlocks), dim3(kProbeThreads), 0,
                        (hipStream_t)stream, (const u32x4_t*)buf, bytes / 16, sink);
     w4h::set_last_variant("bw_probe blocks=%d threads=%d", kProbeBlocks, kProbeThreads);

@@ -360,6 +360,7 @@ extern "C" int w2t_pack(const int32_t* codes_canon, const uint16_t* scales_canon
         return W4A16_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
     const size_t qd = (size_t)pad_n(N) * pad_k2(K) / 16;
+    w4h::begin_launches();
     hipLaunchKernelGGL(w2_pack_q_kernel, dim3(grid_for(qd, 256)), dim3(256), 0, s,
                        (const uint32_t*)codes_canon, (uint32_t*)qweight, N, K, qd);
     const size_t sd = (size_t)pad_n(N) * (pad_k2(K) / group);
@@ -378,6 +379,7 @@ extern "C" int w2t_unpack(const void* qweight, const void* scales, int32_t* code
         return W4A16_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
     const size_t qc = (size_t)N * (K / 16);
+    w4h::begin_launches();
     hipLaunchKernelGGL(w2_unpack_q_kernel, dim3(grid_for(qc, 256)), dim3(256), 0, s,
                        (const uint32_t*)qweight, (uint32_t*)codes_canon, N, K);
     const size_t sc = (size_t)N * (K / group);
@@ -394,6 +396,7 @@ extern "C" int w2t_dequant(const void* qweight, const void* scales, float* w, in
     if (!w4h::aligned16(qweight) || !w4h::aligned16(scales) || !w4h::aligned16(w))
         return W4A16_ERR_ALIGN;
     const size_t total = (size_t)K * N;
+    w4h::begin_launches();
     hipLaunchKernelGGL(w2_dequant_kernel, dim3(grid_for(total, 256)), dim3(256), 0,
                        (hipStream_t)stream, (const uint32_t*)qweight, (const uint16_t*)scales, w, N,
                        K, group);
@@ -436,6 +439,7 @@ extern "C" int w2t_gemv(const void* x, int x_dtype, const void* qweight, const v
     w2_kernel_t k = bf16 ? pick2<true>(group) : pick2<false>(group);
     void* out = p.split > 1 ? workspace : y;
     const int odt = p.split > 1 ? W4A16_F32 : y_dtype;
+    w4h::begin_launches();
     hipLaunchKernelGGL(k, dim3(T, p.split), dim3(64 * p.waves), 0, st, (const uint16_t*)x,
                        (const u32x4_t*)qweight, (const uint16_t*)scales, out, odt, M, N, K, p.split);
     if (p.split > 1) {

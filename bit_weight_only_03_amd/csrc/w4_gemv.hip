@@ -363,6 +363,7 @@ extern "C" int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const
     w4_kernel_t k = pick_kernel(bf16, group, p.depth);
     void* out = p.split > 1 ? workspace : y;
     const int odt = p.split > 1 ? W4A16_F32 : y_dtype;
+    w4h::begin_launches();
     hipLaunchKernelGGL(k, dim3(T, p.split), dim3(64 * p.waves), 0, st, (const uint16_t*)x,
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros,
                        out, odt, M, N, K, p.split);

@@ -151,6 +151,7 @@ extern "C" int w4a16_pack(const int32_t* qweight_canon, const uint16_t* scales_c
         return W4A16_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
     const size_t qd = (size_t)pad_n(N) * pad_k(K) / 8;
+    w4h::begin_launches();
     hipLaunchKernelGGL(w4_pack_q_kernel, dim3(grid_for(qd, 256)), dim3(256), 0, s,
                        (const uint32_t*)qweight_canon, (uint32_t*)qweight, N, K, qd);
     const size_t sd = (size_t)pad_n(N) * (pad_k(K) / group);
@@ -173,6 +174,7 @@ extern "C" int w4a16_unpack(const void* qweight, const void* scales, const void*
         return W4A16_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
     const size_t qc = (size_t)N * (K / 8);
+    w4h::begin_launches();
     hipLaunchKernelGGL(w4_unpack_q_kernel, dim3(grid_for(qc, 256)), dim3(256), 0, s,
                        (const uint32_t*)qweight, (uint32_t*)qweight_canon, N, K);
     const size_t sc = (size_t)N * (K / group);
@@ -191,6 +193,7 @@ extern "C" int w4a16_dequant(const void* qweight, const void* scales, const void
         !w4h::aligned16(w))
         return W4A16_ERR_ALIGN;
     const size_t total = (size_t)K * N;
+    w4h::begin_launches();
     hipLaunchKernelGGL(w4_dequant_kernel, dim3(grid_for(total, 256)), dim3(256), 0,
                        (hipStream_t)stream, (const uint32_t*)qweight, (const uint16_t*)scales,
                        (const uint32_t*)zeros, w, N, K, group);

@@ -156,6 +156,10 @@ const char* w4a16_status_string(int status);
  * Host string owned by the library, valid until the next call on the thread. */
 const char* w4a16_last_variant(void);
 
+/* HIP error name behind the most recent W4A16_ERR_HIP on this host thread
+ * ("none" if there was none).  Static host string. */
+const char* w4a16_last_error(void);
+
 #ifdef __cplusplus
 }
 #endif
