@@ -84,6 +84,9 @@ class Sweep:
                                              outlier_frac=0.01 if outliers else 0.0))
             self.ys.append(torch.empty((M, N), dtype=torch.float32, device="cuda"))
         self.bytes = sum(alg_bytes(M, N, K, GROUP) for (_, _, K, N, _) in self.mats_meta)
+        # One workspace serves every call: calls on one stream run one after another.
+        self.ws_bytes = max(L.w4a16_workspace_bytes(M, N, K, GROUP) for (_, _, K, N, _) in self.mats)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda") if self.ws_bytes else None
 
     @property
     def mats_meta(self):
@@ -110,7 +113,7 @@ class Sweep:
     def launch(self, i, stream):
         layer, name, K, N, (q, s, z) = self.mats[i]
         self.L.w4a16_gemv(self.xs[i], self.x_dtype, q, s, z, self.ys[i], "f32", self.M, N, K,
-                          GROUP, None, 0, stream)
+                          GROUP, self.ws, self.ws_bytes, stream)
 
     def run_all(self, stream):
         for i in range(len(self.mats)):
@@ -196,11 +199,12 @@ def parity_guard(L, torch, synth, oracle_mod, sweep):
     return worst
 
 
-def cpu_baseline(torch, synth, oracle_mod, budget_s=20.0):
-    """The fp64 oracle on the host cores, on a bounded sample: full layers of
-    the sweep (4 matrices, M = 1) until about budget_s seconds have passed."""
+def cpu_baseline(torch, synth, oracle_mod, budget_s=12.0):
+    """The fp64 oracle on the host cores, on a bounded sample: whole layers of
+    the sweep (4 matrices, M = 1) until about budget_s seconds of oracle time
+    have passed."""
     t_total, nbytes, layers = 0.0, 0, 0
-    while t_total < budget_s and layers < 4:
+    while t_total < budget_s and layers < N_LAYERS:
         for mi, (name, K, N) in enumerate(SHAPES):
             w = synth.gen_w4_torch((1, layers, mi), N, K, GROUP)
             wq = w["qweight"].cpu().numpy()
@@ -212,7 +216,8 @@ def cpu_baseline(torch, synth, oracle_mod, budget_s=20.0):
             t_total += time.perf_counter() - t0
             nbytes += alg_bytes(1, N, K, GROUP)
         layers += 1
-        log(f"cpu oracle: {layers} layer(s), {t_total:.1f} s")
+        if layers % 4 == 0:
+            log(f"cpu oracle: {layers} layer(s), {t_total:.1f} s")
     return {"value": round(gbps(nbytes, t_total), 4), "unit": "GB/s",
             "cores": oracle_mod.num_threads(), "kind": "oracle",
             "sample": f"{layers} full decoder layer(s) of the M=1 sweep (qkv, o_proj, gate_up, "

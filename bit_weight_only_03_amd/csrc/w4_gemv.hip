@@ -50,7 +50,7 @@ using namespace w4k;
 
 namespace {
 
-constexpr int kMaxWaves = 8;     // waves per workgroup (launch bound 512 threads)
+constexpr int kMaxWaves = 16;    // waves per workgroup
 constexpr int kMaxRows = 16;     // rows per MFMA
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return bitcast<half2_t>(v); }
@@ -97,134 +97,201 @@ struct Slot {
     uint32_t z[NG];
 };
 
-// Steps (32-k slices) per group SPG = group / 32; NG = groups touched per unit.
-template <bool BF16, int SPG, int D>
+// Launch description shared by host and kernel.
+struct GemvLaunch {
+    int M, N, K;
+    int U;        // 128-k units per column (K rounded up)
+    int S;        // K slices: workgroups (t, s) cover units [s*U/S, (s+1)*U/S) of tile t
+    int xstride;  // LDS row stride of a wave's staged x, in halves
+    int out_dtype;
+};
+
+// Slots of the register ring for UPW units per wave: all loads are issued
+// up front when they fit, otherwise the first D and a refill per consumed
+// slot (the ring never holds more than the VGPR budget allows).
+template <int SPG>
+constexpr int max_slots() { return SPG >= 4 ? 9 : (SPG == 2 ? 7 : 5); }
+
+// One workgroup per (16-column tile, K slice); its W waves split the slice's
+// 128-k units into contiguous ranges of at most UPW units.  Each wave
+//   1. stages its own range of x (all M rows, zeros past K) in its own LDS
+//      region -- no other wave's x is on its critical path;
+//   2. issues the loads of its units (16 weight bytes, scale and zero point
+//      per lane) -- all of them up front when UPW fits the register ring,
+//      otherwise with one refill per consumed slot on a fixed schedule, so
+//      the code is straight-line and every wait covers exactly one slot;
+//   3. dequantizes and multiplies each unit as its slot arrives;
+// then the waves add their partial sums through LDS in wave order and the
+// workgroup stores the tile (or its fp32 slice partial).
+//
+// A wave whose range is shorter than UPW gives its missing units an offset
+// past the buffer resource's size: such loads return zeros without touching
+// memory, and the units are skipped.
+template <bool BF16, int SPG, int UPW>
 __global__ __launch_bounds__(512) void w4_gemv_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ qdev,
     const uint16_t* __restrict__ sdev, const uint32_t* __restrict__ zdev, void* __restrict__ out,
-    int out_dtype, int M, int N, int K, int S) {
-    static_assert(D % 2 == 0, "x double buffer alternates with the ring index");
+    GemvLaunch a) {
     constexpr int NG = SPG >= 4 ? 1 : 4 / SPG;          // groups per unit
     constexpr int SPU = SPG >= 4 ? 4 : SPG;             // steps per group inside one unit
-    __shared__ float red[kMaxWaves][kMaxRows][kTileN];
+    constexpr int D = UPW < max_slots<SPG>() ? UPW : max_slots<SPG>();
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+    const int M = a.M, K = a.K, U = a.U;
+    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int t = blockIdx.x, split = blockIdx.y;
-    const int U = (K + kUnitK - 1) / kUnitK;
+    const int r0 = split * U / a.S, r1 = (split + 1) * U / a.S;
+    const int w0 = r0 + wave * (r1 - r0) / W, w1 = r0 + (wave + 1) * (r1 - r0) / W;
+    const int nu = w1 - w0;                                           // units of this wave
     const int Gp = U * kUnitK / (SPG * 32);
-    const int su0 = (int)((long long)split * U / S);
-    const int su1 = (int)((long long)(split + 1) * U / S);
-    const int u0 = su0 + wave * (su1 - su0) / nw;
-    const int u1 = su0 + (wave + 1) * (su1 - su0) / nw;
     const int c = lane & 15, kc = lane >> 4;
-    // Per-workgroup buffer resources.  The weights, scales and zero points of
-    // tile t are contiguous; x is addressed as a whole so that the padded k
-    // tail reads either the next row (finite values times weights that are
-    // exactly 0) or, past the end of x, zeros from the range check.
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qdev + (size_t)t * U * kLanes, (uint32_t)U * 1024u);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdev + (size_t)t * Gp * kTileN, (uint32_t)Gp * 32u);
-    const __amdgpu_buffer_rsrc_t rz = make_rsrc(zdev + (size_t)t * Gp * 2, (uint32_t)Gp * 8u);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
-    const uint32_t wlane = (uint32_t)lane * 16u;
-    const uint32_t slane = (uint32_t)c * 2u;
-    const uint32_t zlane = (uint32_t)(c >> 3) * 4u;
-    // Lane l supplies x row l % 16 to the A operand.  Rows >= M only feed
-    // output rows that are never stored, so those lanes re-read row M - 1.
-    const int xm = c < M ? c : M - 1;
-    const uint32_t xlane = ((uint32_t)xm * (uint32_t)K + 8u * (uint32_t)kc) * 2u;
-    const int zshift = 4 * (c & 7);
-    const uint32_t magic = BF16 ? 0x43004300u : 0x64006400u;   // 128.0 / 1024.0 pairs
 
-    auto load_slot = [&](int u, Slot<NG>& r) {
-        r.w = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rw, wlane, u * 1024, kAuxNT));
+    // LDS: wave w's x range [M][xstride] halves at w * M * xstride, then the
+    // reduction buffer [W][M][16] floats.
+    uint16_t* xs = (uint16_t*)smem + (size_t)wave * M * a.xstride;
+    float* red = (float*)(smem + (size_t)W * M * a.xstride * 2);
+
+    // 1) x range -> LDS.  At most 16 chunks of 16 bytes per lane (the planner
+    //    keeps M * UPW <= 64); the loads go first so the wait for them never
+    //    waits on weight loads.
+    {
+        const int cpr = nu * (kUnitK / 8);   // 16-byte chunks per row
+        const int xch = M * cpr;
+        const uint32_t xbytes = (uint32_t)M * (uint32_t)K * 2u;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xbytes);
+        u32x4_t xv[16];
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-            const int g = (u * 4) / SPG + gi;
-            r.s[gi] = __builtin_amdgcn_raw_buffer_load_b16(rs, slane, g * 32, 0);
-            r.z[gi] = __builtin_amdgcn_raw_buffer_load_b32(rz, zlane, g * 8, 0);
+        for (int i = 0; i < 16; ++i) {
+            if (i * 64 < xch) {              // wave-uniform; a real branch, not 16 dummy loads
+                asm volatile("" ::: "memory");
+                const int ci = i * 64 + lane;
+                const int m = ci / cpr, kk = (ci % cpr) * 8;
+                const int kg = w0 * kUnitK + kk;
+                const uint32_t off = (ci < xch && kg < K) ? (uint32_t)(m * K + kg) * 2u : xbytes;
+                xv[i] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+            }
         }
-    };
-    auto load_x = [&](int u, u32x4_t (&xa)[4]) {
-        const uint32_t off = xlane + (uint32_t)u * (kUnitK * 2);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            xa[j] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rx, off + 64u * j, 0, 0));
-    };
-
-    float4_t total = {0.f, 0.f, 0.f, 0.f};
-    Slot<NG> ring[D];
-    u32x4_t xb[2][4];
-#pragma unroll
-    for (int i = 0; i < D; ++i)
-        if (u0 + i < u1) load_slot(u0 + i, ring[i]);
-    if (u0 < u1) load_x(u0, xb[0]);
-
-    for (int ub = u0; ub < u1; ub += D) {
-#pragma unroll
-        for (int i = 0; i < D; ++i) {
-            const int u = ub + i;
-            if (u < u1) {
-                u32x4_t (&xcur)[4] = xb[i & 1];
-                if (u + 1 < u1) load_x(u + 1, xb[(i + 1) & 1]);
-                Slot<NG>& sl = ring[i];
-#pragma unroll
-                for (int gi = 0; gi < NG; ++gi) {
-                    const uint32_t zq = (sl.z[gi] >> zshift) & 15u;
-                    float4_t acc = {0.f, 0.f, 0.f, 0.f};
-                    if constexpr (!BF16) {
-                        uint32_t nz1024 = 0xE400u + zq;          // fp16 -(1024 + z)
-                        nz1024 |= nz1024 << 16;
-                        uint32_t nz64 = 0xD400u + (zq << 4);     // fp16 -(64 + z)
-                        nz64 |= nz64 << 16;
-#pragma unroll
-                        for (int js = 0; js < SPU; ++js) {
-                            const int j = gi * SPU + js;
-                            const half8_t b = dequant_f16(sl.w[j], magic, nz1024, nz64);
-                            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                bitcast<half8_t>(xcur[j]), b, acc, 0, 0, 0);
-                        }
-                    } else {
-                        uint32_t nb = 0xC300u + zq;              // bf16 -(128 + z)
-                        nb |= nb << 16;
-                        const bf16x8_t bias = bitcast<bf16x8_t>(u32x4_t{nb, nb, nb, nb});
-#pragma unroll
-                        for (int js = 0; js < SPU; ++js) {
-                            const int j = gi * SPU + js;
-                            const bf16x8_t a = bitcast<bf16x8_t>(xcur[j]);
-                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                a, biased_bf16(sl.w[j], magic), acc, 0, 0, 0);
-                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bias, acc, 0, 0, 0);
-                        }
-                    }
-                    const float sf = f16_bits_to_f32((uint16_t)sl.s[gi]);
-                    total[0] = __builtin_fmaf(sf, acc[0], total[0]);
-                    total[1] = __builtin_fmaf(sf, acc[1], total[1]);
-                    total[2] = __builtin_fmaf(sf, acc[2], total[2]);
-                    total[3] = __builtin_fmaf(sf, acc[3], total[3]);
-                }
-                // Refill the slot just consumed with the unit D ahead.
-                if (u + D < u1) load_slot(u + D, sl);
+        for (int i = 0; i < 16; ++i) {
+            const int ci = i * 64 + lane;
+            if (i * 64 < xch && ci < xch) {
+                const int m = ci / cpr, kk = (ci % cpr) * 8;
+                *(u32x4_t*)(xs + m * a.xstride + kk) = xv[i];
             }
         }
     }
+    // Weight loads must not be hoisted above the x stores (loads return in
+    // issue order, so the stores would then wait for the weights as well).
+    __builtin_amdgcn_sched_barrier(0);
 
-    // Lane l holds rows 4*(l/16) + r of column l % 16.
-    const int rb = 4 * kc;
+    // 2) Weight / scale / zero-point loads of this wave's units.
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qdev + (size_t)t * U * kLanes, (uint32_t)U * 1024u);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdev + (size_t)t * Gp * kTileN, (uint32_t)Gp * 32u);
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(zdev + (size_t)t * Gp * 2, (uint32_t)Gp * 8u);
+    const uint32_t wlane = (uint32_t)lane * 16u;
+    const uint32_t slane = (uint32_t)c * 2u;
+    const uint32_t zlane = (uint32_t)(c >> 3) * 4u;
+    const uint32_t wend = (uint32_t)U * 1024u, send = (uint32_t)Gp * 32u, zend = (uint32_t)Gp * 8u;
+
+    auto load_slot = [&](int i, Slot<NG>& r) {   // unit w0 + i
+        const bool valid = i < nu;
+        const int u = w0 + i;
+        r.w = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
+            rw, valid ? wlane + (uint32_t)u * 1024u : wend, 0, kAuxNT));
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-        if (rb + r < M) red[wave][rb + r][c] = total[r];
+        for (int gi = 0; gi < NG; ++gi) {
+            const int g = (u * 4) / SPG + gi;
+            r.s[gi] = __builtin_amdgcn_raw_buffer_load_b16(rs, valid ? slane + (uint32_t)g * 32u : send, 0, 0);
+            r.z[gi] = __builtin_amdgcn_raw_buffer_load_b32(rz, valid ? zlane + (uint32_t)g * 8u : zend, 0, 0);
+        }
+    };
+
+    Slot<NG> ring[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        load_slot(i, ring[i]);
+        __builtin_amdgcn_sched_barrier(0);   // slots issue in ring order
+    }
+
+    // 3) Dequantize and multiply, unit by unit.
+    const int zshift = 4 * (c & 7);
+    const uint32_t magic = BF16 ? 0x43004300u : 0x64006400u;   // 128.0 / 1024.0 pairs
+    const bool xrow = c < M;                                    // lane supplies x row c
+    const uint8_t* xlane = (const uint8_t*)xs + (uint32_t)(c * a.xstride + 8 * kc) * 2u;
+    float4_t total = {0.f, 0.f, 0.f, 0.f};
+    u32x4_t xa[4] = {};
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+        Slot<NG>& sl = ring[i % D];
+        if (i < nu) {
+            if (xrow) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xa[j] = *(const u32x4_t*)(xlane + (uint32_t)i * (kUnitK * 2) + 64 * j);
+            }
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const uint32_t zq = (sl.z[gi] >> zshift) & 15u;
+                float4_t acc = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (!BF16) {
+                    uint32_t nz1024 = 0xE400u + zq;          // fp16 -(1024 + z)
+                    nz1024 |= nz1024 << 16;
+                    uint32_t nz64 = 0xD400u + (zq << 4);     // fp16 -(64 + z)
+                    nz64 |= nz64 << 16;
+#pragma unroll
+                    for (int js = 0; js < SPU; ++js) {
+                        const int j = gi * SPU + js;
+                        const half8_t b = dequant_f16(sl.w[j], magic, nz1024, nz64);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(xa[j]), b, acc,
+                                                                     0, 0, 0);
+                    }
+                } else {
+                    uint32_t nb = 0xC300u + zq;              // bf16 -(128 + z)
+                    nb |= nb << 16;
+                    const bf16x8_t bias = bitcast<bf16x8_t>(u32x4_t{nb, nb, nb, nb});
+#pragma unroll
+                    for (int js = 0; js < SPU; ++js) {
+                        const int j = gi * SPU + js;
+                        const bf16x8_t av = bitcast<bf16x8_t>(xa[j]);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, biased_bf16(sl.w[j], magic),
+                                                                      acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bias, acc, 0, 0, 0);
+                    }
+                }
+                const float sf = f16_bits_to_f32((uint16_t)sl.s[gi]);
+                total[0] = __builtin_fmaf(sf, acc[0], total[0]);
+                total[1] = __builtin_fmaf(sf, acc[1], total[1]);
+                total[2] = __builtin_fmaf(sf, acc[2], total[2]);
+                total[3] = __builtin_fmaf(sf, acc[3], total[3]);
+            }
+        }
+        if (i + D < UPW) {                 // fixed refill schedule: unit i + D into this slot
+            __builtin_amdgcn_sched_barrier(0);
+            load_slot(i + D, sl);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // units in order: each waits for its own slot only
+    }
+
+    // 4) Wave partials (lane l holds rows 4*(l/16) + r of column l % 16) ->
+    //    LDS, then M x 16 threads add them in wave order and store.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kc + r;
+        if (m < M) red[(wave * M + m) * kTileN + c] = total[r];
+    }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < M * kTileN; idx += blockDim.x) {
-        const int mm = idx >> 4, cc = idx & 15;
+    if ((int)threadIdx.x < M * kTileN) {
+        const int m = threadIdx.x >> 4, cc = threadIdx.x & 15;
         float v = 0.f;
-        for (int w = 0; w < nw; ++w) v += red[w][mm][cc];
+        for (int w = 0; w < W; ++w) v += red[(w * M + m) * kTileN + cc];
         const int n = t * kTileN + cc;
-        if (n < N) {
-            const size_t o = (size_t)split * M * N + (size_t)mm * N + n;
-            if (out_dtype == W4A16_F32)
+        if (n < a.N) {
+            const size_t o = (size_t)split * M * a.N + (size_t)m * a.N + n;
+            if (a.out_dtype == W4A16_F32)
                 ((float*)out)[o] = v;
-            else if (out_dtype == W4A16_F16)
+            else if (a.out_dtype == W4A16_F16)
                 ((_Float16*)out)[o] = (_Float16)v;
             else
                 ((uint16_t*)out)[o] = f32_to_bf16_bits(v);
@@ -249,14 +316,8 @@ __global__ void splitk_merge_kernel(const float* __restrict__ ws, void* __restri
 
 // ------------------------------------------------------------------ dispatch
 
-struct Plan {
-    int waves;   // waves per workgroup
-    int split;   // K slices (grid.y)
-    int depth;   // weight ring depth
-};
-
 struct Tuning {
-    int waves = 0, split = 0, depth = 0;  // 0 = automatic
+    int waves = 0, split = 0;  // 0 = automatic
 };
 
 const Tuning& tuning() {
@@ -267,55 +328,128 @@ const Tuning& tuning() {
     std::call_once(once, [] {
         if (const char* e = getenv("W4A16_WAVES")) t.waves = atoi(e);
         if (const char* e = getenv("W4A16_SPLIT")) t.split = atoi(e);
-        if (const char* e = getenv("W4A16_DEPTH")) t.depth = atoi(e);
     });
     return t;
 }
 
-Plan make_plan(int M, int N, int K, int unit_k) {
-    (void)M;
-    const int U = (K + unit_k - 1) / unit_k;
-    const int T = pad_n(N) / kTileN;
+// Compute units of the current device (queried once; 256 on MI355X).
+int cu_count() {
+    static int n = 0;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+            prop.multiProcessorCount > 0)
+            n = prop.multiProcessorCount;
+        else
+            n = 256;
+    });
+    return n;
+}
+
+constexpr size_t kLdsPerCu = 160 * 1024;      // gfx950
+constexpr int kWaves = 8;                     // waves per workgroup (two workgroups per CU)
+constexpr int kUpwSet[] = {1, 2, 3, 4, 5, 6, 8, 9, 12, 17};   // compiled units-per-wave
+
+struct Plan {
+    GemvLaunch l;
+    int waves;
+    int upw;
+    size_t lds;
+    int tiles;
+};
+
+// Smallest compiled units-per-wave >= need (0 if none).
+int pick_upw(int need) {
+    for (int u : kUpwSet)
+        if (u >= need) return u;
+    return 0;
+}
+
+Plan make_plan(int M, int N, int K, int cus) {
     Plan p;
-    // About four units per wave, at most eight waves per workgroup.
-    p.waves = (U + 3) / 4;
-    if (p.waves > kMaxWaves) p.waves = kMaxWaves;
-    if (p.waves < 1) p.waves = 1;
-    // Split K across workgroups only when the tiles alone cannot give every
-    // CU a workgroup (narrow N: one GPU's share of a column-split layer), and
-    // keep at least two units per wave (a split with too little k per slice
-    // loses: NINFER tuning page, section 五, item 21).
-    p.split = 1;
-    if (T < 256) {
-        int s = (512 + T - 1) / T;
-        int smax = U / (2 * p.waves);
-        if (smax < 1) smax = 1;
-        p.split = s < smax ? s : smax;
-    }
-    p.depth = 8;
     const Tuning& tu = tuning();
-    if (tu.waves >= 1 && tu.waves <= kMaxWaves) p.waves = tu.waves;
-    if (tu.split >= 1 && tu.split <= U) p.split = tu.split;
-    if (tu.depth == 4 || tu.depth == 8) p.depth = tu.depth;
+    const int U = (K + kUnitK - 1) / kUnitK;
+    const int T = pad_n(N) / kTileN;
+    int W = kWaves;
+    if (tu.waves >= 1 && tu.waves <= kMaxWaves) W = tu.waves;
+    // K slices: a wave's range must fit a compiled UPW, its x range at most
+    // 16 chunks per lane (M * UPW <= 64), and the workgroup's x plus the
+    // reduction buffer the LDS of a CU.
+    auto fits = [&](int S, int& upw, size_t& lds, int& xstride) {
+        const int RU = (U + S - 1) / S;
+        const int w = W < RU ? W : RU;
+        upw = pick_upw((RU + w - 1) / w);
+        if (!upw || M * upw > 64) return false;
+        xstride = upw * kUnitK + 8;  // +16 bytes per row spreads rows over LDS banks
+        lds = (size_t)W * M * xstride * 2 + (size_t)W * M * kTileN * 4;
+        return lds <= kLdsPerCu;
+    };
+    int S = 1, upw = 0, xstride = 0;
+    size_t lds = 0;
+    while (S < U && !fits(S, upw, lds, xstride)) S *= 2;
+    // Narrow N (e.g. one GPU's column share of a layer): more slices so every
+    // CU gets a workgroup, as long as each wave keeps at least two units per
+    // slice (a split with too little k per slice loses: NINFER tuning page,
+    // section 五, item 21).
+    while ((long long)T * S < cus && U / (2 * S) >= 2 * W && fits(2 * S, upw, lds, xstride)) S *= 2;
+    if (tu.split >= 1 && tu.split <= U) S = tu.split;
+    if (!fits(S, upw, lds, xstride)) upw = 0;   // an override that cannot run is refused
+    p.l = GemvLaunch{M, N, K, U, S, xstride, W4A16_F32};
+    p.waves = W;
+    p.upw = upw;
+    p.lds = lds;
+    p.tiles = T;
     return p;
 }
 
 typedef void (*w4_kernel_t)(const uint16_t*, const u32x4_t*, const uint16_t*, const uint32_t*,
-                            void*, int, int, int, int, int);
+                            void*, GemvLaunch);
 
-template <bool BF16, int D>
-w4_kernel_t pick_spg(int group) {
-    switch (group) {
-        case 32: return w4_gemv_kernel<BF16, 1, D>;
-        case 64: return w4_gemv_kernel<BF16, 2, D>;
-        case 128: return w4_gemv_kernel<BF16, 4, D>;
-        default: return w4_gemv_kernel<BF16, 8, D>;
+template <bool BF16, int SPG>
+w4_kernel_t pick_upw_kernel(int upw) {
+    switch (upw) {
+        case 1: return w4_gemv_kernel<BF16, SPG, 1>;
+        case 2: return w4_gemv_kernel<BF16, SPG, 2>;
+        case 3: return w4_gemv_kernel<BF16, SPG, 3>;
+        case 4: return w4_gemv_kernel<BF16, SPG, 4>;
+        case 5: return w4_gemv_kernel<BF16, SPG, 5>;
+        case 6: return w4_gemv_kernel<BF16, SPG, 6>;
+        case 8: return w4_gemv_kernel<BF16, SPG, 8>;
+        case 9: return w4_gemv_kernel<BF16, SPG, 9>;
+        case 12: return w4_gemv_kernel<BF16, SPG, 12>;
+        default: return w4_gemv_kernel<BF16, SPG, 17>;
     }
 }
 
-w4_kernel_t pick_kernel(bool bf16, int group, int depth) {
-    if (bf16) return depth == 4 ? pick_spg<true, 4>(group) : pick_spg<true, 8>(group);
-    return depth == 4 ? pick_spg<false, 4>(group) : pick_spg<false, 8>(group);
+template <bool BF16>
+w4_kernel_t pick_group(int group, int upw) {
+    switch (group) {
+        case 32: return pick_upw_kernel<BF16, 1>(upw);
+        case 64: return pick_upw_kernel<BF16, 2>(upw);
+        case 128: return pick_upw_kernel<BF16, 4>(upw);
+        default: return pick_upw_kernel<BF16, 8>(upw);
+    }
+}
+
+w4_kernel_t pick_kernel(bool bf16, int group, int upw) {
+    return bf16 ? pick_group<true>(group, upw) : pick_group<false>(group, upw);
+}
+
+// Allow every GEMV kernel the whole LDS of a CU, once per process (before any
+// graph capture can be in progress for the common case of a warm-up call).
+void allow_full_lds() {
+    static std::once_flag once;
+    std::call_once(once, [] {
+        for (int bf = 0; bf < 2; ++bf)
+            for (int g : {32, 64, 128, 256})
+                for (int u : kUpwSet)
+                    (void)hipFuncSetAttribute((const void*)pick_kernel(bf, g, u),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                                              (int)kLdsPerCu);
+        (void)hipGetLastError();
+    });
 }
 
 int check_gemv_args(const void* x, int x_dtype, const void* q, const void* s, const void* z,
@@ -340,8 +474,8 @@ extern "C" int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* byt
     if (M < 1 || M > kMaxRows) return W4A16_ERR_SHAPE;
     int rc = w4h::check_w4_shape(N, K, group);
     if (rc) return rc;
-    const Plan p = make_plan(M, N, K, kUnitK);
-    *bytes = p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0;
+    const Plan p = make_plan(M, N, K, cu_count());
+    *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     return W4A16_OK;
 }
 
@@ -350,29 +484,30 @@ extern "C" int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const
                           void* workspace, size_t workspace_bytes, w4a16_stream_t stream) {
     int rc = check_gemv_args(x, x_dtype, qweight, scales, zeros, y, y_dtype, M, N, K, group);
     if (rc) return rc;
-    const Plan p = make_plan(M, N, K, kUnitK);
-    const size_t need = p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0;
+    Plan p = make_plan(M, N, K, cu_count());
+    if (!p.upw) return W4A16_ERR_UNSUPPORTED;
+    const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     if (need) {
         if (!workspace) return W4A16_ERR_NULL;
         if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
         if (!w4h::aligned16(workspace)) return W4A16_ERR_ALIGN;
     }
+    allow_full_lds();
     hipStream_t st = (hipStream_t)stream;
-    const int T = pad_n(N) / kTileN;
     const bool bf16 = x_dtype == W4A16_BF16;
-    w4_kernel_t k = pick_kernel(bf16, group, p.depth);
-    void* out = p.split > 1 ? workspace : y;
-    const int odt = p.split > 1 ? W4A16_F32 : y_dtype;
+    w4_kernel_t k = pick_kernel(bf16, group, p.upw);
+    void* out = p.l.S > 1 ? workspace : y;
+    p.l.out_dtype = p.l.S > 1 ? W4A16_F32 : y_dtype;
     w4h::begin_launches();
-    hipLaunchKernelGGL(k, dim3(T, p.split), dim3(64 * p.waves), 0, st, (const uint16_t*)x,
+    hipLaunchKernelGGL(k, dim3(p.tiles, p.l.S), dim3(64 * p.waves), p.lds, st, (const uint16_t*)x,
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros,
-                       out, odt, M, N, K, p.split);
-    if (p.split > 1) {
+                       out, p.l);
+    if (p.l.S > 1) {
         const int MN = M * N;
         hipLaunchKernelGGL(splitk_merge_kernel, dim3((MN + 255) / 256), dim3(256), 0, st,
-                           (const float*)workspace, y, y_dtype, MN, p.split);
+                           (const float*)workspace, y, y_dtype, MN, p.l.S);
     }
-    w4h::set_last_variant("w4_mfma16 %s g%d tiles=%d waves=%d split=%d depth=%d",
-                          bf16 ? "bf16" : "f16", group, T, p.waves, p.split, p.depth);
+    w4h::set_last_variant("w4_mfma16 %s g%d tiles=%d slices=%d waves=%d upw=%d lds=%zu",
+                          bf16 ? "bf16" : "f16", group, p.tiles, p.l.S, p.waves, p.upw, p.lds);
     return w4h::launch_status();
 }

@@ -242,13 +242,15 @@ def test_repeat_calls_and_graph_replay_are_bitwise_identical():
     for _ in range(20):
         assert torch.equal(P.gemv(x, "bf16", M), y0)
     y = torch.empty_like(y0)
+    wsb = L.w4a16_workspace_bytes(M, N, K, g)
+    ws = empty_bytes(wsb) if wsb else None
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        L.w4a16_gemv(x, "bf16", P.q, P.s, P.z, y, "f32", M, N, K, g, stream=s)  # warm up
+        L.w4a16_gemv(x, "bf16", P.q, P.s, P.z, y, "f32", M, N, K, g, ws, wsb, stream=s)  # warm up
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=s):
-        L.w4a16_gemv(x, "bf16", P.q, P.s, P.z, y, "f32", M, N, K, g, stream=s)
+        L.w4a16_gemv(x, "bf16", P.q, P.s, P.z, y, "f32", M, N, K, g, ws, wsb, stream=s)
     for r in range(5):
         y.fill_(float("nan"))
         graph.replay()
@@ -273,7 +275,7 @@ def test_split_k_narrow_shard_parity_and_poisoned_workspace():
     torch.cuda.synchronize()
     variant = L.w4a16_last_variant()
     say("  variant: " + variant)
-    assert "split=1 " not in variant
+    assert "slices=1 " not in variant
     ref = oracle.w4_gemv(x, "bf16", w["qweight"], w["scales"], w["zeros"], M, N, K, g)
     assert_parity(to_f64(y), ref, "split-K")
     work.view(torch.float32)[:] = float("inf")
