@@ -10,17 +10,28 @@ HIP graph and replayed.  `value` is the effective bandwidth of that sweep
 + x + y), with inputs resident in HBM.
 
 Also reported: the same sweep at M = 4 (bf16 x with 1% outliers of magnitude
-20), per-shape microseconds per call, the read-only bandwidth probe, a roofline
-object for the GEMV kernel and the CPU oracle timed on a bounded sample.
+20), microseconds per call for each shape (a graph of that shape's 64 calls on
+distinct buffers, replayed; replay time / 64), the read-only bandwidth probe, a
+roofline object for the dominant kernel instantiation (the one with the most
+time in the M = 1 sweep) and the CPU oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+
+HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of
+this same script (FETCH_SIZE, then WRITE_SIZE), each calibrated by the counter
+value of a plain 1 GiB device copy made in the same run, folded into
+profiles/w4_gemv_traffic.json by
+
+    python bench.py --ingest-pmc FETCH.csv WRITE.csv --pmc-command "..."
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -37,6 +48,8 @@ SHAPES = (("qkv", 5120, 7168), ("o_proj", 5120, 5120), ("gate_up", 5120, 34816),
 N_LAYERS = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4_gemv_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "bit_weight_only_03_amd", "csrc", "w4_gemv.hip")
+CALIB_BYTES = 1 << 30       # the plain device copy the counter runs are calibrated with
+KERNEL_RE = re.compile(r"w4_gemv_kernel<[^>]*>")
 
 
 def log(msg):
@@ -58,9 +71,16 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic():
-    """Per-dispatch HBM bytes of the GEMV kernel from committed rocprofv3 PMC
-    summaries, if they were taken on the current kernel source."""
+def kernel_key(name):
+    """'w4_gemv_kernel<false, 4, 5>' out of a variant string or a profiler's
+    demangled kernel name (spaces normalised)."""
+    m = KERNEL_RE.search(name)
+    return re.sub(r"\s+", " ", m.group(0)) if m else None
+
+
+def load_traffic(kernel):
+    """Mean HBM bytes per dispatch of `kernel` from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -68,7 +88,65 @@ def load_traffic():
         return None
     if t.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return t.get("bytes_per_dispatch")
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_dispatch")
+
+
+def _pmc_rows(path, counter):
+    """(kernel name, value) per dispatch from a rocprofv3 counter_collection
+    CSV holding one counter."""
+    out = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name", counter) != counter:
+                continue
+            out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if not out:
+        raise SystemExit(f"{path}: no {counter} rows")
+    return out
+
+
+def ingest_pmc(fetch_csv, write_csv, command):
+    """Fold two counter runs into TRAFFIC_FILE.  FETCH_SIZE and WRITE_SIZE are
+    KiB per dispatch; each is scaled by known / counted bytes of the largest
+    plain device copy in its run (the 1 GiB calibration copy), and the result
+    is the mean per dispatch of every w4_gemv_kernel instantiation seen."""
+    res = {"kernel_source_sha256_16": kernel_source_hash(), "command": command,
+           "calibration": {}, "kernels": {}}
+    per = {}
+    for label, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"),
+                                 ("write", write_csv, "WRITE_SIZE")):
+        rows = _pmc_rows(path, counter)
+        # torch runs the contiguous 1 GiB device copy as the runtime's own
+        # copy kernel; it is by far the largest copy dispatch in the run.
+        copies = [(v, n) for n, v in rows if "copy" in n.lower()]
+        if not copies:
+            raise SystemExit(f"{path}: no device copy kernel to calibrate against")
+        v, cname = max(copies)
+        counted = v * 1024.0
+        factor = CALIB_BYTES / counted
+        if not 0.25 <= factor <= 4.0:
+            raise SystemExit(f"{path}: largest copy ({cname[:60]}) counted {counted:.3e} B, "
+                             f"not the {CALIB_BYTES} B calibration copy")
+        res["calibration"][label] = {"counter": counter, "kernel": cname[:80],
+                                     "known_bytes": CALIB_BYTES, "counted_bytes": counted,
+                                     "factor": round(factor, 5)}
+        for n, v in rows:
+            k = kernel_key(n)
+            if k:
+                per.setdefault(k, {}).setdefault(label, []).append(v * 1024.0 * factor)
+    for k, d in sorted(per.items()):
+        f, w = d.get("fetch", []), d.get("write", [])
+        if not f or not w:
+            continue
+        res["kernels"][k] = {"dispatches": [len(f), len(w)],
+                             "fetch_bytes_per_dispatch": round(float(np.mean(f))),
+                             "write_bytes_per_dispatch": round(float(np.mean(w))),
+                             "bytes_per_dispatch": round(float(np.mean(f) + np.mean(w)))}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(res, indent=1))
 
 
 class Sweep:
@@ -119,12 +197,30 @@ class Sweep:
         for i in range(len(self.mats)):
             self.launch(i, stream)
 
-    def capture(self, stream):
+    def capture(self, stream, calls=None):
         torch = self.torch
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            self.run_all(stream)
+            for i in (range(len(self.mats)) if calls is None else calls):
+                self.launch(i, stream)
         return g
+
+    def per_shape(self, stream, steps, warmup):
+        """Microseconds per call of each shape: a graph of that shape's
+        N_LAYERS calls (distinct buffers), timed with events over replays.
+        Also the kernel instantiation each shape dispatches to."""
+        out = {}
+        for mi, (name, K, N) in enumerate(SHAPES):
+            self.launch(mi, stream)
+            variant = self.L.w4a16_last_variant()
+            calls = list(range(mi, len(self.mats), len(SHAPES)))
+            g = self.capture(stream, calls)
+            t = self.time_graph(g, stream, steps, warmup) / len(calls)
+            del g
+            b = alg_bytes(self.M, N, K, GROUP, x_bytes=2, y_bytes=4)
+            out[name] = {"us": round(t * 1e6, 3), "GBps": round(gbps(b, t), 1),
+                         "bytes": b, "kernel": kernel_key(variant), "variant": variant}
+        return out
 
     def time_graph(self, graph, stream, steps, warmup):
         torch = self.torch
@@ -140,26 +236,6 @@ class Sweep:
             e1.record(stream)
             torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3 / steps
-
-    def time_launches(self, stream, reps=3):
-        """Per-launch kernel time with HIP events bracketing each launch on
-        its stream (eager).  Returns seconds per call, median of reps, in
-        call order."""
-        torch = self.torch
-        n = len(self.mats)
-        out = np.zeros((reps, n))
-        with torch.cuda.stream(stream):
-            for r in range(reps):
-                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                      for _ in range(n)]
-                torch.cuda.synchronize()
-                for i in range(n):
-                    ev[i][0].record(stream)
-                    self.launch(i, stream)
-                    ev[i][1].record(stream)
-                torch.cuda.synchronize()
-                out[r] = [a.elapsed_time(b) / 1e3 for a, b in ev]
-        return np.median(out, axis=0)
 
     def time_eager(self, stream, steps):
         torch = self.torch
@@ -239,8 +315,27 @@ def bw_probe(L, torch, nbytes=4 << 30, reps=5):
     e1.record(s)
     torch.cuda.synchronize()
     t = e0.elapsed_time(e1) / 1e3 / reps
-    del buf
+    # The plain device copy of known size that the counter runs calibrate
+    # FETCH_SIZE and WRITE_SIZE against (1 GiB read, 1 GiB written).
+    dst = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    dst.copy_(buf[:CALIB_BYTES])
+    torch.cuda.synchronize()
+    del buf, dst
     return gbps(nbytes, t)
+
+
+def dominant(per_shape):
+    """The kernel instantiation with the most time in one sweep, and its
+    algorithmic GB/s per launch (equal call counts per shape, so total bytes
+    over total time of its shapes)."""
+    tot = {}
+    for name, d in per_shape.items():
+        b, t = tot.get(d["kernel"], (0, 0.0))
+        tot[d["kernel"]] = (b + d["bytes"], t + d["us"] * 1e-6)
+    k = max(tot, key=lambda k: tot[k][1])
+    shapes = [n for n, d in per_shape.items() if d["kernel"] == k]
+    b, t = tot[k]
+    return k, shapes, b / len(shapes), t / len(shapes)
 
 
 def main():
@@ -250,7 +345,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m4", action="store_true")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="fold two rocprofv3 counter runs of this script into "
+                         "profiles/w4_gemv_traffic.json and exit (no GPU work)")
+    ap.add_argument("--pmc-command", default="", help="the command the counter runs used")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.pmc_command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library has no multi-GPU path "
               f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
@@ -271,7 +373,6 @@ def main():
     torch.cuda.synchronize()
     s1.run_all(stream)
     torch.cuda.synchronize()
-    log("variant (last call): " + L.w4a16_last_variant())
 
     import oracle as oracle_mod
     worst = parity_guard(L, torch, synth, oracle_mod, s1)
@@ -280,21 +381,18 @@ def main():
     g1 = s1.capture(stream)
     t1 = s1.time_graph(g1, stream, args.steps, args.warmup)
     log(f"M=1 sweep: {t1 * 1e3:.4f} ms/token, {gbps(s1.bytes, t1):.1f} GB/s")
+    del g1
     te1 = s1.time_eager(stream, max(2, args.steps // 4))
-    per_call = s1.time_launches(stream)
-    per_shape = {}
-    for mi, (name, K, N) in enumerate(SHAPES):
-        us = float(np.median(per_call[mi::4]) * 1e6)
-        per_shape[name] = {"us": round(us, 3),
-                           "GBps": round(alg_bytes(1, N, K, GROUP) / (us * 1e-6) / 1e9, 1)}
-    mean_launch = float(np.mean(per_call))
-    mean_bytes = s1.bytes / len(s1.mats)
-    achieved = gbps(mean_bytes, mean_launch)
-    traffic = load_traffic()
+    shapes1 = s1.per_shape(stream, args.steps, args.warmup)
+    for name, d in shapes1.items():
+        log(f"  {name}: {d['us']:.2f} us/call, {d['GBps']:.0f} GB/s  [{d['variant']}]")
+    kern, kshapes, kbytes, ktime = dominant(shapes1)
+    achieved = gbps(kbytes, ktime)
+    traffic = load_traffic(kern)
 
-    extra = {"device": dev_name, "sweep_bytes": s1.bytes, "pct_of_peak": round(100 * gbps(s1.bytes, t1) / PEAK_GBPS, 2),
-             "m1_eager_ms": round(te1 * 1e3, 4), "m1_per_shape": per_shape,
-             "variant": L.w4a16_last_variant()}
+    extra = {"device": dev_name, "sweep_bytes": s1.bytes,
+             "pct_of_peak": round(100 * gbps(s1.bytes, t1) / PEAK_GBPS, 2),
+             "m1_eager_ms": round(te1 * 1e3, 4), "m1_per_shape": shapes1}
 
     if not args.no_m4:
         log("M=4 sweep (bf16 x, 1% outliers), same weights")
@@ -304,14 +402,15 @@ def main():
         w4 = parity_guard(L, torch, synth, oracle_mod, s4)
         g4 = s4.capture(stream)
         t4 = s4.time_graph(g4, stream, args.steps, args.warmup)
-        pc4 = s4.time_launches(stream, reps=1)
+        del g4
+        shapes4 = s4.per_shape(stream, args.steps, args.warmup)
         extra["m4_sweep"] = {"ms_per_token": round(t4 * 1e3, 4), "GBps": round(gbps(s4.bytes, t4), 1),
                              "pct_of_peak": round(100 * gbps(s4.bytes, t4) / PEAK_GBPS, 2),
-                             "bytes": s4.bytes, "parity_worst_rel": w4,
-                             "per_shape_us": {name: round(float(np.median(pc4[mi::4]) * 1e6), 3)
-                                              for mi, (name, K, N) in enumerate(SHAPES)}}
+                             "bytes": s4.bytes, "parity_worst_rel": w4, "per_shape": shapes4}
         log(f"M=4 sweep: {t4 * 1e3:.4f} ms/token, {gbps(s4.bytes, t4):.1f} GB/s")
-        del g4, s4
+        for name, d in shapes4.items():
+            log(f"  {name}: {d['us']:.2f} us/call, {d['GBps']:.0f} GB/s  [{d['variant']}]")
+        del s4
 
     probe = bw_probe(L, torch)
     extra["bw_probe_GBps"] = round(probe, 1)
@@ -341,9 +440,9 @@ def main():
                    "M": 1, "group": GROUP, "layers": N_LAYERS, "x": "f16", "y": "f32"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
-                     "traffic": traffic,
-                     "kernel": "w4_gemv_kernel<f16, group 128, depth 8>",
-                     "per_launch_alg_bytes": round(mean_bytes), "per_launch_us": round(mean_launch * 1e6, 3)},
+                     "traffic": traffic, "kernel": kern, "shapes": kshapes,
+                     "per_launch_alg_bytes": round(kbytes), "per_launch_us": round(ktime * 1e6, 3),
+                     "timing": "HIP events around replays of a graph of the shape's 64 calls"},
         "cpu_baseline": cpu,
         "extra": extra,
     }

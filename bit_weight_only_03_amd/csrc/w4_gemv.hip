@@ -50,7 +50,7 @@ using namespace w4k;
 
 namespace {
 
-constexpr int kMaxWaves = 16;    // waves per workgroup
+constexpr int kMaxWaves = 8;     // waves per workgroup (the kernel's 512-thread launch bound)
 constexpr int kMaxRows = 16;     // rows per MFMA
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return bitcast<half2_t>(v); }
@@ -507,7 +507,9 @@ extern "C" int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const
         hipLaunchKernelGGL(splitk_merge_kernel, dim3((MN + 255) / 256), dim3(256), 0, st,
                            (const float*)workspace, y, y_dtype, MN, p.l.S);
     }
-    w4h::set_last_variant("w4_mfma16 %s g%d tiles=%d slices=%d waves=%d upw=%d lds=%zu",
-                          bf16 ? "bf16" : "f16", group, p.tiles, p.l.S, p.waves, p.upw, p.lds);
+    w4h::set_last_variant("w4_mfma16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d> tiles=%d slices=%d "
+                          "waves=%d upw=%d lds=%zu",
+                          bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.upw,
+                          p.tiles, p.l.S, p.waves, p.upw, p.lds);
     return w4h::launch_status();
 }

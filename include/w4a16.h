@@ -151,7 +151,8 @@ int w4a16_bw_probe_sink_floats(void);
 const char* w4a16_status_string(int status);
 
 /* Name of the kernel variant the most recent gemv call on this host thread
- * chose, with its launch shape, e.g. "w4_mfma16 f16 tiles=320 waves=8 split=1"
+ * chose, with the kernel instantiation and launch shape, e.g.
+ * "w4_mfma16 f16 g128 kernel=w4_gemv_kernel<false, 4, 5> tiles=320 slices=1 waves=8 upw=5 lds=10880"
  * (every dispatch branch reports itself: NINFER tuning page, section 二).
  * Host string owned by the library, valid until the next call on the thread. */
 const char* w4a16_last_variant(void);
