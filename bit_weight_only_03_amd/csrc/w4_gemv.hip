@@ -7,13 +7,14 @@
 // bandwidth ceiling; the Z100 vLLM article, section 五, lost 27% to zero-point
 // unpacking).
 //
-// Work decomposition.  One workgroup owns one 16-column tile (and, when the
-// tile count is too small to fill the GPU, one of S slices of K); its waves
-// split the tile's 128-k units evenly.  Per unit every lane issues one
-// non-temporal 16-byte load (1 KiB per wave, fully coalesced), so a wave
-// keeps D units in flight in a register ring (software pipelining of the
-// weight stream: Ninfer V100 article, section 十四, issue several loads
-// before computing).
+// Work decomposition.  One workgroup owns TPW consecutive 16-column tiles
+// (TPW = 1 unless there are many more tiles than the GPU holds at once) and,
+// when the tile count is too small to fill the GPU, one of S slices of K; its
+// waves split the 128-k units evenly, and each wave walks its units for all
+// TPW tiles as one chain.  Per unit every lane issues one non-temporal
+// 16-byte load (1 KiB per wave, fully coalesced), so a wave keeps D units in
+// flight in a register ring (software pipelining of the weight stream: Ninfer
+// V100 article, section 十四, issue several loads before computing).
 //
 // Dequantization in registers.  A dword of 8 nibbles becomes four fp16 pairs
 // with one AND-OR against the magic exponent of 1024 (the "place the integer
@@ -102,6 +103,7 @@ struct GemvLaunch {
     int M, N, K;
     int U;        // 128-k units per column (K rounded up)
     int S;        // K slices: workgroups (t, s) cover units [s*U/S, (s+1)*U/S) of tile t
+    int T;        // 16-column tiles
     int xstride;  // LDS row stride of a wave's staged x, in halves
     int out_dtype;
 };
@@ -112,36 +114,49 @@ struct GemvLaunch {
 template <int SPG>
 constexpr int max_slots() { return SPG >= 4 ? 9 : (SPG == 2 ? 7 : 5); }
 
-// One workgroup per (16-column tile, K slice); its W waves split the slice's
-// 128-k units into contiguous ranges of at most UPW units.  Each wave
+// One workgroup per (TPW 16-column tiles, K slice); its W waves split the
+// slice's 128-k units into contiguous ranges of at most UPW units.  Each wave
 //   1. stages its own range of x (all M rows, zeros past K) in its own LDS
 //      region -- no other wave's x is on its critical path;
-//   2. issues the loads of its units (16 weight bytes, scale and zero point
-//      per lane) -- all of them up front when UPW fits the register ring,
-//      otherwise with one refill per consumed slot on a fixed schedule, so
-//      the code is straight-line and every wait covers exactly one slot;
+//   2. issues the loads of its chain of TPW x UPW units (16 weight bytes,
+//      scale and zero point per lane; unit-major, so one x fragment serves
+//      the TPW tiles back to back) -- all of them up front when the chain
+//      fits the register ring, otherwise with one refill per consumed slot
+//      on a fixed schedule, so the code is straight-line and every wait
+//      covers exactly one slot;
 //   3. dequantizes and multiplies each unit as its slot arrives;
 // then the waves add their partial sums through LDS in wave order and the
-// workgroup stores the tile (or its fp32 slice partial).
+// workgroup stores its tiles (or their fp32 slice partials).
 //
-// A wave whose range is shorter than UPW gives its missing units an offset
-// past the buffer resource's size: such loads return zeros without touching
-// memory, and the units are skipped.
-template <bool BF16, int SPG, int UPW>
-__global__ __launch_bounds__(512) void w4_gemv_kernel(
+// A wave whose range is shorter than UPW (or a workgroup with fewer than TPW
+// tiles left) gives its missing units an offset past the buffer resource's
+// size: such loads return zeros without touching memory, and the units are
+// skipped or add exactly zero.
+//
+// Eight waves per SIMD (at most 64 VGPRs) for the short chains, where the
+// register budget allows it without spilling.
+template <int SPG, int UPW>
+constexpr int min_waves() { return (SPG >= 4 && UPW <= 5) || (SPG == 2 && UPW <= 3) ? 8 : 1; }
+
+template <bool BF16, int SPG, int UPW, int TPW>
+__global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4_gemv_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ qdev,
     const uint16_t* __restrict__ sdev, const uint32_t* __restrict__ zdev, void* __restrict__ out,
     GemvLaunch a) {
     constexpr int NG = SPG >= 4 ? 1 : 4 / SPG;          // groups per unit
     constexpr int SPU = SPG >= 4 ? 4 : SPG;             // steps per group inside one unit
-    constexpr int D = UPW < max_slots<SPG>() ? UPW : max_slots<SPG>();
+    constexpr int L = UPW * TPW;                         // units in this wave's chain
+    constexpr int DM = TPW > 1 ? 5 : max_slots<SPG>();
+    constexpr int D = L < DM ? L : DM;
+    constexpr bool kUncond = SPG >= 4 || (SPG == 2 && UPW <= 6) || UPW <= 2;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int M = a.M, K = a.K, U = a.U;
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int t = blockIdx.x, split = blockIdx.y;
+    const int t0 = blockIdx.x * TPW, split = blockIdx.y;
+    const int nt = a.T - t0 < TPW ? a.T - t0 : TPW;                   // tiles of this workgroup
     const int r0 = split * U / a.S, r1 = (split + 1) * U / a.S;
     const int w0 = r0 + wave * (r1 - r0) / W, w1 = r0 + (wave + 1) * (r1 - r0) / W;
     const int nu = w1 - w0;                                           // units of this wave
@@ -161,24 +176,32 @@ __global__ __launch_bounds__(512) void w4_gemv_kernel(
         const int xch = M * cpr;
         const uint32_t xbytes = (uint32_t)M * (uint32_t)K * 2u;
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xbytes);
-        u32x4_t xv[16];
+        // Four chunks per lane at a time keep only 16 VGPRs of x live; M = 1
+        // needs a single batch for up to 16 units per wave.
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (i * 64 < xch) {              // wave-uniform; a real branch, not 16 dummy loads
-                asm volatile("" ::: "memory");
-                const int ci = i * 64 + lane;
-                const int m = ci / cpr, kk = (ci % cpr) * 8;
-                const int kg = w0 * kUnitK + kk;
-                const uint32_t off = (ci < xch && kg < K) ? (uint32_t)(m * K + kg) * 2u : xbytes;
-                xv[i] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
-            }
-        }
+        for (int b = 0; b < 4; ++b) {
+            if (b * 256 < xch) {             // wave-uniform
+                u32x4_t xv[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int ci = i * 64 + lane;
-            if (i * 64 < xch && ci < xch) {
-                const int m = ci / cpr, kk = (ci % cpr) * 8;
-                *(u32x4_t*)(xs + m * a.xstride + kk) = xv[i];
+                for (int i = 0; i < 4; ++i) {
+                    const int ii = 4 * b + i;
+                    if (ii * 64 < xch) {     // wave-uniform; a real branch, not dummy loads
+                        asm volatile("" ::: "memory");
+                        const int ci = ii * 64 + lane;
+                        const int m = ci / cpr, kk = (ci % cpr) * 8;
+                        const int kg = w0 * kUnitK + kk;
+                        const uint32_t off = (ci < xch && kg < K) ? (uint32_t)(m * K + kg) * 2u : xbytes;
+                        xv[i] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ci = (4 * b + i) * 64 + lane;
+                    if ((4 * b + i) * 64 < xch && ci < xch) {
+                        const int m = ci / cpr, kk = (ci % cpr) * 8;
+                        *(u32x4_t*)(xs + m * a.xstride + kk) = xv[i];
+                    }
+                }
             }
         }
     }
@@ -187,22 +210,27 @@ __global__ __launch_bounds__(512) void w4_gemv_kernel(
     __builtin_amdgcn_sched_barrier(0);
 
     // 2) Weight / scale / zero-point loads of this wave's units.
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qdev + (size_t)t * U * kLanes, (uint32_t)U * 1024u);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdev + (size_t)t * Gp * kTileN, (uint32_t)Gp * 32u);
-    const __amdgpu_buffer_rsrc_t rz = make_rsrc(zdev + (size_t)t * Gp * 2, (uint32_t)Gp * 8u);
+    // The workgroup's nt tiles are contiguous in all three arrays.
+    const uint32_t wend = (uint32_t)nt * U * 1024u, send = (uint32_t)nt * Gp * 32u,
+                   zend = (uint32_t)nt * Gp * 8u;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qdev + (size_t)t0 * U * kLanes, wend);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdev + (size_t)t0 * Gp * kTileN, send);
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(zdev + (size_t)t0 * Gp * 2, zend);
     const uint32_t wlane = (uint32_t)lane * 16u;
     const uint32_t slane = (uint32_t)c * 2u;
     const uint32_t zlane = (uint32_t)(c >> 3) * 4u;
-    const uint32_t wend = (uint32_t)U * 1024u, send = (uint32_t)Gp * 32u, zend = (uint32_t)Gp * 8u;
 
-    auto load_slot = [&](int i, Slot<NG>& r) {   // unit w0 + i
-        const bool valid = i < nu;
+    // Chain position q = unit i (of this wave's range) x tile j, unit-major,
+    // so one x fragment serves the workgroup's TPW tiles back to back.
+    auto load_slot = [&](int q, Slot<NG>& r) {
+        const int i = q / TPW, j = q % TPW;
+        const bool valid = i < nu && j < nt;
         const int u = w0 + i;
         r.w = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
-            rw, valid ? wlane + (uint32_t)u * 1024u : wend, 0, kAuxNT));
+            rw, valid ? wlane + (uint32_t)(j * U + u) * 1024u : wend, 0, kAuxNT));
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
-            const int g = (u * 4) / SPG + gi;
+            const int g = j * Gp + (u * 4) / SPG + gi;
             r.s[gi] = __builtin_amdgcn_raw_buffer_load_b16(rs, valid ? slane + (uint32_t)g * 32u : send, 0, 0);
             r.z[gi] = __builtin_amdgcn_raw_buffer_load_b32(rz, valid ? zlane + (uint32_t)g * 8u : zend, 0, 0);
         }
@@ -220,17 +248,25 @@ __global__ __launch_bounds__(512) void w4_gemv_kernel(
     const uint32_t magic = BF16 ? 0x43004300u : 0x64006400u;   // 128.0 / 1024.0 pairs
     const bool xrow = c < M;                                    // lane supplies x row c
     const uint8_t* xlane = (const uint8_t*)xs + (uint32_t)(c * a.xstride + 8 * kc) * 2u;
-    float4_t total = {0.f, 0.f, 0.f, 0.f};
+    float4_t total[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) total[j] = float4_t{0.f, 0.f, 0.f, 0.f};
     u32x4_t xa[4] = {};
 #pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-        Slot<NG>& sl = ring[i % D];
-        if (i < nu) {
-            if (xrow) {
+    for (int q = 0; q < L; ++q) {
+        const int i = q / TPW, tj = q % TPW;
+        Slot<NG>& sl = ring[q % D];
+        if (tj == 0 && i < nu && xrow) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    xa[j] = *(const u32x4_t*)(xlane + (uint32_t)i * (kUnitK * 2) + 64 * j);
-            }
+            for (int j = 0; j < 4; ++j)
+                xa[j] = *(const u32x4_t*)(xlane + (uint32_t)i * (kUnitK * 2) + 64 * j);
+        }
+        // Units past this wave's range arrived as zeros (q = z = 0, s = +0) and
+        // add exactly 0 with the finite x the lane still holds, so where the
+        // register budget allows, the arithmetic runs unconditionally: then no
+        // slot's loads get sunk into a conditional block next to their only use
+        // (which would make the first unit wait for the whole ring).
+        if (kUncond || (i < nu && tj < nt)) {
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const uint32_t zq = (sl.z[gi] >> zshift) & 15u;
@@ -261,15 +297,15 @@ __global__ __launch_bounds__(512) void w4_gemv_kernel(
                     }
                 }
                 const float sf = f16_bits_to_f32((uint16_t)sl.s[gi]);
-                total[0] = __builtin_fmaf(sf, acc[0], total[0]);
-                total[1] = __builtin_fmaf(sf, acc[1], total[1]);
-                total[2] = __builtin_fmaf(sf, acc[2], total[2]);
-                total[3] = __builtin_fmaf(sf, acc[3], total[3]);
+                total[tj][0] = __builtin_fmaf(sf, acc[0], total[tj][0]);
+                total[tj][1] = __builtin_fmaf(sf, acc[1], total[tj][1]);
+                total[tj][2] = __builtin_fmaf(sf, acc[2], total[tj][2]);
+                total[tj][3] = __builtin_fmaf(sf, acc[3], total[tj][3]);
             }
         }
-        if (i + D < UPW) {                 // fixed refill schedule: unit i + D into this slot
+        if (q + D < L) {                   // fixed refill schedule: position q + D into this slot
             __builtin_amdgcn_sched_barrier(0);
-            load_slot(i + D, sl);
+            load_slot(q + D, sl);
         }
         __builtin_amdgcn_sched_barrier(0);   // units in order: each waits for its own slot only
     }
@@ -277,17 +313,20 @@ __global__ __launch_bounds__(512) void w4_gemv_kernel(
     // 4) Wave partials (lane l holds rows 4*(l/16) + r of column l % 16) ->
     //    LDS, then M x 16 threads add them in wave order and store.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int m = 4 * kc + r;
-        if (m < M) red[(wave * M + m) * kTileN + c] = total[r];
-    }
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * kc + r;
+            if (m < M) red[((j * W + wave) * M + m) * kTileN + c] = total[j][r];
+        }
     __syncthreads();
-    if ((int)threadIdx.x < M * kTileN) {
-        const int m = threadIdx.x >> 4, cc = threadIdx.x & 15;
+    for (int idx = threadIdx.x; idx < TPW * M * kTileN; idx += blockDim.x) {
+        const int j = idx / (M * kTileN), rem = idx % (M * kTileN);
+        const int m = rem >> 4, cc = rem & 15;
         float v = 0.f;
-        for (int w = 0; w < W; ++w) v += red[(w * M + m) * kTileN + cc];
-        const int n = t * kTileN + cc;
-        if (n < a.N) {
+        for (int w = 0; w < W; ++w) v += red[((j * W + w) * M + m) * kTileN + cc];
+        const int n = (t0 + j) * kTileN + cc;
+        if (j < nt && n < a.N) {
             const size_t o = (size_t)split * M * a.N + (size_t)m * a.N + n;
             if (a.out_dtype == W4A16_F32)
                 ((float*)out)[o] = v;
@@ -317,7 +356,7 @@ __global__ void splitk_merge_kernel(const float* __restrict__ ws, void* __restri
 // ------------------------------------------------------------------ dispatch
 
 struct Tuning {
-    int waves = 0, split = 0;  // 0 = automatic
+    int waves = 0, split = 0, tpw = 0;  // 0 = automatic
 };
 
 const Tuning& tuning() {
@@ -328,6 +367,7 @@ const Tuning& tuning() {
     std::call_once(once, [] {
         if (const char* e = getenv("W4A16_WAVES")) t.waves = atoi(e);
         if (const char* e = getenv("W4A16_SPLIT")) t.split = atoi(e);
+        if (const char* e = getenv("W4A16_TPW")) t.tpw = atoi(e);
     });
     return t;
 }
@@ -356,6 +396,7 @@ struct Plan {
     GemvLaunch l;
     int waves;
     int upw;
+    int tpw;
     size_t lds;
     int tiles;
 };
@@ -367,7 +408,8 @@ int pick_upw(int need) {
     return 0;
 }
 
-Plan make_plan(int M, int N, int K, int cus) {
+Plan make_plan(int M, int N, int K, int group, int cus) {
+    const bool group_tpw_ok = group == 128;   // multi-tile kernels are compiled for g128
     Plan p;
     const Tuning& tu = tuning();
     const int U = (K + kUnitK - 1) / kUnitK;
@@ -396,9 +438,22 @@ Plan make_plan(int M, int N, int K, int cus) {
     while ((long long)T * S < cus && U / (2 * S) >= 2 * W && fits(2 * S, upw, lds, xstride)) S *= 2;
     if (tu.split >= 1 && tu.split <= U) S = tu.split;
     if (!fits(S, upw, lds, xstride)) upw = 0;   // an override that cannot run is refused
-    p.l = GemvLaunch{M, N, K, U, S, xstride, W4A16_F32};
+    p.l = GemvLaunch{M, N, K, U, S, T, xstride, W4A16_F32};
     p.waves = W;
     p.upw = upw;
+    // Several tiles per workgroup when there are many more tiles than the GPU
+    // holds at once: each wave then streams a chain of TPW x upw units with a
+    // refill ring instead of issuing everything and going idle, and the
+    // workgroup stages x once for all its tiles.
+    p.tpw = 1;
+    if (group_tpw_ok && upw <= 6 && S == 1 && T >= 6 * cus) p.tpw = 3;
+    if (tu.tpw >= 1 && tu.tpw <= 4 && upw <= 6 && group_tpw_ok) p.tpw = tu.tpw;
+    // The reduction buffer holds one [W][M][16] block per tile.
+    const size_t red_more = (size_t)(p.tpw - 1) * W * M * kTileN * 4;
+    if (lds + red_more <= kLdsPerCu)
+        lds += red_more;
+    else
+        p.tpw = 1;
     p.lds = lds;
     p.tiles = T;
     return p;
@@ -407,34 +462,48 @@ Plan make_plan(int M, int N, int K, int cus) {
 typedef void (*w4_kernel_t)(const uint16_t*, const u32x4_t*, const uint16_t*, const uint32_t*,
                             void*, GemvLaunch);
 
-template <bool BF16, int SPG>
-w4_kernel_t pick_upw_kernel(int upw) {
+template <bool BF16, int SPG, int TPW>
+w4_kernel_t pick_small_upw(int upw) {
     switch (upw) {
-        case 1: return w4_gemv_kernel<BF16, SPG, 1>;
-        case 2: return w4_gemv_kernel<BF16, SPG, 2>;
-        case 3: return w4_gemv_kernel<BF16, SPG, 3>;
-        case 4: return w4_gemv_kernel<BF16, SPG, 4>;
-        case 5: return w4_gemv_kernel<BF16, SPG, 5>;
-        case 6: return w4_gemv_kernel<BF16, SPG, 6>;
-        case 8: return w4_gemv_kernel<BF16, SPG, 8>;
-        case 9: return w4_gemv_kernel<BF16, SPG, 9>;
-        case 12: return w4_gemv_kernel<BF16, SPG, 12>;
-        default: return w4_gemv_kernel<BF16, SPG, 17>;
+        case 1: return w4_gemv_kernel<BF16, SPG, 1, TPW>;
+        case 2: return w4_gemv_kernel<BF16, SPG, 2, TPW>;
+        case 3: return w4_gemv_kernel<BF16, SPG, 3, TPW>;
+        case 4: return w4_gemv_kernel<BF16, SPG, 4, TPW>;
+        case 5: return w4_gemv_kernel<BF16, SPG, 5, TPW>;
+        default: return w4_gemv_kernel<BF16, SPG, 6, TPW>;
+    }
+}
+
+template <bool BF16, int SPG>
+w4_kernel_t pick_upw_kernel(int upw, int tpw) {
+    if (upw <= 6) {
+        if constexpr (SPG == 4) {
+            if (tpw == 2) return pick_small_upw<BF16, SPG, 2>(upw);
+            if (tpw == 3) return pick_small_upw<BF16, SPG, 3>(upw);
+            if (tpw == 4) return pick_small_upw<BF16, SPG, 4>(upw);
+        }
+        return pick_small_upw<BF16, SPG, 1>(upw);
+    }
+    switch (upw) {
+        case 8: return w4_gemv_kernel<BF16, SPG, 8, 1>;
+        case 9: return w4_gemv_kernel<BF16, SPG, 9, 1>;
+        case 12: return w4_gemv_kernel<BF16, SPG, 12, 1>;
+        default: return w4_gemv_kernel<BF16, SPG, 17, 1>;
     }
 }
 
 template <bool BF16>
-w4_kernel_t pick_group(int group, int upw) {
+w4_kernel_t pick_group(int group, int upw, int tpw) {
     switch (group) {
-        case 32: return pick_upw_kernel<BF16, 1>(upw);
-        case 64: return pick_upw_kernel<BF16, 2>(upw);
-        case 128: return pick_upw_kernel<BF16, 4>(upw);
-        default: return pick_upw_kernel<BF16, 8>(upw);
+        case 32: return pick_upw_kernel<BF16, 1>(upw, tpw);
+        case 64: return pick_upw_kernel<BF16, 2>(upw, tpw);
+        case 128: return pick_upw_kernel<BF16, 4>(upw, tpw);
+        default: return pick_upw_kernel<BF16, 8>(upw, tpw);
     }
 }
 
-w4_kernel_t pick_kernel(bool bf16, int group, int upw) {
-    return bf16 ? pick_group<true>(group, upw) : pick_group<false>(group, upw);
+w4_kernel_t pick_kernel(bool bf16, int group, int upw, int tpw) {
+    return bf16 ? pick_group<true>(group, upw, tpw) : pick_group<false>(group, upw, tpw);
 }
 
 // Allow every GEMV kernel the whole LDS of a CU, once per process (before any
@@ -445,7 +514,8 @@ void allow_full_lds() {
         for (int bf = 0; bf < 2; ++bf)
             for (int g : {32, 64, 128, 256})
                 for (int u : kUpwSet)
-                    (void)hipFuncSetAttribute((const void*)pick_kernel(bf, g, u),
+                  for (int tp = 1; tp <= 4; ++tp)
+                    (void)hipFuncSetAttribute((const void*)pick_kernel(bf, g, u, tp),
                                               hipFuncAttributeMaxDynamicSharedMemorySize,
                                               (int)kLdsPerCu);
         (void)hipGetLastError();
@@ -474,7 +544,7 @@ extern "C" int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* byt
     if (M < 1 || M > kMaxRows) return W4A16_ERR_SHAPE;
     int rc = w4h::check_w4_shape(N, K, group);
     if (rc) return rc;
-    const Plan p = make_plan(M, N, K, cu_count());
+    const Plan p = make_plan(M, N, K, group, cu_count());
     *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     return W4A16_OK;
 }
@@ -484,7 +554,7 @@ extern "C" int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const
                           void* workspace, size_t workspace_bytes, w4a16_stream_t stream) {
     int rc = check_gemv_args(x, x_dtype, qweight, scales, zeros, y, y_dtype, M, N, K, group);
     if (rc) return rc;
-    Plan p = make_plan(M, N, K, cu_count());
+    Plan p = make_plan(M, N, K, group, cu_count());
     if (!p.upw) return W4A16_ERR_UNSUPPORTED;
     const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     if (need) {
@@ -495,11 +565,12 @@ extern "C" int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const
     allow_full_lds();
     hipStream_t st = (hipStream_t)stream;
     const bool bf16 = x_dtype == W4A16_BF16;
-    w4_kernel_t k = pick_kernel(bf16, group, p.upw);
+    w4_kernel_t k = pick_kernel(bf16, group, p.upw, p.tpw);
     void* out = p.l.S > 1 ? workspace : y;
     p.l.out_dtype = p.l.S > 1 ? W4A16_F32 : y_dtype;
     w4h::begin_launches();
-    hipLaunchKernelGGL(k, dim3(p.tiles, p.l.S), dim3(64 * p.waves), p.lds, st, (const uint16_t*)x,
+    hipLaunchKernelGGL(k, dim3((p.tiles + p.tpw - 1) / p.tpw, p.l.S), dim3(64 * p.waves), p.lds, st,
+                       (const uint16_t*)x,
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros,
                        out, p.l);
     if (p.l.S > 1) {
@@ -507,9 +578,9 @@ extern "C" int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const
         hipLaunchKernelGGL(splitk_merge_kernel, dim3((MN + 255) / 256), dim3(256), 0, st,
                            (const float*)workspace, y, y_dtype, MN, p.l.S);
     }
-    w4h::set_last_variant("w4_mfma16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d> tiles=%d slices=%d "
-                          "waves=%d upw=%d lds=%zu",
+    w4h::set_last_variant("w4_mfma16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, %d> tiles=%d slices=%d "
+                          "waves=%d upw=%d tpw=%d lds=%zu",
                           bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.upw,
-                          p.tiles, p.l.S, p.waves, p.upw, p.lds);
+                          p.tpw, p.tiles, p.l.S, p.waves, p.upw, p.tpw, p.lds);
     return w4h::launch_status();
 }

@@ -282,6 +282,26 @@ def test_split_k_narrow_shard_parity_and_poisoned_workspace():
     assert torch.equal(P.gemv(dev(x), "bf16", M, workspace=work), y)
 
 
+@pytest.mark.parametrize("M,K,xdt", [(1, 1152, "f16"), (8, 1152, "bf16"), (3, 640, "f16"),
+                                       (16, 256, "bf16")])
+def test_multi_tile_workgroups_ragged(M, K, xdt):
+    # Many more tiles than the GPU holds at once: each workgroup takes three
+    # tiles, and 1537 tiles leave a last workgroup with a single one.
+    N, g = 24592, 128
+    say(f"multi-tile M={M} N={N} K={K} x={xdt}")
+    key = (113, M, K)
+    w = synth.gen_w4(key, N, K, g)
+    x = synth.gen_x(key, M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    P = PackedW4(w, N, K, g)
+    y = P.gemv(dev(x), xdt, M)
+    torch.cuda.synchronize()
+    variant = L.w4a16_last_variant()
+    say("  variant: " + variant)
+    assert "tpw=3 " in variant
+    ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g)
+    assert_parity(to_f64(y), ref, f"multi-tile M={M} K={K}")
+
+
 # ----------------------------------------------- full 27B-class shapes, sampled ---
 
 FULL = [("qkv", 5120, 7168), ("o_proj", 5120, 5120), ("gate_up", 5120, 34816),
