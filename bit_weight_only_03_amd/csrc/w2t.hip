@@ -18,13 +18,14 @@
 // (f = 1, 4, 16, 64, 256 by bit position) and one packed fma by 1/f with
 // -(1024/f + 1) gives c - 1 exactly; for bf16 activations the pairs are
 // 128 + c and a second MFMA against the constant -129 removes the bias.
+#include <mutex>
+
 #include "common.h"
 
 using namespace w4k;
 
 namespace {
 
-constexpr int kMaxWaves = 8;
 constexpr int kMaxRows = 16;
 
 __host__ __device__ constexpr int field_step(int p) { return (p >> 2) & 1; }
@@ -157,15 +158,250 @@ __device__ __forceinline__ void biased_w2_bf16(uint32_t d, bf16x8_t& b0, bf16x8_
     b1 = bitcast<bf16x8_t>(v1);
 }
 
+// One ring slot: a unit's 16 weight bytes for this lane plus the scales of
+// the groups the unit covers.
 template <int NG>
 struct Slot2 {
     u32x4_t w;
     uint32_t s[NG];
 };
 
+// Launch description shared by host and kernel.
+struct W2Launch {
+    int M, N, K;
+    int U;        // 256-k units per column (K rounded up)
+    int S;        // K slices: workgroups (t, s) cover units [s*U/S, (s+1)*U/S) of tile t
+    int xstride;  // LDS row stride of a wave's staged x, in halves
+    int out_dtype;
+};
+
+// Register-ring depth by group size (more groups per unit = more scale words
+// per slot).
+template <int SPG>
+constexpr int max_slots2() { return SPG >= 4 ? 6 : (SPG == 2 ? 5 : 3); }
+
+// Eight waves per SIMD (at most 64 VGPRs) where the chain is short enough.
+template <int SPG, int UPW>
+constexpr int min_waves2() { return SPG >= 4 && UPW <= 4 ? 8 : 1; }
+
+// The ternary GEMV has the same structure as the 4-bit one: one workgroup per
+// (16-column tile, K slice), W waves splitting the slice's 256-k units into
+// contiguous ranges of at most UPW units; each wave stages its own x range in
+// its own LDS region, issues the weight and scale loads of its units up front
+// (or D of them and one refill per consumed slot, straight-line), and
+// dequantizes and multiplies each unit as its slot arrives; the waves then add
+// their partial sums through LDS in wave order.
+//
+// A wave's missing units load as zeros (code 0 and scale +0): the group sums
+// they feed are multiplied by a zero scale and add exactly 0, so the
+// arithmetic runs unconditionally and each wait covers one slot.
+template <bool BF16, int SPG, int UPW>
+__global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel(
+    const uint16_t* __restrict__ x, const u32x4_t* __restrict__ qdev,
+    const uint16_t* __restrict__ sdev, void* __restrict__ out, W2Launch a) {
+    constexpr int NG = SPG >= 8 ? 1 : 8 / SPG;   // groups per unit
+    constexpr int SPU = SPG >= 8 ? 8 : SPG;      // 32-k steps per group inside one unit
+    constexpr int D = UPW < max_slots2<SPG>() ? UPW : max_slots2<SPG>();
+    // Unconditional arithmetic where the register budget allows (see below).
+    constexpr bool kUncond = SPG >= 4 || UPW <= 2;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int M = a.M, K = a.K, U = a.U;
+    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int t = blockIdx.x, split = blockIdx.y;
+    const int r0 = split * U / a.S, r1 = (split + 1) * U / a.S;
+    const int w0 = r0 + wave * (r1 - r0) / W, w1 = r0 + (wave + 1) * (r1 - r0) / W;
+    const int nu = w1 - w0;                                           // units of this wave
+    const int Gp = U * kUnitK2 / (SPG * 32);
+    const int c = lane & 15, kc = lane >> 4;
+
+    // LDS: wave w's x range [M][xstride] halves at w * M * xstride, then the
+    // reduction buffer [W][M][16] floats.
+    uint16_t* xs = (uint16_t*)smem + (size_t)wave * M * a.xstride;
+    float* red = (float*)(smem + (size_t)W * M * a.xstride * 2);
+
+    // 1) x range -> LDS, four 16-byte chunks per lane at a time (the planner
+    //    keeps M * UPW <= 32, so at most 16 chunks per lane).
+    {
+        const int cpr = nu * (kUnitK2 / 8);   // 16-byte chunks per row
+        const int xch = M * cpr;
+        const uint32_t xbytes = (uint32_t)M * (uint32_t)K * 2u;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xbytes);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (b * 256 < xch) {             // wave-uniform
+                u32x4_t xv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ii = 4 * b + i;
+                    if (ii * 64 < xch) {     // wave-uniform; a real branch, not dummy loads
+                        asm volatile("" ::: "memory");
+                        const int ci = ii * 64 + lane;
+                        const int m = ci / cpr, kk = (ci % cpr) * 8;
+                        const int kg = w0 * kUnitK2 + kk;
+                        const uint32_t off = (ci < xch && kg < K) ? (uint32_t)(m * K + kg) * 2u : xbytes;
+                        xv[i] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ci = (4 * b + i) * 64 + lane;
+                    if ((4 * b + i) * 64 < xch && ci < xch) {
+                        const int m = ci / cpr, kk = (ci % cpr) * 8;
+                        *(u32x4_t*)(xs + m * a.xstride + kk) = xv[i];
+                    }
+                }
+            }
+        }
+    }
+    // Weight loads must not be hoisted above the x stores.
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2) Weight and scale loads of this wave's units.
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qdev + (size_t)t * U * kLanes, (uint32_t)U * 1024u);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdev + (size_t)t * Gp * kTileN, (uint32_t)Gp * 32u);
+    const uint32_t wlane = (uint32_t)lane * 16u;
+    const uint32_t slane = (uint32_t)c * 2u;
+    const uint32_t wend = (uint32_t)U * 1024u, send = (uint32_t)Gp * 32u;
+
+    auto load_slot = [&](int i, Slot2<NG>& r) {   // unit w0 + i
+        const bool valid = i < nu;
+        const int u = w0 + i;
+        r.w = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
+            rw, valid ? wlane + (uint32_t)u * 1024u : wend, 0, kAuxNT));
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+            r.s[gi] = __builtin_amdgcn_raw_buffer_load_b16(
+                rs, valid ? slane + (uint32_t)(u * NG + gi) * 32u : send, 0, 0);
+    };
+
+    Slot2<NG> ring[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        load_slot(i, ring[i]);
+        __builtin_amdgcn_sched_barrier(0);   // slots issue in ring order
+    }
+
+    // 3) Dequantize and multiply, unit by unit, two 32-k steps per dword.
+    const bool xrow = c < M;                                    // lane supplies x row c
+    const uint8_t* xlane = (const uint8_t*)xs + (uint32_t)(c * a.xstride + 8 * kc) * 2u;
+    const bf16x8_t bias = bitcast<bf16x8_t>(
+        u32x4_t{0xC301C301u, 0xC301C301u, 0xC301C301u, 0xC301C301u});   // bf16 -129
+    float4_t total = {0.f, 0.f, 0.f, 0.f};
+    u32x4_t xa[2] = {};
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+        Slot2<NG>& sl = ring[i % D];
+        if (kUncond || i < nu) {
+            float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd) {
+                if (i < nu && xrow) {
+                    xa[0] = *(const u32x4_t*)(xlane + (uint32_t)i * (kUnitK2 * 2) + 128 * dd);
+                    xa[1] = *(const u32x4_t*)(xlane + (uint32_t)i * (kUnitK2 * 2) + 128 * dd + 64);
+                }
+                // The dword's two steps as B operands.
+                u32x4_t bw[2];
+                if constexpr (!BF16) {
+                    half8_t b0, b1;
+                    dequant_w2_f16(sl.w[dd], b0, b1);
+                    bw[0] = bitcast<u32x4_t>(b0);
+                    bw[1] = bitcast<u32x4_t>(b1);
+                } else {
+                    bf16x8_t b0, b1;
+                    biased_w2_bf16(sl.w[dd], b0, b1);
+                    bw[0] = bitcast<u32x4_t>(b0);
+                    bw[1] = bitcast<u32x4_t>(b1);
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int st = 2 * dd + h;
+                    if constexpr (!BF16) {
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            bitcast<half8_t>(xa[h]), bitcast<half8_t>(bw[h]), acc, 0, 0, 0);
+                    } else {
+                        const bf16x8_t av = bitcast<bf16x8_t>(xa[h]);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bitcast<bf16x8_t>(bw[h]),
+                                                                      acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bias, acc, 0, 0, 0);
+                    }
+                    if ((st + 1) % SPU == 0) {    // group complete: scale once, in fp32
+                        const float sf = f16_bits_to_f32((uint16_t)sl.s[st / SPU]);
+                        total[0] = __builtin_fmaf(sf, acc[0], total[0]);
+                        total[1] = __builtin_fmaf(sf, acc[1], total[1]);
+                        total[2] = __builtin_fmaf(sf, acc[2], total[2]);
+                        total[3] = __builtin_fmaf(sf, acc[3], total[3]);
+                        acc = float4_t{0.f, 0.f, 0.f, 0.f};
+                    }
+                }
+            }
+        }
+        if (i + D < UPW) {                 // fixed refill schedule: unit i + D into this slot
+            __builtin_amdgcn_sched_barrier(0);
+            load_slot(i + D, sl);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // units in order: each waits for its own slot only
+    }
+
+    // 4) Wave partials -> LDS, then M x 16 threads add them in wave order.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kc + r;
+        if (m < M) red[(wave * M + m) * kTileN + c] = total[r];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < M * kTileN; idx += blockDim.x) {
+        const int m = idx >> 4, cc = idx & 15;
+        float v = 0.f;
+        for (int w = 0; w < W; ++w) v += red[(w * M + m) * kTileN + cc];
+        const int n = t * kTileN + cc;
+        if (n < a.N) {
+            const size_t o = (size_t)split * M * a.N + (size_t)m * a.N + n;
+            if (a.out_dtype == W4A16_F32)
+                ((float*)out)[o] = v;
+            else if (a.out_dtype == W4A16_F16)
+                ((_Float16*)out)[o] = (_Float16)v;
+            else
+                ((uint16_t*)out)[o] = f32_to_bf16_bits(v);
+        }
+    }
+}
+
+__global__ void w2_merge_kernel(const float* __restrict__ ws, void* __restrict__ y, int out_dtype,
+                                int MN, int S) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= MN) return;
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += ws[(size_t)s * MN + i];
+    if (out_dtype == W4A16_F32)
+        ((float*)y)[i] = v;
+    else if (out_dtype == W4A16_F16)
+        ((_Float16*)y)[i] = (_Float16)v;
+    else
+        ((uint16_t*)y)[i] = f32_to_bf16_bits(v);
+}
+
+// ------------------------------------------------- direct-x variant (larger M)
+//
+// The staged kernel above keeps M x (K slice) x 2 bytes of x in LDS per
+// workgroup, which for several rows and a long K leaves one workgroup per CU
+// or forces a K split.  This variant reads each unit's x fragment for the
+// lane's row straight from L2 into registers, double-buffered one unit ahead,
+// and keeps a four-deep weight ring; it needs no LDS for x.
+
+constexpr int kMaxWavesX = 8;
+
+template <int NG>
+struct SlotX {
+    u32x4_t w;
+    uint32_t s[NG];
+};
+
 // SPG = group / 32 steps per group; a unit has 8 steps (256 k).
 template <bool BF16, int SPG, int D>
-__global__ __launch_bounds__(512) void w2t_gemv_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(512) void w2t_gemv_direct_kernel(const uint16_t* __restrict__ x,
                                                        const u32x4_t* __restrict__ qdev,
                                                        const uint16_t* __restrict__ sdev,
                                                        void* __restrict__ out, int out_dtype, int M,
@@ -173,7 +409,7 @@ __global__ __launch_bounds__(512) void w2t_gemv_kernel(const uint16_t* __restric
     static_assert(D % 2 == 0, "x double buffer alternates with the ring index");
     constexpr int NG = SPG >= 8 ? 1 : 8 / SPG;   // groups per unit
     constexpr int SPU = SPG >= 8 ? 8 : SPG;      // steps per group inside one unit
-    __shared__ float red[kMaxWaves][kMaxRows][kTileN];
+    __shared__ float red[kMaxWavesX][kMaxRows][kTileN];
 
     const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -193,7 +429,7 @@ __global__ __launch_bounds__(512) void w2t_gemv_kernel(const uint16_t* __restric
     const int xm = c < M ? c : M - 1;   // rows >= M feed output rows that are never stored
     const uint32_t xlane = ((uint32_t)xm * (uint32_t)K + 8u * (uint32_t)kc) * 2u;
 
-    auto load_slot = [&](int u, Slot2<NG>& r) {
+    auto load_slot = [&](int u, SlotX<NG>& r) {
         r.w = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rw, wlane, u * 1024, kAuxNT));
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi)
@@ -213,7 +449,7 @@ __global__ __launch_bounds__(512) void w2t_gemv_kernel(const uint16_t* __restric
     };
 
     float4_t total = {0.f, 0.f, 0.f, 0.f};
-    Slot2<NG> ring[D];
+    SlotX<NG> ring[D];
     u32x4_t xb[2][8];
 #pragma unroll
     for (int i = 0; i < D; ++i)
@@ -227,7 +463,7 @@ __global__ __launch_bounds__(512) void w2t_gemv_kernel(const uint16_t* __restric
             if (u < u1) {
                 u32x4_t (&xcur)[8] = xb[i & 1];
                 if (u + 1 < u1) load_x(u + 1, xb[(i + 1) & 1]);
-                Slot2<NG>& sl = ring[i];
+                SlotX<NG>& sl = ring[i];
                 float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int st = 0; st < 8; st += 2) {
@@ -282,30 +518,16 @@ __global__ __launch_bounds__(512) void w2t_gemv_kernel(const uint16_t* __restric
     }
 }
 
-__global__ void w2_merge_kernel(const float* __restrict__ ws, void* __restrict__ y, int out_dtype,
-                                int MN, int S) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= MN) return;
-    float v = 0.f;
-    for (int s = 0; s < S; ++s) v += ws[(size_t)s * MN + i];
-    if (out_dtype == W4A16_F32)
-        ((float*)y)[i] = v;
-    else if (out_dtype == W4A16_F16)
-        ((_Float16*)y)[i] = (_Float16)v;
-    else
-        ((uint16_t*)y)[i] = f32_to_bf16_bits(v);
-}
-
-struct Plan2 {
+struct PlanX {
     int waves, split, depth;
 };
 
-Plan2 make_plan2(int N, int K) {
+PlanX make_planx(int N, int K) {
     const int U = (K + kUnitK2 - 1) / kUnitK2;
     const int T = pad_n(N) / kTileN;
-    Plan2 p;
+    PlanX p;
     p.waves = (U + 1) / 2;  // about two 256-k units per wave
-    if (p.waves > kMaxWaves) p.waves = kMaxWaves;
+    if (p.waves > kMaxWavesX) p.waves = kMaxWavesX;
     if (p.waves < 1) p.waves = 1;
     p.split = 1;
     if (T < 256) {
@@ -318,17 +540,134 @@ Plan2 make_plan2(int N, int K) {
     return p;
 }
 
-typedef void (*w2_kernel_t)(const uint16_t*, const u32x4_t*, const uint16_t*, void*, int, int, int,
-                            int, int);
+typedef void (*w2x_kernel_t)(const uint16_t*, const u32x4_t*, const uint16_t*, void*, int, int, int,
+                             int, int);
 
 template <bool BF16>
-w2_kernel_t pick2(int group) {
+w2x_kernel_t pickx(int group) {
     switch (group) {
-        case 32: return w2t_gemv_kernel<BF16, 1, 4>;
-        case 64: return w2t_gemv_kernel<BF16, 2, 4>;
-        case 128: return w2t_gemv_kernel<BF16, 4, 4>;
-        default: return w2t_gemv_kernel<BF16, 8, 4>;
+        case 32: return w2t_gemv_direct_kernel<BF16, 1, 4>;
+        case 64: return w2t_gemv_direct_kernel<BF16, 2, 4>;
+        case 128: return w2t_gemv_direct_kernel<BF16, 4, 4>;
+        default: return w2t_gemv_direct_kernel<BF16, 8, 4>;
     }
+}
+
+
+// ------------------------------------------------------------------ dispatch
+
+// Compute units of the current device (queried once; 256 on MI355X).
+int cu_count2() {
+    static int n = 0;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+            prop.multiProcessorCount > 0)
+            n = prop.multiProcessorCount;
+        else
+            n = 256;
+    });
+    return n;
+}
+
+constexpr size_t kLdsPerCu2 = 160 * 1024;      // gfx950
+constexpr int kWaves2 = 8;
+constexpr int kUpwSet2[] = {1, 2, 3, 4, 5, 6, 8, 9, 12, 17};
+
+struct Plan2 {
+    W2Launch l;
+    int waves, upw, tiles;
+    size_t lds;
+};
+
+int pick_upw2(int need) {
+    for (int u : kUpwSet2)
+        if (u >= need) return u;
+    return 0;
+}
+
+// Same rules as the 4-bit planner: slices only when the compiled ranges or
+// LDS require them, or when the tile count leaves CUs idle and each wave
+// keeps at least two units per slice.
+Plan2 make_plan2(int M, int N, int K, int cus) {
+    Plan2 p;
+    const int U = (K + kUnitK2 - 1) / kUnitK2;
+    const int T = pad_n(N) / kTileN;
+    const int W = kWaves2;
+    auto fits = [&](int S, int& upw, size_t& lds, int& xstride) {
+        const int RU = (U + S - 1) / S;
+        const int w = W < RU ? W : RU;
+        upw = pick_upw2((RU + w - 1) / w);
+        if (!upw || M * upw > 32) return false;
+        xstride = upw * kUnitK2 + 8;   // +16 bytes per row spreads rows over LDS banks
+        lds = (size_t)W * M * xstride * 2 + (size_t)W * M * kTileN * 4;
+        return lds <= kLdsPerCu2;
+    };
+    int S = 1, upw = 0, xstride = 0;
+    size_t lds = 0;
+    while (S < U && !fits(S, upw, lds, xstride)) S *= 2;
+    while ((long long)T * S < cus && U / (2 * S) >= 2 * W && fits(2 * S, upw, lds, xstride)) S *= 2;
+    if (!fits(S, upw, lds, xstride)) upw = 0;
+    p.l = W2Launch{M, N, K, U, S, xstride, W4A16_F32};
+    p.waves = W;
+    p.upw = upw;
+    p.tiles = T;
+    p.lds = lds;
+    return p;
+}
+
+typedef void (*w2_kernel_t)(const uint16_t*, const u32x4_t*, const uint16_t*, void*, W2Launch);
+
+template <bool BF16, int SPG>
+w2_kernel_t pick_upw2_kernel(int upw) {
+    switch (upw) {
+        case 1: return w2t_gemv_kernel<BF16, SPG, 1>;
+        case 2: return w2t_gemv_kernel<BF16, SPG, 2>;
+        case 3: return w2t_gemv_kernel<BF16, SPG, 3>;
+        case 4: return w2t_gemv_kernel<BF16, SPG, 4>;
+        case 5: return w2t_gemv_kernel<BF16, SPG, 5>;
+        case 6: return w2t_gemv_kernel<BF16, SPG, 6>;
+        case 8: return w2t_gemv_kernel<BF16, SPG, 8>;
+        case 9: return w2t_gemv_kernel<BF16, SPG, 9>;
+        case 12: return w2t_gemv_kernel<BF16, SPG, 12>;
+        default: return w2t_gemv_kernel<BF16, SPG, 17>;
+    }
+}
+
+template <bool BF16>
+w2_kernel_t pick2_group(int group, int upw) {
+    switch (group) {
+        case 32: return pick_upw2_kernel<BF16, 1>(upw);
+        case 64: return pick_upw2_kernel<BF16, 2>(upw);
+        case 128: return pick_upw2_kernel<BF16, 4>(upw);
+        default: return pick_upw2_kernel<BF16, 8>(upw);
+    }
+}
+
+w2_kernel_t pick2(bool bf16, int group, int upw) {
+    return bf16 ? pick2_group<true>(group, upw) : pick2_group<false>(group, upw);
+}
+
+// The staged kernel when it runs unsplit with at most this much LDS per
+// workgroup (two or more workgroups per CU), the direct-x kernel otherwise.
+constexpr size_t kStagedLdsMax = 56 * 1024;
+
+bool use_staged(const Plan2& p) { return p.upw && p.l.S == 1 && p.lds <= kStagedLdsMax; }
+
+// Allow every ternary GEMV kernel the whole LDS of a CU, once per process.
+void allow_full_lds2() {
+    static std::once_flag once;
+    std::call_once(once, [] {
+        for (int bf = 0; bf < 2; ++bf)
+            for (int g : {32, 64, 128, 256})
+                for (int u : kUpwSet2)
+                    (void)hipFuncSetAttribute((const void*)pick2(bf, g, u),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                                              (int)kLdsPerCu2);
+        (void)hipGetLastError();
+    });
 }
 
 inline unsigned grid_for(size_t work, unsigned block) {
@@ -336,6 +675,41 @@ inline unsigned grid_for(size_t work, unsigned block) {
     if (g > 65536u * 4) g = 65536u * 4;
     if (g == 0) g = 1;
     return (unsigned)g;
+}
+
+}  // namespace
+
+namespace {
+
+int launch_direct(const void* x, int x_dtype, const void* qweight, const void* scales, void* y,
+                  int y_dtype, int M, int N, int K, int group, void* workspace,
+                  size_t workspace_bytes, w4a16_stream_t stream) {
+    const PlanX p = make_planx(N, K);
+    const size_t need = p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0;
+    if (need) {
+        if (!workspace) return W4A16_ERR_NULL;
+        if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+        if (!w4h::aligned16(workspace)) return W4A16_ERR_ALIGN;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    const int T = pad_n(N) / kTileN;
+    const bool bf16 = x_dtype == W4A16_BF16;
+    w2x_kernel_t k = bf16 ? pickx<true>(group) : pickx<false>(group);
+    void* out = p.split > 1 ? workspace : y;
+    const int odt = p.split > 1 ? W4A16_F32 : y_dtype;
+    w4h::begin_launches();
+    hipLaunchKernelGGL(k, dim3(T, p.split), dim3(64 * p.waves), 0, st, (const uint16_t*)x,
+                       (const u32x4_t*)qweight, (const uint16_t*)scales, out, odt, M, N, K, p.split);
+    if (p.split > 1) {
+        const int MN = M * N;
+        hipLaunchKernelGGL(w2_merge_kernel, dim3((MN + 255) / 256), dim3(256), 0, st,
+                           (const float*)workspace, y, y_dtype, MN, p.split);
+    }
+    w4h::set_last_variant("w2t_mfma16 %s g%d kernel=w2t_gemv_direct_kernel<%s, %d, 4> tiles=%d "
+                          "slices=%d waves=%d",
+                          bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, T,
+                          p.split, p.waves);
+    return w4h::launch_status();
 }
 
 }  // namespace
@@ -408,8 +782,13 @@ extern "C" int w2t_workspace_bytes(int M, int N, int K, int group, size_t* bytes
     if (M < 1 || M > kMaxRows) return W4A16_ERR_SHAPE;
     int rc = w4h::check_w2_shape(N, K, group);
     if (rc) return rc;
-    const Plan2 p = make_plan2(N, K);
-    *bytes = p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0;
+    const Plan2 p = make_plan2(M, N, K, cu_count2());
+    if (use_staged(p)) {
+        *bytes = 0;
+    } else {
+        const PlanX px = make_planx(N, K);
+        *bytes = px.split > 1 ? (size_t)px.split * M * N * sizeof(float) : 0;
+    }
     return W4A16_OK;
 }
 
@@ -426,28 +805,32 @@ extern "C" int w2t_gemv(const void* x, int x_dtype, const void* qweight, const v
     if (!w4h::aligned16(x) || !w4h::aligned16(qweight) || !w4h::aligned16(scales) ||
         !w4h::aligned16(y))
         return W4A16_ERR_ALIGN;
-    const Plan2 p = make_plan2(N, K);
-    const size_t need = p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0;
+    Plan2 p = make_plan2(M, N, K, cu_count2());
+    if (!use_staged(p)) return launch_direct(x, x_dtype, qweight, scales, y, y_dtype, M, N, K, group,
+                                             workspace, workspace_bytes, stream);
+    const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     if (need) {
         if (!workspace) return W4A16_ERR_NULL;
         if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
         if (!w4h::aligned16(workspace)) return W4A16_ERR_ALIGN;
     }
+    allow_full_lds2();
     hipStream_t st = (hipStream_t)stream;
-    const int T = pad_n(N) / kTileN;
     const bool bf16 = x_dtype == W4A16_BF16;
-    w2_kernel_t k = bf16 ? pick2<true>(group) : pick2<false>(group);
-    void* out = p.split > 1 ? workspace : y;
-    const int odt = p.split > 1 ? W4A16_F32 : y_dtype;
+    w2_kernel_t k = pick2(bf16, group, p.upw);
+    void* out = p.l.S > 1 ? workspace : y;
+    p.l.out_dtype = p.l.S > 1 ? W4A16_F32 : y_dtype;
     w4h::begin_launches();
-    hipLaunchKernelGGL(k, dim3(T, p.split), dim3(64 * p.waves), 0, st, (const uint16_t*)x,
-                       (const u32x4_t*)qweight, (const uint16_t*)scales, out, odt, M, N, K, p.split);
-    if (p.split > 1) {
+    hipLaunchKernelGGL(k, dim3(p.tiles, p.l.S), dim3(64 * p.waves), p.lds, st, (const uint16_t*)x,
+                       (const u32x4_t*)qweight, (const uint16_t*)scales, out, p.l);
+    if (p.l.S > 1) {
         const int MN = M * N;
         hipLaunchKernelGGL(w2_merge_kernel, dim3((MN + 255) / 256), dim3(256), 0, st,
-                           (const float*)workspace, y, y_dtype, MN, p.split);
+                           (const float*)workspace, y, y_dtype, MN, p.l.S);
     }
-    w4h::set_last_variant("w2t_mfma16 %s g%d tiles=%d waves=%d split=%d depth=%d",
-                          bf16 ? "bf16" : "f16", group, T, p.waves, p.split, p.depth);
+    w4h::set_last_variant("w2t_mfma16 %s g%d kernel=w2t_gemv_kernel<%s, %d, %d> tiles=%d slices=%d "
+                          "waves=%d upw=%d lds=%zu",
+                          bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.upw,
+                          p.tiles, p.l.S, p.waves, p.upw, p.lds);
     return w4h::launch_status();
 }
