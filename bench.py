@@ -13,7 +13,12 @@ Also reported: the same sweep at M = 4 (bf16 x with 1% outliers of magnitude
 20), microseconds per call for each shape (a graph of that shape's 64 calls on
 distinct buffers, replayed; replay time / 64), the read-only bandwidth probe, a
 roofline object for the dominant kernel instantiation (the one with the most
-time in the M = 1 sweep) and the CPU oracle timed on a bounded sample.
+time in the M = 1 sweep) and the CPU oracle timed on a bounded sample.  Under
+`extra`: the skinny sweep (M in 1, 2, 3, 4, 6, 8 x group 64, 128 x K = N in
+4096, 5120, 8192, and an lm_head-like N = 152064, K = 5120) and the ternary
+variant (K = 5120, N in 7168, 34816 and K = 17408, N = 5120 at M = 1, 4, 8),
+each shape packed into enough distinct copies to span 2 GiB and timed as a
+graph over them (one fp16 x per M), each with a sampled parity check.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 
@@ -301,6 +306,102 @@ def cpu_baseline(torch, synth, oracle_mod, budget_s=12.0):
                       f"{t_total:.1f} s; GB/s over that sample"}
 
 
+ROT_BYTES = 2 << 30   # distinct copies per shape, so no shape sits in the 256 MB cache
+SKINNY_M = (1, 2, 3, 4, 6, 8)
+SKINNY_KN = (4096, 5120, 8192)
+LM_HEAD = (5120, 152064)
+TERNARY = ((5120, 7168), (5120, 34816), (17408, 5120))
+TERNARY_M = (1, 4, 8)
+
+
+def w2t_bytes(M, N, K, g, x_bytes=2, y_bytes=4):
+    """Algorithmic bytes of one ternary call: 2-bit codes + fp16 scales + x + y."""
+    return N * K // 4 + (K // g) * N * 2 + M * K * x_bytes + M * N * y_bytes
+
+
+def rotation_sweep(L, torch, synth, oracle_mod, kind, K, N, g, Ms, steps, warmup, stream, key):
+    """µs per call of one shape at each M: copies of one packed matrix spanning
+    ROT_BYTES, a graph of one call per copy, events around the replays."""
+    if kind == "w4":
+        w = synth.gen_w4_torch(key, N, K, g)
+        sizes = L.w4a16_packed_sizes(N, K, g)
+    else:
+        w = synth.gen_w2t_torch(key, N, K, g)
+        sizes = L.w2t_packed_sizes(N, K, g)
+    copies = max(2, -(-ROT_BYTES // sum(sizes)))
+    mats = []
+    for _ in range(copies):
+        bufs = [torch.empty(b, dtype=torch.uint8, device="cuda") for b in sizes]
+        if kind == "w4":
+            L.w4a16_pack(w["qweight"], w["scales"], w["zeros"], *bufs, N, K, g)
+        else:
+            L.w2t_pack(w["codes"], w["scales"], *bufs, N, K, g)
+        mats.append(bufs)
+    # The packs ran on torch's current stream; the calls below use `stream`.
+    torch.cuda.synchronize()
+    out = []
+    rng = np.random.default_rng(1)
+    for M in Ms:
+        x = synth.gen_x_torch(key + (M,), M, K, "f16")
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        if kind == "w4":
+            wsb = L.w4a16_workspace_bytes(M, N, K, g)
+        else:
+            wsb = L.w2t_workspace_bytes(M, N, K, g)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+
+        def call(bufs):
+            if kind == "w4":
+                L.w4a16_gemv(x, "f16", *bufs, y, "f32", M, N, K, g, ws, wsb, stream)
+            else:
+                L.w2t_gemv(x, "f16", *bufs, y, "f32", M, N, K, g, ws, wsb, stream)
+
+        with torch.cuda.stream(stream):
+            call(mats[0])
+        torch.cuda.synchronize()
+        variant = L.w4a16_last_variant()
+        cols = np.sort(rng.choice(N, size=min(32, N), replace=False)).astype(np.int64)
+        xh = x.cpu().numpy().view(np.uint16)
+        if kind == "w4":
+            ref = oracle_mod.w4_gemv(xh, "f16", w["qweight"].cpu().numpy(),
+                                     w["scales"].cpu().numpy().view(np.uint16),
+                                     w["zeros"].cpu().numpy(), M, N, K, g, cols=cols)
+        else:
+            ref = oracle_mod.w2t_gemv(xh, "f16", w["codes"].cpu().numpy(),
+                                      w["scales"].cpu().numpy().view(np.uint16), M, N, K, g,
+                                      cols=cols)
+        got = y.cpu().numpy().astype(np.float64)[:, cols]
+        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        mx = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+        if rel > 1e-3 or mx > 4e-3:
+            raise SystemExit(f"parity guard failed: {kind} M={M} K={K} N={N} g={g}: rel={rel:.2e}")
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for bufs in mats:
+                call(bufs)
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3 / steps / copies
+        del graph
+        b = alg_bytes(M, N, K, g) if kind == "w4" else w2t_bytes(M, N, K, g)
+        out.append({"M": M, "K": K, "N": N, "group": g, "us": round(t * 1e6, 3),
+                    "GBps": round(gbps(b, t), 1), "pct_of_peak": round(100 * gbps(b, t) / PEAK_GBPS, 2),
+                    "bytes": b, "copies": copies, "parity_rel": rel,
+                    "kernel": variant.split("kernel=")[1].split(">")[0] + ">" if "kernel=" in variant else variant})
+    del mats
+    torch.cuda.synchronize()
+    return out
+
+
 def bw_probe(L, torch, nbytes=4 << 30, reps=5):
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
@@ -345,6 +446,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m4", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the skinny-sweep and ternary measurements")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="fold two rocprofv3 counter runs of this script into "
                          "profiles/w4_gemv_traffic.json and exit (no GPU work)")
@@ -411,6 +514,29 @@ def main():
         for name, d in shapes4.items():
             log(f"  {name}: {d['us']:.2f} us/call, {d['GBps']:.0f} GB/s  [{d['variant']}]")
         del s4
+
+    if not args.no_extra:
+        steps_x, warm_x = max(5, args.steps // 2), max(2, args.warmup)
+        skinny = []
+        for kn in SKINNY_KN:
+            for g in (128, 64):
+                skinny += rotation_sweep(L, torch, synth, oracle_mod, "w4", kn, kn, g, SKINNY_M,
+                                         steps_x, warm_x, stream, (4, kn, g))
+                log(f"skinny K=N={kn} g={g}: " + ", ".join(
+                    f"M{r['M']} {r['us']:.2f}us" for r in skinny[-len(SKINNY_M):]))
+        for g in (128, 64):
+            skinny += rotation_sweep(L, torch, synth, oracle_mod, "w4", LM_HEAD[0], LM_HEAD[1], g,
+                                     SKINNY_M, steps_x, warm_x, stream, (4, 152064, g))
+            log(f"lm_head g={g}: " + ", ".join(f"M{r['M']} {r['us']:.2f}us"
+                                               for r in skinny[-len(SKINNY_M):]))
+        extra["skinny_sweep"] = skinny
+        tern = []
+        for K, N in TERNARY:
+            tern += rotation_sweep(L, torch, synth, oracle_mod, "w2t", K, N, GROUP, TERNARY_M,
+                                   steps_x, warm_x, stream, (5, K, N))
+            log(f"ternary K={K} N={N}: " + ", ".join(
+                f"M{r['M']} {r['us']:.2f}us {r['GBps']:.0f}GB/s" for r in tern[-len(TERNARY_M):]))
+        extra["ternary"] = tern
 
     probe = bw_probe(L, torch)
     extra["bw_probe_GBps"] = round(probe, 1)
