@@ -27,6 +27,7 @@ using namespace w4k;
 namespace {
 
 constexpr int kMaxRows = 16;
+constexpr int kWaves2 = 8;       // waves per workgroup of the staged ternary kernel
 
 __host__ __device__ constexpr int field_step(int p) { return (p >> 2) & 1; }
 __host__ __device__ constexpr int field_elem(int p) { return 2 * (p & 3) + (p >> 3); }
@@ -354,8 +355,17 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
     __syncthreads();
     for (int idx = threadIdx.x; idx < M * kTileN; idx += blockDim.x) {
         const int m = idx >> 4, cc = idx & 15;
+        // All W partials are read before the first add, then added in wave order.
         float v = 0.f;
-        for (int w = 0; w < W; ++w) v += red[(w * M + m) * kTileN + cc];
+        if (W == kWaves2) {
+            float pw[kWaves2];
+#pragma unroll
+            for (int w = 0; w < kWaves2; ++w) pw[w] = red[(w * M + m) * kTileN + cc];
+#pragma unroll
+            for (int w = 0; w < kWaves2; ++w) v += pw[w];
+        } else {
+            for (int w = 0; w < W; ++w) v += red[(w * M + m) * kTileN + cc];
+        }
         const int n = t * kTileN + cc;
         if (n < a.N) {
             const size_t o = (size_t)split * M * a.N + (size_t)m * a.N + n;
@@ -573,7 +583,6 @@ int cu_count2() {
 }
 
 constexpr size_t kLdsPerCu2 = 160 * 1024;      // gfx950
-constexpr int kWaves2 = 8;
 constexpr int kUpwSet2[] = {1, 2, 3, 4, 5, 6, 8, 9, 12, 17};
 
 struct Plan2 {

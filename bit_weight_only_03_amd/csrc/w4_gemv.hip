@@ -323,8 +323,18 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     for (int idx = threadIdx.x; idx < TPW * M * kTileN; idx += blockDim.x) {
         const int j = idx / (M * kTileN), rem = idx % (M * kTileN);
         const int m = rem >> 4, cc = rem & 15;
+        // All W partials are read before the first add (one LDS round trip),
+        // then added in wave order.
         float v = 0.f;
-        for (int w = 0; w < W; ++w) v += red[((j * W + w) * M + m) * kTileN + cc];
+        if (W == kMaxWaves) {
+            float pw[kMaxWaves];
+#pragma unroll
+            for (int w = 0; w < kMaxWaves; ++w) pw[w] = red[((j * kMaxWaves + w) * M + m) * kTileN + cc];
+#pragma unroll
+            for (int w = 0; w < kMaxWaves; ++w) v += pw[w];
+        } else {
+            for (int w = 0; w < W; ++w) v += red[((j * W + w) * M + m) * kTileN + cc];
+        }
         const int n = (t0 + j) * kTileN + cc;
         if (j < nt && n < a.N) {
             const size_t o = (size_t)split * M * a.N + (size_t)m * a.N + n;
@@ -338,19 +348,60 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     }
 }
 
-// y = sum over slices of the fp32 partials, in slice order.
-__global__ void splitk_merge_kernel(const float* __restrict__ ws, void* __restrict__ y,
-                                    int out_dtype, int MN, int S) {
+// y = sum over slices of the fp32 partials, in slice order.  Each thread
+// takes four consecutive outputs and issues all S loads before the first add
+// (a loop of load-then-add would wait on every slice in turn).
+__device__ __forceinline__ void store4(void* y, int out_dtype, int i4, float4_t v) {
+    if (out_dtype == W4A16_F32) {
+        ((float4_t*)y)[i4] = v;
+    } else if (out_dtype == W4A16_F16) {
+        typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+        ((half4_t*)y)[i4] = half4_t{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    } else {
+        const uint32_t lo = f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+        const uint32_t hi = f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+        ((uint2*)y)[i4] = uint2{lo, hi};
+    }
+}
+
+template <int S>
+__global__ void splitk_merge_kernel(const float4_t* __restrict__ ws, void* __restrict__ y,
+                                    int out_dtype, int MN4) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= MN) return;
-    float v = 0.f;
-    for (int s = 0; s < S; ++s) v += ws[(size_t)s * MN + i];
-    if (out_dtype == W4A16_F32)
-        ((float*)y)[i] = v;
-    else if (out_dtype == W4A16_F16)
-        ((_Float16*)y)[i] = (_Float16)v;
-    else
-        ((uint16_t*)y)[i] = f32_to_bf16_bits(v);
+    if (i >= MN4) return;
+    float4_t p[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) p[s] = ws[(size_t)s * MN4 + i];
+    float4_t v = p[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) v += p[s];
+    store4(y, out_dtype, i, v);
+}
+
+// Any slice count (only reachable through the slice override).
+__global__ void splitk_merge_any_kernel(const float4_t* __restrict__ ws, void* __restrict__ y,
+                                        int out_dtype, int MN4, int S) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= MN4) return;
+    float4_t v = ws[i];
+    for (int s = 1; s < S; ++s) v += ws[(size_t)s * MN4 + i];
+    store4(y, out_dtype, i, v);
+}
+
+typedef void (*merge_kernel_t)(const float4_t*, void*, int, int);
+
+merge_kernel_t pick_merge(int S) {
+    switch (S) {
+        case 2: return splitk_merge_kernel<2>;
+        case 3: return splitk_merge_kernel<3>;
+        case 4: return splitk_merge_kernel<4>;
+        case 5: return splitk_merge_kernel<5>;
+        case 6: return splitk_merge_kernel<6>;
+        case 7: return splitk_merge_kernel<7>;
+        case 8: return splitk_merge_kernel<8>;
+        case 16: return splitk_merge_kernel<16>;
+        default: return nullptr;
+    }
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -409,7 +460,9 @@ int pick_upw(int need) {
 }
 
 Plan make_plan(int M, int N, int K, int group, int cus) {
-    const bool group_tpw_ok = group == 128;   // multi-tile kernels are compiled for g128
+    // Multi-tile kernels are compiled for g = 64 and 128; at g = 64 they pay
+    // off only with several rows (measured on lm_head-sized layers).
+    const bool group_tpw_ok = group == 128 || (group == 64 && M >= 2);
     Plan p;
     const Tuning& tu = tuning();
     const int U = (K + kUnitK - 1) / kUnitK;
@@ -477,7 +530,7 @@ w4_kernel_t pick_small_upw(int upw) {
 template <bool BF16, int SPG>
 w4_kernel_t pick_upw_kernel(int upw, int tpw) {
     if (upw <= 6) {
-        if constexpr (SPG == 4) {
+        if constexpr (SPG == 2 || SPG == 4) {
             if (tpw == 2) return pick_small_upw<BF16, SPG, 2>(upw);
             if (tpw == 3) return pick_small_upw<BF16, SPG, 3>(upw);
             if (tpw == 4) return pick_small_upw<BF16, SPG, 4>(upw);
@@ -574,9 +627,14 @@ extern "C" int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros,
                        out, p.l);
     if (p.l.S > 1) {
-        const int MN = M * N;
-        hipLaunchKernelGGL(splitk_merge_kernel, dim3((MN + 255) / 256), dim3(256), 0, st,
-                           (const float*)workspace, y, y_dtype, MN, p.l.S);
+        const int MN4 = M * N / 4;   // N % 8 == 0
+        const dim3 grid((MN4 + 255) / 256);
+        if (merge_kernel_t mk = pick_merge(p.l.S))
+            hipLaunchKernelGGL(mk, grid, dim3(256), 0, st, (const float4_t*)workspace, y, y_dtype,
+                               MN4);
+        else
+            hipLaunchKernelGGL(splitk_merge_any_kernel, grid, dim3(256), 0, st,
+                               (const float4_t*)workspace, y, y_dtype, MN4, p.l.S);
     }
     w4h::set_last_variant("w4_mfma16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, %d> tiles=%d slices=%d "
                           "waves=%d upw=%d tpw=%d lds=%zu",

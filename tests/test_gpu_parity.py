@@ -282,14 +282,15 @@ def test_split_k_narrow_shard_parity_and_poisoned_workspace():
     assert torch.equal(P.gemv(dev(x), "bf16", M, workspace=work), y)
 
 
-@pytest.mark.parametrize("M,K,xdt", [(1, 1152, "f16"), (8, 1152, "bf16"), (3, 640, "f16"),
-                                       (16, 256, "bf16")])
-def test_multi_tile_workgroups_ragged(M, K, xdt):
+@pytest.mark.parametrize("M,K,g,xdt", [(1, 1152, 128, "f16"), (8, 1152, 128, "bf16"),
+                                         (3, 640, 128, "f16"), (16, 256, 128, "bf16"),
+                                         (2, 1152, 64, "f16"), (4, 640, 64, "bf16")])
+def test_multi_tile_workgroups_ragged(M, K, g, xdt):
     # Many more tiles than the GPU holds at once: each workgroup takes three
     # tiles, and 1537 tiles leave a last workgroup with a single one.
-    N, g = 24592, 128
-    say(f"multi-tile M={M} N={N} K={K} x={xdt}")
-    key = (113, M, K)
+    N = 24592
+    say(f"multi-tile M={M} N={N} K={K} g={g} x={xdt}")
+    key = (113, M, K, g)
     w = synth.gen_w4(key, N, K, g)
     x = synth.gen_x(key, M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
     P = PackedW4(w, N, K, g)
