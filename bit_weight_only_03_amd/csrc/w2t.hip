@@ -28,6 +28,7 @@ namespace {
 
 constexpr int kMaxRows = 16;
 constexpr int kWaves2 = 8;       // waves per workgroup of the staged ternary kernel
+constexpr int kMaxXLoads2 = 17;  // x load instructions per wave: M * (32 UPW + 1) <= 64 * 17
 
 __host__ __device__ constexpr int field_step(int p) { return (p >> 2) & 1; }
 __host__ __device__ constexpr int field_elem(int p) { return 2 * (p & 3) + (p >> 3); }
@@ -188,7 +189,7 @@ constexpr int min_waves2() { return SPG >= 4 && UPW <= 4 ? 8 : 1; }
 // The ternary GEMV has the same structure as the 4-bit one: one workgroup per
 // (16-column tile, K slice), W waves splitting the slice's 256-k units into
 // contiguous ranges of at most UPW units; each wave stages its own x range in
-// its own LDS region, issues the weight and scale loads of its units up front
+// its own LDS region (straight into LDS), issues the weight and scale loads of its units up front
 // (or D of them and one refill per consumed slot, straight-line), and
 // dequantizes and multiplies each unit as its slot arrives; the waves then add
 // their partial sums through LDS in wave order.
@@ -223,41 +224,35 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
     uint16_t* xs = (uint16_t*)smem + (size_t)wave * M * a.xstride;
     float* red = (float*)(smem + (size_t)W * M * a.xstride * 2);
 
-    // 1) x range -> LDS, four 16-byte chunks per lane at a time (the planner
-    //    keeps M * UPW <= 32, so at most 16 chunks per lane).
+    // 1) x range -> this wave's LDS region, straight from memory into LDS in
+    //    one round trip (the 4-bit kernel's scheme: lane l of load i fills
+    //    chunk 64 i + l of the padded region; pad chunks skipped, chunks past
+    //    K zeroed; x staging is the wave's first memory access).
     {
-        const int cpr = nu * (kUnitK2 / 8);   // 16-byte chunks per row
+        const int cpr = a.xstride / 8;
+        const int live = nu * (kUnitK2 / 8);         // chunks of a row this wave reads
         const int xch = M * cpr;
         const uint32_t xbytes = (uint32_t)M * (uint32_t)K * 2u;
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xbytes);
+        uint8_t* xsb = (uint8_t*)xs;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            if (b * 256 < xch) {             // wave-uniform
-                u32x4_t xv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ii = 4 * b + i;
-                    if (ii * 64 < xch) {     // wave-uniform; a real branch, not dummy loads
-                        asm volatile("" ::: "memory");
-                        const int ci = ii * 64 + lane;
-                        const int m = ci / cpr, kk = (ci % cpr) * 8;
-                        const int kg = w0 * kUnitK2 + kk;
-                        const uint32_t off = (ci < xch && kg < K) ? (uint32_t)(m * K + kg) * 2u : xbytes;
-                        xv[i] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ci = (4 * b + i) * 64 + lane;
-                    if ((4 * b + i) * 64 < xch && ci < xch) {
-                        const int m = ci / cpr, kk = (ci % cpr) * 8;
-                        *(u32x4_t*)(xs + m * a.xstride + kk) = xv[i];
-                    }
+        for (int i = 0; i < kMaxXLoads2; ++i) {
+            if (i * 64 < xch) {                    // wave-uniform
+                const int ci = i * 64 + lane;
+                const int m = ci / cpr, kk = (ci % cpr) * 8;
+                const int kg = w0 * kUnitK2 + kk;
+                if (m < M && kk < live * 8) {
+                    if (kg < K)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rx, (__attribute__((address_space(3))) void*)(xsb + i * 1024), 16,
+                            (uint32_t)(m * K + kg) * 2u, 0, 0, 0);
+                    else
+                        *(u32x4_t*)(xsb + (uint32_t)ci * 16u) = u32x4_t{0u, 0u, 0u, 0u};
                 }
             }
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    // Weight loads must not be hoisted above the x stores.
     __builtin_amdgcn_sched_barrier(0);
 
     // 2) Weight and scale loads of this wave's units.

@@ -53,6 +53,7 @@ namespace {
 
 constexpr int kMaxWaves = 8;     // waves per workgroup (the kernel's 512-thread launch bound)
 constexpr int kMaxRows = 16;     // rows per MFMA
+constexpr int kMaxXLoads = 17;   // x load instructions per wave: M * (16 UPW + 1) <= 64 * 17
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return bitcast<half2_t>(v); }
 __device__ __forceinline__ uint32_t as_u(half2_t v) { return bitcast<uint32_t>(v); }
@@ -117,7 +118,8 @@ constexpr int max_slots() { return SPG >= 4 ? 9 : (SPG == 2 ? 7 : 5); }
 // One workgroup per (TPW 16-column tiles, K slice); its W waves split the
 // slice's 128-k units into contiguous ranges of at most UPW units.  Each wave
 //   1. stages its own range of x (all M rows, zeros past K) in its own LDS
-//      region -- no other wave's x is on its critical path;
+//      region, loading it straight into LDS in one round trip -- no other
+//      wave's x is on its critical path;
 //   2. issues the loads of its chain of TPW x UPW units (16 weight bytes,
 //      scale and zero point per lane; unit-major, so one x fragment serves
 //      the TPW tiles back to back) -- all of them up front when the chain
@@ -168,45 +170,39 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     uint16_t* xs = (uint16_t*)smem + (size_t)wave * M * a.xstride;
     float* red = (float*)(smem + (size_t)W * M * a.xstride * 2);
 
-    // 1) x range -> LDS.  At most 16 chunks of 16 bytes per lane (the planner
-    //    keeps M * UPW <= 64); the loads go first so the wait for them never
-    //    waits on weight loads.
+    // 1) x range -> this wave's LDS region, straight from memory into LDS
+    //    (no VGPRs, one round trip whatever M is).  Chunk ci of the padded
+    //    region [M][xstride / 8 chunks of 16 bytes] is row ci / cpr, chunk
+    //    ci % cpr; one load instruction fills 64 consecutive chunks (lane l ->
+    //    chunk 64 i + l).  Pad chunks are skipped; chunks past K (a ragged
+    //    last unit) are zeroed with ordinary LDS stores.  x staging is the
+    //    wave's first memory access, so waiting for every load in flight
+    //    waits for exactly these.
     {
-        const int cpr = nu * (kUnitK / 8);   // 16-byte chunks per row
+        const int cpr = a.xstride / 8;
+        const int live = nu * (kUnitK / 8);          // chunks of a row this wave reads
         const int xch = M * cpr;
         const uint32_t xbytes = (uint32_t)M * (uint32_t)K * 2u;
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xbytes);
-        // Four chunks per lane at a time keep only 16 VGPRs of x live; M = 1
-        // needs a single batch for up to 16 units per wave.
+        uint8_t* xsb = (uint8_t*)xs;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            if (b * 256 < xch) {             // wave-uniform
-                u32x4_t xv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ii = 4 * b + i;
-                    if (ii * 64 < xch) {     // wave-uniform; a real branch, not dummy loads
-                        asm volatile("" ::: "memory");
-                        const int ci = ii * 64 + lane;
-                        const int m = ci / cpr, kk = (ci % cpr) * 8;
-                        const int kg = w0 * kUnitK + kk;
-                        const uint32_t off = (ci < xch && kg < K) ? (uint32_t)(m * K + kg) * 2u : xbytes;
-                        xv[i] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ci = (4 * b + i) * 64 + lane;
-                    if ((4 * b + i) * 64 < xch && ci < xch) {
-                        const int m = ci / cpr, kk = (ci % cpr) * 8;
-                        *(u32x4_t*)(xs + m * a.xstride + kk) = xv[i];
-                    }
+        for (int i = 0; i < kMaxXLoads; ++i) {
+            if (i * 64 < xch) {                    // wave-uniform
+                const int ci = i * 64 + lane;
+                const int m = ci / cpr, kk = (ci % cpr) * 8;
+                const int kg = w0 * kUnitK + kk;
+                if (m < M && kk < live * 8) {
+                    if (kg < K)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rx, (__attribute__((address_space(3))) void*)(xsb + i * 1024), 16,
+                            (uint32_t)(m * K + kg) * 2u, 0, 0, 0);
+                    else
+                        *(u32x4_t*)(xsb + (uint32_t)ci * 16u) = u32x4_t{0u, 0u, 0u, 0u};
                 }
             }
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    // Weight loads must not be hoisted above the x stores (loads return in
-    // issue order, so the stores would then wait for the weights as well).
     __builtin_amdgcn_sched_barrier(0);
 
     // 2) Weight / scale / zero-point loads of this wave's units.
