@@ -227,7 +227,9 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
     // 1) x range -> this wave's LDS region, straight from memory into LDS in
     //    one round trip (the 4-bit kernel's scheme: lane l of load i fills
     //    chunk 64 i + l of the padded region; pad chunks skipped, chunks past
-    //    K zeroed; x staging is the wave's first memory access).
+    //    K zeroed).  These are the wave's first memory accesses; where its
+    //    arithmetic is unconditional it waits for them after issuing its
+    //    weight ring, so the round trips overlap.
     {
         const int cpr = a.xstride / 8;
         const int live = nu * (kUnitK2 / 8);         // chunks of a row this wave reads
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
                 }
             }
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (!kUncond) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -279,6 +281,12 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
         load_slot(i, ring[i]);
         __builtin_amdgcn_sched_barrier(0);   // slots issue in ring order
     }
+    // Loads complete in issue order: with at most the ring's D * (1 + NG)
+    // loads outstanding, the x loads issued before them have landed -- as
+    // long as every ring load is issued here, which holds only where the
+    // arithmetic is unconditional (as in the 4-bit kernel).
+    if constexpr (kUncond) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D * (1 + NG)) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
 
     // 3) Dequantize and multiply, unit by unit, two 32-k steps per dword.
     const bool xrow = c < M;                                    // lane supplies x row c

@@ -117,9 +117,9 @@ constexpr int max_slots() { return SPG >= 4 ? 9 : (SPG == 2 ? 7 : 5); }
 
 // One workgroup per (TPW 16-column tiles, K slice); its W waves split the
 // slice's 128-k units into contiguous ranges of at most UPW units.  Each wave
-//   1. stages its own range of x (all M rows, zeros past K) in its own LDS
-//      region, loading it straight into LDS in one round trip -- no other
-//      wave's x is on its critical path;
+//   1. starts staging its own range of x (all M rows, zeros past K) in its
+//      own LDS region, loading it straight into LDS -- no other wave's x is
+//      on its critical path;
 //   2. issues the loads of its chain of TPW x UPW units (16 weight bytes,
 //      scale and zero point per lane; unit-major, so one x fragment serves
 //      the TPW tiles back to back) -- all of them up front when the chain
@@ -175,9 +175,10 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     //    region [M][xstride / 8 chunks of 16 bytes] is row ci / cpr, chunk
     //    ci % cpr; one load instruction fills 64 consecutive chunks (lane l ->
     //    chunk 64 i + l).  Pad chunks are skipped; chunks past K (a ragged
-    //    last unit) are zeroed with ordinary LDS stores.  x staging is the
-    //    wave's first memory access, so waiting for every load in flight
-    //    waits for exactly these.
+    //    last unit) are zeroed with ordinary LDS stores.  These are the
+    //    wave's first memory accesses; where its arithmetic is unconditional
+    //    the wave waits for them only after issuing its weight ring (below),
+    //    so the two round trips overlap.
     {
         const int cpr = a.xstride / 8;
         const int live = nu * (kUnitK / 8);          // chunks of a row this wave reads
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
                 }
             }
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (!kUncond) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -238,6 +239,16 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
         load_slot(i, ring[i]);
         __builtin_amdgcn_sched_barrier(0);   // slots issue in ring order
     }
+    // Vector memory loads complete in issue order, so once no more than the
+    // ring's D * (1 + 2 NG) loads are outstanding, every x load issued before
+    // them has landed in LDS.  This needs every ring load issued here, after
+    // the x loads: the weight loads count as invariant, so the compiler may
+    // sink a slot's loads into a conditional block that uses them, and then
+    // the wait falls short.  Hence the overlap only where the arithmetic is
+    // unconditional (elsewhere the wait above, after the x loads, covers
+    // them); a host-side test checks the compiled kernels for this.
+    if constexpr (kUncond) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D * (1 + 2 * NG)) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
 
     // 3) Dequantize and multiply, unit by unit.
     const int zshift = 4 * (c & 7);

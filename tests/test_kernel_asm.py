@@ -1,0 +1,101 @@
+"""Host-side checks of the gfx950 assembly the GEMV kernels compile to.
+
+The staging kernels load their x range straight into LDS and only then issue
+their weight ring; one explicit `s_waitcnt vmcnt(N)` (N = the ring's load
+count) then waits for the x loads alone, relying on vector memory loads
+completing in issue order.  The compiler does not track LDS writes made by
+such loads, so nothing else guards that wait: it is only correct if at least
+N vector memory loads are issued, in straight-line code, between the last x
+load and the wait, and if no LDS read comes before it.  This test compiles
+the kernel sources to assembly and checks that for every instantiation.
+"""
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "bit_weight_only_03_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+SOURCES = ["w4_gemv.hip", "w2t.hip"]
+
+pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+
+
+def compile_asm(src, out):
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           f"-I{CSRC}", "-o", out, os.path.join(CSRC, src)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return out
+
+
+@pytest.fixture(scope="module")
+def asm_files():
+    d = tempfile.mkdtemp(prefix="w4asm")
+    try:
+        with ThreadPoolExecutor(len(SOURCES)) as ex:
+            outs = list(ex.map(lambda s: compile_asm(s, os.path.join(d, s + ".s")), SOURCES))
+        yield {s: open(o).read() for s, o in zip(SOURCES, outs)}
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+
+
+def functions(text):
+    for m in re.finditer(r"^(_Z\w+):", text, re.M):
+        end = text.index(".Lfunc_end", m.start())
+        yield m.group(1), [l.strip() for l in text[m.start():end].split("\n") if l.strip()]
+
+
+def is_vmem_load(line):
+    return re.match(r"(buffer|global)_load", line) is not None
+
+
+def check_x_wait(lines):
+    """Returns None if the function's explicit x wait is safe, else a reason."""
+    waits = [i for i, l in enumerate(lines)
+             if re.fullmatch(r"s_waitcnt vmcnt\(\d+\)", l) and lines[i - 1].startswith(";;#ASMSTART")]
+    if len(waits) != 1:
+        return f"{len(waits)} explicit vmcnt waits"
+    w = waits[0]
+    n = int(re.search(r"\((\d+)\)", lines[w]).group(1))
+    # Walk back from the wait through straight-line code: the n most recent
+    # vector memory loads on every path into the wait must be ring loads.
+    count = 0
+    for line in reversed(lines[:w]):
+        if count >= n:
+            break
+        if line.startswith(";"):
+            continue
+        if is_vmem_load(line):
+            if " lds" in line:
+                return f"only {count} loads between the last x load and vmcnt({n})"
+            count += 1
+        elif line.endswith(":") or line.startswith(("s_cbranch", "s_branch", "s_setpc")):
+            return f"control flow after only {count} of {n} ring loads ({line})"
+    if count < n:
+        return f"only {count} loads before vmcnt({n})"
+    if any(l.startswith("ds_read") for l in lines[:w]):
+        return "an LDS read precedes the x wait"
+    return None
+
+
+def test_x_wait_covers_the_x_loads(asm_files):
+    checked = 0
+    bad = []
+    for src, text in asm_files.items():
+        for name, lines in functions(text):
+            if not any(is_vmem_load(l) and " lds" in l for l in lines):
+                continue            # no LDS-direct x staging in this kernel
+            checked += 1
+            why = check_x_wait(lines)
+            if why:
+                bad.append(f"{src} {name}: {why}")
+    # every 4-bit and staged ternary instantiation stages x this way
+    assert checked >= 150, checked
+    assert not bad, "\n".join(bad[:20])
