@@ -169,7 +169,7 @@ class Sweep:
         self.bytes = sum(alg_bytes(M, N, K, GROUP) for (_, _, K, N, _) in self.mats_meta)
         # One workspace serves every call: calls on one stream run one after another.
         self.ws_bytes = max(L.w4a16_workspace_bytes(M, N, K, GROUP) for (_, _, K, N, _) in self.mats)
-        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda") if self.ws_bytes else None
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device="cuda") if self.ws_bytes else None
 
     @property
     def mats_meta(self):
@@ -348,7 +348,7 @@ def rotation_sweep(L, torch, synth, oracle_mod, kind, K, N, g, Ms, steps, warmup
             wsb = L.w4a16_workspace_bytes(M, N, K, g)
         else:
             wsb = L.w2t_workspace_bytes(M, N, K, g)
-        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
 
         def call(bufs):
             if kind == "w4":

@@ -33,6 +33,11 @@ def empty_bytes(n: int) -> torch.Tensor:
     return torch.empty(max(n, 16), dtype=torch.uint8, device=DEV)
 
 
+def workspace_bytes(n: int) -> torch.Tensor:
+    """A GEMV workspace: zero-filled before first use, as the library requires."""
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=DEV)
+
+
 class PackedW4:
     """A 4-bit matrix packed on the device with w4a16_pack."""
 
@@ -49,7 +54,7 @@ class PackedW4:
         y = torch.empty((M, self.N), dtype=ydt, device=DEV)
         ws_bytes = L.w4a16_workspace_bytes(M, self.N, self.K, self.group)
         if ws_bytes and workspace is None:
-            workspace = empty_bytes(ws_bytes)
+            workspace = workspace_bytes(ws_bytes)
         L.w4a16_gemv(x, x_dtype, self.q, self.s, self.z, y, y_dtype, M, self.N, self.K,
                      self.group, workspace, workspace.numel() if workspace is not None else 0)
         return y
@@ -69,7 +74,7 @@ class PackedW2T:
         ydt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[y_dtype]
         y = torch.empty((M, self.N), dtype=ydt, device=DEV)
         ws_bytes = L.w2t_workspace_bytes(M, self.N, self.K, self.group)
-        ws = empty_bytes(ws_bytes) if ws_bytes else None
+        ws = workspace_bytes(ws_bytes) if ws_bytes else None
         L.w2t_gemv(x, x_dtype, self.q, self.s, y, y_dtype, M, self.N, self.K, self.group, ws,
                    ws_bytes)
         return y

@@ -20,7 +20,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 import bit_weight_only_03_amd as L  # noqa: E402
-from gpu_util import (PackedW2T, PackedW4, assert_parity, dev, empty_bytes, host_bits,  # noqa: E402
+from gpu_util import (DEV, PackedW2T, PackedW4, assert_parity, dev, empty_bytes, host_bits,  # noqa: E402
                       to_f64)
 
 
@@ -280,6 +280,65 @@ def test_split_k_narrow_shard_parity_and_poisoned_workspace():
     assert_parity(to_f64(y), ref, "split-K")
     work.view(torch.float32)[:] = float("inf")
     assert torch.equal(P.gemv(dev(x), "bf16", M, workspace=work), y)
+
+
+def test_split_k_workspace_reused_across_shapes_and_graph_replays():
+    # One workspace, sized for the largest call and poisoned beforehand,
+    # serves a sequence of split calls of different shapes and slice counts
+    # on one stream, also inside a graph replayed many times with eager calls
+    # through the same workspace in between.  The ternary GEMV's split path
+    # (the direct-x kernel) follows the same contract.
+    cases = [(1, 640, 17408, 128, "f16"), (4, 2048, 8192, 64, "bf16"), (3, 1024, 12288, 128, "f16"),
+             (2, 640, 17408, 128, "bf16")]
+    packs, xs, refs, sizes = [], [], [], []
+    for i, (M, N, K, g, xdt) in enumerate(cases):
+        w = synth.gen_w4((115, i), N, K, g)
+        x = synth.gen_x((115, i), M, K, xdt)
+        packs.append(PackedW4(w, N, K, g))
+        xs.append(dev(x))
+        refs.append(oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g))
+        sizes.append(L.w4a16_workspace_bytes(M, N, K, g))
+    assert all(b > 0 for b in sizes), sizes
+    M2, N2, K2, g2 = 8, 640, 17408, 128          # the ternary call at the end
+    wsb2 = L.w2t_workspace_bytes(M2, N2, K2, g2)
+    assert wsb2 > 0
+    work = empty_bytes(max(sizes + [wsb2]))
+    work.view(torch.float32)[:] = float("nan")
+    ys = [torch.empty((M, N), dtype=torch.float32, device=DEV) for (M, N, _, _, _) in cases]
+    s = torch.cuda.Stream()
+
+    def run_all():
+        for (M, N, K, g, xdt), P, x, y in zip(cases, packs, xs, ys):
+            L.w4a16_gemv(x, xdt, P.q, P.s, P.z, y, "f32", M, N, K, g, work, work.numel(), stream=s)
+
+    with torch.cuda.stream(s):
+        run_all()
+    torch.cuda.synchronize()
+    first = [y.clone() for y in ys]
+    for (M, N, K, g, xdt), y, ref in zip(cases, first, refs):
+        assert_parity(to_f64(y), ref, f"shared workspace M={M} N={N} K={K} g={g}")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        run_all()
+    for r in range(8):
+        for y in ys:
+            y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for y, y0 in zip(ys, first):
+            assert torch.equal(y, y0), f"replay {r}"
+        M, N, K, g, xdt = cases[1]
+        assert torch.equal(packs[1].gemv(xs[1], xdt, M, workspace=work), first[1])
+    M, N, K, g = M2, N2, K2, g2
+    w2 = synth.gen_w2t((116,), N, K, g)
+    x2 = synth.gen_x((116,), M, K, "f16")
+    P2 = PackedW2T(w2, N, K, g)
+    y2 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    L.w2t_gemv(dev(x2), "f16", P2.q, P2.s, y2, "f32", M, N, K, g, work, work.numel())
+    torch.cuda.synchronize()
+    assert "slices=1 " not in L.w4a16_last_variant()
+    assert_parity(to_f64(y2), oracle.w2t_gemv(x2, "f16", w2["codes"], w2["scales"], M, N, K, g),
+                  "ternary split, shared workspace")
 
 
 @pytest.mark.parametrize("M,K,g,xdt", [(1, 1152, 128, "f16"), (8, 1152, 128, "bf16"),
