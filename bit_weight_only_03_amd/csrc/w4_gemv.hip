@@ -496,6 +496,12 @@ Plan make_plan(int M, int N, int K, int group, int cus) {
     // slice (a split with too little k per slice loses: NINFER tuning page,
     // section 五, item 21).
     while ((long long)T * S < cus && U / (2 * S) >= 2 * W && fits(2 * S, upw, lds, xstride)) S *= 2;
+    // A shape whose x range forces a split pays the merge anyway; on a small
+    // grid one more halving of the slices (each wave keeping at least four
+    // units) spreads the work more evenly: the 27B down shape at M = 4 runs
+    // 17.9 us at two slices and 17.0 us at four.
+    if (S > 1 && (long long)T * S < 4LL * cus && U / (2 * S) >= 4 * W && fits(2 * S, upw, lds, xstride))
+        S *= 2;
     if (tu.split >= 1 && tu.split <= U) S = tu.split;
     if (!fits(S, upw, lds, xstride)) upw = 0;   // an override that cannot run is refused
     p.l = GemvLaunch{M, N, K, U, S, T, xstride, W4A16_F32};
