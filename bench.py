@@ -308,6 +308,7 @@ def cpu_baseline(torch, synth, oracle_mod, budget_s=12.0):
 
 ROT_BYTES = 2 << 30   # distinct copies per shape, so no shape sits in the 256 MB cache
 SKINNY_M = (1, 2, 3, 4, 6, 8)
+BATCH_M = (16, 32, 64)            # rows of the batch sweeps (M-tiled kernel)
 SKINNY_KN = (4096, 5120, 8192)
 LM_HEAD = (5120, 152064)
 TERNARY = ((5120, 7168), (5120, 34816), (17408, 5120))
@@ -516,6 +517,26 @@ def main():
         del s4
 
     if not args.no_extra:
+        # Several rows at once (a batch of decode tokens): the same 64 layers
+        # at M = 16, 32 and 64, which the M-tiled kernel serves.
+        batch = []
+        for mb in BATCH_M:
+            sb = Sweep(L, torch, synth, mb, "f16", outliers=False, mats=s1.mats)
+            sb.run_all(stream)
+            torch.cuda.synchronize()
+            wb = parity_guard(L, torch, synth, oracle_mod, sb)
+            gb = sb.capture(stream)
+            tb = sb.time_graph(gb, stream, args.steps, args.warmup)
+            del gb
+            shb = sb.per_shape(stream, args.steps, args.warmup)
+            batch.append({"M": mb, "ms_per_step": round(tb * 1e3, 4), "tokens_per_s": round(mb / tb, 1),
+                          "GBps": round(gbps(sb.bytes, tb), 1), "bytes": sb.bytes,
+                          "parity_worst_rel": wb, "per_shape": shb})
+            log(f"M={mb} sweep (fp16 x): {tb * 1e3:.4f} ms/step, {mb / tb:.0f} tokens/s, "
+                f"{gbps(sb.bytes, tb):.1f} GB/s; " + ", ".join(
+                    f"{k} {d['us']:.1f}us" for k, d in shb.items()))
+            del sb
+        extra["batch_sweeps"] = batch
         steps_x, warm_x = max(5, args.steps // 2), max(2, args.warmup)
         skinny = []
         for kn in SKINNY_KN:

@@ -66,10 +66,60 @@ __host__ __device__ inline uint16_t f32_to_bf16_bits(float f) {
     return (uint16_t)(b >> 16);
 }
 
+// y[o] = v in the output dtype (f32, f16, or bf16 rounded to nearest even).
+__device__ __forceinline__ void store_out(void* out, int out_dtype, size_t o, float v) {
+    if (out_dtype == W4A16_F32)
+        ((float*)out)[o] = v;
+    else if (out_dtype == W4A16_F16)
+        ((_Float16*)out)[o] = (_Float16)v;
+    else
+        ((uint16_t*)out)[o] = f32_to_bf16_bits(v);
+}
+
 // Streamed, read-once loads: non-temporal so the weights do not evict x and
 // the scales from the caches.
 __device__ __forceinline__ u32x4_t load_nt(const u32x4_t* p) {
     return __builtin_nontemporal_load(p);
+}
+
+__device__ __forceinline__ half2_t as_h2(uint32_t v) { return bitcast<half2_t>(v); }
+__device__ __forceinline__ uint32_t as_u(half2_t v) { return bitcast<uint32_t>(v); }
+
+// (a & mask) | (b & ~mask) in one v_bfi_b32.  The magic exponents below never
+// overlap the nibble masks, so bfi(mask, d, magic) = (d & mask) | magic.
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(mask), "v"(a), "v"(b));
+    return r;
+}
+
+// Dequantization in registers, shared by the GEMV and the M-tiled kernel.
+// The device dword of a lane holds 8 nibbles; a half pair takes nibbles
+// (0, 4), (1, 5), (2, 6), (3, 7), which the pack kernel places at the k
+// positions the MFMA B operand expects.
+//
+// B operand (8 fp16 = q - z, exact) for the 8 weights of one device dword.
+__device__ __forceinline__ half8_t dequant_f16(uint32_t d, uint32_t magic, uint32_t nz1024,
+                                               uint32_t nz64) {
+    const half2_t sixteenth = as_h2(0x2C002C00u);  // fp16 1/16
+    const uint32_t t = d >> 8;
+    const uint32_t p0 = bfi(0x000F000Fu, d, magic);  // 1024 + q   (elements 0, 1)
+    const uint32_t p1 = bfi(0x00F000F0u, d, magic);  // 1024 + 16q (elements 2, 3)
+    const uint32_t p2 = bfi(0x000F000Fu, t, magic);  // 1024 + q   (elements 4, 5)
+    const uint32_t p3 = bfi(0x00F000F0u, t, magic);  // 1024 + 16q (elements 6, 7)
+    const half2_t w0 = as_h2(p0) + as_h2(nz1024);
+    const half2_t w1 = __builtin_elementwise_fma(as_h2(p1), sixteenth, as_h2(nz64));
+    const half2_t w2 = as_h2(p2) + as_h2(nz1024);
+    const half2_t w3 = __builtin_elementwise_fma(as_h2(p3), sixteenth, as_h2(nz64));
+    u32x4_t v = {as_u(w0), as_u(w1), as_u(w2), as_u(w3)};
+    return bitcast<half8_t>(v);
+}
+
+// B operand (8 bf16 = 128 + q, exact) for the 8 weights of one device dword.
+__device__ __forceinline__ bf16x8_t biased_bf16(uint32_t d, uint32_t magic) {
+    u32x4_t v = {bfi(0x000F000Fu, d, magic), bfi(0x000F000Fu, d >> 4, magic),
+                 bfi(0x000F000Fu, d >> 8, magic), bfi(0x000F000Fu, d >> 12, magic)};
+    return bitcast<bf16x8_t>(v);
 }
 
 // Raw buffer resources: a wave-uniform 128-bit descriptor (base, byte size)
@@ -124,5 +174,19 @@ inline int launch_status() {
     set_last_error(hipGetErrorName(e));
     return W4A16_ERR_HIP;
 }
+
+// The M-tiled path (w4_gemm.hip) for rows the GEMV does not take.
+constexpr int kMaxRowsGemm = 64;
+constexpr int kMaxSplitGemm = 16;
+struct GemmPlan {
+    int rb;                 // 16-row blocks
+    int tn;                 // 16-column tiles per wave
+    int split;              // K slices
+    long long workgroups;   // tile columns of workgroups (grid x)
+};
+GemmPlan gemm_plan(int M, int N, int K, int group, int cus);
+int gemm_launch(const GemmPlan& p, const void* x, bool bf16, const void* qweight, const void* scales,
+                const void* zeros, void* y, int y_dtype, int M, int N, int K, int group,
+                void* workspace, hipStream_t st);
 
 }  // namespace w4h

@@ -1,0 +1,311 @@
+// w4_gemm.hip -- the M-tiled path of y[M,N] = x[M,K] . ((q - z) * s)[K,N] on
+// gfx950, for up to 64 activation rows (several tokens of a batch or several
+// speculative drafts at once).
+//
+// The GEMV kernel gives each wave a range of K and stages that range of x
+// per wave, so its LDS holds M x K halves per workgroup: fine for a few rows,
+// impossible at M = 64 (655 KB for K = 5120).  Here the roles turn around.
+// Each wave owns TN 16-column tiles over the workgroup's whole K range, and
+// the workgroup streams x through LDS one 128-k unit at a time, shared by all
+// its waves (double-buffered: the next unit is loaded while the current one
+// is multiplied, one barrier per unit).  Every weight is still read from HBM
+// once and dequantized once per call (the Z100 article, section 五: dequantize
+// once, use for every row), then multiplied with up to four 16-row blocks of
+// x: one v_mfma_f32_16x16x32 per row block and 32-k step.  The crossover
+// against the GEMV kernel (which dispatches which rows) is measured, not
+// assumed (NINFER ternary tuning page, sections 五 and 七: the small-T ladder
+// rungs were placed by measurement).
+//
+// Weights, scales and zero points use the device layout of w4_pack and the
+// same register dequantization as the GEMV (common.h).  Partials of a K split
+// go to the caller's workspace [S][M][N] and are added in slice order by the
+// GEMV file's merge kernel.
+#include <stdlib.h>
+
+#include "common.h"
+
+using namespace w4k;
+
+namespace {
+
+constexpr int kGemmWaves = 4;             // waves per workgroup
+// Units of weight loads in flight per wave (even).  Four, or a guard that
+// skips the tail units of the last ring turn, measured slower (gate_up at
+// M = 64: 57 us with two, 70 us with four, 61 us guarded).
+constexpr int kRing = 2;
+constexpr int kXStride = kUnitK + 8;      // halves per staged x row (+16 B spreads rows over banks)
+
+struct GemmLaunch {
+    int M, N, K;
+    int U;   // 128-k units per column (K rounded up)
+    int S;   // K slices
+    int T;   // 16-column tiles
+    int out_dtype;
+};
+
+// A unit's loads for one tile: 16 weight bytes per lane, plus the scale and
+// zero-point words of the groups the unit touches.
+template <int NG>
+struct GSlot {
+    u32x4_t w;
+    uint32_t s[NG];
+    uint32_t z[NG];
+};
+
+// One workgroup per (4 x TN tiles, K slice).  Wave w owns tiles
+// [t0 + w TN, t0 + (w + 1) TN).  Per 128-k unit u of the slice:
+//   - all threads have staged x[0:M, u's 128 k] in LDS buffer u % 2 (zeros
+//     past K; rows >= M are never staged, their outputs never stored);
+//   - every wave multiplies its tiles' unit u, whose loads were issued kRing
+//     units earlier (a ring of kRing units per tile), while the loads of
+//     unit u+1's x are in flight; then it stores that x into the other
+//     buffer and the workgroup meets at a barrier.
+// Units past the slice (and tiles past N) load as zeros -- q = z = 0, s = +0 --
+// and add exactly 0 against the finite x, so the loop body is uniform.
+template <bool BF16, int SPG, int RB, int TN>
+__global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict__ x,
+                                                      const u32x4_t* __restrict__ qdev,
+                                                      const uint16_t* __restrict__ sdev,
+                                                      const uint32_t* __restrict__ zdev,
+                                                      void* __restrict__ out, GemmLaunch a) {
+    constexpr int NG = SPG >= 4 ? 1 : 4 / SPG;    // groups per unit
+    constexpr int SPU = SPG >= 4 ? 4 : SPG;       // 32-k steps per group inside one unit
+    constexpr int ROWS = 16 * RB;
+    constexpr int XCH = ROWS * (kUnitK / 8);      // 16-byte chunks of one staged unit
+    constexpr int XPT = (XCH + 255) / 256;        // chunks per thread
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][ROWS][kXStride];
+
+    const int M = a.M, N = a.N, K = a.K, U = a.U, T = a.T;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int c = lane & 15, kc = lane >> 4;
+    const int split = blockIdx.y;
+    const int r0 = split * U / a.S, r1 = (split + 1) * U / a.S;          // the slice's units
+    const int nu = r1 - r0;
+    const int tw = (blockIdx.x * kGemmWaves + wave) * TN;                // the wave's first tile
+    const int nt = T - tw < 0 ? 0 : (T - tw < TN ? T - tw : TN);         // its tiles inside N
+    const int Gp = U * kUnitK / (SPG * 32);
+
+    // Buffer resources over the wave's tiles; a missing unit or tile takes an
+    // offset at the resource's end, so each of its lanes reads zeros.
+    const uint32_t wend = (uint32_t)nt * U * 1024u, send = (uint32_t)nt * Gp * 32u,
+                   zend = (uint32_t)nt * Gp * 8u;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qdev + (size_t)tw * U * kLanes, wend);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdev + (size_t)tw * Gp * kTileN, send);
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(zdev + (size_t)tw * Gp * 2, zend);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    const uint32_t wlane = (uint32_t)lane * 16u, slane = (uint32_t)c * 2u,
+                   zlane = (uint32_t)(c >> 3) * 4u;
+
+    auto load_unit = [&](int i, GSlot<NG> (&r)[TN]) {   // unit r0 + i of every tile
+        const int u = r0 + i;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const bool valid = i < nu && j < nt;
+            r[j].w = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
+                rw, valid ? wlane + (uint32_t)(j * U + u) * 1024u : wend, 0, kAuxNT));
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const int g = j * Gp + (u * 4) / SPG + gi;
+                r[j].s[gi] = __builtin_amdgcn_raw_buffer_load_b16(
+                    rs, valid ? slane + (uint32_t)g * 32u : send, 0, 0);
+                r[j].z[gi] = __builtin_amdgcn_raw_buffer_load_b32(
+                    rz, valid ? zlane + (uint32_t)g * 8u : zend, 0, 0);
+            }
+        }
+    };
+
+    // x of unit r0 + i: chunk ch = row ch / 16, k offset 8 (ch % 16).
+    u32x4_t xr[XPT];
+    auto load_x = [&](int i) {
+        const int kb = (r0 + i) * kUnitK;
+#pragma unroll
+        for (int p = 0; p < XPT; ++p) {
+            const int ch = threadIdx.x + 256 * p;
+            const int m = ch >> 4, k = kb + 8 * (ch & 15);
+            xr[p] = u32x4_t{0u, 0u, 0u, 0u};
+            if (ch < XCH && m < M && k < K && i < nu)
+                xr[p] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
+                    rx, (uint32_t)(m * K + k) * 2u, 0, 0));
+        }
+    };
+    auto store_x = [&](int b) {
+#pragma unroll
+        for (int p = 0; p < XPT; ++p) {
+            const int ch = threadIdx.x + 256 * p;
+            const int m = ch >> 4;
+            if (ch < XCH && m < M) *(u32x4_t*)&xs[b][m][8 * (ch & 15)] = xr[p];
+        }
+    };
+
+    const int zshift = 4 * (c & 7);
+    const uint32_t magic = BF16 ? 0x43004300u : 0x64006400u;   // 128.0 / 1024.0 pairs
+    float4_t total[TN][RB];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) total[j][rb] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const GSlot<NG> (&r)[TN], int b) {
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            float4_t acc[TN][RB];
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) acc[j][rb] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int js = 0; js < SPU; ++js) {
+                const int st = gi * SPU + js;   // 32-k step inside the unit
+                u32x4_t av[RB];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    av[rb] = *(const u32x4_t*)&xs[b][16 * rb + c][32 * st + 8 * kc];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const uint32_t zq = (r[j].z[gi] >> zshift) & 15u;
+                    if constexpr (!BF16) {
+                        uint32_t nz1024 = 0xE400u + zq;          // fp16 -(1024 + z)
+                        nz1024 |= nz1024 << 16;
+                        uint32_t nz64 = 0xD400u + (zq << 4);     // fp16 -(64 + z)
+                        nz64 |= nz64 << 16;
+                        const half8_t bq = dequant_f16(r[j].w[st], magic, nz1024, nz64);
+#pragma unroll
+                        for (int rb = 0; rb < RB; ++rb)
+                            acc[j][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                bitcast<half8_t>(av[rb]), bq, acc[j][rb], 0, 0, 0);
+                    } else {
+                        uint32_t nb = 0xC300u + zq;              // bf16 -(128 + z)
+                        nb |= nb << 16;
+                        const bf16x8_t bias = bitcast<bf16x8_t>(u32x4_t{nb, nb, nb, nb});
+                        const bf16x8_t bq = biased_bf16(r[j].w[st], magic);
+#pragma unroll
+                        for (int rb = 0; rb < RB; ++rb) {
+                            const bf16x8_t ax = bitcast<bf16x8_t>(av[rb]);
+                            acc[j][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bq, acc[j][rb], 0, 0, 0);
+                            acc[j][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bias, acc[j][rb], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const float sf = f16_bits_to_f32((uint16_t)r[j].s[gi]);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        total[j][rb][q] = __builtin_fmaf(sf, acc[j][rb][q], total[j][rb][q]);
+            }
+        }
+    };
+
+    // Prologue: loads of the first kRing units, x of unit 0 staged.
+    GSlot<NG> ring[kRing][TN];
+#pragma unroll
+    for (int d = 0; d < kRing; ++d) load_unit(d, ring[d]);
+    load_x(0);
+    store_x(0);
+    __syncthreads();
+    for (int i = 0; i < nu; i += kRing) {
+#pragma unroll
+        for (int d = 0; d < kRing; ++d) {
+            load_x(i + d + 1);
+            compute(ring[d], d & 1);       // unit i + d sits in buffer (i + d) % 2
+            load_unit(i + d + kRing, ring[d]);
+            store_x((d + 1) & 1);
+            __syncthreads();
+        }
+    }
+
+    // Lane l holds rows 16 rb + 4 (l / 16) + q of column l % 16 of each tile.
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int n = (tw + j) * kTileN + c;
+        if (j >= nt || n >= N) continue;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = 16 * rb + 4 * kc + q;
+                if (m >= M) continue;
+                const size_t o = (size_t)m * N + n;
+                if (a.S > 1)
+                    ((float*)out)[(size_t)split * M * N + o] = total[j][rb][q];
+                else
+                    store_out(out, a.out_dtype, o, total[j][rb][q]);
+            }
+    }
+}
+
+typedef void (*gemm_kernel_t)(const uint16_t*, const u32x4_t*, const uint16_t*, const uint32_t*,
+                              void*, GemmLaunch);
+
+template <bool BF16, int SPG, int TN>
+gemm_kernel_t pick_rb(int rb) {
+    switch (rb) {
+        case 1: return w4_gemm_kernel<BF16, SPG, 1, TN>;
+        case 2: return w4_gemm_kernel<BF16, SPG, 2, TN>;
+        case 3: return w4_gemm_kernel<BF16, SPG, 3, TN>;
+        default: return w4_gemm_kernel<BF16, SPG, 4, TN>;
+    }
+}
+
+template <bool BF16, int SPG>
+gemm_kernel_t pick_tn(int rb, int tn) {
+    return tn == 1 ? pick_rb<BF16, SPG, 1>(rb) : pick_rb<BF16, SPG, 2>(rb);
+}
+
+gemm_kernel_t pick_gemm(bool bf16, int group, int rb, int tn) {
+    switch (group) {
+        case 32: return bf16 ? pick_tn<true, 1>(rb, tn) : pick_tn<false, 1>(rb, tn);
+        case 64: return bf16 ? pick_tn<true, 2>(rb, tn) : pick_tn<false, 2>(rb, tn);
+        case 128: return bf16 ? pick_tn<true, 4>(rb, tn) : pick_tn<false, 4>(rb, tn);
+        default: return bf16 ? pick_tn<true, 8>(rb, tn) : pick_tn<false, 8>(rb, tn);
+    }
+}
+
+}  // namespace
+
+namespace w4h {
+
+// Plan of the M-tiled path for one shape: row blocks, tiles per wave, K
+// slices (so that the grid gives every CU at least two workgroups while each
+// slice keeps at least eight units).
+GemmPlan gemm_plan(int M, int N, int K, int group, int cus) {
+    GemmPlan p;
+    const int U = (K + kUnitK - 1) / kUnitK;
+    const int T = pad_n(N) / kTileN;
+    p.rb = (M + 15) / 16;
+    // One tile per wave: the two-tile build needs 212 VGPRs (two waves per
+    // SIMD) and measured slower (gate_up at M = 64: 64.9 us against 57.6 us).
+    p.tn = 1;
+    if (const char* e = getenv("W4A16_GEMM_TN")) {
+        const int t = atoi(e);
+        if (t == 1 || t == 2) p.tn = t;
+    }
+    const long long cols = (T + kGemmWaves * p.tn - 1) / (kGemmWaves * p.tn);
+    p.split = 1;
+    while (cols * p.split < 2LL * cus && U / (2 * p.split) >= 8 && p.split < kMaxSplitGemm) p.split *= 2;
+    if (const char* e = getenv("W4A16_GEMM_SPLIT")) {
+        const int s = atoi(e);
+        if (s >= 1 && s <= U && s <= kMaxSplitGemm) p.split = s;
+    }
+    p.workgroups = cols;
+    return p;
+}
+
+int gemm_launch(const GemmPlan& p, const void* x, bool bf16, const void* qweight, const void* scales,
+                const void* zeros, void* y, int y_dtype, int M, int N, int K, int group,
+                void* workspace, hipStream_t st) {
+    const int U = (K + kUnitK - 1) / kUnitK;
+    const int T = pad_n(N) / kTileN;
+    GemmLaunch l{M, N, K, U, p.split, T, y_dtype};
+    gemm_kernel_t k = pick_gemm(bf16, group, p.rb, p.tn);
+    hipLaunchKernelGGL(k, dim3((unsigned)p.workgroups, p.split), dim3(64 * kGemmWaves), 0, st,
+                       (const uint16_t*)x, (const u32x4_t*)qweight, (const uint16_t*)scales,
+                       (const uint32_t*)zeros, p.split > 1 ? workspace : y, l);
+    return W4A16_OK;
+}
+
+}  // namespace w4h

@@ -55,41 +55,6 @@ constexpr int kMaxWaves = 8;     // waves per workgroup (the kernel's 512-thread
 constexpr int kMaxRows = 16;     // rows per MFMA
 constexpr int kMaxXLoads = 17;   // x load instructions per wave: M * (16 UPW + 1) <= 64 * 17
 
-__device__ __forceinline__ half2_t as_h2(uint32_t v) { return bitcast<half2_t>(v); }
-__device__ __forceinline__ uint32_t as_u(half2_t v) { return bitcast<uint32_t>(v); }
-
-// (a & mask) | (b & ~mask) in one v_bfi_b32.  The magic exponents below never
-// overlap the nibble masks, so bfi(mask, d, magic) = (d & mask) | magic.
-__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
-    uint32_t r;
-    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(mask), "v"(a), "v"(b));
-    return r;
-}
-
-// B operand (8 fp16 = q - z, exact) for the 8 weights of one device dword.
-__device__ __forceinline__ half8_t dequant_f16(uint32_t d, uint32_t magic, uint32_t nz1024,
-                                               uint32_t nz64) {
-    const half2_t sixteenth = as_h2(0x2C002C00u);  // fp16 1/16
-    const uint32_t t = d >> 8;
-    const uint32_t p0 = bfi(0x000F000Fu, d, magic);  // 1024 + q   (elements 0, 1)
-    const uint32_t p1 = bfi(0x00F000F0u, d, magic);  // 1024 + 16q (elements 2, 3)
-    const uint32_t p2 = bfi(0x000F000Fu, t, magic);  // 1024 + q   (elements 4, 5)
-    const uint32_t p3 = bfi(0x00F000F0u, t, magic);  // 1024 + 16q (elements 6, 7)
-    const half2_t w0 = as_h2(p0) + as_h2(nz1024);
-    const half2_t w1 = __builtin_elementwise_fma(as_h2(p1), sixteenth, as_h2(nz64));
-    const half2_t w2 = as_h2(p2) + as_h2(nz1024);
-    const half2_t w3 = __builtin_elementwise_fma(as_h2(p3), sixteenth, as_h2(nz64));
-    u32x4_t v = {as_u(w0), as_u(w1), as_u(w2), as_u(w3)};
-    return bitcast<half8_t>(v);
-}
-
-// B operand (8 bf16 = 128 + q, exact) for the 8 weights of one device dword.
-__device__ __forceinline__ bf16x8_t biased_bf16(uint32_t d, uint32_t magic) {
-    u32x4_t v = {bfi(0x000F000Fu, d, magic), bfi(0x000F000Fu, d >> 4, magic),
-                 bfi(0x000F000Fu, d >> 8, magic), bfi(0x000F000Fu, d >> 12, magic)};
-    return bitcast<bf16x8_t>(v);
-}
-
 // One ring slot: a unit's 16 weight bytes for this lane plus the scale and
 // zero-point words of the groups it touches.
 template <int NG>
@@ -415,6 +380,7 @@ merge_kernel_t pick_merge(int S) {
 
 struct Tuning {
     int waves = 0, split = 0, tpw = 0;  // 0 = automatic
+    int gemm_min_m = 0;                 // rows from which the M-tiled kernel runs (0 = automatic)
 };
 
 const Tuning& tuning() {
@@ -426,6 +392,7 @@ const Tuning& tuning() {
         if (const char* e = getenv("W4A16_WAVES")) t.waves = atoi(e);
         if (const char* e = getenv("W4A16_SPLIT")) t.split = atoi(e);
         if (const char* e = getenv("W4A16_TPW")) t.tpw = atoi(e);
+        if (const char* e = getenv("W4A16_GEMM_MIN_M")) t.gemm_min_m = atoi(e);
     });
     return t;
 }
@@ -588,13 +555,42 @@ void allow_full_lds() {
     });
 }
 
+Plan make_plan(int M, int N, int K, int group, int cus);
+
+// Whether the M-tiled kernel (w4_gemm.hip) takes the call: every M above the
+// GEMV's 16, and below that from the measured crossover on.  Measured per
+// call on the 27B-class layers (us, GEMV / tiled):
+//   qkv      M = 6: 8.0 / 10.5   M = 8: 10.6 / 10.5   M = 12: 12.2 / 10.7
+//   o_proj   M = 8: 10.3 / 10.1  M = 12: 11.9 / 10.2
+//   gate_up  M = 8: 26.4 / 30.0  M = 12: 30.0 / 30.9  M = 16: 80.4 / 31.3
+//   down     M = 6: 18.4 / 17.4  M = 8: 26.2 / 17.5
+//   K = N = 4096  M = 8: 5.6 / 8.2
+// The GEMV falls off once its workgroup needs more than half a CU's LDS (one
+// workgroup per CU): 87 KB for qkv and o_proj at M = 8, 71 KB for
+// K = N = 4096.  So the tiled kernel takes M > 12, and M = 8..12 where the
+// GEMV would run one tile per workgroup with more than half the LDS (on wide
+// layers the GEMV streams several tiles per workgroup and stays ahead).
+bool use_gemm(int M, int N, int K, int group) {
+    const int t = tuning().gemm_min_m;
+    if (M > kMaxRows) return true;
+    if (t >= 1) return M >= t;
+    if (M > 12) return true;
+    if (M < 8) return false;
+    const Plan p = make_plan(M, N, K, group, cu_count());
+    return p.tpw == 1 && p.lds > kLdsPerCu / 2;
+}
+
+size_t gemm_workspace(const w4h::GemmPlan& p, int M, int N) {
+    return p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0;
+}
+
 int check_gemv_args(const void* x, int x_dtype, const void* q, const void* s, const void* z,
                     const void* y, int y_dtype, int M, int N, int K, int group) {
     if (!x || !q || !s || !z || !y) return W4A16_ERR_NULL;
     if (x_dtype != W4A16_F16 && x_dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
     if (y_dtype != W4A16_F32 && y_dtype != W4A16_F16 && y_dtype != W4A16_BF16)
         return W4A16_ERR_DTYPE;
-    if (M < 1 || M > kMaxRows) return W4A16_ERR_SHAPE;
+    if (M < 1 || M > w4h::kMaxRowsGemm) return W4A16_ERR_SHAPE;
     int rc = w4h::check_w4_shape(N, K, group);
     if (rc) return rc;
     if (!w4h::aligned16(x) || !w4h::aligned16(q) || !w4h::aligned16(s) || !w4h::aligned16(z) ||
@@ -603,13 +599,49 @@ int check_gemv_args(const void* x, int x_dtype, const void* q, const void* s, co
     return W4A16_OK;
 }
 
+// y = the slice-order sum of S fp32 partials [S][M][N] in the workspace.
+void launch_merge(const void* workspace, void* y, int y_dtype, int M, int N, int S, hipStream_t st) {
+    const int MN4 = M * N / 4;   // N % 8 == 0
+    const dim3 grid((MN4 + 255) / 256);
+    if (merge_kernel_t mk = pick_merge(S))
+        hipLaunchKernelGGL(mk, grid, dim3(256), 0, st, (const float4_t*)workspace, y, y_dtype, MN4);
+    else
+        hipLaunchKernelGGL(splitk_merge_any_kernel, grid, dim3(256), 0, st,
+                           (const float4_t*)workspace, y, y_dtype, MN4, S);
+}
+
+int launch_gemm(const void* x, int x_dtype, const void* qweight, const void* scales, const void* zeros,
+                void* y, int y_dtype, int M, int N, int K, int group, void* workspace,
+                size_t workspace_bytes, hipStream_t st) {
+    const w4h::GemmPlan p = w4h::gemm_plan(M, N, K, group, cu_count());
+    const size_t need = gemm_workspace(p, M, N);
+    if (need) {
+        if (!workspace) return W4A16_ERR_NULL;
+        if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+        if (!w4h::aligned16(workspace)) return W4A16_ERR_ALIGN;
+    }
+    const bool bf16 = x_dtype == W4A16_BF16;
+    w4h::begin_launches();
+    w4h::gemm_launch(p, x, bf16, qweight, scales, zeros, y, y_dtype, M, N, K, group, workspace, st);
+    if (p.split > 1) launch_merge(workspace, y, y_dtype, M, N, p.split, st);
+    w4h::set_last_variant("w4_gemm16 %s g%d kernel=w4_gemm_kernel<%s, %d, %d, %d> tiles=%d slices=%d "
+                          "workgroups=%lld",
+                          bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.rb, p.tn,
+                          pad_n(N) / kTileN, p.split, p.workgroups);
+    return w4h::launch_status();
+}
+
 }  // namespace
 
 extern "C" int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* bytes) {
     if (!bytes) return W4A16_ERR_NULL;
-    if (M < 1 || M > kMaxRows) return W4A16_ERR_SHAPE;
+    if (M < 1 || M > w4h::kMaxRowsGemm) return W4A16_ERR_SHAPE;
     int rc = w4h::check_w4_shape(N, K, group);
     if (rc) return rc;
+    if (use_gemm(M, N, K, group)) {
+        *bytes = gemm_workspace(w4h::gemm_plan(M, N, K, group, cu_count()), M, N);
+        return W4A16_OK;
+    }
     const Plan p = make_plan(M, N, K, group, cu_count());
     *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     return W4A16_OK;
@@ -620,6 +652,8 @@ extern "C" int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const
                           void* workspace, size_t workspace_bytes, w4a16_stream_t stream) {
     int rc = check_gemv_args(x, x_dtype, qweight, scales, zeros, y, y_dtype, M, N, K, group);
     if (rc) return rc;
+    if (use_gemm(M, N, K, group)) return launch_gemm(x, x_dtype, qweight, scales, zeros, y, y_dtype, M, N, K, group,
+                                        workspace, workspace_bytes, (hipStream_t)stream);
     Plan p = make_plan(M, N, K, group, cu_count());
     if (!p.upw) return W4A16_ERR_UNSUPPORTED;
     const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
@@ -639,16 +673,7 @@ extern "C" int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const
                        (const uint16_t*)x,
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros,
                        out, p.l);
-    if (p.l.S > 1) {
-        const int MN4 = M * N / 4;   // N % 8 == 0
-        const dim3 grid((MN4 + 255) / 256);
-        if (merge_kernel_t mk = pick_merge(p.l.S))
-            hipLaunchKernelGGL(mk, grid, dim3(256), 0, st, (const float4_t*)workspace, y, y_dtype,
-                               MN4);
-        else
-            hipLaunchKernelGGL(splitk_merge_any_kernel, grid, dim3(256), 0, st,
-                               (const float4_t*)workspace, y, y_dtype, MN4, p.l.S);
-    }
+    if (p.l.S > 1) launch_merge(workspace, y, y_dtype, M, N, p.l.S, st);
     w4h::set_last_variant("w4_mfma16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, %d> tiles=%d slices=%d "
                           "waves=%d upw=%d tpw=%d lds=%zu",
                           bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.upw,

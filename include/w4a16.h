@@ -75,7 +75,7 @@ typedef enum { W4A16_F16 = 0, W4A16_BF16 = 1, W4A16_F32 = 2 } w4a16_dtype;
 
 /* Shape contract shared by the 4-bit functions:
  *   1 <= N, 1 <= K, N % 8 == 0, K % group == 0, K % 8 == 0,
- *   group in {32, 64, 128, 256}; for the GEMV also 1 <= M <= 16. */
+ *   group in {32, 64, 128, 256}; for the GEMV also 1 <= M <= 64. */
 
 /* Bytes of the device layout for an N x K matrix with the given group.  Host
  * only.  Returns W4A16_OK or W4A16_ERR_SHAPE / W4A16_ERR_NULL. */
@@ -102,7 +102,12 @@ int w4a16_unpack(const void* qweight, const void* scales, const void* zeros,
  * (NINFER tuning page, section 五: declare workspace capacity up front). */
 int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* bytes);
 
-/* y[M,N] = x[M,K] . ((q - z) * s)[K,N] from the packed device layout.
+/* y[M,N] = x[M,K] . ((q - z) * s)[K,N] from the packed device layout, for
+ * 1 <= M <= 64 (the Z100 article, section 五: the weights are read and
+ * dequantized once for every row).  A few rows run a GEMV kernel whose waves
+ * split K; larger M (from a crossover measured per layer shape; always above
+ * 16) runs an M-tiled kernel whose waves split N and share x through LDS.
+ * w4a16_last_variant() names the kernel that ran.
  * x_dtype: W4A16_F16 or W4A16_BF16.  y_dtype: W4A16_F32, W4A16_F16 or
  * W4A16_BF16 (rounded to nearest even from the fp32 result).  Products and
  * sums are fp32; the result is deterministic: the same inputs give the same

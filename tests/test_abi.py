@@ -72,7 +72,7 @@ def test_gemv_argument_checks_return_before_launch():
     assert rc(zeros=0) == -1
     assert rc(x_dtype=2) == -4          # x must be f16 or bf16
     assert rc(y_dtype=7) == -4
-    assert rc(M=0) == -2 and rc(M=17) == -2
+    assert rc(M=0) == -2 and rc(M=65) == -2       # 1 <= M <= 64
     assert rc(N=0) == -2 and rc(N=4100) == -2
     assert rc(K=4100) == -2 and rc(group=100) == -2
     assert rc(x=good + 8) == -3 and rc(y=good + 4) == -3

@@ -130,6 +130,63 @@ def test_w4_gemv_matches_oracle(M, N, K, g, xdt):
     assert_parity(to_f64(yb), ref, "bf16 out", extra_rel=2.0 ** -8)
 
 
+# M-tiled kernel (more rows than one MFMA block): 2 to 4 row blocks, one or
+# two tiles per wave, every group size, ragged N (a last tile of 8 columns)
+# and ragged K (a last unit of 64 k), with and without K slices.
+GEMM_CASES = [
+    # (M, N, K, group, x dtype)
+    (17, 264, 1216, 64, "f16"),
+    (24, 136, 896, 128, "bf16"),
+    (32, 520, 2048, 128, "f16"),
+    (33, 40, 384, 32, "bf16"),
+    (48, 1032, 1536, 256, "f16"),
+    (64, 264, 4352, 128, "bf16"),
+    (64, 4104, 640, 64, "f16"),
+    (20, 8, 128, 128, "f16"),
+    (40, 33808, 512, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,g,xdt", GEMM_CASES)
+def test_w4_gemm_matches_oracle(M, N, K, g, xdt):
+    say(f"w4 gemm M={M} N={N} K={K} g={g} x={xdt}")
+    key = (117, M, N, K, g)
+    w = synth.gen_w4(key, N, K, g)
+    x = synth.gen_x(key, M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    P = PackedW4(w, N, K, g)
+    xd = dev(x)
+    y = P.gemv(xd, xdt, M, "f32")
+    torch.cuda.synchronize()
+    variant = L.w4a16_last_variant()
+    say("  variant: " + variant)
+    assert "w4_gemm_kernel" in variant
+    cols = np.arange(N) if N <= 4200 else np.sort(np.random.default_rng(1).choice(N, 700, replace=False))
+    ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g, cols=cols.astype(np.int64))
+    assert_parity(to_f64(y)[:, cols], ref, f"M={M} N={N} K={K} g={g} {xdt}")
+    y16 = P.gemv(xd, xdt, M, "f16")
+    assert_parity(to_f64(y16)[:, cols], ref, "f16 out", extra_rel=2.0 ** -11)
+    # repeat calls give the same bits
+    assert torch.equal(P.gemv(xd, xdt, M, "f32"), y)
+
+
+@pytest.mark.parametrize("M,xdt", [(64, "bf16"), (32, "f16")])
+def test_w4_gemm_full_size_sampled(M, xdt):
+    # The 27B-class gate_up and down layers with a batch of rows: sampled
+    # columns against the oracle (which computes them one by one).
+    for (N, K) in [(34816, 5120), (5120, 17408)]:
+        say(f"w4 gemm full size M={M} N={N} K={K} x={xdt}")
+        key = (118, M, N, K)
+        w = synth.gen_w4(key, N, K, 128)
+        x = synth.gen_x(key, M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+        P = PackedW4(w, N, K, 128)
+        y = P.gemv(dev(x), xdt, M, "f32")
+        torch.cuda.synchronize()
+        say("  variant: " + L.w4a16_last_variant())
+        cols = np.sort(np.random.default_rng(2).choice(N, 96, replace=False)).astype(np.int64)
+        ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, 128, cols=cols)
+        assert_parity(to_f64(y)[:, cols], ref, f"full size M={M} N={N} K={K}")
+
+
 W2_GEMV_CASES = [
     (1, 7, 32, 32, "f16"),
     (4, 40, 768, 128, "f16"),
@@ -342,7 +399,7 @@ def test_split_k_workspace_reused_across_shapes_and_graph_replays():
 
 
 @pytest.mark.parametrize("M,K,g,xdt", [(1, 1152, 128, "f16"), (8, 1152, 128, "bf16"),
-                                         (3, 640, 128, "f16"), (16, 256, 128, "bf16"),
+                                         (3, 640, 128, "f16"), (12, 256, 128, "bf16"),
                                          (2, 1152, 64, "f16"), (4, 640, 64, "bf16")])
 def test_multi_tile_workgroups_ragged(M, K, g, xdt):
     # Many more tiles than the GPU holds at once: each workgroup takes three
