@@ -320,6 +320,71 @@ def w2t_bytes(M, N, K, g, x_bytes=2, y_bytes=4):
     return N * K // 4 + (K // g) * N * 2 + M * K * x_bytes + M * N * y_bytes
 
 
+def residual_fusion(L, torch, synth, oracle_mod, K, N, g, steps, warmup, stream, key):
+    """µs per call of h += x . W (fp16 hidden state h, M = 1) two ways: fused
+    (w4a16_gemv_add in place) and unfused (w4a16_gemv into an fp16 temporary,
+    then torch's add), each as a graph over copies of one packed matrix."""
+    M = 1
+    w = synth.gen_w4_torch(key, N, K, g)
+    sizes = L.w4a16_packed_sizes(N, K, g)
+    copies = max(2, -(-ROT_BYTES // sum(sizes)))
+    mats = []
+    for _ in range(copies):
+        bufs = [torch.empty(b, dtype=torch.uint8, device="cuda") for b in sizes]
+        L.w4a16_pack(w["qweight"], w["scales"], w["zeros"], *bufs, N, K, g)
+        mats.append(bufs)
+    torch.cuda.synchronize()
+    x = synth.gen_x_torch(key + (M,), M, K, "f16")
+    h0 = (torch.randn((M, N), generator=torch.Generator().manual_seed(7)) * 4).half().cuda()
+    h = h0.clone()
+    t = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    wsb = L.w4a16_workspace_bytes(M, N, K, g)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
+
+    def fused(bufs):
+        L.w4a16_gemv_add(x, "f16", *bufs, h, "f16", h, "f16", M, N, K, g, ws, wsb, stream)
+
+    def unfused(bufs):
+        L.w4a16_gemv(x, "f16", *bufs, t, "f16", M, N, K, g, ws, wsb, stream)
+        h.add_(t)
+
+    xh = x.cpu().numpy().view(np.uint16)
+    cols = np.sort(np.random.default_rng(3).choice(N, size=64, replace=False)).astype(np.int64)
+    ref = oracle_mod.w4_gemv(xh, "f16", w["qweight"].cpu().numpy(),
+                             w["scales"].cpu().numpy().view(np.uint16),
+                             w["zeros"].cpu().numpy(), M, N, K, g, cols=cols)
+    ref = ref + h0.double().cpu().numpy()[:, cols]
+    out = {"K": K, "N": N, "group": g, "M": M, "copies": copies}
+    for name, call in (("fused", fused), ("unfused", unfused)):
+        h.copy_(h0)
+        with torch.cuda.stream(stream):
+            call(mats[0])
+        torch.cuda.synchronize()
+        got = h.double().cpu().numpy()[:, cols]
+        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        if rel > 1e-3 + 2.0 ** -11:
+            raise SystemExit(f"parity guard failed: residual {name} K={K} N={N}: rel={rel:.2e}")
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for bufs in mats:
+                call(bufs)
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        del graph
+        out[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / steps / copies, 3)
+        out[name + "_parity_rel"] = rel
+    return out
+
+
 def rotation_sweep(L, torch, synth, oracle_mod, kind, K, N, g, Ms, steps, warmup, stream, key):
     """µs per call of one shape at each M: copies of one packed matrix spanning
     ROT_BYTES, a graph of one call per copy, events around the replays."""
@@ -537,6 +602,16 @@ def main():
                     f"{k} {d['us']:.1f}us" for k, d in shb.items()))
             del sb
         extra["batch_sweeps"] = batch
+        # The residual add of o_proj and down, fused into the GEMV's output
+        # stage or done as a separate add.
+        fusion = []
+        for (name, K, N) in (("o_proj", 5120, 5120), ("down", 17408, 5120)):
+            r = residual_fusion(L, torch, synth, oracle_mod, K, N, GROUP, max(5, args.steps // 2),
+                                max(2, args.warmup), stream, (5, K, N))
+            r["shape"] = name
+            fusion.append(r)
+            log(f"residual add {name}: fused {r['fused_us']:.2f} us, unfused {r['unfused_us']:.2f} us")
+        extra["residual_fusion"] = fusion
         steps_x, warm_x = max(5, args.steps // 2), max(2, args.warmup)
         skinny = []
         for kn in SKINNY_KN:

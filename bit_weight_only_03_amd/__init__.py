@@ -39,6 +39,7 @@ _SIGS = {
     "w4a16_unpack": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "w4a16_workspace_bytes": [_I, _I, _I, _I, _PSZ],
     "w4a16_gemv": [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P],
+    "w4a16_gemv_add": [_P, _I, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _SZ, _P],
     "w4a16_dequant": [_P, _P, _P, _P, _I, _I, _I, _P],
     "w2t_packed_sizes": [_I, _I, _I, _PSZ, _PSZ],
     "w2t_pack": [_P, _P, _P, _P, _I, _I, _I, _P],
@@ -154,6 +155,14 @@ def w4a16_gemv(x, x_dtype, qweight, scales, zeros, y, y_dtype, M, N, K, group, w
     _check("w4a16_gemv", _lib.w4a16_gemv(_ptr(x), _dt(x_dtype), _ptr(qweight), _ptr(scales),
                                          _ptr(zeros), _ptr(y), _dt(y_dtype), M, N, K, group,
                                          _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def w4a16_gemv_add(x, x_dtype, qweight, scales, zeros, residual, residual_dtype, y, y_dtype, M, N, K,
+                   group, workspace=None, workspace_bytes=0, stream=None):
+    _check("w4a16_gemv_add", _lib.w4a16_gemv_add(
+        _ptr(x), _dt(x_dtype), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(residual),
+        _dt(residual_dtype), _ptr(y), _dt(y_dtype), M, N, K, group, _ptr(workspace),
+        workspace_bytes, _stream(stream)))
 
 
 def w4a16_dequant(qweight, scales, zeros, w, N, K, group, stream=None):

@@ -66,6 +66,17 @@ __host__ __device__ inline uint16_t f32_to_bf16_bits(float f) {
     return (uint16_t)(b >> 16);
 }
 
+// v + r[o], with r read in its dtype (f32, f16 or bf16); no residual: v.
+// The fused residual add of the GEMV epilogues (Ninfer V100 article, section
+// 十四: adding the input back inside the matmul's output stage saves a pass
+// through memory).
+__device__ __forceinline__ float add_residual(float v, const void* r, int r_dtype, size_t o) {
+    if (!r) return v;
+    if (r_dtype == W4A16_F32) return v + ((const float*)r)[o];
+    if (r_dtype == W4A16_F16) return v + (float)((const _Float16*)r)[o];
+    return v + __builtin_bit_cast(float, (uint32_t)((const uint16_t*)r)[o] << 16);
+}
+
 // y[o] = v in the output dtype (f32, f16, or bf16 rounded to nearest even).
 __device__ __forceinline__ void store_out(void* out, int out_dtype, size_t o, float v) {
     if (out_dtype == W4A16_F32)
@@ -186,7 +197,7 @@ struct GemmPlan {
 };
 GemmPlan gemm_plan(int M, int N, int K, int group, int cus);
 int gemm_launch(const GemmPlan& p, const void* x, bool bf16, const void* qweight, const void* scales,
-                const void* zeros, void* y, int y_dtype, int M, int N, int K, int group,
-                void* workspace, hipStream_t st);
+                const void* zeros, void* y, int y_dtype, const void* res, int res_dtype, int M, int N,
+                int K, int group, void* workspace, hipStream_t st);
 
 }  // namespace w4h

@@ -41,6 +41,8 @@ struct GemmLaunch {
     int S;   // K slices
     int T;   // 16-column tiles
     int out_dtype;
+    const void* res;   // residual added to y (unsplit calls), or null
+    int res_dtype;
 };
 
 // A unit's loads for one tile: 16 weight bytes per lane, plus the scale and
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
                                                       const u32x4_t* __restrict__ qdev,
                                                       const uint16_t* __restrict__ sdev,
                                                       const uint32_t* __restrict__ zdev,
-                                                      void* __restrict__ out, GemmLaunch a) {
+                                                      void* out, GemmLaunch a) {
     constexpr int NG = SPG >= 4 ? 1 : 4 / SPG;    // groups per unit
     constexpr int SPU = SPG >= 4 ? 4 : SPG;       // 32-k steps per group inside one unit
     constexpr int ROWS = 16 * RB;
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
                 if (a.S > 1)
                     ((float*)out)[(size_t)split * M * N + o] = total[j][rb][q];
                 else
-                    store_out(out, a.out_dtype, o, total[j][rb][q]);
+                    store_out(out, a.out_dtype, o, add_residual(total[j][rb][q], a.res, a.res_dtype, o));
             }
     }
 }
@@ -296,11 +298,11 @@ GemmPlan gemm_plan(int M, int N, int K, int group, int cus) {
 }
 
 int gemm_launch(const GemmPlan& p, const void* x, bool bf16, const void* qweight, const void* scales,
-                const void* zeros, void* y, int y_dtype, int M, int N, int K, int group,
-                void* workspace, hipStream_t st) {
+                const void* zeros, void* y, int y_dtype, const void* res, int res_dtype, int M, int N,
+                int K, int group, void* workspace, hipStream_t st) {
     const int U = (K + kUnitK - 1) / kUnitK;
     const int T = pad_n(N) / kTileN;
-    GemmLaunch l{M, N, K, U, p.split, T, y_dtype};
+    GemmLaunch l{M, N, K, U, p.split, T, y_dtype, res, res_dtype};
     gemm_kernel_t k = pick_gemm(bf16, group, p.rb, p.tn);
     hipLaunchKernelGGL(k, dim3((unsigned)p.workgroups, p.split), dim3(64 * kGemmWaves), 0, st,
                        (const uint16_t*)x, (const u32x4_t*)qweight, (const uint16_t*)scales,

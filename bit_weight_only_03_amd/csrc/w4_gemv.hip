@@ -72,6 +72,8 @@ struct GemvLaunch {
     int T;        // 16-column tiles
     int xstride;  // LDS row stride of a wave's staged x, in halves
     int out_dtype;
+    const void* res;   // residual added to y (unsplit calls), or null
+    int res_dtype;
 };
 
 // Slots of the register ring for UPW units per wave: all loads are issued
@@ -108,7 +110,7 @@ constexpr int min_waves() { return (SPG >= 4 && UPW <= 5) || (SPG == 2 && UPW <=
 template <bool BF16, int SPG, int UPW, int TPW>
 __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4_gemv_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ qdev,
-    const uint16_t* __restrict__ sdev, const uint32_t* __restrict__ zdev, void* __restrict__ out,
+    const uint16_t* __restrict__ sdev, const uint32_t* __restrict__ zdev, void* out,
     GemvLaunch a) {
     constexpr int NG = SPG >= 4 ? 1 : 4 / SPG;          // groups per unit
     constexpr int SPU = SPG >= 4 ? 4 : SPG;             // steps per group inside one unit
@@ -309,13 +311,11 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
         }
         const int n = (t0 + j) * kTileN + cc;
         if (j < nt && n < a.N) {
-            const size_t o = (size_t)split * M * a.N + (size_t)m * a.N + n;
-            if (a.out_dtype == W4A16_F32)
-                ((float*)out)[o] = v;
-            else if (a.out_dtype == W4A16_F16)
-                ((_Float16*)out)[o] = (_Float16)v;
+            const size_t o = (size_t)m * a.N + n;
+            if (a.S > 1)   // fp32 slice partials; the merge adds the residual
+                ((float*)out)[(size_t)split * M * a.N + o] = v;
             else
-                ((uint16_t*)out)[o] = f32_to_bf16_bits(v);
+                store_out(out, a.out_dtype, o, add_residual(v, a.res, a.res_dtype, o));
         }
     }
 }
@@ -336,9 +336,15 @@ __device__ __forceinline__ void store4(void* y, int out_dtype, int i4, float4_t 
     }
 }
 
+__device__ __forceinline__ float4_t add_residual4(float4_t v, const void* r, int r_dtype, int i4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = add_residual(v[q], r, r_dtype, (size_t)4 * i4 + q);
+    return v;
+}
+
 template <int S>
-__global__ void splitk_merge_kernel(const float4_t* __restrict__ ws, void* __restrict__ y,
-                                    int out_dtype, int MN4) {
+__global__ void splitk_merge_kernel(const float4_t* __restrict__ ws, void* y, int out_dtype,
+                                    int MN4, const void* res, int res_dtype) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= MN4) return;
     float4_t p[S];
@@ -347,20 +353,20 @@ __global__ void splitk_merge_kernel(const float4_t* __restrict__ ws, void* __res
     float4_t v = p[0];
 #pragma unroll
     for (int s = 1; s < S; ++s) v += p[s];
-    store4(y, out_dtype, i, v);
+    store4(y, out_dtype, i, add_residual4(v, res, res_dtype, i));
 }
 
 // Any slice count (only reachable through the slice override).
-__global__ void splitk_merge_any_kernel(const float4_t* __restrict__ ws, void* __restrict__ y,
-                                        int out_dtype, int MN4, int S) {
+__global__ void splitk_merge_any_kernel(const float4_t* __restrict__ ws, void* y, int out_dtype,
+                                        int MN4, const void* res, int res_dtype, int S) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= MN4) return;
     float4_t v = ws[i];
     for (int s = 1; s < S; ++s) v += ws[(size_t)s * MN4 + i];
-    store4(y, out_dtype, i, v);
+    store4(y, out_dtype, i, add_residual4(v, res, res_dtype, i));
 }
 
-typedef void (*merge_kernel_t)(const float4_t*, void*, int, int);
+typedef void (*merge_kernel_t)(const float4_t*, void*, int, int, const void*, int);
 
 merge_kernel_t pick_merge(int S) {
     switch (S) {
@@ -471,7 +477,7 @@ Plan make_plan(int M, int N, int K, int group, int cus) {
         S *= 2;
     if (tu.split >= 1 && tu.split <= U) S = tu.split;
     if (!fits(S, upw, lds, xstride)) upw = 0;   // an override that cannot run is refused
-    p.l = GemvLaunch{M, N, K, U, S, T, xstride, W4A16_F32};
+    p.l = GemvLaunch{M, N, K, U, S, T, xstride, W4A16_F32, nullptr, W4A16_F32};
     p.waves = W;
     p.upw = upw;
     // Several tiles per workgroup when there are many more tiles than the GPU
@@ -600,19 +606,21 @@ int check_gemv_args(const void* x, int x_dtype, const void* q, const void* s, co
 }
 
 // y = the slice-order sum of S fp32 partials [S][M][N] in the workspace.
-void launch_merge(const void* workspace, void* y, int y_dtype, int M, int N, int S, hipStream_t st) {
+void launch_merge(const void* workspace, void* y, int y_dtype, const void* res, int res_dtype, int M,
+                  int N, int S, hipStream_t st) {
     const int MN4 = M * N / 4;   // N % 8 == 0
     const dim3 grid((MN4 + 255) / 256);
     if (merge_kernel_t mk = pick_merge(S))
-        hipLaunchKernelGGL(mk, grid, dim3(256), 0, st, (const float4_t*)workspace, y, y_dtype, MN4);
+        hipLaunchKernelGGL(mk, grid, dim3(256), 0, st, (const float4_t*)workspace, y, y_dtype, MN4,
+                           res, res_dtype);
     else
         hipLaunchKernelGGL(splitk_merge_any_kernel, grid, dim3(256), 0, st,
-                           (const float4_t*)workspace, y, y_dtype, MN4, S);
+                           (const float4_t*)workspace, y, y_dtype, MN4, res, res_dtype, S);
 }
 
 int launch_gemm(const void* x, int x_dtype, const void* qweight, const void* scales, const void* zeros,
-                void* y, int y_dtype, int M, int N, int K, int group, void* workspace,
-                size_t workspace_bytes, hipStream_t st) {
+                void* y, int y_dtype, const void* res, int res_dtype, int M, int N, int K, int group,
+                void* workspace, size_t workspace_bytes, hipStream_t st) {
     const w4h::GemmPlan p = w4h::gemm_plan(M, N, K, group, cu_count());
     const size_t need = gemm_workspace(p, M, N);
     if (need) {
@@ -622,8 +630,9 @@ int launch_gemm(const void* x, int x_dtype, const void* qweight, const void* sca
     }
     const bool bf16 = x_dtype == W4A16_BF16;
     w4h::begin_launches();
-    w4h::gemm_launch(p, x, bf16, qweight, scales, zeros, y, y_dtype, M, N, K, group, workspace, st);
-    if (p.split > 1) launch_merge(workspace, y, y_dtype, M, N, p.split, st);
+    w4h::gemm_launch(p, x, bf16, qweight, scales, zeros, y, y_dtype, res, res_dtype, M, N, K, group,
+                     workspace, st);
+    if (p.split > 1) launch_merge(workspace, y, y_dtype, res, res_dtype, M, N, p.split, st);
     w4h::set_last_variant("w4_gemm16 %s g%d kernel=w4_gemm_kernel<%s, %d, %d, %d> tiles=%d slices=%d "
                           "workgroups=%lld",
                           bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.rb, p.tn,
@@ -647,13 +656,16 @@ extern "C" int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* byt
     return W4A16_OK;
 }
 
-extern "C" int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const void* scales,
-                          const void* zeros, void* y, int y_dtype, int M, int N, int K, int group,
-                          void* workspace, size_t workspace_bytes, w4a16_stream_t stream) {
+namespace {
+
+int gemv_impl(const void* x, int x_dtype, const void* qweight, const void* scales, const void* zeros,
+              const void* res, int res_dtype, void* y, int y_dtype, int M, int N, int K, int group,
+              void* workspace, size_t workspace_bytes, w4a16_stream_t stream) {
     int rc = check_gemv_args(x, x_dtype, qweight, scales, zeros, y, y_dtype, M, N, K, group);
     if (rc) return rc;
-    if (use_gemm(M, N, K, group)) return launch_gemm(x, x_dtype, qweight, scales, zeros, y, y_dtype, M, N, K, group,
-                                        workspace, workspace_bytes, (hipStream_t)stream);
+    if (use_gemm(M, N, K, group))
+        return launch_gemm(x, x_dtype, qweight, scales, zeros, y, y_dtype, res, res_dtype, M, N, K,
+                           group, workspace, workspace_bytes, (hipStream_t)stream);
     Plan p = make_plan(M, N, K, group, cu_count());
     if (!p.upw) return W4A16_ERR_UNSUPPORTED;
     const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
@@ -668,15 +680,38 @@ extern "C" int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const
     w4_kernel_t k = pick_kernel(bf16, group, p.upw, p.tpw);
     void* out = p.l.S > 1 ? workspace : y;
     p.l.out_dtype = p.l.S > 1 ? W4A16_F32 : y_dtype;
+    p.l.res = res;
+    p.l.res_dtype = res_dtype;
     w4h::begin_launches();
     hipLaunchKernelGGL(k, dim3((p.tiles + p.tpw - 1) / p.tpw, p.l.S), dim3(64 * p.waves), p.lds, st,
                        (const uint16_t*)x,
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros,
                        out, p.l);
-    if (p.l.S > 1) launch_merge(workspace, y, y_dtype, M, N, p.l.S, st);
+    if (p.l.S > 1) launch_merge(workspace, y, y_dtype, res, res_dtype, M, N, p.l.S, st);
     w4h::set_last_variant("w4_mfma16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, %d> tiles=%d slices=%d "
                           "waves=%d upw=%d tpw=%d lds=%zu",
                           bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.upw,
                           p.tpw, p.tiles, p.l.S, p.waves, p.upw, p.tpw, p.lds);
     return w4h::launch_status();
+}
+
+}  // namespace
+
+extern "C" int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const void* scales,
+                          const void* zeros, void* y, int y_dtype, int M, int N, int K, int group,
+                          void* workspace, size_t workspace_bytes, w4a16_stream_t stream) {
+    return gemv_impl(x, x_dtype, qweight, scales, zeros, nullptr, W4A16_F32, y, y_dtype, M, N, K, group,
+                     workspace, workspace_bytes, stream);
+}
+
+extern "C" int w4a16_gemv_add(const void* x, int x_dtype, const void* qweight, const void* scales,
+                              const void* zeros, const void* residual, int residual_dtype, void* y,
+                              int y_dtype, int M, int N, int K, int group, void* workspace,
+                              size_t workspace_bytes, w4a16_stream_t stream) {
+    if (!residual) return W4A16_ERR_NULL;
+    if (residual_dtype != W4A16_F32 && residual_dtype != W4A16_F16 && residual_dtype != W4A16_BF16)
+        return W4A16_ERR_DTYPE;
+    if (!w4h::aligned16(residual)) return W4A16_ERR_ALIGN;
+    return gemv_impl(x, x_dtype, qweight, scales, zeros, residual, residual_dtype, y, y_dtype, M, N, K,
+                     group, workspace, workspace_bytes, stream);
 }

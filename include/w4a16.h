@@ -119,6 +119,19 @@ int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const void* scal
                const void* zeros, void* y, int y_dtype, int M, int N, int K, int group,
                void* workspace, size_t workspace_bytes, w4a16_stream_t stream);
 
+/* y = x . ((q - z) * s) + residual, with the residual added in the output
+ * stage of the same call (Ninfer V100 article, section 十四: adding the input
+ * back inside the matmul's output stage saves a pass through memory).  Same
+ * arguments, contract and workspace as w4a16_gemv, plus residual [M][N]
+ * (row-major, 16-byte aligned) of residual_dtype W4A16_F32, W4A16_F16 or
+ * W4A16_BF16, read once per element and added to the fp32 result before the
+ * output rounding.  residual may be y itself (y += x . W, in place); it must
+ * not overlap y otherwise.  A NULL residual returns W4A16_ERR_NULL. */
+int w4a16_gemv_add(const void* x, int x_dtype, const void* qweight, const void* scales,
+                   const void* zeros, const void* residual, int residual_dtype, void* y, int y_dtype,
+                   int M, int N, int K, int group, void* workspace, size_t workspace_bytes,
+                   w4a16_stream_t stream);
+
 /* Debug / parity: the dequantized matrix w[K][N] = (q - z) * s as fp32 from the
  * packed layout.  Exact, since |q - z| <= 15 times an fp16 scale fits in fp32. */
 int w4a16_dequant(const void* qweight, const void* scales, const void* zeros, float* w, int N,

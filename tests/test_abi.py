@@ -22,7 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("w4a16_pack", "w4a16_unpack", "w4a16_gemv", "w4a16_dequant", "w4a16_packed_sizes",
+    for n in ("w4a16_pack", "w4a16_unpack", "w4a16_gemv", "w4a16_gemv_add", "w4a16_dequant",
+              "w4a16_packed_sizes",
               "w4a16_workspace_bytes", "w2t_pack", "w2t_unpack", "w2t_gemv", "w2t_dequant",
               "w2t_packed_sizes", "w2t_workspace_bytes", "w4a16_bw_probe", "w4a16_status_string",
               "w4a16_last_variant"):
@@ -108,3 +109,21 @@ def test_ternary_argument_checks():
     with pytest.raises(lib.W4A16Error) as e:
         lib.w2t_pack(good, good, 0, good, 16, 256, 128, stream=0)
     assert e.value.status == -1
+
+
+def test_gemv_add_argument_checks():
+    # The residual is checked on the host before anything is launched.
+    good = 1 << 20
+
+    def rc(residual=good, residual_dtype=1, M=4):
+        try:
+            lib.w4a16_gemv_add(good, 0, good, good, good, residual, residual_dtype, good, 2, M, 4096,
+                               4096, 128, stream=0)
+        except lib.W4A16Error as e:
+            return e.status
+        return 0
+
+    assert rc(residual=0) == -1
+    assert rc(residual_dtype=7) == -4
+    assert rc(residual=good + 4) == -3
+    assert rc(M=65) == -2

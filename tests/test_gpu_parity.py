@@ -21,7 +21,7 @@ if not torch.cuda.is_available():
 
 import bit_weight_only_03_amd as L  # noqa: E402
 from gpu_util import (DEV, PackedW2T, PackedW4, assert_parity, dev, empty_bytes, host_bits,  # noqa: E402
-                      to_f64)
+                      to_f64, workspace_bytes)
 
 
 def say(msg):
@@ -185,6 +185,69 @@ def test_w4_gemm_full_size_sampled(M, xdt):
         cols = np.sort(np.random.default_rng(2).choice(N, 96, replace=False)).astype(np.int64)
         ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, 128, cols=cols)
         assert_parity(to_f64(y)[:, cols], ref, f"full size M={M} N={N} K={K}")
+
+
+# Fused residual add: GEMV unsplit and split (merge kernel), tiled unsplit and
+# split, residual in every dtype, in place (residual is y) and not.
+GEMV_ADD_CASES = [
+    # (M, N, K, group, x dtype, residual dtype, y dtype, in place)
+    (1, 4096, 4096, 128, "f16", "f32", "f32", False),
+    (1, 5120, 5120, 128, "f16", "f16", "f16", True),
+    (4, 640, 17408, 128, "bf16", "bf16", "bf16", True),
+    (3, 264, 2176, 64, "f16", "f16", "f32", False),
+    (32, 520, 2048, 128, "f16", "f16", "f16", True),
+    (64, 264, 4352, 128, "bf16", "f32", "f32", True),
+    (20, 4104, 640, 64, "f16", "bf16", "f32", False),
+]
+_TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+_ROUND = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+@pytest.mark.parametrize("M,N,K,g,xdt,rdt,ydt,inplace", GEMV_ADD_CASES)
+def test_w4_gemv_add_matches_oracle(M, N, K, g, xdt, rdt, ydt, inplace):
+    say(f"w4 gemv_add M={M} N={N} K={K} g={g} x={xdt} r={rdt} y={ydt} inplace={inplace}")
+    key = (119, M, N, K, g)
+    w = synth.gen_w4(key, N, K, g)
+    x = synth.gen_x(key, M, K, xdt)
+    P = PackedW4(w, N, K, g)
+    rng = np.random.default_rng(key)
+    r64 = rng.standard_normal((M, N)) * 4.0
+    r = torch.from_numpy(r64).to(_TORCH_DT[rdt]).cuda()
+    rref = r.double().cpu().numpy()                 # the residual as stored
+    if inplace:
+        assert rdt == ydt
+        y = r.clone()
+        res = y
+    else:
+        y = torch.full((M, N), float("nan"), dtype=_TORCH_DT[ydt], device=DEV)
+        res = r
+    wsb = L.w4a16_workspace_bytes(M, N, K, g)
+    ws = workspace_bytes(wsb) if wsb else None
+    L.w4a16_gemv_add(dev(x), xdt, P.q, P.s, P.z, res, rdt, y, ydt, M, N, K, g, ws, wsb)
+    torch.cuda.synchronize()
+    say("  variant: " + L.w4a16_last_variant())
+    ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g) + rref
+    assert_parity(to_f64(y), ref, f"gemv_add M={M} N={N} K={K}", extra_rel=_ROUND[ydt])
+    if not inplace:
+        assert torch.equal(r, res)                  # the residual is only read
+
+
+def test_w4_gemv_add_zero_residual_is_bitwise_gemv():
+    # v + 0 = v in fp32: a zero residual reproduces w4a16_gemv bit for bit,
+    # through the GEMV, its split merge and the tiled kernel.
+    for (M, N, K, g) in [(1, 1032, 2048, 128), (4, 640, 17408, 128), (24, 264, 1024, 64)]:
+        say(f"gemv_add zero residual M={M} N={N} K={K} g={g}")
+        w = synth.gen_w4((120, M, N, K), N, K, g)
+        xd = dev(synth.gen_x((120, M, K), M, K, "f16"))
+        P = PackedW4(w, N, K, g)
+        y0 = P.gemv(xd, "f16", M, "f32")
+        y1 = torch.empty_like(y0)
+        zero = torch.zeros((M, N), dtype=torch.float32, device=DEV)
+        wsb = L.w4a16_workspace_bytes(M, N, K, g)
+        ws = workspace_bytes(wsb) if wsb else None
+        L.w4a16_gemv_add(xd, "f16", P.q, P.s, P.z, zero, "f32", y1, "f32", M, N, K, g, ws, wsb)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1)
 
 
 W2_GEMV_CASES = [
