@@ -254,3 +254,48 @@ int oracle_w2t_gemv(const uint16_t* x, int x_is_bf16, const int32_t* codes,
     }
     return ORACLE_OK;
 }
+
+/* ---- 16-bit weights (W16A16) --------------------------------------------
+ * The Z100 article, section 六, measures the same small-M linear layer with
+ * FP16/BF16 weights (no quantization): y[m][n] = sum_k x[m][k] * w[n][k],
+ * with w stored as the layer's own [N][K] matrix of 16-bit values of the
+ * same type as x.  Both factors decode exactly and their product (at most 22
+ * significant bits) is exact in binary64; the sum runs in ascending k. */
+static int w16_shape_ok(int M, int N, int K) { return M > 0 && N > 0 && K > 0; }
+
+int oracle_w16_gemv(const uint16_t* x, int is_bf16, const uint16_t* w, int M, int N, int K,
+                    double* y)
+{
+    if (!w16_shape_ok(M, N, K)) return ORACLE_EINVAL;
+    #pragma omp parallel for schedule(static)
+    for (int n = 0; n < N; ++n) {
+        for (int m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k)
+                acc += decode_x(x, is_bf16, (size_t)m * K + k) *
+                       decode_x(w, is_bf16, (size_t)n * K + k);
+            y[(size_t)m * N + n] = acc;
+        }
+    }
+    return ORACLE_OK;
+}
+
+int oracle_w16_gemv_cols(const uint16_t* x, int is_bf16, const uint16_t* w, int M, int N, int K,
+                         const int64_t* cols, int ncols, double* y)
+{
+    if (!w16_shape_ok(M, N, K) || ncols < 0) return ORACLE_EINVAL;
+    for (int c = 0; c < ncols; ++c)
+        if (cols[c] < 0 || cols[c] >= N) return ORACLE_EINVAL;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int c = 0; c < ncols; ++c) {
+        int n = (int)cols[c];
+        for (int m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k)
+                acc += decode_x(x, is_bf16, (size_t)m * K + k) *
+                       decode_x(w, is_bf16, (size_t)n * K + k);
+            y[(size_t)m * ncols + c] = acc;
+        }
+    }
+    return ORACLE_OK;
+}

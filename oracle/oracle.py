@@ -54,8 +54,11 @@ def _load():
         lib.oracle_w2t_dequant.argtypes = [P, P, I, I, I, P]
         lib.oracle_w2t_gemv.argtypes = [P, I, P, P, I, I, I, I, P]
         lib.oracle_w2t_gemv_cols.argtypes = [P, I, P, P, I, I, I, I, P, I, P]
+        lib.oracle_w16_gemv.argtypes = [P, I, P, I, I, I, P]
+        lib.oracle_w16_gemv_cols.argtypes = [P, I, P, I, I, I, P, I, P]
         for f in ("oracle_w4_dequant", "oracle_w4_gemv", "oracle_w4_gemv_cols",
-                  "oracle_w2t_dequant", "oracle_w2t_gemv", "oracle_w2t_gemv_cols"):
+                  "oracle_w2t_dequant", "oracle_w2t_gemv", "oracle_w2t_gemv_cols",
+                  "oracle_w16_gemv", "oracle_w16_gemv_cols"):
             getattr(lib, f).restype = I
         _lib = lib
     return _lib
@@ -138,4 +141,21 @@ def w2t_gemv(x, x_dtype: str, codes, scales, M: int, N: int, K: int, group: int,
         y = np.empty((M, len(cc)), dtype=np.float64)
         _check(lib.oracle_w2t_gemv_cols(_ptr(xb), bf, _ptr(c), _ptr(s), M, N, K, group,
                                         _ptr(cc), len(cc), _ptr(y)), "w2t_gemv_cols")
+    return y
+
+
+def w16_gemv(x, dtype: str, w, M: int, N: int, K: int, cols=None) -> np.ndarray:
+    """y[M][N] (or the listed columns) = x . w^T in float64, for 16-bit
+    weights w[N][K] of the same dtype as x (bit patterns as uint16)."""
+    xb, wb = _c(x, np.uint16), _c(w, np.uint16)
+    bf = 1 if dtype == "bf16" else 0
+    lib = _load()
+    if cols is None:
+        y = np.empty((M, N), dtype=np.float64)
+        _check(lib.oracle_w16_gemv(_ptr(xb), bf, _ptr(wb), M, N, K, _ptr(y)), "w16_gemv")
+    else:
+        c = _c(cols, np.int64)
+        y = np.empty((M, len(c)), dtype=np.float64)
+        _check(lib.oracle_w16_gemv_cols(_ptr(xb), bf, _ptr(wb), M, N, K, _ptr(c), len(c), _ptr(y)),
+               "w16_gemv_cols")
     return y

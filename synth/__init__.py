@@ -11,6 +11,8 @@ Canonical format (the library's boundary input):
   zeros   int32 [K/g][N/8] nibble i of word (gi, j) holds z[gi][8j+i]
   codes   int32 [N][K/16]  2-bit field i of word (n, j) holds c[k=16j+i][n], c in {0,1,2}
   x       uint16 [M][K]    binary16 or bfloat16 bit patterns
+  w16     uint16 [N][K]    16-bit weights (the linear layer's own layout),
+                           same type as x
 
 Distributions (the layer shapes are the 27B-class projections the Z100 vLLM
 article, section 四/五, and the ternary tuning page, section 六, time; the
@@ -23,6 +25,8 @@ pages give no value distributions, so these are stated choices):
   s       uniform on [lo, hi] in float64, rounded to nearest-even fp16.
   c       iid with P(c=0)=1/4, P(c=1)=1/2, P(c=2)=1/4, i.e. the sum of two fair
           bits, so weight = c - 1 is -1/0/+1 with probability 1/4, 1/2, 1/4.
+  w16     normal with standard deviation sigma (default 0.02, a typical
+          linear-layer weight scale), rounded like x.
 """
 from __future__ import annotations
 
@@ -88,6 +92,16 @@ def gen_w4(key, N: int, K: int, group: int, s_lo: float = 0.002, s_hi: float = 0
     scales = f64_to_f16_bits(rs.uniform(s_lo, s_hi, size=(G, N)))
     zeros = random_words(rz, G * (N // 8)).reshape(G, N // 8)
     return {"qweight": qweight, "scales": scales, "zeros": zeros}
+
+
+def gen_w16(key, N: int, K: int, dtype: str = "f16", sigma: float = 0.02) -> np.ndarray:
+    """16-bit weights as uint16 bit patterns [N][K]."""
+    v = rng_for(*key, 3).standard_normal((N, K)) * sigma
+    if dtype == "f16":
+        return f64_to_f16_bits(v)
+    if dtype == "bf16":
+        return f64_to_bf16_bits(v)
+    raise ValueError(dtype)
 
 
 def pack_codes(c: np.ndarray) -> np.ndarray:
@@ -195,3 +209,15 @@ def gen_w2t_torch(key, N: int, K: int, group: int, device="cuda", s_lo: float = 
     u = torch.rand((G, N), dtype=torch.float64, device=device, generator=g)
     s = (s_lo + (s_hi - s_lo) * u).to(torch.float16).view(torch.int16)
     return {"codes": words, "scales": s}
+
+
+def gen_w16_torch(key, N: int, K: int, dtype: str = "f16", sigma: float = 0.02, device="cuda"):
+    """16-bit weights as an int16 device tensor of bit patterns [N][K]."""
+    import torch
+    g = _torch_gen(key, device)
+    v = torch.randn((N, K), dtype=torch.float64, device=device, generator=g) * sigma
+    if dtype == "f16":
+        return v.to(torch.float16).view(torch.int16)
+    if dtype == "bf16":
+        return v.to(torch.float32).to(torch.bfloat16).view(torch.int16)
+    raise ValueError(dtype)

@@ -277,3 +277,41 @@ def test_oracle_rejects_bad_shapes():
         oracle.w4_gemv(x, "f16", w["qweight"], w["scales"], w["zeros"], 1, 16, 256, 96)
     with pytest.raises(ValueError):   # column out of range
         oracle.w4_gemv(x, "f16", w["qweight"], w["scales"], w["zeros"], 1, 16, 256, 128, cols=[16])
+
+
+# ------------------------------------------------------------ 16-bit weights ---
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_w16_matches_exact_rational(seed, dtype):
+    # y[m][n] = sum_k x[m][k] w[n][k], every value decoded through numpy
+    # (fp16, or bf16 as the upper half of a float32) into exact fractions.
+    rng = np.random.default_rng(1300 + seed)
+    M, N, K = 1 + seed, 8 + 3 * seed, 32 + 40 * seed
+    to_bits = synth.f64_to_bf16_bits if dtype == "bf16" else synth.f64_to_f16_bits
+    dec = frac_bf16 if dtype == "bf16" else frac_f16
+    xbits = to_bits(rng.standard_normal((M, K)))
+    wbits = to_bits(rng.standard_normal((N, K)) * 0.02)
+    got = oracle.w16_gemv(xbits, dtype, wbits, M, N, K)
+    for m in range(M):
+        for n in range(N):
+            prods = [dec(xbits[m, k]) * dec(wbits[n, k]) for k in range(K)]
+            bound = K * 2.0 ** -53 * float(sum(abs(p) for p in prods))
+            assert abs(got[m, n] - float(sum(prods))) <= bound + 1e-300
+
+
+def test_w16_one_hot_rows_select_weight_columns():
+    # x = e_k reproduces w[:, k] exactly, and only the listed columns are
+    # computed by the sampled variant.
+    N, K = 24, 96
+    wbits = synth.gen_w16((9,), N, K, "f16")
+    ks = [0, 1, 31, 32, 95]
+    x = np.zeros((len(ks), K), dtype=np.uint16)
+    for r, k in enumerate(ks):
+        x[r, k] = 0x3C00                     # fp16 1.0
+    y = oracle.w16_gemv(x, "f16", wbits, len(ks), N, K)
+    wf = wbits.view(np.float16).astype(np.float64)
+    for r, k in enumerate(ks):
+        assert np.array_equal(y[r], wf[:, k])
+    cols = np.array([23, 0, 7], dtype=np.int64)
+    assert np.array_equal(oracle.w16_gemv(x, "f16", wbits, len(ks), N, K, cols=cols), y[:, cols])
