@@ -52,9 +52,12 @@ SHAPES = (("qkv", 5120, 7168), ("o_proj", 5120, 5120), ("gate_up", 5120, 34816),
           ("down", 17408, 5120))
 N_LAYERS = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4_gemv_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "bit_weight_only_03_amd", "csrc", "w4_gemv.hip")
+# The sources that define the 4-bit GEMV kernel (its counters are only valid
+# for the code they were taken on).
+KERNEL_SRCS = [os.path.join(ROOT, "bit_weight_only_03_amd", "csrc", f) for f in ("w4_gemv.hip", "common.h")]
 CALIB_BYTES = 1 << 30       # the plain device copy the counter runs are calibrated with
-KERNEL_RE = re.compile(r"w4_gemv_kernel<[^>]*>")
+KERNEL_RE = re.compile(r"(?:w4_gemv_kernel|w4_gemm_kernel|w16_gemv_kernel|w2t_gemv_kernel|"
+                       r"w2t_gemv_direct_kernel)<[^>]*>")
 
 
 def log(msg):
@@ -72,8 +75,11 @@ def gbps(nbytes, seconds):
 
 
 def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def kernel_key(name):
@@ -309,6 +315,7 @@ def cpu_baseline(torch, synth, oracle_mod, budget_s=12.0):
 ROT_BYTES = 2 << 30   # distinct copies per shape, so no shape sits in the 256 MB cache
 SKINNY_M = (1, 2, 3, 4, 6, 8)
 BATCH_M = (16, 32, 64)            # rows of the batch sweeps (M-tiled kernel)
+W16_M = (1, 2, 4, 8)               # rows of the W16A16 measurements
 SKINNY_KN = (4096, 5120, 8192)
 LM_HEAD = (5120, 152064)
 TERNARY = ((5120, 7168), (5120, 34816), (17408, 5120))
@@ -382,6 +389,59 @@ def residual_fusion(L, torch, synth, oracle_mod, K, N, g, steps, warmup, stream,
         del graph
         out[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / steps / copies, 3)
         out[name + "_parity_rel"] = rel
+    return out
+
+
+def w16_sweep(L, torch, synth, oracle_mod, K, N, Ms, steps, warmup, stream, key):
+    """µs per call of the W16A16 layer (fp16 weights [N][K]) at each M: copies
+    of one weight matrix spanning ROT_BYTES, a graph of one call per copy."""
+    w = synth.gen_w16_torch(key, N, K, "f16")
+    copies = max(2, -(-ROT_BYTES // (N * K * 2)))
+    mats = [w.clone() for _ in range(copies)]
+    torch.cuda.synchronize()
+    out = []
+    rng = np.random.default_rng(2)
+    wh = w.cpu().numpy().view(np.uint16)
+    for M in Ms:
+        x = synth.gen_x_torch(key + (M,), M, K, "f16")
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        wsb = L.w16a16_workspace_bytes(M, N, K)
+        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
+
+        def call(wm):
+            L.w16a16_gemv(x, wm, "f16", y, "f32", M, N, K, ws, wsb, stream)
+
+        with torch.cuda.stream(stream):
+            call(mats[0])
+        torch.cuda.synchronize()
+        variant = L.w4a16_last_variant()
+        cols = np.sort(rng.choice(N, size=min(32, N), replace=False)).astype(np.int64)
+        ref = oracle_mod.w16_gemv(x.cpu().numpy().view(np.uint16), "f16", wh, M, N, K, cols=cols)
+        got = y.cpu().numpy().astype(np.float64)[:, cols]
+        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        if rel > 1e-3:
+            raise SystemExit(f"parity guard failed: w16 M={M} K={K} N={N}: rel={rel:.2e}")
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for wm in mats:
+                call(wm)
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        del graph
+        t = e0.elapsed_time(e1) / 1e3 / steps / copies
+        b = N * K * 2 + M * K * 2 + M * N * 4
+        out.append({"M": M, "K": K, "N": N, "us": round(t * 1e6, 3), "GBps": round(gbps(b, t), 1),
+                    "pct_of_peak": round(100 * gbps(b, t) / PEAK_GBPS, 2), "bytes": b,
+                    "copies": copies, "parity_rel": rel, "kernel": kernel_key(variant)})
     return out
 
 
@@ -612,6 +672,17 @@ def main():
             fusion.append(r)
             log(f"residual add {name}: fused {r['fused_us']:.2f} us, unfused {r['unfused_us']:.2f} us")
         extra["residual_fusion"] = fusion
+        # 16-bit weights (W16A16) on the same layer shapes.
+        w16 = []
+        for (name, K, N) in SHAPES:
+            rows = w16_sweep(L, torch, synth, oracle_mod, K, N, W16_M, max(5, args.steps // 2),
+                             max(2, args.warmup), stream, (6, K, N))
+            for r in rows:
+                r["shape"] = name
+            w16 += rows
+            log(f"w16a16 {name}: " + ", ".join(f"M{r['M']} {r['us']:.2f}us {r['GBps']:.0f}GB/s"
+                                               for r in rows))
+        extra["w16a16"] = w16
         steps_x, warm_x = max(5, args.steps // 2), max(2, args.warmup)
         skinny = []
         for kn in SKINNY_KN:

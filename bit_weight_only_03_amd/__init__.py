@@ -40,6 +40,8 @@ _SIGS = {
     "w4a16_workspace_bytes": [_I, _I, _I, _I, _PSZ],
     "w4a16_gemv": [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P],
     "w4a16_gemv_add": [_P, _I, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _SZ, _P],
+    "w16a16_workspace_bytes": [_I, _I, _I, _PSZ],
+    "w16a16_gemv": [_P, _P, _I, _P, _I, _I, _I, _I, _P, _SZ, _P],
     "w4a16_dequant": [_P, _P, _P, _P, _I, _I, _I, _P],
     "w2t_packed_sizes": [_I, _I, _I, _PSZ, _PSZ],
     "w2t_pack": [_P, _P, _P, _P, _I, _I, _I, _P],
@@ -163,6 +165,18 @@ def w4a16_gemv_add(x, x_dtype, qweight, scales, zeros, residual, residual_dtype,
         _ptr(x), _dt(x_dtype), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(residual),
         _dt(residual_dtype), _ptr(y), _dt(y_dtype), M, N, K, group, _ptr(workspace),
         workspace_bytes, _stream(stream)))
+
+
+def w16a16_workspace_bytes(M: int, N: int, K: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check("w16a16_workspace_bytes", _lib.w16a16_workspace_bytes(M, N, K, ctypes.byref(b)))
+    return b.value
+
+
+def w16a16_gemv(x, w, dtype, y, y_dtype, M, N, K, workspace=None, workspace_bytes=0, stream=None):
+    _check("w16a16_gemv", _lib.w16a16_gemv(_ptr(x), _ptr(w), _dt(dtype), _ptr(y), _dt(y_dtype),
+                                           M, N, K, _ptr(workspace), workspace_bytes,
+                                           _stream(stream)))
 
 
 def w4a16_dequant(qweight, scales, zeros, w, N, K, group, stream=None):

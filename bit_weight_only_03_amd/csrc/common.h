@@ -96,12 +96,22 @@ __device__ __forceinline__ u32x4_t load_nt(const u32x4_t* p) {
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return bitcast<half2_t>(v); }
 __device__ __forceinline__ uint32_t as_u(half2_t v) { return bitcast<uint32_t>(v); }
 
-// (a & mask) | (b & ~mask) in one v_bfi_b32.  The magic exponents below never
-// overlap the nibble masks, so bfi(mask, d, magic) = (d & mask) | magic.
+// (a & mask) | b, for a b with no bit inside mask (the magic exponents below
+// never overlap the nibble masks): one v_and_or_b32 when b is a VGPR value
+// the compiler cannot fold, which opaque_v gives the kernels' magic words
+// (a folded constant splits it into v_and + v_or).  Plain C on purpose, not an
+// inline-asm v_bfi_b32: an MFMA may only read a VGPR two wait states after
+// the VALU op that wrote it, and the compiler inserts those only for writes it
+// can see -- an asm statement is not one, and a bf16 operand built by asm and
+// read by the next-but-one MFMA came out stale.
 __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
-    uint32_t r;
-    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(mask), "v"(a), "v"(b));
-    return r;
+    return (a & mask) | b;
+}
+
+// v, held in a VGPR the optimiser treats as unknown (emits no instruction).
+__device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
 }
 
 // Dequantization in registers, shared by the GEMV and the M-tiled kernel.
@@ -185,6 +195,10 @@ inline int launch_status() {
     set_last_error(hipGetErrorName(e));
     return W4A16_ERR_HIP;
 }
+
+// y = the slice-order sum of S fp32 partials [S][M][N] (+ residual); N % 8 == 0.
+void launch_merge(const void* workspace, void* y, int y_dtype, const void* res, int res_dtype, int M,
+                  int N, int S, hipStream_t st);
 
 // The M-tiled path (w4_gemm.hip) for rows the GEMV does not take.
 constexpr int kMaxRowsGemm = 64;

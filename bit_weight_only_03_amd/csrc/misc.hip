@@ -67,7 +67,7 @@ extern "C" const char* w4a16_status_string(int status) {
         case W4A16_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
         case W4A16_ERR_DTYPE: return "unknown or disallowed dtype";
         case W4A16_ERR_WORKSPACE: return "workspace smaller than the size query reports";
-        case W4A16_ERR_UNSUPPORTED: return "valid request not implemented by this build";
+        case W4A16_ERR_UNSUPPORTED: return "valid request not implemented by this library";
         case W4A16_ERR_HIP: return "HIP runtime error at launch";
         default: return "unknown status";
     }

@@ -1,0 +1,258 @@
+// w16_gemv.hip -- the W16A16 small-M linear layer on gfx950:
+// y[M,N] = x[M,K] . w[N,K]^T with fp16 or bf16 weights of the same type as
+// x, in the layer's own [N][K] layout (no packing), for M = 1..64.
+//
+// The Z100 article (section 六) measures this layer next to the W4A16 one:
+// large K, a few rows, FP16/BF16 weights read straight from memory.  The
+// weights are four times the bytes of the 4-bit path, so the kernel is the
+// same stream without the dequantization: each wave owns one 16-column tile
+// over its workgroup's K slice, the workgroup streams x through LDS one
+// 128-k unit at a time (double-buffered, shared by its waves), and every
+// 16-byte chunk a lane loads is directly the MFMA B operand.
+//
+// Layout of one unit for one tile: lane l serves column n = 16 t + l % 16 and
+// loads the 64 contiguous bytes w[n][128 u + 32 (l / 16) .. + 32), split into
+// four 8-element steps.  The product only needs x and w paired on the same
+// k, so the A operand (x rows) is read from LDS in that same order: step j of
+// lane l takes x[row][128 u + 32 (l / 16) + 8 j .. + 8].  Each row of a tile
+// is then read as 256 contiguous bytes per unit.
+#include <stdlib.h>
+
+#include "common.h"
+
+using namespace w4k;
+
+namespace {
+
+constexpr int kW16Waves = 4;            // waves per workgroup, one tile each
+constexpr int kW16Ring = 2;             // units of weight loads in flight per wave
+constexpr int kW16XStride = kUnitK + 8; // halves per staged x row (+16 B spreads rows over banks)
+constexpr int kW16MaxRows = 64;
+constexpr int kW16MaxSplit = 16;
+
+struct W16Launch {
+    int M, N, K;
+    int U;   // 128-k units (K rounded up)
+    int S;   // K slices
+    int T;   // 16-column tiles
+    int out_dtype;
+};
+
+// One workgroup per (4 tiles, K slice); per unit of the slice: x of the unit
+// staged in LDS buffer u % 2 by all threads (zeros past K and in rows >= M,
+// whose outputs are never stored), every wave multiplies its tile's unit
+// (loaded kW16Ring units earlier) while the next unit's x is in flight, then
+// stores that x into the other buffer; one barrier per unit.  Units past the
+// slice and rows past N load as zeros, so the loop body is uniform.
+template <bool BF16, int RB>
+__global__ __launch_bounds__(256) void w16_gemv_kernel(const uint16_t* __restrict__ x,
+                                                       const uint16_t* __restrict__ w, void* out,
+                                                       W16Launch a) {
+    constexpr int ROWS = 16 * RB;
+    constexpr int XCH = ROWS * (kUnitK / 8);   // 16-byte chunks of one staged unit
+    constexpr int XPT = XCH / 256;             // chunks per thread (= RB)
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][ROWS][kW16XStride];
+
+    const int M = a.M, N = a.N, K = a.K, U = a.U, T = a.T;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15, kc = lane >> 4;
+    const int split = blockIdx.y;
+    const int r0 = split * U / a.S, r1 = (split + 1) * U / a.S;
+    const int nu = r1 - r0;
+    const int t = blockIdx.x * kW16Waves + wave;                         // this wave's tile
+    const int rows = t >= T ? 0 : (N - 16 * t < 16 ? N - 16 * t : 16);  // its columns inside N
+
+    // The tile's rows of w as one resource: lane offset (c K + 32 kc) * 2, unit
+    // offset 256 u.  A row past N or a unit past the slice reads zeros; the
+    // tail of a ragged last unit reads the next row, which meets zero x.
+    const uint32_t wend = (uint32_t)rows * (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)16 * t * K, wend);
+    const uint32_t xend = (uint32_t)M * (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xend);
+    const uint32_t wlane = ((uint32_t)c * (uint32_t)K + 32u * kc) * 2u;
+
+    auto load_unit = [&](int i, u32x4_t (&r)[4]) {
+        const uint32_t off = i < nu ? wlane + (uint32_t)(r0 + i) * (kUnitK * 2) : wend;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            r[j] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rw, off + 16u * j, 0, kAuxNT));
+    };
+
+    u32x4_t xr[XPT];
+    auto load_x = [&](int i) {
+        const int kb = (r0 + i) * kUnitK;
+#pragma unroll
+        for (int p = 0; p < XPT; ++p) {
+            // Branch-free: a chunk outside x (row >= M, k >= K, or a unit past
+            // the slice) takes an offset past the resource and reads zeros.
+            // A load under a branch would make the compiler's wait at the
+            // loop head cover every load in flight, draining the weight ring.
+            const int ch = threadIdx.x + 256 * p;   // < XCH: XCH = 256 RB
+            const int m = ch >> 4, k = kb + 8 * (ch & 15);
+            const bool in = m < M && k < K && i < nu;
+            xr[p] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
+                rx, in ? (uint32_t)(m * K + k) * 2u : xend, 0, 0));
+        }
+    };
+    auto store_x = [&](int b) {
+#pragma unroll
+        for (int p = 0; p < XPT; ++p) {
+            const int ch = threadIdx.x + 256 * p;
+            *(u32x4_t*)&xs[b][ch >> 4][8 * (ch & 15)] = xr[p];
+        }
+    };
+
+    float4_t acc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const u32x4_t (&r)[4], int b) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const u32x4_t av = *(const u32x4_t*)&xs[b][16 * rb + c][32 * kc + 8 * j];
+                if constexpr (BF16)
+                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        bitcast<bf16x8_t>(av), bitcast<bf16x8_t>(r[j]), acc[rb], 0, 0, 0);
+                else
+                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        bitcast<half8_t>(av), bitcast<half8_t>(r[j]), acc[rb], 0, 0, 0);
+            }
+        }
+    };
+
+    u32x4_t ring[kW16Ring][4];
+#pragma unroll
+    for (int d = 0; d < kW16Ring; ++d) load_unit(d, ring[d]);
+    load_x(0);
+    store_x(0);
+    __syncthreads();
+    for (int i = 0; i < nu; i += kW16Ring) {
+#pragma unroll
+        for (int d = 0; d < kW16Ring; ++d) {
+            load_x(i + d + 1);
+            compute(ring[d], d & 1);          // unit i + d sits in buffer (i + d) % 2
+            load_unit(i + d + kW16Ring, ring[d]);
+            store_x((d + 1) & 1);
+            __syncthreads();
+        }
+    }
+
+    // Lane l holds rows 16 rb + 4 (l / 16) + q of column l % 16.
+    const int n = 16 * t + c;
+    if (c >= rows) return;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = 16 * rb + 4 * kc + q;
+            if (m >= M) continue;
+            const size_t o = (size_t)m * N + n;
+            if (a.S > 1)
+                ((float*)out)[(size_t)split * M * N + o] = acc[rb][q];
+            else
+                store_out(out, a.out_dtype, o, acc[rb][q]);
+        }
+}
+
+typedef void (*w16_kernel_t)(const uint16_t*, const uint16_t*, void*, W16Launch);
+
+template <bool BF16>
+w16_kernel_t pick_w16_rb(int rb) {
+    switch (rb) {
+        case 1: return w16_gemv_kernel<BF16, 1>;
+        case 2: return w16_gemv_kernel<BF16, 2>;
+        case 3: return w16_gemv_kernel<BF16, 3>;
+        default: return w16_gemv_kernel<BF16, 4>;
+    }
+}
+
+int cu_count16() {
+    static int n = 0;
+    if (!n) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        n = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+             prop.multiProcessorCount > 0)
+                ? prop.multiProcessorCount
+                : 256;
+    }
+    return n;
+}
+
+struct W16Plan {
+    int rb, split;
+    long long workgroups;
+};
+
+// K slices double until every CU has two workgroups, each slice keeping at
+// least four units (4 KB of weights per wave per unit).
+W16Plan w16_plan(int M, int N, int K) {
+    W16Plan p;
+    const int U = (K + kUnitK - 1) / kUnitK;
+    const int T = pad_n(N) / kTileN;
+    p.rb = (M + 15) / 16;
+    p.workgroups = (T + kW16Waves - 1) / kW16Waves;
+    p.split = 1;
+    while (p.workgroups * p.split < 2LL * cu_count16() && U / (2 * p.split) >= 4 &&
+           p.split < kW16MaxSplit)
+        p.split *= 2;
+    if (const char* e = getenv("W16A16_SPLIT")) {
+        const int s = atoi(e);
+        if (s >= 1 && s <= U && s <= kW16MaxSplit) p.split = s;
+    }
+    return p;
+}
+
+int check_w16(int M, int N, int K) {
+    if (M < 1 || M > kW16MaxRows || N < 8 || N % 8 || K < 8 || K % 8) return W4A16_ERR_SHAPE;
+    if ((long long)M * K * 2 > 0xffffffffLL || 16LL * K * 2 > 0xffffffffLL) return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+size_t w16_workspace(const W16Plan& p, int M, int N) {
+    return p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0;
+}
+
+}  // namespace
+
+extern "C" int w16a16_workspace_bytes(int M, int N, int K, size_t* bytes) {
+    if (!bytes) return W4A16_ERR_NULL;
+    if (int rc = check_w16(M, N, K)) return rc;
+    *bytes = w16_workspace(w16_plan(M, N, K), M, N);
+    return W4A16_OK;
+}
+
+extern "C" int w16a16_gemv(const void* x, const void* w, int dtype, void* y, int y_dtype, int M,
+                           int N, int K, void* workspace, size_t workspace_bytes,
+                           w4a16_stream_t stream) {
+    if (!x || !w || !y) return W4A16_ERR_NULL;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (y_dtype != W4A16_F32 && y_dtype != W4A16_F16 && y_dtype != W4A16_BF16)
+        return W4A16_ERR_DTYPE;
+    if (int rc = check_w16(M, N, K)) return rc;
+    if (!w4h::aligned16(x) || !w4h::aligned16(w) || !w4h::aligned16(y)) return W4A16_ERR_ALIGN;
+    const W16Plan p = w16_plan(M, N, K);
+    const size_t need = w16_workspace(p, M, N);
+    if (need) {
+        if (!workspace) return W4A16_ERR_NULL;
+        if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+        if (!w4h::aligned16(workspace)) return W4A16_ERR_ALIGN;
+    }
+    const bool bf16 = dtype == W4A16_BF16;
+    const int U = (K + kUnitK - 1) / kUnitK;
+    const int T = pad_n(N) / kTileN;
+    W16Launch l{M, N, K, U, p.split, T, y_dtype};
+    hipStream_t st = (hipStream_t)stream;
+    w4h::begin_launches();
+    hipLaunchKernelGGL(bf16 ? pick_w16_rb<true>(p.rb) : pick_w16_rb<false>(p.rb),
+                       dim3((unsigned)p.workgroups, p.split), dim3(64 * kW16Waves), 0, st,
+                       (const uint16_t*)x, (const uint16_t*)w, p.split > 1 ? workspace : y, l);
+    if (p.split > 1) w4h::launch_merge(workspace, y, y_dtype, nullptr, W4A16_F32, M, N, p.split, st);
+    w4h::set_last_variant("w16_mfma16 %s kernel=w16_gemv_kernel<%s, %d> tiles=%d slices=%d "
+                          "workgroups=%lld",
+                          bf16 ? "bf16" : "f16", bf16 ? "true" : "false", p.rb, T, p.split,
+                          p.workgroups);
+    return w4h::launch_status();
+}

@@ -57,7 +57,7 @@ struct GSlot {
 // One workgroup per (4 x TN tiles, K slice).  Wave w owns tiles
 // [t0 + w TN, t0 + (w + 1) TN).  Per 128-k unit u of the slice:
 //   - all threads have staged x[0:M, u's 128 k] in LDS buffer u % 2 (zeros
-//     past K; rows >= M are never staged, their outputs never stored);
+//     past K and in rows >= M, whose outputs are never stored);
 //   - every wave multiplies its tiles' unit u, whose loads were issued kRing
 //     units earlier (a ring of kRing units per tile), while the loads of
 //     unit u+1's x are in flight; then it stores that x into the other
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
     constexpr int SPU = SPG >= 4 ? 4 : SPG;       // 32-k steps per group inside one unit
     constexpr int ROWS = 16 * RB;
     constexpr int XCH = ROWS * (kUnitK / 8);      // 16-byte chunks of one staged unit
-    constexpr int XPT = (XCH + 255) / 256;        // chunks per thread
+    constexpr int XPT = XCH / 256;                // chunks per thread (= RB)
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][ROWS][kXStride];
 
     const int M = a.M, N = a.N, K = a.K, U = a.U, T = a.T;
@@ -95,7 +95,8 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(qdev + (size_t)tw * U * kLanes, wend);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdev + (size_t)tw * Gp * kTileN, send);
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(zdev + (size_t)tw * Gp * 2, zend);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    const uint32_t xend = (uint32_t)M * (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xend);
     const uint32_t wlane = (uint32_t)lane * 16u, slane = (uint32_t)c * 2u,
                    zlane = (uint32_t)(c >> 3) * 4u;
 
@@ -123,25 +124,27 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
         const int kb = (r0 + i) * kUnitK;
 #pragma unroll
         for (int p = 0; p < XPT; ++p) {
-            const int ch = threadIdx.x + 256 * p;
+            // Branch-free: a chunk outside x (row >= M, k >= K, or a unit past
+            // the slice) takes an offset past the resource and reads zeros.
+            // A load under a branch would make the compiler's wait at the
+            // loop head cover every load in flight, draining the weight ring.
+            const int ch = threadIdx.x + 256 * p;   // < XCH: XCH = 256 RB
             const int m = ch >> 4, k = kb + 8 * (ch & 15);
-            xr[p] = u32x4_t{0u, 0u, 0u, 0u};
-            if (ch < XCH && m < M && k < K && i < nu)
-                xr[p] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
-                    rx, (uint32_t)(m * K + k) * 2u, 0, 0));
+            const bool in = m < M && k < K && i < nu;
+            xr[p] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
+                rx, in ? (uint32_t)(m * K + k) * 2u : xend, 0, 0));
         }
     };
     auto store_x = [&](int b) {
 #pragma unroll
         for (int p = 0; p < XPT; ++p) {
             const int ch = threadIdx.x + 256 * p;
-            const int m = ch >> 4;
-            if (ch < XCH && m < M) *(u32x4_t*)&xs[b][m][8 * (ch & 15)] = xr[p];
+            *(u32x4_t*)&xs[b][ch >> 4][8 * (ch & 15)] = xr[p];
         }
     };
 
     const int zshift = 4 * (c & 7);
-    const uint32_t magic = BF16 ? 0x43004300u : 0x64006400u;   // 128.0 / 1024.0 pairs
+    const uint32_t magic = opaque_v(BF16 ? 0x43004300u : 0x64006400u);   // 128.0 / 1024.0 pairs
     float4_t total[TN][RB];
 #pragma unroll
     for (int j = 0; j < TN; ++j)

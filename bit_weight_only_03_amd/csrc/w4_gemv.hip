@@ -219,7 +219,7 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
 
     // 3) Dequantize and multiply, unit by unit.
     const int zshift = 4 * (c & 7);
-    const uint32_t magic = BF16 ? 0x43004300u : 0x64006400u;   // 128.0 / 1024.0 pairs
+    const uint32_t magic = opaque_v(BF16 ? 0x43004300u : 0x64006400u);   // 128.0 / 1024.0 pairs
     const bool xrow = c < M;                                    // lane supplies x row c
     const uint8_t* xlane = (const uint8_t*)xs + (uint32_t)(c * a.xstride + 8 * kc) * 2u;
     float4_t total[TPW];
@@ -606,18 +606,6 @@ int check_gemv_args(const void* x, int x_dtype, const void* q, const void* s, co
 }
 
 // y = the slice-order sum of S fp32 partials [S][M][N] in the workspace.
-void launch_merge(const void* workspace, void* y, int y_dtype, const void* res, int res_dtype, int M,
-                  int N, int S, hipStream_t st) {
-    const int MN4 = M * N / 4;   // N % 8 == 0
-    const dim3 grid((MN4 + 255) / 256);
-    if (merge_kernel_t mk = pick_merge(S))
-        hipLaunchKernelGGL(mk, grid, dim3(256), 0, st, (const float4_t*)workspace, y, y_dtype, MN4,
-                           res, res_dtype);
-    else
-        hipLaunchKernelGGL(splitk_merge_any_kernel, grid, dim3(256), 0, st,
-                           (const float4_t*)workspace, y, y_dtype, MN4, res, res_dtype, S);
-}
-
 int launch_gemm(const void* x, int x_dtype, const void* qweight, const void* scales, const void* zeros,
                 void* y, int y_dtype, const void* res, int res_dtype, int M, int N, int K, int group,
                 void* workspace, size_t workspace_bytes, hipStream_t st) {
@@ -632,7 +620,7 @@ int launch_gemm(const void* x, int x_dtype, const void* qweight, const void* sca
     w4h::begin_launches();
     w4h::gemm_launch(p, x, bf16, qweight, scales, zeros, y, y_dtype, res, res_dtype, M, N, K, group,
                      workspace, st);
-    if (p.split > 1) launch_merge(workspace, y, y_dtype, res, res_dtype, M, N, p.split, st);
+    if (p.split > 1) w4h::launch_merge(workspace, y, y_dtype, res, res_dtype, M, N, p.split, st);
     w4h::set_last_variant("w4_gemm16 %s g%d kernel=w4_gemm_kernel<%s, %d, %d, %d> tiles=%d slices=%d "
                           "workgroups=%lld",
                           bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.rb, p.tn,
@@ -641,6 +629,24 @@ int launch_gemm(const void* x, int x_dtype, const void* qweight, const void* sca
 }
 
 }  // namespace
+
+namespace w4h {
+
+// y = the slice-order sum of S fp32 partials [S][M][N] in the workspace (+ the
+// residual, when there is one).
+void launch_merge(const void* workspace, void* y, int y_dtype, const void* res, int res_dtype, int M,
+                  int N, int S, hipStream_t st) {
+    const int MN4 = M * N / 4;   // N % 8 == 0
+    const dim3 grid((MN4 + 255) / 256);
+    if (merge_kernel_t mk = pick_merge(S))
+        hipLaunchKernelGGL(mk, grid, dim3(256), 0, st, (const float4_t*)workspace, y, y_dtype, MN4,
+                           res, res_dtype);
+    else
+        hipLaunchKernelGGL(splitk_merge_any_kernel, grid, dim3(256), 0, st,
+                           (const float4_t*)workspace, y, y_dtype, MN4, res, res_dtype, S);
+}
+
+}  // namespace w4h
 
 extern "C" int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* bytes) {
     if (!bytes) return W4A16_ERR_NULL;
@@ -687,7 +693,7 @@ int gemv_impl(const void* x, int x_dtype, const void* qweight, const void* scale
                        (const uint16_t*)x,
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros,
                        out, p.l);
-    if (p.l.S > 1) launch_merge(workspace, y, y_dtype, res, res_dtype, M, N, p.l.S, st);
+    if (p.l.S > 1) w4h::launch_merge(workspace, y, y_dtype, res, res_dtype, M, N, p.l.S, st);
     w4h::set_last_variant("w4_mfma16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, %d> tiles=%d slices=%d "
                           "waves=%d upw=%d tpw=%d lds=%zu",
                           bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.upw,

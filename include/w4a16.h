@@ -67,7 +67,7 @@ typedef enum {
     W4A16_ERR_ALIGN = -3,        /* a device pointer is not 16-byte aligned */
     W4A16_ERR_DTYPE = -4,        /* unknown or disallowed dtype */
     W4A16_ERR_WORKSPACE = -5,    /* workspace smaller than *_workspace_bytes */
-    W4A16_ERR_UNSUPPORTED = -6,  /* valid request this build does not implement */
+    W4A16_ERR_UNSUPPORTED = -6,  /* valid request this library does not implement */
     W4A16_ERR_HIP = -7           /* the HIP runtime reported an error at launch */
 } w4a16_status;
 
@@ -136,6 +136,19 @@ int w4a16_gemv_add(const void* x, int x_dtype, const void* qweight, const void* 
  * packed layout.  Exact, since |q - z| <= 15 times an fp16 scale fits in fp32. */
 int w4a16_dequant(const void* qweight, const void* scales, const void* zeros, float* w, int N,
                   int K, int group, w4a16_stream_t stream);
+
+/* ---- 16-bit weights (W16A16) ----
+ * The same small-M layer with unquantized FP16/BF16 weights (the Z100
+ * article, section 六, measures it next to W4A16): y[M,N] = x[M,K] . w[N,K]^T,
+ * w in the layer's own row-major [N][K] layout (no packing), of the same
+ * dtype as x (W4A16_F16 or W4A16_BF16).  Shape: 1 <= M <= 64, N % 8 == 0,
+ * K % 8 == 0 (N, K >= 8).  x, w, y 16-byte aligned; y_dtype W4A16_F32,
+ * W4A16_F16 or W4A16_BF16.  Products and sums in fp32, deterministic.
+ * workspace as for w4a16_gemv (NULL when w16a16_workspace_bytes reports 0;
+ * scratch owned by the call). */
+int w16a16_workspace_bytes(int M, int N, int K, size_t* bytes);
+int w16a16_gemv(const void* x, const void* w, int dtype, void* y, int y_dtype, int M, int N, int K,
+                void* workspace, size_t workspace_bytes, w4a16_stream_t stream);
 
 /* ---- ternary 2-bit variant: w = (c - 1) * s, one fp16 scale per group ----
  * Shape contract: 1 <= N, 1 <= K, K % group == 0, K % 16 == 0,

@@ -17,12 +17,13 @@ import bit_weight_only_03_amd as lib
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(w(?:4a16|2t)_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(w(?:4a16|2t|16a16)_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("w4a16_pack", "w4a16_unpack", "w4a16_gemv", "w4a16_gemv_add", "w4a16_dequant",
+              "w16a16_gemv", "w16a16_workspace_bytes",
               "w4a16_packed_sizes",
               "w4a16_workspace_bytes", "w2t_pack", "w2t_unpack", "w2t_gemv", "w2t_dequant",
               "w2t_packed_sizes", "w2t_workspace_bytes", "w4a16_bw_probe", "w4a16_status_string",
@@ -127,3 +128,21 @@ def test_gemv_add_argument_checks():
     assert rc(residual_dtype=7) == -4
     assert rc(residual=good + 4) == -3
     assert rc(M=65) == -2
+
+
+def test_w16a16_argument_checks():
+    good = 1 << 20
+    assert lib.w16a16_workspace_bytes(1, 4096, 4096) % (1 * 4096 * 4) == 0   # S slices of fp32 [M][N]
+    for (M, N, K) in [(0, 64, 64), (65, 64, 64), (1, 12, 64), (1, 64, 100)]:
+        with pytest.raises(lib.W4A16Error) as e:
+            lib.w16a16_workspace_bytes(M, N, K)
+        assert e.value.status == -2
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.w16a16_gemv(good, good, 2, good, 2, 1, 64, 64, stream=0)     # f32 weights
+    assert e.value.status == -4
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.w16a16_gemv(good, good + 8, 0, good, 2, 1, 64, 64, stream=0)
+    assert e.value.status == -3
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.w16a16_gemv(good, 0, 0, good, 2, 1, 64, 64, stream=0)
+    assert e.value.status == -1

@@ -250,6 +250,48 @@ def test_w4_gemv_add_zero_residual_is_bitwise_gemv():
         assert torch.equal(y0, y1)
 
 
+# 16-bit weights: both dtypes, every output dtype, M from 1 to 64, ragged N
+# (a last tile of 8 columns) and ragged K (a last unit of 40 k), with and
+# without K slices.
+W16_CASES = [
+    # (M, N, K, dtype)
+    (1, 264, 1000, "f16"),
+    (2, 520, 4096, "bf16"),
+    (4, 4096, 4096, "f16"),
+    (8, 136, 2048, "bf16"),
+    (16, 1032, 640, "f16"),
+    (24, 40, 8, "bf16"),
+    (64, 264, 1536, "f16"),
+    (3, 12296, 512, "bf16"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,dt", W16_CASES)
+def test_w16a16_gemv_matches_oracle(M, N, K, dt):
+    say(f"w16a16 M={M} N={N} K={K} {dt}")
+    key = (121, M, N, K)
+    w = synth.gen_w16(key, N, K, dt)
+    x = synth.gen_x(key, M, K, dt)
+    wd, xd = dev(w), dev(x)
+    wsb = L.w16a16_workspace_bytes(M, N, K)
+    ws = workspace_bytes(wsb) if wsb else None
+    cols = np.arange(N) if N <= 4200 else np.sort(np.random.default_rng(4).choice(N, 600, replace=False))
+    ref = oracle.w16_gemv(x, dt, w, M, N, K, cols=cols.astype(np.int64))
+    for ydt, extra in (("f32", 0.0), ("f16", 2.0 ** -11), ("bf16", 2.0 ** -8)):
+        y = torch.full((M, N), float("nan"), dtype=_TORCH_DT[ydt], device=DEV)
+        L.w16a16_gemv(xd, wd, dt, y, ydt, M, N, K, ws, wsb)
+        torch.cuda.synchronize()
+        if ydt == "f32":
+            say("  variant: " + L.w4a16_last_variant())
+            assert "w16_gemv_kernel" in L.w4a16_last_variant()
+            y0 = y.clone()
+        assert_parity(to_f64(y)[:, cols], ref, f"w16 M={M} N={N} K={K} {dt} y={ydt}", extra_rel=extra)
+    y1 = torch.empty_like(y0)
+    L.w16a16_gemv(xd, wd, dt, y1, "f32", M, N, K, ws, wsb)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)                           # deterministic
+
+
 W2_GEMV_CASES = [
     (1, 7, 32, 32, "f16"),
     (4, 40, 768, 128, "f16"),

@@ -8,6 +8,11 @@ such loads, so nothing else guards that wait: it is only correct if at least
 N vector memory loads are issued, in straight-line code, between the last x
 load and the wait, and if no LDS read comes before it.  This test compiles
 the kernel sources to assembly and checks that for every instantiation.
+
+It also checks that the kernels hold no other inline assembly.  The compiler
+puts the wait states an MFMA needs after a VALU op that writes one of its
+operands only where it sees that op; an asm statement that writes a VGPR
+hides it, and an operand built that way was once read stale.
 """
 import os
 import re
@@ -21,7 +26,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "bit_weight_only_03_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["w4_gemv.hip", "w2t.hip"]
+SOURCES = ["w4_gemv.hip", "w2t.hip", "w4_gemm.hip", "w16_gemv.hip"]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
 
@@ -99,3 +104,19 @@ def test_x_wait_covers_the_x_loads(asm_files):
     # every 4-bit and staged ternary instantiation stages x this way
     assert checked >= 150, checked
     assert not bad, "\n".join(bad[:20])
+
+
+def test_no_inline_asm_besides_the_x_wait(asm_files):
+    bad = []
+    for src, text in asm_files.items():
+        for name, lines in functions(text):
+            for i, l in enumerate(lines):
+                if l.startswith(";;#ASMSTART"):
+                    body = []
+                    for m in lines[i + 1:]:
+                        if m.startswith(";;#ASMEND"):
+                            break
+                        body.append(m)
+                    if body and not (len(body) == 1 and re.fullmatch(r"s_waitcnt vmcnt\(\d+\)", body[0])):
+                        bad.append(f"{src} {name}: {body}")
+    assert not bad, "\n".join(bad[:10])
