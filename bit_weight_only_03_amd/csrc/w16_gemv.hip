@@ -10,12 +10,16 @@
 // 128-k unit at a time (double-buffered, shared by its waves), and every
 // 16-byte chunk a lane loads is directly the MFMA B operand.
 //
-// Layout of one unit for one tile: lane l serves column n = 16 t + l % 16 and
-// loads the 64 contiguous bytes w[n][128 u + 32 (l / 16) .. + 32), split into
-// four 8-element steps.  The product only needs x and w paired on the same
-// k, so the A operand (x rows) is read from LDS in that same order: step j of
-// lane l takes x[row][128 u + 32 (l / 16) + 8 j .. + 8].  Each row of a tile
-// is then read as 256 contiguous bytes per unit.
+// Layout of one unit for one tile: lane l serves column n = 16 t + l % 16;
+// its j-th 16-byte load (j = 0..3) is w[n][128 u + 32 j + 8 (l / 16) .. + 8],
+// which is also what the 32-k MFMA step j expects from that lane.  One load
+// instruction of a wave thus reads 64 contiguous bytes of each of its 16
+// rows, and two consecutive instructions fill a 128-byte line.  Giving each
+// lane its own contiguous 64 bytes instead (four 16-byte pieces 64 bytes
+// apart per row and instruction) ran at 2.2-2.7 TB/s against 3.4-4.4 TB/s.
+// The loads take the default cache policy: the two instructions that share
+// a line then meet in the vector L1, and the non-temporal hint measured
+// 5-25% slower.
 #include <stdlib.h>
 
 #include "common.h"
@@ -25,7 +29,7 @@ using namespace w4k;
 namespace {
 
 constexpr int kW16Waves = 4;            // waves per workgroup, one tile each
-constexpr int kW16Ring = 2;             // units of weight loads in flight per wave
+constexpr int kW16Ring = 2;             // units of weight loads in flight per wave (4: no gain, 92 VGPRs)
 constexpr int kW16XStride = kUnitK + 8; // halves per staged x row (+16 B spreads rows over banks)
 constexpr int kW16MaxRows = 64;
 constexpr int kW16MaxSplit = 16;
@@ -63,20 +67,20 @@ __global__ __launch_bounds__(256) void w16_gemv_kernel(const uint16_t* __restric
     const int t = blockIdx.x * kW16Waves + wave;                         // this wave's tile
     const int rows = t >= T ? 0 : (N - 16 * t < 16 ? N - 16 * t : 16);  // its columns inside N
 
-    // The tile's rows of w as one resource: lane offset (c K + 32 kc) * 2, unit
-    // offset 256 u.  A row past N or a unit past the slice reads zeros; the
+    // The tile's rows of w as one resource: lane offset 2 c K + 16 kc, unit
+    // offset 256 u, step offset 64 j.  A row past N or a unit past the slice reads zeros; the
     // tail of a ragged last unit reads the next row, which meets zero x.
     const uint32_t wend = (uint32_t)rows * (uint32_t)K * 2u;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)16 * t * K, wend);
     const uint32_t xend = (uint32_t)M * (uint32_t)K * 2u;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xend);
-    const uint32_t wlane = ((uint32_t)c * (uint32_t)K + 32u * kc) * 2u;
+    const uint32_t wlane = (uint32_t)c * (uint32_t)K * 2u + 16u * kc;
 
     auto load_unit = [&](int i, u32x4_t (&r)[4]) {
         const uint32_t off = i < nu ? wlane + (uint32_t)(r0 + i) * (kUnitK * 2) : wend;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            r[j] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rw, off + 16u * j, 0, kAuxNT));
+            r[j] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rw, off + 64u * j, 0, 0));
     };
 
     u32x4_t xr[XPT];
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(256) void w16_gemv_kernel(const uint16_t* __restric
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
-                const u32x4_t av = *(const u32x4_t*)&xs[b][16 * rb + c][32 * kc + 8 * j];
+                const u32x4_t av = *(const u32x4_t*)&xs[b][16 * rb + c][32 * j + 8 * kc];
                 if constexpr (BF16)
                     acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         bitcast<bf16x8_t>(av), bitcast<bf16x8_t>(r[j]), acc[rb], 0, 0, 0);
@@ -186,8 +190,11 @@ struct W16Plan {
     long long workgroups;
 };
 
-// K slices double until every CU has two workgroups, each slice keeping at
-// least four units (4 KB of weights per wave per unit).
+// K slices double while each keeps at least six units (4 KB of weights per
+// wave per unit) and the grid stays under eight workgroups per CU.  The
+// merge of M x N fp32 partials per slice is small next to the 2 N K weight
+// bytes, and the extra workgroups are what keeps enough loads in flight:
+// gate_up (N = 34816, K = 5120) took 80 us unsplit, 67 us in four slices.
 W16Plan w16_plan(int M, int N, int K) {
     W16Plan p;
     const int U = (K + kUnitK - 1) / kUnitK;
@@ -195,7 +202,7 @@ W16Plan w16_plan(int M, int N, int K) {
     p.rb = (M + 15) / 16;
     p.workgroups = (T + kW16Waves - 1) / kW16Waves;
     p.split = 1;
-    while (p.workgroups * p.split < 2LL * cu_count16() && U / (2 * p.split) >= 4 &&
+    while (p.workgroups * p.split < 8LL * cu_count16() && U / (2 * p.split) >= 6 &&
            p.split < kW16MaxSplit)
         p.split *= 2;
     if (const char* e = getenv("W16A16_SPLIT")) {
