@@ -1,6 +1,6 @@
 /*
- * oracle.c -- plain, slow CPU reference for the group-wise 4-bit (W4A16) and
- * ternary 2-bit small-M linear layer.  TEST INFRASTRUCTURE ONLY: nothing in
+ * oracle.c -- plain, slow CPU reference for the group-wise 4-bit (W4A16),
+ * ternary 2-bit, 16-bit (W16A16) and MXFP4 small-M linear layer.  TEST INFRASTRUCTURE ONLY: nothing in
  * the product library links, includes or calls this file; only the tests, the
  * smoke check and the CPU-baseline leg of the benchmark use it.
  *
@@ -297,5 +297,94 @@ int oracle_w16_gemv_cols(const uint16_t* x, int is_bf16, const uint16_t* w, int 
             y[(size_t)m * ncols + c] = acc;
         }
     }
+    return ORACLE_OK;
+}
+
+/* ---- MXFP4 weights --------------------------------------------------------
+ * The Z100 article's closing section names FP4/MXFP4 as the next weight
+ * format: 4-bit floating-point elements sharing one block-level scale
+ * (microscaling), defined publicly by the Open Compute Project's MX
+ * specification, which that section cites.  Readings of that definition
+ * (MX v1.0, MXFP4):
+ *   - blocks of 32 consecutive elements along K share one scale;
+ *   - element: FP4 E2M1 -- bit 3 sign, bits 2..1 exponent (bias 1), bit 0
+ *     mantissa; exponent field 0 is subnormal (0 or 0.5), no inf or NaN;
+ *   - scale: E8M0 -- an unsigned 8-bit exponent, value 2^(E - 127), and the
+ *     code 255 is NaN;
+ *   - the weight is element * scale.
+ * Storage (the pages leave it open): qweight uint8 [N][K/2], element k of
+ * row n in byte k/2, low nibble for even k; scales uint8 [N][K/32].  K must
+ * be a multiple of 32.  Every weight and every product with a 16-bit x is
+ * exact in binary64 (at most 2 + 11 significant bits, exponents within
+ * range); the sum runs in ascending k. */
+double oracle_e2m1_to_f64(int code)
+{
+    int sign = (code >> 3) & 1;
+    int e = (code >> 1) & 3;
+    int m = code & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -v : v;
+}
+
+double oracle_e8m0_to_f64(int code)
+{
+    code &= 0xff;
+    return code == 255 ? NAN : ldexp(1.0, code - 127);
+}
+
+static int mx_shape_ok(int N, int K) { return N > 0 && K > 0 && K % 32 == 0; }
+
+static double mx_weight(const uint8_t* qweight, const uint8_t* scales, int K, int n, int k)
+{
+    const uint8_t b = qweight[(size_t)n * (K / 2) + k / 2];
+    const int code = (k & 1) ? (b >> 4) : (b & 15);
+    return oracle_e2m1_to_f64(code) * oracle_e8m0_to_f64(scales[(size_t)n * (K / 32) + k / 32]);
+}
+
+/* w[n][k] in binary64, [N][K]. */
+int oracle_mx_dequant(const uint8_t* qweight, const uint8_t* scales, int N, int K, double* w)
+{
+    if (!mx_shape_ok(N, K)) return ORACLE_EINVAL;
+    #pragma omp parallel for schedule(static)
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k)
+            w[(size_t)n * K + k] = mx_weight(qweight, scales, K, n, k);
+    return ORACLE_OK;
+}
+
+/* y[m][c] = sum_k x[m][k] w[cols[c]][k] for the listed output columns. */
+int oracle_mx_gemv_cols(const uint16_t* x, int x_is_bf16, const uint8_t* qweight,
+                        const uint8_t* scales, int M, int N, int K, const int64_t* cols, int ncols,
+                        double* y)
+{
+    if (!mx_shape_ok(N, K) || M <= 0 || ncols < 0) return ORACLE_EINVAL;
+    for (int c = 0; c < ncols; ++c)
+        if (cols[c] < 0 || cols[c] >= N) return ORACLE_EINVAL;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int c = 0; c < ncols; ++c) {
+        const int n = (int)cols[c];
+        for (int m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k)
+                acc += decode_x(x, x_is_bf16, (size_t)m * K + k) * mx_weight(qweight, scales, K, n, k);
+            y[(size_t)m * ncols + c] = acc;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* y[M][N] = x[M][K] . w^T. */
+int oracle_mx_gemv(const uint16_t* x, int x_is_bf16, const uint8_t* qweight, const uint8_t* scales,
+                   int M, int N, int K, double* y)
+{
+    if (!mx_shape_ok(N, K) || M <= 0) return ORACLE_EINVAL;
+    #pragma omp parallel for schedule(static)
+    for (int n = 0; n < N; ++n)
+        for (int m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k)
+                acc += decode_x(x, x_is_bf16, (size_t)m * K + k) * mx_weight(qweight, scales, K, n, k);
+            y[(size_t)m * N + n] = acc;
+        }
     return ORACLE_OK;
 }

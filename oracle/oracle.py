@@ -56,9 +56,17 @@ def _load():
         lib.oracle_w2t_gemv_cols.argtypes = [P, I, P, P, I, I, I, I, P, I, P]
         lib.oracle_w16_gemv.argtypes = [P, I, P, I, I, I, P]
         lib.oracle_w16_gemv_cols.argtypes = [P, I, P, I, I, I, P, I, P]
+        lib.oracle_e2m1_to_f64.argtypes = [I]
+        lib.oracle_e2m1_to_f64.restype = ctypes.c_double
+        lib.oracle_e8m0_to_f64.argtypes = [I]
+        lib.oracle_e8m0_to_f64.restype = ctypes.c_double
+        lib.oracle_mx_dequant.argtypes = [P, P, I, I, P]
+        lib.oracle_mx_gemv.argtypes = [P, I, P, P, I, I, I, P]
+        lib.oracle_mx_gemv_cols.argtypes = [P, I, P, P, I, I, I, P, I, P]
         for f in ("oracle_w4_dequant", "oracle_w4_gemv", "oracle_w4_gemv_cols",
                   "oracle_w2t_dequant", "oracle_w2t_gemv", "oracle_w2t_gemv_cols",
-                  "oracle_w16_gemv", "oracle_w16_gemv_cols"):
+                  "oracle_w16_gemv", "oracle_w16_gemv_cols", "oracle_mx_dequant",
+                  "oracle_mx_gemv", "oracle_mx_gemv_cols"):
             getattr(lib, f).restype = I
         _lib = lib
     return _lib
@@ -158,4 +166,39 @@ def w16_gemv(x, dtype: str, w, M: int, N: int, K: int, cols=None) -> np.ndarray:
         y = np.empty((M, len(c)), dtype=np.float64)
         _check(lib.oracle_w16_gemv_cols(_ptr(xb), bf, _ptr(wb), M, N, K, _ptr(c), len(c), _ptr(y)),
                "w16_gemv_cols")
+    return y
+
+
+def e2m1_to_f64(code: int) -> float:
+    """Value of a 4-bit E2M1 element code (MXFP4 element)."""
+    return _load().oracle_e2m1_to_f64(int(code))
+
+
+def e8m0_to_f64(code: int) -> float:
+    """Value of an 8-bit E8M0 scale code: 2^(code - 127), NaN for 255."""
+    return _load().oracle_e8m0_to_f64(int(code))
+
+
+def mx_dequant(qweight, scales, N: int, K: int) -> np.ndarray:
+    """MXFP4 weights w[N][K] in float64 from qweight uint8 [N][K/2] (low
+    nibble = even k) and E8M0 scales uint8 [N][K/32]."""
+    q, s = _c(qweight, np.uint8), _c(scales, np.uint8)
+    w = np.empty((N, K), dtype=np.float64)
+    _check(_load().oracle_mx_dequant(_ptr(q), _ptr(s), N, K, _ptr(w)), "mx_dequant")
+    return w
+
+
+def mx_gemv(x, x_dtype: str, qweight, scales, M: int, N: int, K: int, cols=None) -> np.ndarray:
+    """y[M][N] (or the listed columns) = x . w^T in float64 for MXFP4 w."""
+    xb, q, s = _c(x, np.uint16), _c(qweight, np.uint8), _c(scales, np.uint8)
+    bf = 1 if x_dtype == "bf16" else 0
+    lib = _load()
+    if cols is None:
+        y = np.empty((M, N), dtype=np.float64)
+        _check(lib.oracle_mx_gemv(_ptr(xb), bf, _ptr(q), _ptr(s), M, N, K, _ptr(y)), "mx_gemv")
+    else:
+        c = _c(cols, np.int64)
+        y = np.empty((M, len(c)), dtype=np.float64)
+        _check(lib.oracle_mx_gemv_cols(_ptr(xb), bf, _ptr(q), _ptr(s), M, N, K, _ptr(c), len(c),
+                                       _ptr(y)), "mx_gemv_cols")
     return y

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the W4A16 / ternary small-M linear layer.
+"""Seeded synthetic inputs for the W4A16 / ternary / W16A16 / MXFP4 small-M linear layer.
 
 This module only draws random inputs and packs them into the canonical storage
 format; it holds none of the layer's arithmetic (no dequantization, no
@@ -13,6 +13,9 @@ Canonical format (the library's boundary input):
   x       uint16 [M][K]    binary16 or bfloat16 bit patterns
   w16     uint16 [N][K]    16-bit weights (the linear layer's own layout),
                            same type as x
+  mx      qweight uint8 [N][K/2]: element k of row n in byte k/2, low nibble
+                           for even k (4-bit E2M1 codes); scales uint8
+                           [N][K/32]: one E8M0 code per 32-element block
 
 Distributions (the layer shapes are the 27B-class projections the Z100 vLLM
 article, section 四/五, and the ternary tuning page, section 六, time; the
@@ -27,6 +30,10 @@ pages give no value distributions, so these are stated choices):
           bits, so weight = c - 1 is -1/0/+1 with probability 1/4, 1/2, 1/4.
   w16     normal with standard deviation sigma (default 0.02, a typical
           linear-layer weight scale), rounded like x.
+  mx      element codes iid uniform on 0..15 (uniform random bytes); scale
+          codes iid uniform on [e_lo, e_hi] (default 118..125, i.e. block
+          scales 2^-9 .. 2^-2, where weights of standard deviation ~0.02
+          land once quantized to a largest element of 6).
 """
 from __future__ import annotations
 
@@ -102,6 +109,16 @@ def gen_w16(key, N: int, K: int, dtype: str = "f16", sigma: float = 0.02) -> np.
     if dtype == "bf16":
         return f64_to_bf16_bits(v)
     raise ValueError(dtype)
+
+
+def gen_mx(key, N: int, K: int, e_lo: int = 118, e_hi: int = 125):
+    """Canonical MXFP4 weights: dict(qweight uint8 [N][K/2], scales uint8 [N][K/32])."""
+    if K % 32:
+        raise ValueError("need K % 32 == 0")
+    rng = rng_for(*key, 5)
+    q = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    s = rng.integers(e_lo, e_hi + 1, size=(N, K // 32), dtype=np.uint8)
+    return {"qweight": q, "scales": s}
 
 
 def pack_codes(c: np.ndarray) -> np.ndarray:
@@ -221,3 +238,15 @@ def gen_w16_torch(key, N: int, K: int, dtype: str = "f16", sigma: float = 0.02, 
     if dtype == "bf16":
         return v.to(torch.float32).to(torch.bfloat16).view(torch.int16)
     raise ValueError(dtype)
+
+
+def gen_mx_torch(key, N: int, K: int, device="cuda", e_lo: int = 118, e_hi: int = 125):
+    """MXFP4 weights drawn on the device (same distribution as gen_mx, other
+    bits): dict(qweight uint8 [N][K/2], scales uint8 [N][K/32])."""
+    import torch
+    if K % 32:
+        raise ValueError("need K % 32 == 0")
+    g = _torch_gen(key, device)
+    q = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=device, generator=g)
+    s = torch.randint(e_lo, e_hi + 1, (N, K // 32), dtype=torch.uint8, device=device, generator=g)
+    return {"qweight": q, "scales": s}

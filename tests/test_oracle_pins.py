@@ -315,3 +315,135 @@ def test_w16_one_hot_rows_select_weight_columns():
         assert np.array_equal(y[r], wf[:, k])
     cols = np.array([23, 0, 7], dtype=np.int64)
     assert np.array_equal(oracle.w16_gemv(x, "f16", wbits, len(ks), N, K, cols=cols), y[:, cols])
+
+
+# ------------------------------------------------------------------ MXFP4 ---
+
+GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden")
+
+
+def e2m1_table():
+    """code -> value from the cited fixture (tests/golden/mxfp4_e2m1_values.txt)."""
+    out = {}
+    with open(f"{GOLDEN}/mxfp4_e2m1_values.txt") as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                code, bits, val = line.split()
+                assert int(bits, 2) == int(code)
+                out[int(code)] = float(val)
+    assert sorted(out) == list(range(16))
+    return out
+
+
+def e8m0_torch(codes):
+    """E8M0 scale codes decoded by torch's own float8_e8m0fnu type."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e8m0fnu).to(torch.float32).double().numpy()
+
+
+def unpack_fp4_bytes(qweight):
+    """[N][K/2] bytes -> [N][K] codes, by integer division rather than masks:
+    the even element is byte % 16, the odd one byte // 16."""
+    q = qweight.astype(np.int64)
+    out = np.empty((q.shape[0], 2 * q.shape[1]), dtype=np.int64)
+    out[:, 0::2] = q % 16
+    out[:, 1::2] = q // 16
+    return out
+
+
+def test_e2m1_decode_matches_the_spec_table_including_negative_zero():
+    table = e2m1_table()
+    for code, val in table.items():
+        got = oracle.e2m1_to_f64(code)
+        assert got == val and np.signbit(got) == np.signbit(val), (code, got, val)
+
+
+def test_e8m0_decode_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = e8m0_torch(codes)
+    got = np.array([oracle.e8m0_to_f64(c) for c in range(256)])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127
+
+
+def test_mx_dequant_matches_table_times_torch_scale():
+    N, K = 6, 160
+    w = synth.gen_mx((21,), N, K, e_lo=0, e_hi=254)
+    got = oracle.mx_dequant(w["qweight"], w["scales"], N, K)
+    table = e2m1_table()
+    codes = unpack_fp4_bytes(w["qweight"])
+    sc = e8m0_torch(w["scales"])
+    for n in range(N):
+        for k in range(K):
+            assert got[n, k] == table[codes[n, k]] * sc[n, k // 32], (n, k)
+
+
+@pytest.mark.parametrize("seed,x_dtype", [(0, "f16"), (1, "bf16"), (2, "f16")])
+def test_mx_matches_exact_rational(seed, x_dtype):
+    # Small-integer x (exact in fp16 and bf16) and scales 2^-5 .. 2^-2 keep
+    # every partial sum a multiple of 2^-6 below 2^20, so the fp64 sum is
+    # exact and must equal the rational one.
+    rng = np.random.default_rng(1400 + seed)
+    M, N, K = 1 + 2 * seed, 5 + seed, 64 + 96 * seed
+    xi = rng.integers(-8, 9, size=(M, K))
+    to_bits = synth.f64_to_bf16_bits if x_dtype == "bf16" else synth.f64_to_f16_bits
+    xbits = to_bits(xi.astype(np.float64))
+    w = synth.gen_mx((22, seed), N, K, e_lo=122, e_hi=125)
+    table = {c: Fraction(v) for c, v in e2m1_table().items()}
+    codes = unpack_fp4_bytes(w["qweight"])
+    sc = [[Fraction(float(v)) for v in row] for row in e8m0_torch(w["scales"])]
+    got = oracle.mx_gemv(xbits, x_dtype, w["qweight"], w["scales"], M, N, K)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(int(xi[m, k]) * table[codes[n, k]] * sc[n][k // 32] for k in range(K))
+            assert Fraction(got[m, n]) == exact, (m, n)
+
+
+def test_mx_one_hot_x_selects_nibble_and_block():
+    # x = e_k picks w[n][k]: even k from the low nibble, odd k from the high
+    # one, and the scale of block k // 32.
+    N, K = 9, 128
+    w = synth.gen_mx((23,), N, K, e_lo=110, e_hi=140)
+    ks = [0, 1, 30, 31, 32, 33, 95, 127]
+    x = np.zeros((len(ks), K), dtype=np.uint16)
+    for r, k in enumerate(ks):
+        x[r, k] = 0x3C00                     # fp16 1.0
+    y = oracle.mx_gemv(x, "f16", w["qweight"], w["scales"], len(ks), N, K)
+    table = e2m1_table()
+    sc = e8m0_torch(w["scales"])
+    for r, k in enumerate(ks):
+        byte = w["qweight"][:, k // 2].astype(np.int64)
+        code = (byte >> 4) if k % 2 else (byte & 15)
+        want = np.array([table[int(c)] for c in code]) * sc[:, k // 32]
+        assert np.array_equal(y[r], want), k
+    cols = np.array([8, 0, 3], dtype=np.int64)
+    assert np.array_equal(oracle.mx_gemv(x, "f16", w["qweight"], w["scales"], len(ks), N, K,
+                                         cols=cols), y[:, cols])
+
+
+def test_mx_scale_code_plus_one_doubles_output_exactly():
+    M, N, K = 3, 7, 192
+    w = synth.gen_mx((24,), N, K)
+    x = synth.gen_x((24,), M, K, "bf16")
+    y1 = oracle.mx_gemv(x, "bf16", w["qweight"], w["scales"], M, N, K)
+    y2 = oracle.mx_gemv(x, "bf16", w["qweight"], w["scales"] + np.uint8(1), M, N, K)
+    assert np.array_equal(y2, 2.0 * y1)
+
+
+def test_mx_nan_scale_poisons_only_its_column():
+    M, N, K = 2, 5, 64
+    w = synth.gen_mx((25,), N, K)
+    s = w["scales"].copy()
+    s[3, 1] = 255
+    x = synth.gen_x((25,), M, K, "f16")
+    y = oracle.mx_gemv(x, "f16", w["qweight"], s, M, N, K)
+    assert np.isnan(y[:, 3]).all()
+    assert np.isfinite(np.delete(y, 3, axis=1)).all()
+
+
+def test_mx_rejects_k_not_multiple_of_32():
+    with pytest.raises(Exception):
+        oracle.mx_gemv(np.zeros((1, 48), np.uint16), "f16", np.zeros((1, 24), np.uint8),
+                       np.zeros((1, 1), np.uint8), 1, 1, 48)
