@@ -316,6 +316,7 @@ ROT_BYTES = 2 << 30   # distinct copies per shape, so no shape sits in the 256 M
 SKINNY_M = (1, 2, 3, 4, 6, 8)
 BATCH_M = (16, 32, 64)            # rows of the batch sweeps (M-tiled kernel)
 W16_M = (1, 2, 4, 8)               # rows of the W16A16 measurements
+MX_M = (1, 4, 8)                   # rows of the MXFP4 sweep
 SKINNY_KN = (4096, 5120, 8192)
 LM_HEAD = (5120, 152064)
 TERNARY = ((5120, 7168), (5120, 34816), (17408, 5120))
@@ -325,6 +326,12 @@ TERNARY_M = (1, 4, 8)
 def w2t_bytes(M, N, K, g, x_bytes=2, y_bytes=4):
     """Algorithmic bytes of one ternary call: 2-bit codes + fp16 scales + x + y."""
     return N * K // 4 + (K // g) * N * 2 + M * K * x_bytes + M * N * y_bytes
+
+
+def mx_bytes(M, N, K, g=32, x_bytes=2, y_bytes=4):
+    """Algorithmic bytes of one MXFP4 call: 4-bit elements + one E8M0 byte per
+    32 elements + x + y."""
+    return N * K // 2 + (K // 32) * N + M * K * x_bytes + M * N * y_bytes
 
 
 def residual_fusion(L, torch, synth, oracle_mod, K, N, g, steps, warmup, stream, key):
@@ -451,6 +458,9 @@ def rotation_sweep(L, torch, synth, oracle_mod, kind, K, N, g, Ms, steps, warmup
     if kind == "w4":
         w = synth.gen_w4_torch(key, N, K, g)
         sizes = L.w4a16_packed_sizes(N, K, g)
+    elif kind == "mx":
+        w = synth.gen_mx_torch(key, N, K)
+        sizes = L.mxfp4_packed_sizes(N, K)
     else:
         w = synth.gen_w2t_torch(key, N, K, g)
         sizes = L.w2t_packed_sizes(N, K, g)
@@ -460,6 +470,8 @@ def rotation_sweep(L, torch, synth, oracle_mod, kind, K, N, g, Ms, steps, warmup
         bufs = [torch.empty(b, dtype=torch.uint8, device="cuda") for b in sizes]
         if kind == "w4":
             L.w4a16_pack(w["qweight"], w["scales"], w["zeros"], *bufs, N, K, g)
+        elif kind == "mx":
+            L.mxfp4_pack(w["qweight"], w["scales"], *bufs, N, K)
         else:
             L.w2t_pack(w["codes"], w["scales"], *bufs, N, K, g)
         mats.append(bufs)
@@ -472,6 +484,8 @@ def rotation_sweep(L, torch, synth, oracle_mod, kind, K, N, g, Ms, steps, warmup
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         if kind == "w4":
             wsb = L.w4a16_workspace_bytes(M, N, K, g)
+        elif kind == "mx":
+            wsb = L.mxfp4_workspace_bytes(M, N, K)
         else:
             wsb = L.w2t_workspace_bytes(M, N, K, g)
         ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
@@ -479,6 +493,8 @@ def rotation_sweep(L, torch, synth, oracle_mod, kind, K, N, g, Ms, steps, warmup
         def call(bufs):
             if kind == "w4":
                 L.w4a16_gemv(x, "f16", *bufs, y, "f32", M, N, K, g, ws, wsb, stream)
+            elif kind == "mx":
+                L.mxfp4_gemv(x, "f16", *bufs, y, "f32", M, N, K, ws, wsb, stream)
             else:
                 L.w2t_gemv(x, "f16", *bufs, y, "f32", M, N, K, g, ws, wsb, stream)
 
@@ -492,6 +508,9 @@ def rotation_sweep(L, torch, synth, oracle_mod, kind, K, N, g, Ms, steps, warmup
             ref = oracle_mod.w4_gemv(xh, "f16", w["qweight"].cpu().numpy(),
                                      w["scales"].cpu().numpy().view(np.uint16),
                                      w["zeros"].cpu().numpy(), M, N, K, g, cols=cols)
+        elif kind == "mx":
+            ref = oracle_mod.mx_gemv(xh, "f16", w["qweight"].cpu().numpy(),
+                                     w["scales"].cpu().numpy(), M, N, K, cols=cols)
         else:
             ref = oracle_mod.w2t_gemv(xh, "f16", w["codes"].cpu().numpy(),
                                       w["scales"].cpu().numpy().view(np.uint16), M, N, K, g,
@@ -518,7 +537,7 @@ def rotation_sweep(L, torch, synth, oracle_mod, kind, K, N, g, Ms, steps, warmup
             torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / 1e3 / steps / copies
         del graph
-        b = alg_bytes(M, N, K, g) if kind == "w4" else w2t_bytes(M, N, K, g)
+        b = {"w4": alg_bytes, "mx": mx_bytes, "w2t": w2t_bytes}[kind](M, N, K, g)
         out.append({"M": M, "K": K, "N": N, "group": g, "us": round(t * 1e6, 3),
                     "GBps": round(gbps(b, t), 1), "pct_of_peak": round(100 * gbps(b, t) / PEAK_GBPS, 2),
                     "bytes": b, "copies": copies, "parity_rel": rel,
@@ -683,6 +702,17 @@ def main():
             log(f"w16a16 {name}: " + ", ".join(f"M{r['M']} {r['us']:.2f}us {r['GBps']:.0f}GB/s"
                                                for r in rows))
         extra["w16a16"] = w16
+        # MXFP4 weights on the same layer shapes.
+        mx = []
+        for (name, K, N) in SHAPES:
+            rows = rotation_sweep(L, torch, synth, oracle_mod, "mx", K, N, 32, MX_M,
+                                  max(5, args.steps // 2), max(2, args.warmup), stream, (7, K, N))
+            for r in rows:
+                r["shape"] = name
+            mx += rows
+            log(f"mxfp4 {name}: " + ", ".join(f"M{r['M']} {r['us']:.2f}us {r['GBps']:.0f}GB/s"
+                                              for r in rows))
+        extra["mxfp4"] = mx
         steps_x, warm_x = max(5, args.steps // 2), max(2, args.warmup)
         skinny = []
         for kn in SKINNY_KN:

@@ -43,6 +43,12 @@ _SIGS = {
     "w16a16_workspace_bytes": [_I, _I, _I, _PSZ],
     "w16a16_gemv": [_P, _P, _I, _P, _I, _I, _I, _I, _P, _SZ, _P],
     "w4a16_dequant": [_P, _P, _P, _P, _I, _I, _I, _P],
+    "mxfp4_packed_sizes": [_I, _I, _PSZ, _PSZ],
+    "mxfp4_pack": [_P, _P, _P, _P, _I, _I, _P],
+    "mxfp4_unpack": [_P, _P, _P, _P, _I, _I, _P],
+    "mxfp4_workspace_bytes": [_I, _I, _I, _PSZ],
+    "mxfp4_gemv": [_P, _I, _P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P],
+    "mxfp4_dequant": [_P, _P, _P, _I, _I, _P],
     "w2t_packed_sizes": [_I, _I, _I, _PSZ, _PSZ],
     "w2t_pack": [_P, _P, _P, _P, _I, _I, _I, _P],
     "w2t_unpack": [_P, _P, _P, _P, _I, _I, _I, _P],
@@ -182,6 +188,40 @@ def w16a16_gemv(x, w, dtype, y, y_dtype, M, N, K, workspace=None, workspace_byte
 def w4a16_dequant(qweight, scales, zeros, w, N, K, group, stream=None):
     _check("w4a16_dequant", _lib.w4a16_dequant(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(w),
                                                N, K, group, _stream(stream)))
+
+
+def mxfp4_packed_sizes(N: int, K: int):
+    q, s = _SZ(), _SZ()
+    _check("mxfp4_packed_sizes", _lib.mxfp4_packed_sizes(N, K, ctypes.byref(q), ctypes.byref(s)))
+    return q.value, s.value
+
+
+def mxfp4_pack(qweight_canon, scales_canon, qweight, scales, N, K, stream=None):
+    _check("mxfp4_pack", _lib.mxfp4_pack(_ptr(qweight_canon), _ptr(scales_canon), _ptr(qweight),
+                                         _ptr(scales), N, K, _stream(stream)))
+
+
+def mxfp4_unpack(qweight, scales, qweight_canon, scales_canon, N, K, stream=None):
+    _check("mxfp4_unpack", _lib.mxfp4_unpack(_ptr(qweight), _ptr(scales), _ptr(qweight_canon),
+                                             _ptr(scales_canon), N, K, _stream(stream)))
+
+
+def mxfp4_workspace_bytes(M: int, N: int, K: int) -> int:
+    b = _SZ()
+    _check("mxfp4_workspace_bytes", _lib.mxfp4_workspace_bytes(M, N, K, ctypes.byref(b)))
+    return b.value
+
+
+def mxfp4_gemv(x, x_dtype, qweight, scales, y, y_dtype, M, N, K, workspace=None, workspace_bytes=0,
+               stream=None):
+    _check("mxfp4_gemv", _lib.mxfp4_gemv(_ptr(x), _dt(x_dtype), _ptr(qweight), _ptr(scales), _ptr(y),
+                                         _dt(y_dtype), M, N, K, _ptr(workspace), workspace_bytes,
+                                         _stream(stream)))
+
+
+def mxfp4_dequant(qweight, scales, w, N, K, stream=None):
+    _check("mxfp4_dequant", _lib.mxfp4_dequant(_ptr(qweight), _ptr(scales), _ptr(w), N, K,
+                                               _stream(stream)))
 
 
 def w2t_packed_sizes(N: int, K: int, group: int):

@@ -143,6 +143,35 @@ __device__ __forceinline__ bf16x8_t biased_bf16(uint32_t d, uint32_t magic) {
     return bitcast<bf16x8_t>(v);
 }
 
+// MXFP4 (OCP MX v1.0: E2M1 elements, one E8M0 scale per 32 elements along K).
+// B operand (8 fp16 or bf16 elements) from one device dword of 8 E2M1 codes,
+// element e in bits 4e..4e+3: v_cvt_scalef32_pk_{f16,bf16}_fp4 converts the
+// two codes of one byte, low nibble first, times the power-of-two scale sc.
+// Every E2M1 value (0, +-0.5 .. +-6) times sc is exact in the target type
+// while it stays within its range (fp16: 2^-24 grid, below 65504).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ half8_t fp4x8_to_f16(uint32_t d, float sc) {
+    const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, sc, 0);
+    const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, sc, 1);
+    const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, sc, 2);
+    const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, sc, 3);
+    return bitcast<half8_t>(u32x4_t{as_u(p0), as_u(p1), as_u(p2), as_u(p3)});
+}
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t d, float sc) {
+    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 0);
+    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 1);
+    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 2);
+    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 3);
+    return bitcast<bf16x8_t>(u32x4_t{bitcast<uint32_t>(p0), bitcast<uint32_t>(p1),
+                                     bitcast<uint32_t>(p2), bitcast<uint32_t>(p3)});
+}
+
+// E8M0 scale code e (0..254) -> 2^(e - 127), exact in fp32 (2^-127 is a
+// subnormal).  Code 255, the NaN encoding, is outside the library's contract.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+    return __builtin_ldexpf(0x1p-127f, (int)e);
+}
+
 // Raw buffer resources: a wave-uniform 128-bit descriptor (base, byte size)
 // lets every load take its lane offset from one VGPR and its unit offset from
 // an SGPR, with no per-load 64-bit address arithmetic.  Lanes whose
@@ -171,6 +200,12 @@ inline bool group_ok(int group) {
 inline int check_w4_shape(int N, int K, int group) {
     if (N < 1 || K < 1 || !group_ok(group)) return W4A16_ERR_SHAPE;
     if (N % 8 || K % 8 || K % group) return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+// Shape contract of the MXFP4 functions (see w4a16.h).
+inline int check_mx_shape(int N, int K) {
+    if (N < 8 || K < 32 || N % 8 || K % 32) return W4A16_ERR_SHAPE;
     return W4A16_OK;
 }
 

@@ -64,6 +64,25 @@ struct Slot {
     uint32_t z[NG];
 };
 
+// MXFP4 ring slot: a unit's 16 weight bytes for this lane plus the E8M0 codes
+// of the unit's four 32-k blocks of this lane's column (byte j: block j).
+struct SlotMx {
+    u32x4_t w;
+    uint32_t s;
+};
+// Largest span of scale codes within a unit for which the MXFP4 path folds
+// each block's scale into the element conversion (see the kernel).
+constexpr uint32_t kMxFoldSpan = 36;
+
+template <int NG, bool MX>
+struct SlotSel {
+    using type = Slot<NG>;
+};
+template <int NG>
+struct SlotSel<NG, true> {
+    using type = SlotMx;
+};
+
 // Launch description shared by host and kernel.
 struct GemvLaunch {
     int M, N, K;
@@ -107,7 +126,12 @@ constexpr int max_slots() { return SPG >= 4 ? 9 : (SPG == 2 ? 7 : 5); }
 template <int SPG, int UPW>
 constexpr int min_waves() { return (SPG >= 4 && UPW <= 5) || (SPG == 2 && UPW <= 3) ? 8 : 1; }
 
-template <bool BF16, int SPG, int UPW, int TPW>
+// MX = true runs MXFP4 weights (mxfp4.hip's device layout) instead: no zero
+// points, one E8M0 scale per 32-k block, which is exactly one MFMA step, so
+// each step's fp32 sum is scaled by 2^(E - 127) on its own -- the MX
+// specification's block dot product.  Its slot (5 VGPRs) is the size of a
+// g = 128 slot, so it is instantiated with SPG = 4 for the register plan.
+template <bool BF16, int SPG, int UPW, int TPW, bool MX = false>
 __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4_gemv_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ qdev,
     const uint16_t* __restrict__ sdev, const uint32_t* __restrict__ zdev, void* out,
@@ -118,6 +142,8 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     constexpr int DM = TPW > 1 ? 5 : max_slots<SPG>();
     constexpr int D = L < DM ? L : DM;
     constexpr bool kUncond = SPG >= 4 || (SPG == 2 && UPW <= 6) || UPW <= 2;
+    constexpr int LPS = MX ? 2 : 1 + 2 * NG;              // loads per ring slot
+    using SlotT = typename SlotSel<NG, MX>::type;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int M = a.M, K = a.K, U = a.U;
@@ -175,46 +201,57 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
 
     // 2) Weight / scale / zero-point loads of this wave's units.
     // The workgroup's nt tiles are contiguous in all three arrays.
-    const uint32_t wend = (uint32_t)nt * U * 1024u, send = (uint32_t)nt * Gp * 32u,
-                   zend = (uint32_t)nt * Gp * 8u;
+    // MXFP4: scales are [T][U][16] dwords and there are no zero points.
+    const uint32_t wend = (uint32_t)nt * U * 1024u,
+                   send = MX ? (uint32_t)nt * U * 64u : (uint32_t)nt * Gp * 32u,
+                   zend = MX ? 0u : (uint32_t)nt * Gp * 8u;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(qdev + (size_t)t0 * U * kLanes, wend);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdev + (size_t)t0 * Gp * kTileN, send);
-    const __amdgpu_buffer_rsrc_t rz = make_rsrc(zdev + (size_t)t0 * Gp * 2, zend);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(MX ? (const void*)((const uint8_t*)sdev + (size_t)t0 * U * 64u)
+                     : (const void*)(sdev + (size_t)t0 * Gp * kTileN),
+                  send);
+    const __amdgpu_buffer_rsrc_t rz =
+        make_rsrc(MX ? (const void*)qdev : (const void*)(zdev + (size_t)t0 * Gp * 2), zend);
     const uint32_t wlane = (uint32_t)lane * 16u;
     const uint32_t slane = (uint32_t)c * 2u;
     const uint32_t zlane = (uint32_t)(c >> 3) * 4u;
 
     // Chain position q = unit i (of this wave's range) x tile j, unit-major,
     // so one x fragment serves the workgroup's TPW tiles back to back.
-    auto load_slot = [&](int q, Slot<NG>& r) {
+    auto load_slot = [&](int q, SlotT& r) {
         const int i = q / TPW, j = q % TPW;
         const bool valid = i < nu && j < nt;
         const int u = w0 + i;
         r.w = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
             rw, valid ? wlane + (uint32_t)(j * U + u) * 1024u : wend, 0, kAuxNT));
+        if constexpr (MX) {
+            r.s = __builtin_amdgcn_raw_buffer_load_b32(
+                rs, valid ? (uint32_t)c * 4u + (uint32_t)(j * U + u) * 64u : send, 0, 0);
+        } else {
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-            const int g = j * Gp + (u * 4) / SPG + gi;
-            r.s[gi] = __builtin_amdgcn_raw_buffer_load_b16(rs, valid ? slane + (uint32_t)g * 32u : send, 0, 0);
-            r.z[gi] = __builtin_amdgcn_raw_buffer_load_b32(rz, valid ? zlane + (uint32_t)g * 8u : zend, 0, 0);
+            for (int gi = 0; gi < NG; ++gi) {
+                const int g = j * Gp + (u * 4) / SPG + gi;
+                r.s[gi] = __builtin_amdgcn_raw_buffer_load_b16(rs, valid ? slane + (uint32_t)g * 32u : send, 0, 0);
+                r.z[gi] = __builtin_amdgcn_raw_buffer_load_b32(rz, valid ? zlane + (uint32_t)g * 8u : zend, 0, 0);
+            }
         }
     };
 
-    Slot<NG> ring[D];
+    SlotT ring[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) {
         load_slot(i, ring[i]);
         __builtin_amdgcn_sched_barrier(0);   // slots issue in ring order
     }
     // Vector memory loads complete in issue order, so once no more than the
-    // ring's D * (1 + 2 NG) loads are outstanding, every x load issued before
+    // ring's D * LPS loads are outstanding, every x load issued before
     // them has landed in LDS.  This needs every ring load issued here, after
     // the x loads: the weight loads count as invariant, so the compiler may
     // sink a slot's loads into a conditional block that uses them, and then
     // the wait falls short.  Hence the overlap only where the arithmetic is
     // unconditional (elsewhere the wait above, after the x loads, covers
     // them); a host-side test checks the compiled kernels for this.
-    if constexpr (kUncond) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D * (1 + 2 * NG)) : "memory");
+    if constexpr (kUncond) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D * LPS) : "memory");
     __builtin_amdgcn_sched_barrier(0);
 
     // 3) Dequantize and multiply, unit by unit.
@@ -229,7 +266,7 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
 #pragma unroll
     for (int q = 0; q < L; ++q) {
         const int i = q / TPW, tj = q % TPW;
-        Slot<NG>& sl = ring[q % D];
+        SlotT& sl = ring[q % D];
         if (tj == 0 && i < nu && xrow) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -240,7 +277,59 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
         // register budget allows, the arithmetic runs unconditionally: then no
         // slot's loads get sunk into a conditional block next to their only use
         // (which would make the first unit wait for the whole ring).
-        if (kUncond || (i < nu && tj < nt)) {
+        if constexpr (MX) {
+            // The unit's four blocks (one per MFMA step) of this lane's column
+            // have scale codes e_j.  With R = max e_j - 13, step j's elements
+            // convert with the scale 2^(e_j - R) folded in -- exact in fp16
+            // while e_j >= R - 23, i.e. while the four codes span at most 36
+            // (every product lands on fp16's 2^-24 grid and stays below
+            // 6 * 2^13) -- the steps chain in one accumulator, and the unit's
+            // sum takes the remaining 2^(R - 127) once.  A wave with a wider
+            // span in any of its columns takes the unit step by step instead,
+            // each step's fp32 sum times its own 2^(e_j - 127).  Units past the
+            // range load zeros: codes 0 and scale codes 0 add exactly 0.
+            uint32_t e[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) e[j] = (sl.s >> (8 * j)) & 255u;
+            const uint32_t emax = max(max(e[0], e[1]), max(e[2], e[3]));
+            const uint32_t emin = min(min(e[0], e[1]), min(e[2], e[3]));
+            if (__builtin_amdgcn_ballot_w64(emax - emin > kMxFoldSpan) == 0) {
+                float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // 2^(e_j - R) as fp32 bits: exponent field e_j - emax + 140.
+                    const float sj = __builtin_bit_cast(float, (e[j] + 140u - emax) << 23);
+                    if constexpr (!BF16)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            bitcast<half8_t>(xa[j]), fp4x8_to_f16(sl.w[j], sj), acc, 0, 0, 0);
+                    else
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            bitcast<bf16x8_t>(xa[j]), fp4x8_to_bf16(sl.w[j], sj), acc, 0, 0, 0);
+                }
+                const float sf = __builtin_ldexpf(1.0f, (int)emax - 140);   // 2^(R - 127)
+                total[tj][0] = __builtin_fmaf(sf, acc[0], total[tj][0]);
+                total[tj][1] = __builtin_fmaf(sf, acc[1], total[tj][1]);
+                total[tj][2] = __builtin_fmaf(sf, acc[2], total[tj][2]);
+                total[tj][3] = __builtin_fmaf(sf, acc[3], total[tj][3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (!BF16)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            bitcast<half8_t>(xa[j]), fp4x8_to_f16(sl.w[j], 1.0f), acc, 0, 0, 0);
+                    else
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            bitcast<bf16x8_t>(xa[j]), fp4x8_to_bf16(sl.w[j], 1.0f), acc, 0, 0, 0);
+                    const float sf = e8m0_to_f32(e[j]);
+                    total[tj][0] = __builtin_fmaf(sf, acc[0], total[tj][0]);
+                    total[tj][1] = __builtin_fmaf(sf, acc[1], total[tj][1]);
+                    total[tj][2] = __builtin_fmaf(sf, acc[2], total[tj][2]);
+                    total[tj][3] = __builtin_fmaf(sf, acc[3], total[tj][3]);
+                    __builtin_amdgcn_sched_barrier(0);   // one step's sum live at a time
+                }
+            }
+        } else if (kUncond || (i < nu && tj < nt)) {
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const uint32_t zq = (sl.z[gi] >> zshift) & 15u;
@@ -545,6 +634,39 @@ w4_kernel_t pick_kernel(bool bf16, int group, int upw, int tpw) {
     return bf16 ? pick_group<true>(group, upw, tpw) : pick_group<false>(group, upw, tpw);
 }
 
+// MXFP4 kernels (register plan of g = 128, see the kernel).
+template <bool BF16, int TPW>
+w4_kernel_t pick_mx_small_upw(int upw) {
+    switch (upw) {
+        case 1: return w4_gemv_kernel<BF16, 4, 1, TPW, true>;
+        case 2: return w4_gemv_kernel<BF16, 4, 2, TPW, true>;
+        case 3: return w4_gemv_kernel<BF16, 4, 3, TPW, true>;
+        case 4: return w4_gemv_kernel<BF16, 4, 4, TPW, true>;
+        case 5: return w4_gemv_kernel<BF16, 4, 5, TPW, true>;
+        default: return w4_gemv_kernel<BF16, 4, 6, TPW, true>;
+    }
+}
+
+template <bool BF16>
+w4_kernel_t pick_mx_upw(int upw, int tpw) {
+    if (upw <= 6) {
+        if (tpw == 2) return pick_mx_small_upw<BF16, 2>(upw);
+        if (tpw == 3) return pick_mx_small_upw<BF16, 3>(upw);
+        if (tpw == 4) return pick_mx_small_upw<BF16, 4>(upw);
+        return pick_mx_small_upw<BF16, 1>(upw);
+    }
+    switch (upw) {
+        case 8: return w4_gemv_kernel<BF16, 4, 8, 1, true>;
+        case 9: return w4_gemv_kernel<BF16, 4, 9, 1, true>;
+        case 12: return w4_gemv_kernel<BF16, 4, 12, 1, true>;
+        default: return w4_gemv_kernel<BF16, 4, 17, 1, true>;
+    }
+}
+
+w4_kernel_t pick_mx_kernel(bool bf16, int upw, int tpw) {
+    return bf16 ? pick_mx_upw<true>(upw, tpw) : pick_mx_upw<false>(upw, tpw);
+}
+
 // Allow every GEMV kernel the whole LDS of a CU, once per process (before any
 // graph capture can be in progress for the common case of a warm-up call).
 void allow_full_lds() {
@@ -555,6 +677,12 @@ void allow_full_lds() {
                 for (int u : kUpwSet)
                   for (int tp = 1; tp <= 4; ++tp)
                     (void)hipFuncSetAttribute((const void*)pick_kernel(bf, g, u, tp),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                                              (int)kLdsPerCu);
+        for (int bf = 0; bf < 2; ++bf)
+            for (int u : kUpwSet)
+                for (int tp = 1; tp <= 4; ++tp)
+                    (void)hipFuncSetAttribute((const void*)pick_mx_kernel(bf, u, tp),
                                               hipFuncAttributeMaxDynamicSharedMemorySize,
                                               (int)kLdsPerCu);
         (void)hipGetLastError();
@@ -720,4 +848,66 @@ extern "C" int w4a16_gemv_add(const void* x, int x_dtype, const void* qweight, c
     if (!w4h::aligned16(residual)) return W4A16_ERR_ALIGN;
     return gemv_impl(x, x_dtype, qweight, scales, zeros, residual, residual_dtype, y, y_dtype, M, N, K,
                      group, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------------------------ MXFP4
+
+namespace {
+
+// The MXFP4 GEMV runs the 4-bit kernel's plan as for g = 128 (same slot size,
+// same units): rows 1..16, one MFMA block.
+constexpr int kMxPlanGroup = 128;
+
+int check_mx_args(const void* x, int x_dtype, const void* q, const void* s, const void* y,
+                  int y_dtype, int M, int N, int K) {
+    if (!x || !q || !s || !y) return W4A16_ERR_NULL;
+    if (x_dtype != W4A16_F16 && x_dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (y_dtype != W4A16_F32 && y_dtype != W4A16_F16 && y_dtype != W4A16_BF16)
+        return W4A16_ERR_DTYPE;
+    if (M < 1 || M > kMaxRows) return W4A16_ERR_SHAPE;
+    if (int rc = w4h::check_mx_shape(N, K)) return rc;
+    if (!w4h::aligned16(x) || !w4h::aligned16(q) || !w4h::aligned16(s) || !w4h::aligned16(y))
+        return W4A16_ERR_ALIGN;
+    return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" int mxfp4_workspace_bytes(int M, int N, int K, size_t* bytes) {
+    if (!bytes) return W4A16_ERR_NULL;
+    if (M < 1 || M > kMaxRows) return W4A16_ERR_SHAPE;
+    if (int rc = w4h::check_mx_shape(N, K)) return rc;
+    const Plan p = make_plan(M, N, K, kMxPlanGroup, cu_count());
+    *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
+    return W4A16_OK;
+}
+
+extern "C" int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const void* scales, void* y,
+                          int y_dtype, int M, int N, int K, void* workspace, size_t workspace_bytes,
+                          w4a16_stream_t stream) {
+    if (int rc = check_mx_args(x, x_dtype, qweight, scales, y, y_dtype, M, N, K)) return rc;
+    Plan p = make_plan(M, N, K, kMxPlanGroup, cu_count());
+    if (!p.upw) return W4A16_ERR_UNSUPPORTED;
+    const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
+    if (need) {
+        if (!workspace) return W4A16_ERR_NULL;
+        if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+        if (!w4h::aligned16(workspace)) return W4A16_ERR_ALIGN;
+    }
+    allow_full_lds();
+    hipStream_t st = (hipStream_t)stream;
+    const bool bf16 = x_dtype == W4A16_BF16;
+    w4_kernel_t k = pick_mx_kernel(bf16, p.upw, p.tpw);
+    void* out = p.l.S > 1 ? workspace : y;
+    p.l.out_dtype = p.l.S > 1 ? W4A16_F32 : y_dtype;
+    w4h::begin_launches();
+    hipLaunchKernelGGL(k, dim3((p.tiles + p.tpw - 1) / p.tpw, p.l.S), dim3(64 * p.waves), p.lds, st,
+                       (const uint16_t*)x, (const u32x4_t*)qweight, (const uint16_t*)scales,
+                       (const uint32_t*)nullptr, out, p.l);
+    if (p.l.S > 1) w4h::launch_merge(workspace, y, y_dtype, nullptr, W4A16_F32, M, N, p.l.S, st);
+    w4h::set_last_variant("mxfp4_mfma16 %s kernel=w4_gemv_kernel<%s, 4, %d, %d, true> tiles=%d "
+                          "slices=%d waves=%d upw=%d tpw=%d lds=%zu",
+                          bf16 ? "bf16" : "f16", bf16 ? "true" : "false", p.upw, p.tpw, p.tiles, p.l.S,
+                          p.waves, p.upw, p.tpw, p.lds);
+    return w4h::launch_status();
 }

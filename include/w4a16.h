@@ -150,6 +150,46 @@ int w16a16_workspace_bytes(int M, int N, int K, size_t* bytes);
 int w16a16_gemv(const void* x, const void* w, int dtype, void* y, int y_dtype, int M, int N, int K,
                 void* workspace, size_t workspace_bytes, w4a16_stream_t stream);
 
+/* ---- MXFP4 weights: w = element * 2^(E - 127) ----
+ * The Z100 article's closing section names MXFP4 as the next weight format:
+ * 4-bit floating-point elements sharing a block-level scale, as the OCP
+ * Microscaling (MX) specification it cites defines them (v1.0 MXFP4): E2M1
+ * elements (values 0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6), one E8M0 scale
+ * code E per 32 consecutive elements along K, scale 2^(E - 127).
+ * Canonical layout (host or device memory as each call states):
+ *   qweight_canon uint8 [N][K/2]: element k of row n in byte k/2, low nibble
+ *                 for even k (bit 3 sign, bits 2..1 exponent, bit 0 mantissa);
+ *   scales_canon  uint8 [N][K/32]: the E8M0 code of block k/32 of row n.
+ * Shape contract: N >= 8, N % 8 == 0, K >= 32, K % 32 == 0; for the GEMV
+ * also 1 <= M <= 16.  Scale codes 0..254; code 255 (the specification's NaN)
+ * is outside the contract (its block's results are unspecified).
+ * mxfp4_packed_sizes: device bytes of the packed weights and scales.
+ * mxfp4_pack / mxfp4_unpack: canonical <-> device layout, exact inverses;
+ *   all pointers are device memory, 16-byte aligned (scales_canon any
+ *   alignment), caller-owned; enqueued on stream. */
+int mxfp4_packed_sizes(int N, int K, size_t* q_bytes, size_t* s_bytes);
+int mxfp4_pack(const uint8_t* qweight_canon, const uint8_t* scales_canon, void* qweight,
+               void* scales, int N, int K, w4a16_stream_t stream);
+int mxfp4_unpack(const void* qweight, const void* scales, uint8_t* qweight_canon,
+                 uint8_t* scales_canon, int N, int K, w4a16_stream_t stream);
+
+/* y[M,N] = x[M,K] . w[N,K]^T from the packed device layout.  Each 32-k
+ * block's product is summed in fp32 and then scaled by 2^(E - 127) (the MX
+ * specification's block dot product), so every scale code is handled
+ * exactly; products and sums fp32, deterministic.  Dtypes, alignment,
+ * workspace and overlap rules as for w4a16_gemv; workspace size from
+ * mxfp4_workspace_bytes. */
+int mxfp4_workspace_bytes(int M, int N, int K, size_t* bytes);
+int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const void* scales, void* y,
+               int y_dtype, int M, int N, int K, void* workspace, size_t workspace_bytes,
+               w4a16_stream_t stream);
+
+/* Debug / parity: w[N][K] = element * 2^(E - 127) as fp32 from the packed
+ * layout, row-major [N][K].  Exact wherever the value is a finite fp32
+ * (scale codes up to 253 for elements up to 6). */
+int mxfp4_dequant(const void* qweight, const void* scales, float* w, int N, int K,
+                  w4a16_stream_t stream);
+
 /* ---- ternary 2-bit variant: w = (c - 1) * s, one fp16 scale per group ----
  * Shape contract: 1 <= N, 1 <= K, K % group == 0, K % 16 == 0,
  * group in {32, 64, 128, 256}; for the GEMV also 1 <= M <= 16.

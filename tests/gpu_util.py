@@ -80,6 +80,27 @@ class PackedW2T:
         return y
 
 
+class PackedMX:
+    """An MXFP4 matrix packed on the device with mxfp4_pack."""
+
+    def __init__(self, w: dict, N: int, K: int):
+        self.N, self.K = N, K
+        qb, sb = L.mxfp4_packed_sizes(N, K)
+        self.q, self.s = empty_bytes(qb), empty_bytes(sb)
+        q, sc = w["qweight"], w["scales"]
+        self.canon = (q if isinstance(q, torch.Tensor) else dev(q),
+                      sc if isinstance(sc, torch.Tensor) else dev(sc))
+        L.mxfp4_pack(*self.canon, self.q, self.s, N, K)
+
+    def gemv(self, x: torch.Tensor, x_dtype: str, M: int, y_dtype: str = "f32") -> torch.Tensor:
+        ydt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[y_dtype]
+        y = torch.empty((M, self.N), dtype=ydt, device=DEV)
+        ws_bytes = L.mxfp4_workspace_bytes(M, self.N, self.K)
+        ws = workspace_bytes(ws_bytes) if ws_bytes else None
+        L.mxfp4_gemv(x, x_dtype, self.q, self.s, y, y_dtype, M, self.N, self.K, ws, ws_bytes)
+        return y
+
+
 def to_f64(y: torch.Tensor) -> np.ndarray:
     return y.float().cpu().numpy().astype(np.float64)
 

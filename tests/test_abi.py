@@ -17,13 +17,14 @@ import bit_weight_only_03_amd as lib
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(w(?:4a16|2t|16a16)_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*((?:w4a16|w2t|w16a16|mxfp4)_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("w4a16_pack", "w4a16_unpack", "w4a16_gemv", "w4a16_gemv_add", "w4a16_dequant",
-              "w16a16_gemv", "w16a16_workspace_bytes",
+              "w16a16_gemv", "w16a16_workspace_bytes", "mxfp4_packed_sizes", "mxfp4_pack",
+              "mxfp4_unpack", "mxfp4_workspace_bytes", "mxfp4_gemv", "mxfp4_dequant",
               "w4a16_packed_sizes",
               "w4a16_workspace_bytes", "w2t_pack", "w2t_unpack", "w2t_gemv", "w2t_dequant",
               "w2t_packed_sizes", "w2t_workspace_bytes", "w4a16_bw_probe", "w4a16_status_string",
@@ -146,3 +147,35 @@ def test_w16a16_argument_checks():
     with pytest.raises(lib.W4A16Error) as e:
         lib.w16a16_gemv(good, 0, 0, good, 2, 1, 64, 64, stream=0)
     assert e.value.status == -1
+
+
+def test_mxfp4_sizes_and_argument_checks():
+    # 4096 x 4096: 8 MiB of codes, one scale byte per 32 elements; ragged
+    # N = 24 pads to 32 columns, K = 96 to one 128-k unit.
+    assert lib.mxfp4_packed_sizes(4096, 4096) == (8388608, 524288)
+    assert lib.mxfp4_packed_sizes(24, 96) == (32 * 128 // 2, 32 * 128 // 32)
+    for (N, K) in [(0, 64), (12, 64), (8, 48), (8, 16), (8, 0)]:
+        with pytest.raises(lib.W4A16Error) as e:
+            lib.mxfp4_packed_sizes(N, K)
+        assert e.value.status == -2
+    for M in (0, 17):
+        with pytest.raises(lib.W4A16Error) as e:
+            lib.mxfp4_workspace_bytes(M, 64, 64)
+        assert e.value.status == -2
+    assert lib.mxfp4_workspace_bytes(1, 4096, 4096) % (4096 * 4) == 0
+    good = 1 << 20
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.mxfp4_gemv(good, 2, good, good, good, 2, 1, 64, 64, stream=0)     # f32 x
+    assert e.value.status == -4
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.mxfp4_gemv(good, 0, good + 4, good, good, 2, 1, 64, 64, stream=0)
+    assert e.value.status == -3
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.mxfp4_gemv(good, 0, good, 0, good, 2, 1, 64, 64, stream=0)
+    assert e.value.status == -1
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.mxfp4_pack(good, good, good, good, 64, 40, stream=0)
+    assert e.value.status == -2
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.mxfp4_dequant(good, good, good + 8, 64, 64, stream=0)
+    assert e.value.status == -3

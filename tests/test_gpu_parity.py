@@ -20,8 +20,8 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 import bit_weight_only_03_amd as L  # noqa: E402
-from gpu_util import (DEV, PackedW2T, PackedW4, assert_parity, dev, empty_bytes, host_bits,  # noqa: E402
-                      to_f64, workspace_bytes)
+from gpu_util import (DEV, PackedMX, PackedW2T, PackedW4, assert_parity, dev, empty_bytes,  # noqa: E402
+                      host_bits, to_f64, workspace_bytes)
 
 
 def say(msg):
@@ -522,6 +522,149 @@ def test_multi_tile_workgroups_ragged(M, K, g, xdt):
     assert "tpw=3 " in variant
     ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g)
     assert_parity(to_f64(y), ref, f"multi-tile M={M} K={K}")
+
+
+# ------------------------------------------------------------------ MXFP4 ---
+
+# (N, K): one tile, ragged N (a last tile of 8 columns), K with a ragged last
+# 128-k unit (K % 128 = 32, 64, 96), several tiles.
+MX_SHAPES = [(8, 32), (24, 96), (40, 160), (136, 1184), (264, 4160), (4104, 640)]
+
+
+@pytest.mark.parametrize("N,K", MX_SHAPES)
+def test_mxfp4_pack_unpack_roundtrip_bitexact(N, K):
+    say(f"mxfp4 pack N={N} K={K}")
+    w = synth.gen_mx((120, N, K), N, K, e_lo=0, e_hi=254)
+    P = PackedMX(w, N, K)
+    q2 = torch.empty((N, K // 2), dtype=torch.uint8, device=DEV)
+    s2 = torch.empty((N, K // 32), dtype=torch.uint8, device=DEV)
+    L.mxfp4_unpack(P.q, P.s, q2, s2, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(q2.cpu().numpy(), w["qweight"])
+    assert np.array_equal(s2.cpu().numpy(), w["scales"])
+
+
+@pytest.mark.parametrize("N,K", MX_SHAPES + [(5120, 17408)])
+def test_mxfp4_dequant_bitexact(N, K):
+    # Every byte value (two codes, negative zero included) under scale codes
+    # 0 (subnormal 2^-127) .. 252, through the GEMV's own element conversion;
+    # compared bit for bit, sign of zero included.
+    say(f"mxfp4 dequant N={N} K={K}")
+    w = synth.gen_mx((121, N, K), N, K, e_lo=0, e_hi=252)
+    q = w["qweight"].copy()
+    flat = q.reshape(-1)
+    flat[: min(256, flat.size)] = np.arange(min(256, flat.size), dtype=np.uint8)
+    w["qweight"] = q
+    P = PackedMX(w, N, K)
+    out = torch.empty((N, K), dtype=torch.float32, device=DEV)
+    L.mxfp4_dequant(P.q, P.s, out, N, K)
+    torch.cuda.synchronize()
+    ref = oracle.mx_dequant(q, w["scales"], N, K).astype(np.float32)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+MX_GEMV_CASES = [
+    # (M, N, K, x dtype)
+    (1, 8, 32, "f16"),
+    (1, 24, 96, "bf16"),
+    (3, 40, 160, "f16"),
+    (1, 136, 1184, "f16"),
+    (2, 136, 1184, "bf16"),
+    (4, 264, 4160, "f16"),
+    (8, 520, 4096, "bf16"),
+    (16, 264, 896, "f16"),
+    (7, 4104, 640, "f16"),
+    (1, 4096, 4096, "f16"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,xdt", MX_GEMV_CASES)
+def test_mxfp4_gemv_matches_oracle(M, N, K, xdt):
+    say(f"mxfp4 gemv M={M} N={N} K={K} x={xdt}")
+    key = (122, M, N, K)
+    w = synth.gen_mx(key, N, K)
+    x = synth.gen_x(key, M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    P = PackedMX(w, N, K)
+    xd = dev(x)
+    y = P.gemv(xd, xdt, M, "f32")
+    torch.cuda.synchronize()
+    say("  variant: " + L.w4a16_last_variant())
+    ref = oracle.mx_gemv(x, xdt, w["qweight"], w["scales"], M, N, K)
+    assert_parity(to_f64(y), ref, f"M={M} N={N} K={K} {xdt}")
+    assert_parity(to_f64(P.gemv(xd, xdt, M, "f16")), ref, "f16 out", extra_rel=2.0 ** -11)
+    assert_parity(to_f64(P.gemv(xd, xdt, M, "bf16")), ref, "bf16 out", extra_rel=2.0 ** -8)
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_mxfp4_gemv_wide_scale_range(xdt):
+    # Scale codes 0..200 (2^-127 .. 2^73): each block's fp32 sum is scaled on
+    # its own, so no conversion of a scaled element has to fit fp16.
+    M, N, K = 4, 264, 2048
+    key = (123, M, N, K)
+    w = synth.gen_mx(key, N, K, e_lo=0, e_hi=200)
+    x = synth.gen_x(key, M, K, xdt)
+    P = PackedMX(w, N, K)
+    y = P.gemv(dev(x), xdt, M)
+    torch.cuda.synchronize()
+    assert_parity(to_f64(y), oracle.mx_gemv(x, xdt, w["qweight"], w["scales"], M, N, K), "wide scales")
+
+
+@pytest.mark.parametrize("span,xdt", [(36, "f16"), (37, "f16"), (36, "bf16"), (60, "bf16")])
+def test_mxfp4_scale_span_within_a_unit(span, xdt):
+    # Within each 128-k unit a column's four blocks carry codes
+    # [hi, hi - span, hi - span, hi].  Span 36 is the widest the kernel folds
+    # into the element conversion (the small blocks' elements land exactly on
+    # fp16's smallest subnormal step); wider spans take the exact per-step
+    # path.  Row 0 of x is nonzero only on the small-scale blocks, so any
+    # underflow there would be the whole result; row 1 is dense.
+    M, N, K, hi = 2, 64, 512, 150
+    key = (126, span)
+    w = synth.gen_mx(key, N, K)
+    sc = np.empty((N, K // 32), dtype=np.uint8)
+    for b in range(K // 32):
+        sc[:, b] = hi if b % 4 in (0, 3) else hi - span
+    w["scales"] = sc
+    x = synth.gen_x(key, M, K, xdt)
+    small = np.array([(k // 32) % 4 in (1, 2) for k in range(K)])
+    x[0, ~small] = 0
+    P = PackedMX(w, N, K)
+    y = P.gemv(dev(x), xdt, M)
+    torch.cuda.synchronize()
+    ref = oracle.mx_gemv(x, xdt, w["qweight"], w["scales"], M, N, K)
+    assert_parity(to_f64(y)[:1], ref[:1], f"span {span}, small blocks only")
+    assert_parity(to_f64(y), ref, f"span {span}")
+
+
+def test_mxfp4_split_and_multi_tile_launches():
+    # A narrow, long shape runs K slices (workspace and merge); a wide one
+    # runs three tiles per workgroup.
+    for (M, N, K) in [(4, 520, 17408), (2, 24592, 640)]:
+        key = (124, M, N, K)
+        w = synth.gen_mx(key, N, K)
+        x = synth.gen_x(key, M, K, "f16")
+        P = PackedMX(w, N, K)
+        y = P.gemv(dev(x), "f16", M)
+        torch.cuda.synchronize()
+        variant = L.w4a16_last_variant()
+        say(f"  mxfp4 M={M} N={N} K={K}: {variant}")
+        assert ("slices=1 " not in variant) if N == 520 else ("tpw=3 " in variant)
+        assert_parity(to_f64(y), oracle.mx_gemv(x, "f16", w["qweight"], w["scales"], M, N, K),
+                      f"mxfp4 M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("name,K,N", [("qkv", 5120, 7168), ("gate_up", 5120, 34816),
+                                      ("down", 17408, 5120)])
+@pytest.mark.parametrize("M,xdt", [(1, "f16"), (8, "bf16")])
+def test_mxfp4_full_size_sampled_columns(name, K, N, M, xdt):
+    say(f"mxfp4 full {name} K={K} N={N} M={M} x={xdt}")
+    key = (125, K, N, M)
+    w = synth.gen_mx(key, N, K)
+    x = synth.gen_x(key, M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    P = PackedMX(w, N, K)
+    y = to_f64(P.gemv(dev(x), xdt, M))
+    cols = sample_cols(N, np.random.default_rng(N + M + 7))
+    ref = oracle.mx_gemv(x, xdt, w["qweight"], w["scales"], M, N, K, cols=cols)
+    assert_parity(y[:, cols], ref, "mxfp4 " + name)
 
 
 # ----------------------------------------------- full 27B-class shapes, sampled ---
