@@ -86,7 +86,14 @@ def kernel_key(name):
     """'w4_gemv_kernel<false, 4, 5>' out of a variant string or a profiler's
     demangled kernel name (spaces normalised)."""
     m = KERNEL_RE.search(name)
-    return re.sub(r"\s+", " ", m.group(0)) if m else None
+    if not m:
+        return None
+    k = re.sub(r"\s+", " ", m.group(0))
+    # The 4-bit GEMV's fifth template argument (MXFP4 mode) defaults to false
+    # and the variant strings leave it out; profiler names spell it.
+    if k.startswith("w4_gemv_kernel<") and k.count(",") == 4 and k.endswith(", false>"):
+        k = k[: -len(", false>")] + ">"
+    return k
 
 
 def load_traffic(kernel):
