@@ -45,8 +45,10 @@ struct W16Launch {
 // One workgroup per (4 tiles, K slice); per unit of the slice: x of the unit
 // staged in LDS buffer u % 2 by all threads (zeros past K and in rows >= M,
 // whose outputs are never stored), every wave multiplies its tile's unit
-// (loaded kW16Ring units earlier) while the next unit's x is in flight, then
-// stores that x into the other buffer; one barrier per unit.  Units past the
+// (loaded kW16Ring units earlier) while the x of unit u + 2 loads into one
+// of two register sets, then stores the x of unit u + 1 (loaded one unit
+// earlier, before unit u + 1's weights, so the store does not wait for
+// them) into the other buffer; one barrier per unit.  Units past the
 // slice and rows past N load as zeros, so the loop body is uniform.
 template <bool BF16, int RB>
 __global__ __launch_bounds__(256) void w16_gemv_kernel(const uint16_t* __restrict__ x,
@@ -83,8 +85,8 @@ __global__ __launch_bounds__(256) void w16_gemv_kernel(const uint16_t* __restric
             r[j] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rw, off + 64u * j, 0, 0));
     };
 
-    u32x4_t xr[XPT];
-    auto load_x = [&](int i) {
+    u32x4_t xr[2][XPT];
+    auto load_x = [&](int i, int slot) {
         const int kb = (r0 + i) * kUnitK;
 #pragma unroll
         for (int p = 0; p < XPT; ++p) {
@@ -95,15 +97,15 @@ __global__ __launch_bounds__(256) void w16_gemv_kernel(const uint16_t* __restric
             const int ch = threadIdx.x + 256 * p;   // < XCH: XCH = 256 RB
             const int m = ch >> 4, k = kb + 8 * (ch & 15);
             const bool in = m < M && k < K && i < nu;
-            xr[p] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
+            xr[slot][p] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
                 rx, in ? (uint32_t)(m * K + k) * 2u : xend, 0, 0));
         }
     };
-    auto store_x = [&](int b) {
+    auto store_x = [&](int b, int slot) {
 #pragma unroll
         for (int p = 0; p < XPT; ++p) {
             const int ch = threadIdx.x + 256 * p;
-            *(u32x4_t*)&xs[b][ch >> 4][8 * (ch & 15)] = xr[p];
+            *(u32x4_t*)&xs[b][ch >> 4][8 * (ch & 15)] = xr[slot][p];
         }
     };
 
@@ -127,18 +129,19 @@ __global__ __launch_bounds__(256) void w16_gemv_kernel(const uint16_t* __restric
     };
 
     u32x4_t ring[kW16Ring][4];
+    load_x(0, 0);
 #pragma unroll
     for (int d = 0; d < kW16Ring; ++d) load_unit(d, ring[d]);
-    load_x(0);
-    store_x(0);
+    load_x(1, 1);
+    store_x(0, 0);
     __syncthreads();
     for (int i = 0; i < nu; i += kW16Ring) {
 #pragma unroll
         for (int d = 0; d < kW16Ring; ++d) {
-            load_x(i + d + 1);
-            compute(ring[d], d & 1);          // unit i + d sits in buffer (i + d) % 2
+            load_x(i + d + 2, d & 1);           // slot (i + d) % 2: x of unit i + d is in LDS
+            compute(ring[d], d & 1);            // unit i + d sits in buffer (i + d) % 2
             load_unit(i + d + kW16Ring, ring[d]);
-            store_x((d + 1) & 1);
+            store_x((d + 1) & 1, (d + 1) & 1);  // x of unit i + d + 1, loaded one unit ago
             __syncthreads();
         }
     }

@@ -29,9 +29,11 @@ using namespace w4k;
 namespace {
 
 constexpr int kGemmWaves = 4;             // waves per workgroup
-// Units of weight loads in flight per wave (even).  Four, or a guard that
+// Units of weight loads in flight per wave (even: the x register sets and
+// LDS buffers alternate with the ring position).  Four, or a guard that
 // skips the tail units of the last ring turn, measured slower (gate_up at
-// M = 64: 57 us with two, 70 us with four, 61 us guarded).
+// M = 64: 57 us with two, 70 us with four, 61 us guarded; with x loaded two
+// units ahead, four again lost: 71 us against 61 us).
 constexpr int kRing = 2;
 constexpr int kXStride = kUnitK + 8;      // halves per staged x row (+16 B spreads rows over banks)
 
@@ -59,9 +61,13 @@ struct GSlot {
 //   - all threads have staged x[0:M, u's 128 k] in LDS buffer u % 2 (zeros
 //     past K and in rows >= M, whose outputs are never stored);
 //   - every wave multiplies its tiles' unit u, whose loads were issued kRing
-//     units earlier (a ring of kRing units per tile), while the loads of
-//     unit u+1's x are in flight; then it stores that x into the other
-//     buffer and the workgroup meets at a barrier.
+//     units earlier (a ring of kRing units per tile), while the x of unit
+//     u+2 is loading into one of two register sets; then it stores the x of
+//     unit u+1 (loaded one unit earlier) into the other LDS buffer and the
+//     workgroup meets at a barrier.  Loading x two units ahead keeps that
+//     store's wait off the weight loads: loads complete in issue order, and
+//     x of unit u+1 went out before the weights of unit u+1, so the store
+//     waits for nothing issued after unit u's weights.
 // Units past the slice (and tiles past N) load as zeros -- q = z = 0, s = +0 --
 // and add exactly 0 against the finite x, so the loop body is uniform.
 template <bool BF16, int SPG, int RB, int TN>
@@ -119,8 +125,8 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
     };
 
     // x of unit r0 + i: chunk ch = row ch / 16, k offset 8 (ch % 16).
-    u32x4_t xr[XPT];
-    auto load_x = [&](int i) {
+    u32x4_t xr[2][XPT];
+    auto load_x = [&](int i, int slot) {
         const int kb = (r0 + i) * kUnitK;
 #pragma unroll
         for (int p = 0; p < XPT; ++p) {
@@ -131,15 +137,15 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
             const int ch = threadIdx.x + 256 * p;   // < XCH: XCH = 256 RB
             const int m = ch >> 4, k = kb + 8 * (ch & 15);
             const bool in = m < M && k < K && i < nu;
-            xr[p] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
+            xr[slot][p] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
                 rx, in ? (uint32_t)(m * K + k) * 2u : xend, 0, 0));
         }
     };
-    auto store_x = [&](int b) {
+    auto store_x = [&](int b, int slot) {
 #pragma unroll
         for (int p = 0; p < XPT; ++p) {
             const int ch = threadIdx.x + 256 * p;
-            *(u32x4_t*)&xs[b][ch >> 4][8 * (ch & 15)] = xr[p];
+            *(u32x4_t*)&xs[b][ch >> 4][8 * (ch & 15)] = xr[slot][p];
         }
     };
 
@@ -207,18 +213,19 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
 
     // Prologue: loads of the first kRing units, x of unit 0 staged.
     GSlot<NG> ring[kRing][TN];
+    load_x(0, 0);
 #pragma unroll
     for (int d = 0; d < kRing; ++d) load_unit(d, ring[d]);
-    load_x(0);
-    store_x(0);
+    load_x(1, 1);
+    store_x(0, 0);
     __syncthreads();
     for (int i = 0; i < nu; i += kRing) {
 #pragma unroll
         for (int d = 0; d < kRing; ++d) {
-            load_x(i + d + 1);
-            compute(ring[d], d & 1);       // unit i + d sits in buffer (i + d) % 2
+            load_x(i + d + 2, d & 1);           // slot (i + d) % 2: x of unit i + d is in LDS
+            compute(ring[d], d & 1);            // unit i + d sits in buffer (i + d) % 2
             load_unit(i + d + kRing, ring[d]);
-            store_x((d + 1) & 1);
+            store_x((d + 1) & 1, (d + 1) & 1);  // x of unit i + d + 1, loaded one unit ago
             __syncthreads();
         }
     }
