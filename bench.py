@@ -323,7 +323,7 @@ ROT_BYTES = 2 << 30   # distinct copies per shape, so no shape sits in the 256 M
 SKINNY_M = (1, 2, 3, 4, 6, 8)
 BATCH_M = (16, 32, 64)            # rows of the batch sweeps (M-tiled kernel)
 W16_M = (1, 2, 4, 8)               # rows of the W16A16 measurements
-MX_M = (1, 4, 8)                   # rows of the MXFP4 sweep
+MX_M = (1, 4, 8, 64)               # rows of the MXFP4 sweep (64: the M-tiled kernel)
 SKINNY_KN = (4096, 5120, 8192)
 LM_HEAD = (5120, 152064)
 TERNARY = ((5120, 7168), (5120, 34816), (17408, 5120))

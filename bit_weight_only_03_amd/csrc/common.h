@@ -172,6 +172,39 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
     return __builtin_ldexpf(0x1p-127f, (int)e);
 }
 
+// The scales of one 128-k unit of one column: the E8M0 codes e_j of its four
+// 32-k blocks (byte j of the unit's scale dword), which are the four MFMA
+// steps.  With R = max e_j - 13, step j converts its elements with the scale
+// 2^(e_j - R) folded in: exact in fp16 while e_j >= R - 23, i.e. while the
+// four codes span at most kMxFoldSpan (every value lands on fp16's 2^-24 grid
+// and stays below 6 * 2^13; bf16 has range to spare).  The steps then chain
+// in one accumulator and the unit's sum takes 2^(R - 127) once.  A unit with
+// a wider span is taken step by step, each step's fp32 sum times its own
+// 2^(e_j - 127) -- the MX specification's block dot product.
+constexpr uint32_t kMxFoldSpan = 36;
+struct MxUnit {
+    uint32_t e[4];
+    uint32_t emax;
+    bool wide;   // the four codes span more than kMxFoldSpan
+};
+__device__ __forceinline__ MxUnit mx_unit(uint32_t s) {
+    MxUnit u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) u.e[j] = (s >> (8 * j)) & 255u;
+    u.emax = max(max(u.e[0], u.e[1]), max(u.e[2], u.e[3]));
+    const uint32_t emin = min(min(u.e[0], u.e[1]), min(u.e[2], u.e[3]));
+    u.wide = u.emax - emin > kMxFoldSpan;
+    return u;
+}
+// 2^(e - R) as fp32 bits: exponent field e - emax + 140 (104..140 when folded).
+__device__ __forceinline__ float mx_fold_scale(uint32_t e, uint32_t emax) {
+    return __builtin_bit_cast(float, (e + 140u - emax) << 23);
+}
+// 2^(R - 127) = 2^(emax - 140), a subnormal for emax < 14.
+__device__ __forceinline__ float mx_unit_scale(uint32_t emax) {
+    return __builtin_ldexpf(1.0f, (int)emax - 140);
+}
+
 // Raw buffer resources: a wave-uniform 128-bit descriptor (base, byte size)
 // lets every load take its lane offset from one VGPR and its unit offset from
 // an SGPR, with no per-load 64-bit address arithmetic.  Lanes whose
@@ -245,8 +278,9 @@ struct GemmPlan {
     long long workgroups;   // tile columns of workgroups (grid x)
 };
 GemmPlan gemm_plan(int M, int N, int K, int group, int cus);
+// mx: MXFP4 weights (mxfp4.hip's layout; zeros unused), else 4-bit integers.
 int gemm_launch(const GemmPlan& p, const void* x, bool bf16, const void* qweight, const void* scales,
                 const void* zeros, void* y, int y_dtype, const void* res, int res_dtype, int M, int N,
-                int K, int group, void* workspace, hipStream_t st);
+                int K, int group, void* workspace, hipStream_t st, bool mx = false);
 
 }  // namespace w4h

@@ -55,6 +55,19 @@ struct GSlot {
     uint32_t s[NG];
     uint32_t z[NG];
 };
+// MXFP4: 16 weight bytes plus the dword of the unit's four E8M0 codes.
+struct GSlotMx {
+    u32x4_t w;
+    uint32_t s;
+};
+template <int NG, bool MX>
+struct GSlotSel {
+    using type = GSlot<NG>;
+};
+template <int NG>
+struct GSlotSel<NG, true> {
+    using type = GSlotMx;
+};
 
 // One workgroup per (4 x TN tiles, K slice).  Wave w owns tiles
 // [t0 + w TN, t0 + (w + 1) TN).  Per 128-k unit u of the slice:
@@ -70,7 +83,10 @@ struct GSlot {
 //     waits for nothing issued after unit u's weights.
 // Units past the slice (and tiles past N) load as zeros -- q = z = 0, s = +0 --
 // and add exactly 0 against the finite x, so the loop body is uniform.
-template <bool BF16, int SPG, int RB, int TN>
+// MX = true takes MXFP4 weights (mxfp4.hip's layout, instantiated with
+// SPG = 4): no zero points, each unit's four block scales folded into the
+// element conversion or applied step by step (mx_unit in common.h).
+template <bool BF16, int SPG, int RB, int TN, bool MX = false>
 __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict__ x,
                                                       const u32x4_t* __restrict__ qdev,
                                                       const uint16_t* __restrict__ sdev,
@@ -81,6 +97,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
     constexpr int ROWS = 16 * RB;
     constexpr int XCH = ROWS * (kUnitK / 8);      // 16-byte chunks of one staged unit
     constexpr int XPT = XCH / 256;                // chunks per thread (= RB)
+    using SlotT = typename GSlotSel<NG, MX>::type;
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][ROWS][kXStride];
 
     const int M = a.M, N = a.N, K = a.K, U = a.U, T = a.T;
@@ -96,30 +113,41 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
 
     // Buffer resources over the wave's tiles; a missing unit or tile takes an
     // offset at the resource's end, so each of its lanes reads zeros.
-    const uint32_t wend = (uint32_t)nt * U * 1024u, send = (uint32_t)nt * Gp * 32u,
-                   zend = (uint32_t)nt * Gp * 8u;
+    // MXFP4: scales are [T][U][16] dwords and there are no zero points.
+    const uint32_t wend = (uint32_t)nt * U * 1024u,
+                   send = MX ? (uint32_t)nt * U * 64u : (uint32_t)nt * Gp * 32u,
+                   zend = MX ? 0u : (uint32_t)nt * Gp * 8u;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(qdev + (size_t)tw * U * kLanes, wend);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdev + (size_t)tw * Gp * kTileN, send);
-    const __amdgpu_buffer_rsrc_t rz = make_rsrc(zdev + (size_t)tw * Gp * 2, zend);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(MX ? (const void*)((const uint8_t*)sdev + (size_t)tw * U * 64u)
+                     : (const void*)(sdev + (size_t)tw * Gp * kTileN),
+                  send);
+    const __amdgpu_buffer_rsrc_t rz =
+        make_rsrc(MX ? (const void*)qdev : (const void*)(zdev + (size_t)tw * Gp * 2), zend);
     const uint32_t xend = (uint32_t)M * (uint32_t)K * 2u;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xend);
     const uint32_t wlane = (uint32_t)lane * 16u, slane = (uint32_t)c * 2u,
                    zlane = (uint32_t)(c >> 3) * 4u;
 
-    auto load_unit = [&](int i, GSlot<NG> (&r)[TN]) {   // unit r0 + i of every tile
+    auto load_unit = [&](int i, SlotT (&r)[TN]) {   // unit r0 + i of every tile
         const int u = r0 + i;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const bool valid = i < nu && j < nt;
             r[j].w = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
                 rw, valid ? wlane + (uint32_t)(j * U + u) * 1024u : wend, 0, kAuxNT));
+            if constexpr (MX) {
+                r[j].s = __builtin_amdgcn_raw_buffer_load_b32(
+                    rs, valid ? (uint32_t)c * 4u + (uint32_t)(j * U + u) * 64u : send, 0, 0);
+            } else {
 #pragma unroll
-            for (int gi = 0; gi < NG; ++gi) {
-                const int g = j * Gp + (u * 4) / SPG + gi;
-                r[j].s[gi] = __builtin_amdgcn_raw_buffer_load_b16(
-                    rs, valid ? slane + (uint32_t)g * 32u : send, 0, 0);
-                r[j].z[gi] = __builtin_amdgcn_raw_buffer_load_b32(
-                    rz, valid ? zlane + (uint32_t)g * 8u : zend, 0, 0);
+                for (int gi = 0; gi < NG; ++gi) {
+                    const int g = j * Gp + (u * 4) / SPG + gi;
+                    r[j].s[gi] = __builtin_amdgcn_raw_buffer_load_b16(
+                        rs, valid ? slane + (uint32_t)g * 32u : send, 0, 0);
+                    r[j].z[gi] = __builtin_amdgcn_raw_buffer_load_b32(
+                        rz, valid ? zlane + (uint32_t)g * 8u : zend, 0, 0);
+                }
             }
         }
     };
@@ -157,7 +185,88 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) total[j][rb] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const GSlot<NG> (&r)[TN], int b) {
+    // MXFP4: per unit, every step's elements convert once per tile and serve
+    // the RB row blocks; the steps chain with the scales folded in, or (for a
+    // wave with any wide unit) each step's sums take their own scale.
+    auto compute_mx = [&](const auto& r, int b) {   // generic: compiled for MX only
+        MxUnit mu[TN];
+        bool wide = false;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            mu[j] = mx_unit(r[j].s);
+            wide = wide || mu[j].wide;
+        }
+        auto bop = [&](int j, int st, float sc) {
+            if constexpr (BF16)
+                return bitcast<u32x4_t>(fp4x8_to_bf16(r[j].w[st], sc));
+            else
+                return bitcast<u32x4_t>(fp4x8_to_f16(r[j].w[st], sc));
+        };
+        auto mfma = [&](const u32x4_t& av, const u32x4_t& bq, float4_t acc) {
+            if constexpr (BF16)
+                return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(av),
+                                                               bitcast<bf16x8_t>(bq), acc, 0, 0, 0);
+            else
+                return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(av),
+                                                              bitcast<half8_t>(bq), acc, 0, 0, 0);
+        };
+        if (__builtin_amdgcn_ballot_w64(wide) == 0) {
+            float4_t acc[TN][RB];
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) acc[j][rb] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                u32x4_t av[RB];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    av[rb] = *(const u32x4_t*)&xs[b][16 * rb + c][32 * st + 8 * kc];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const u32x4_t bq = bop(j, st, mx_fold_scale(mu[j].e[st], mu[j].emax));
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) acc[j][rb] = mfma(av[rb], bq, acc[j][rb]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const float sf = mx_unit_scale(mu[j].emax);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        total[j][rb][q] = __builtin_fmaf(sf, acc[j][rb][q], total[j][rb][q]);
+            }
+        } else {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                u32x4_t av[RB];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    av[rb] = *(const u32x4_t*)&xs[b][16 * rb + c][32 * st + 8 * kc];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const u32x4_t bq = bop(j, st, 1.0f);
+                    const float sf = e8m0_to_f32(mu[j].e[st]);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        const float4_t acc = mfma(av[rb], bq, float4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            total[j][rb][q] = __builtin_fmaf(sf, acc[q], total[j][rb][q]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);   // one step's sums live at a time
+            }
+        }
+    };
+
+    auto compute = [&](const SlotT (&r)[TN], int b) {
+        if constexpr (MX) {
+            compute_mx(r, b);
+            return;
+        } else {
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
             float4_t acc[TN][RB];
@@ -209,10 +318,11 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
                         total[j][rb][q] = __builtin_fmaf(sf, acc[j][rb][q], total[j][rb][q]);
             }
         }
+        }
     };
 
     // Prologue: loads of the first kRing units, x of unit 0 staged.
-    GSlot<NG> ring[kRing][TN];
+    SlotT ring[kRing][TN];
     load_x(0, 0);
 #pragma unroll
     for (int d = 0; d < kRing; ++d) load_unit(d, ring[d]);
@@ -253,19 +363,25 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
 typedef void (*gemm_kernel_t)(const uint16_t*, const u32x4_t*, const uint16_t*, const uint32_t*,
                               void*, GemmLaunch);
 
-template <bool BF16, int SPG, int TN>
+template <bool BF16, int SPG, int TN, bool MX = false>
 gemm_kernel_t pick_rb(int rb) {
     switch (rb) {
-        case 1: return w4_gemm_kernel<BF16, SPG, 1, TN>;
-        case 2: return w4_gemm_kernel<BF16, SPG, 2, TN>;
-        case 3: return w4_gemm_kernel<BF16, SPG, 3, TN>;
-        default: return w4_gemm_kernel<BF16, SPG, 4, TN>;
+        case 1: return w4_gemm_kernel<BF16, SPG, 1, TN, MX>;
+        case 2: return w4_gemm_kernel<BF16, SPG, 2, TN, MX>;
+        case 3: return w4_gemm_kernel<BF16, SPG, 3, TN, MX>;
+        default: return w4_gemm_kernel<BF16, SPG, 4, TN, MX>;
     }
 }
 
 template <bool BF16, int SPG>
 gemm_kernel_t pick_tn(int rb, int tn) {
     return tn == 1 ? pick_rb<BF16, SPG, 1>(rb) : pick_rb<BF16, SPG, 2>(rb);
+}
+
+// MXFP4 (register plan of g = 128).
+gemm_kernel_t pick_gemm_mx(bool bf16, int rb, int tn) {
+    if (bf16) return tn == 1 ? pick_rb<true, 4, 1, true>(rb) : pick_rb<true, 4, 2, true>(rb);
+    return tn == 1 ? pick_rb<false, 4, 1, true>(rb) : pick_rb<false, 4, 2, true>(rb);
 }
 
 gemm_kernel_t pick_gemm(bool bf16, int group, int rb, int tn) {
@@ -309,11 +425,11 @@ GemmPlan gemm_plan(int M, int N, int K, int group, int cus) {
 
 int gemm_launch(const GemmPlan& p, const void* x, bool bf16, const void* qweight, const void* scales,
                 const void* zeros, void* y, int y_dtype, const void* res, int res_dtype, int M, int N,
-                int K, int group, void* workspace, hipStream_t st) {
+                int K, int group, void* workspace, hipStream_t st, bool mx) {
     const int U = (K + kUnitK - 1) / kUnitK;
     const int T = pad_n(N) / kTileN;
     GemmLaunch l{M, N, K, U, p.split, T, y_dtype, res, res_dtype};
-    gemm_kernel_t k = pick_gemm(bf16, group, p.rb, p.tn);
+    gemm_kernel_t k = mx ? pick_gemm_mx(bf16, p.rb, p.tn) : pick_gemm(bf16, group, p.rb, p.tn);
     hipLaunchKernelGGL(k, dim3((unsigned)p.workgroups, p.split), dim3(64 * kGemmWaves), 0, st,
                        (const uint16_t*)x, (const u32x4_t*)qweight, (const uint16_t*)scales,
                        (const uint32_t*)zeros, p.split > 1 ? workspace : y, l);

@@ -70,10 +70,6 @@ struct SlotMx {
     u32x4_t w;
     uint32_t s;
 };
-// Largest span of scale codes within a unit for which the MXFP4 path folds
-// each block's scale into the element conversion (see the kernel).
-constexpr uint32_t kMxFoldSpan = 36;
-
 template <int NG, bool MX>
 struct SlotSel {
     using type = Slot<NG>;
@@ -127,10 +123,11 @@ template <int SPG, int UPW>
 constexpr int min_waves() { return (SPG >= 4 && UPW <= 5) || (SPG == 2 && UPW <= 3) ? 8 : 1; }
 
 // MX = true runs MXFP4 weights (mxfp4.hip's device layout) instead: no zero
-// points, one E8M0 scale per 32-k block, which is exactly one MFMA step, so
-// each step's fp32 sum is scaled by 2^(E - 127) on its own -- the MX
-// specification's block dot product.  Its slot (5 VGPRs) is the size of a
-// g = 128 slot, so it is instantiated with SPG = 4 for the register plan.
+// points, one E8M0 scale per 32-k block, which is exactly one MFMA step; the
+// scales fold into the element conversion where a unit's codes allow it and
+// apply step by step otherwise (mx_unit in common.h).  Its slot (5 VGPRs) is
+// the size of a g = 128 slot, so it is instantiated with SPG = 4 for the
+// register plan.
 template <bool BF16, int SPG, int UPW, int TPW, bool MX = false>
 __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4_gemv_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ qdev,
@@ -278,27 +275,17 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
         // slot's loads get sunk into a conditional block next to their only use
         // (which would make the first unit wait for the whole ring).
         if constexpr (MX) {
-            // The unit's four blocks (one per MFMA step) of this lane's column
-            // have scale codes e_j.  With R = max e_j - 13, step j's elements
-            // convert with the scale 2^(e_j - R) folded in -- exact in fp16
-            // while e_j >= R - 23, i.e. while the four codes span at most 36
-            // (every product lands on fp16's 2^-24 grid and stays below
-            // 6 * 2^13) -- the steps chain in one accumulator, and the unit's
-            // sum takes the remaining 2^(R - 127) once.  A wave with a wider
-            // span in any of its columns takes the unit step by step instead,
-            // each step's fp32 sum times its own 2^(e_j - 127).  Units past the
-            // range load zeros: codes 0 and scale codes 0 add exactly 0.
-            uint32_t e[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) e[j] = (sl.s >> (8 * j)) & 255u;
-            const uint32_t emax = max(max(e[0], e[1]), max(e[2], e[3]));
-            const uint32_t emin = min(min(e[0], e[1]), min(e[2], e[3]));
-            if (__builtin_amdgcn_ballot_w64(emax - emin > kMxFoldSpan) == 0) {
+            // Scales folded into the conversion where the unit's codes allow
+            // it (mx_unit), else step by step.  Units past the range load
+            // zeros: codes 0 and scale codes 0 add exactly 0.
+            const MxUnit mu = mx_unit(sl.s);
+            const uint32_t* e = mu.e;
+            const uint32_t emax = mu.emax;
+            if (__builtin_amdgcn_ballot_w64(mu.wide) == 0) {
                 float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    // 2^(e_j - R) as fp32 bits: exponent field e_j - emax + 140.
-                    const float sj = __builtin_bit_cast(float, (e[j] + 140u - emax) << 23);
+                    const float sj = mx_fold_scale(e[j], emax);
                     if constexpr (!BF16)
                         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                             bitcast<half8_t>(xa[j]), fp4x8_to_f16(sl.w[j], sj), acc, 0, 0, 0);
@@ -306,7 +293,7 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
                         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             bitcast<bf16x8_t>(xa[j]), fp4x8_to_bf16(sl.w[j], sj), acc, 0, 0, 0);
                 }
-                const float sf = __builtin_ldexpf(1.0f, (int)emax - 140);   // 2^(R - 127)
+                const float sf = mx_unit_scale(emax);
                 total[tj][0] = __builtin_fmaf(sf, acc[0], total[tj][0]);
                 total[tj][1] = __builtin_fmaf(sf, acc[1], total[tj][1]);
                 total[tj][2] = __builtin_fmaf(sf, acc[2], total[tj][2]);
@@ -854,8 +841,8 @@ extern "C" int w4a16_gemv_add(const void* x, int x_dtype, const void* qweight, c
 
 namespace {
 
-// The MXFP4 GEMV runs the 4-bit kernel's plan as for g = 128 (same slot size,
-// same units): rows 1..16, one MFMA block.
+// MXFP4 runs the 4-bit kernels' plans as for g = 128 (same slot size, same
+// units, same GEMV / M-tiled crossover): rows 1..64.
 constexpr int kMxPlanGroup = 128;
 
 int check_mx_args(const void* x, int x_dtype, const void* q, const void* s, const void* y,
@@ -864,7 +851,7 @@ int check_mx_args(const void* x, int x_dtype, const void* q, const void* s, cons
     if (x_dtype != W4A16_F16 && x_dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
     if (y_dtype != W4A16_F32 && y_dtype != W4A16_F16 && y_dtype != W4A16_BF16)
         return W4A16_ERR_DTYPE;
-    if (M < 1 || M > kMaxRows) return W4A16_ERR_SHAPE;
+    if (M < 1 || M > w4h::kMaxRowsGemm) return W4A16_ERR_SHAPE;
     if (int rc = w4h::check_mx_shape(N, K)) return rc;
     if (!w4h::aligned16(x) || !w4h::aligned16(q) || !w4h::aligned16(s) || !w4h::aligned16(y))
         return W4A16_ERR_ALIGN;
@@ -875,8 +862,12 @@ int check_mx_args(const void* x, int x_dtype, const void* q, const void* s, cons
 
 extern "C" int mxfp4_workspace_bytes(int M, int N, int K, size_t* bytes) {
     if (!bytes) return W4A16_ERR_NULL;
-    if (M < 1 || M > kMaxRows) return W4A16_ERR_SHAPE;
+    if (M < 1 || M > w4h::kMaxRowsGemm) return W4A16_ERR_SHAPE;
     if (int rc = w4h::check_mx_shape(N, K)) return rc;
+    if (use_gemm(M, N, K, kMxPlanGroup)) {
+        *bytes = gemm_workspace(w4h::gemm_plan(M, N, K, kMxPlanGroup, cu_count()), M, N);
+        return W4A16_OK;
+    }
     const Plan p = make_plan(M, N, K, kMxPlanGroup, cu_count());
     *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     return W4A16_OK;
@@ -886,6 +877,27 @@ extern "C" int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const
                           int y_dtype, int M, int N, int K, void* workspace, size_t workspace_bytes,
                           w4a16_stream_t stream) {
     if (int rc = check_mx_args(x, x_dtype, qweight, scales, y, y_dtype, M, N, K)) return rc;
+    if (use_gemm(M, N, K, kMxPlanGroup)) {
+        // Rows past the GEMV's crossover: the M-tiled kernel's MXFP4 mode.
+        const w4h::GemmPlan gp = w4h::gemm_plan(M, N, K, kMxPlanGroup, cu_count());
+        const size_t need = gemm_workspace(gp, M, N);
+        if (need) {
+            if (!workspace) return W4A16_ERR_NULL;
+            if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+            if (!w4h::aligned16(workspace)) return W4A16_ERR_ALIGN;
+        }
+        const bool bf16 = x_dtype == W4A16_BF16;
+        hipStream_t st = (hipStream_t)stream;
+        w4h::begin_launches();
+        w4h::gemm_launch(gp, x, bf16, qweight, scales, nullptr, y, y_dtype, nullptr, W4A16_F32, M, N, K,
+                         kMxPlanGroup, workspace, st, true);
+        if (gp.split > 1) w4h::launch_merge(workspace, y, y_dtype, nullptr, W4A16_F32, M, N, gp.split, st);
+        w4h::set_last_variant("mxfp4_gemm16 %s kernel=w4_gemm_kernel<%s, 4, %d, %d, true> tiles=%d "
+                              "slices=%d workgroups=%lld",
+                              bf16 ? "bf16" : "f16", bf16 ? "true" : "false", gp.rb, gp.tn,
+                              pad_n(N) / kTileN, gp.split, gp.workgroups);
+        return w4h::launch_status();
+    }
     Plan p = make_plan(M, N, K, kMxPlanGroup, cu_count());
     if (!p.upw) return W4A16_ERR_UNSUPPORTED;
     const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;

@@ -161,7 +161,8 @@ int w16a16_gemv(const void* x, const void* w, int dtype, void* y, int y_dtype, i
  *                 for even k (bit 3 sign, bits 2..1 exponent, bit 0 mantissa);
  *   scales_canon  uint8 [N][K/32]: the E8M0 code of block k/32 of row n.
  * Shape contract: N >= 8, N % 8 == 0, K >= 32, K % 32 == 0; for the GEMV
- * also 1 <= M <= 16.  Scale codes 0..254; code 255 (the specification's NaN)
+ * also 1 <= M <= 64 (a few rows run the GEMV kernel, more rows the M-tiled
+ * kernel, with the crossover of w4a16_gemv at g = 128).  Scale codes 0..254; code 255 (the specification's NaN)
  * is outside the contract (its block's results are unspecified).
  * mxfp4_packed_sizes: device bytes of the packed weights and scales.
  * mxfp4_pack / mxfp4_unpack: canonical <-> device layout, exact inverses;

@@ -595,6 +595,59 @@ def test_mxfp4_gemv_matches_oracle(M, N, K, xdt):
     assert_parity(to_f64(P.gemv(xd, xdt, M, "bf16")), ref, "bf16 out", extra_rel=2.0 ** -8)
 
 
+# M-tiled MXFP4 (more rows than one MFMA block): 2 to 4 row blocks, ragged N
+# and K (a last unit of 32 or 64 k), with and without K slices.
+MX_GEMM_CASES = [
+    (17, 264, 896, "f16"),
+    (24, 40, 4160, "bf16"),
+    (32, 520, 1184, "f16"),
+    (48, 136, 640, "bf16"),
+    (64, 264, 4352, "f16"),
+    (64, 4104, 640, "bf16"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,xdt", MX_GEMM_CASES)
+def test_mxfp4_gemm_matches_oracle(M, N, K, xdt):
+    say(f"mxfp4 gemm M={M} N={N} K={K} x={xdt}")
+    key = (127, M, N, K)
+    w = synth.gen_mx(key, N, K)
+    x = synth.gen_x(key, M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    P = PackedMX(w, N, K)
+    xd = dev(x)
+    y = P.gemv(xd, xdt, M, "f32")
+    torch.cuda.synchronize()
+    variant = L.w4a16_last_variant()
+    say("  variant: " + variant)
+    assert "w4_gemm_kernel" in variant
+    ref = oracle.mx_gemv(x, xdt, w["qweight"], w["scales"], M, N, K)
+    assert_parity(to_f64(y), ref, f"M={M} N={N} K={K} {xdt}")
+    assert_parity(to_f64(P.gemv(xd, xdt, M, "bf16")), ref, "bf16 out", extra_rel=2.0 ** -8)
+
+
+@pytest.mark.parametrize("span,M", [(36, 24), (37, 24), (90, 40)])
+def test_mxfp4_gemm_scale_span_within_a_unit(span, M):
+    # The tiled kernel's fold / per-step split, as in the GEMV test: row 0 of
+    # x lives only on the small-scale blocks.
+    N, K, hi = 72, 512, 150
+    key = (128, span, M)
+    w = synth.gen_mx(key, N, K)
+    sc = np.empty((N, K // 32), dtype=np.uint8)
+    for b in range(K // 32):
+        sc[:, b] = hi if b % 4 in (0, 3) else hi - span
+    w["scales"] = sc
+    x = synth.gen_x(key, M, K, "f16")
+    small = np.array([(k // 32) % 4 in (1, 2) for k in range(K)])
+    x[0, ~small] = 0
+    P = PackedMX(w, N, K)
+    y = P.gemv(dev(x), "f16", M)
+    torch.cuda.synchronize()
+    assert "w4_gemm_kernel" in L.w4a16_last_variant()
+    ref = oracle.mx_gemv(x, "f16", w["qweight"], w["scales"], M, N, K)
+    assert_parity(to_f64(y)[:1], ref[:1], f"span {span}, small blocks only")
+    assert_parity(to_f64(y), ref, f"span {span}")
+
+
 @pytest.mark.parametrize("xdt", ["f16", "bf16"])
 def test_mxfp4_gemv_wide_scale_range(xdt):
     # Scale codes 0..200 (2^-127 .. 2^73): each block's fp32 sum is scaled on
@@ -654,7 +707,7 @@ def test_mxfp4_split_and_multi_tile_launches():
 
 @pytest.mark.parametrize("name,K,N", [("qkv", 5120, 7168), ("gate_up", 5120, 34816),
                                       ("down", 17408, 5120)])
-@pytest.mark.parametrize("M,xdt", [(1, "f16"), (8, "bf16")])
+@pytest.mark.parametrize("M,xdt", [(1, "f16"), (8, "bf16"), (64, "f16")])
 def test_mxfp4_full_size_sampled_columns(name, K, N, M, xdt):
     say(f"mxfp4 full {name} K={K} N={N} M={M} x={xdt}")
     key = (125, K, N, M)
