@@ -7,17 +7,15 @@
 //   qweight_dev uint32 [Np/16][Kp/256][64 lanes][4 dwords]
 //   lane l: column 16t + (l & 15), k-block kc = l >> 4.
 //   Dword d of lane l in unit u carries the two 32-k steps j = 2d + h (h = 0, 1);
-//   step j covers k = 256u + 32j + 8kc + e, e = 0..7.  Two-bit field p of the
-//   dword (bits 2p, 2p+1) holds step h = (p >> 2) & 1, element
-//   e = 2(p & 3) + (p >> 3), so masks 0x00030003 << 2i applied to the dword
-//   (and to the dword >> 8) give the element pairs of both steps.
+//   step j covers k = 256u + 32j + 8kc + e, e = 0..7.  The weight w = c - 1
+//   of (h, e) is two bits: "nonzero" at bit 4e + 1 - h and "negative" at bit
+//   4e + 3 - h.  So d & 0xAAAAAAAA (step h = 0) and (d << 1) & 0xAAAAAAAA
+//   (step h = 1) hold, per nibble e, the FP4 E2M1 code of w itself -- sign
+//   bit and the low exponent bit, 1.0 or 0 -- and gfx950's
+//   v_cvt_scalef32_pk_{f16,bf16}_fp4 turns each byte into the element pair
+//   (2i, 2i + 1) of the MFMA B operand: -1, 0, +1 exactly, no bias term.
 //   scales_dev uint16 [Np/16][Kp/group][16]
-// Padding holds code 1 (weight 0) and scale +0.
-//
-// Dequantization: for fp16 activations each pair is (1024 + f*c) in fp16
-// (f = 1, 4, 16, 64, 256 by bit position) and one packed fma by 1/f with
-// -(1024/f + 1) gives c - 1 exactly; for bf16 activations the pairs are
-// 128 + c and a second MFMA against the constant -129 removes the bias.
+// Padding holds zero bits (weight 0) and scale +0.
 #include <mutex>
 
 #include "common.h"
@@ -30,9 +28,16 @@ constexpr int kMaxRows = 16;
 constexpr int kWaves2 = 8;       // waves per workgroup of the staged ternary kernel
 constexpr int kMaxXLoads2 = 17;  // x load instructions per wave: M * (32 UPW + 1) <= 64 * 17
 
-__host__ __device__ constexpr int field_step(int p) { return (p >> 2) & 1; }
-__host__ __device__ constexpr int field_elem(int p) { return 2 * (p & 3) + (p >> 3); }
-__host__ __device__ constexpr int elem_field(int h, int e) { return (e & 1) * 8 + h * 4 + (e >> 1); }
+// Bits of the weight of step h (0, 1), element e (0..7) in its device dword.
+__host__ __device__ constexpr int nz_bit(int h, int e) { return 4 * e + 1 - h; }
+__host__ __device__ constexpr int neg_bit(int h, int e) { return 4 * e + 3 - h; }
+// Canonical code c (0, 1, 2 = weight -1, 0, +1) <-> the device bit pair.
+__host__ __device__ inline uint32_t w2_bits(uint32_t c, int h, int e) {
+    return (uint32_t)(c != 1u) << nz_bit(h, e) | (uint32_t)(c == 0u) << neg_bit(h, e);
+}
+__host__ __device__ inline uint32_t w2_code(uint32_t dv, int h, int e) {
+    return ((dv >> nz_bit(h, e)) & 1u) ? (((dv >> neg_bit(h, e)) & 1u) ? 0u : 2u) : 1u;
+}
 
 __global__ void w2_pack_q_kernel(const uint32_t* __restrict__ canon, uint32_t* __restrict__ dev,
                                  int N, int K, size_t total) {
@@ -47,12 +52,14 @@ __global__ void w2_pack_q_kernel(const uint32_t* __restrict__ canon, uint32_t* _
         const int n = t * kTileN + (l & 15), kc = l >> 4;
         uint32_t out = 0;
 #pragma unroll
-        for (int p = 0; p < 16; ++p) {
-            const int k = u * kUnitK2 + 32 * (2 * d + field_step(p)) + 8 * kc + field_elem(p);
-            uint32_t code = 1u;  // padding: weight 0
-            if (n < N && k < K) code = (canon[(size_t)n * KW + k / 16] >> (2 * (k % 16))) & 3u;
-            out |= code << (2 * p);
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int k = u * kUnitK2 + 32 * (2 * d + h) + 8 * kc + e;
+                uint32_t code = 1u;  // padding: weight 0
+                if (n < N && k < K) code = (canon[(size_t)n * KW + k / 16] >> (2 * (k % 16))) & 3u;
+                out |= w2_bits(code, h, e);
+            }
         dev[i] = out;
     }
 }
@@ -71,7 +78,7 @@ __global__ void w2_unpack_q_kernel(const uint32_t* __restrict__ dev, uint32_t* _
             const int k = 16 * kw + f;
             const int u = k / kUnitK2, j = (k % kUnitK2) / 32, kc = (k % 32) / 8, e = k % 8;
             const uint32_t dv = dev[(((size_t)t * U + u) * kLanes + (kc * 16 + c)) * 4 + j / 2];
-            word |= ((dv >> (2 * elem_field(j & 1, e))) & 3u) << (2 * f);
+            word |= w2_code(dv, j & 1, e) << (2 * f);
         }
         canon[i] = word;
     }
@@ -112,52 +119,25 @@ __global__ void w2_dequant_kernel(const uint32_t* __restrict__ qdev, const uint1
         const int t = n / kTileN, c = n % kTileN;
         const int u = k / kUnitK2, j = (k % kUnitK2) / 32, kc = (k % 32) / 8, e = k % 8;
         const uint32_t dv = qdev[(((size_t)t * U + u) * kLanes + (kc * 16 + c)) * 4 + j / 2];
-        const int code = (int)((dv >> (2 * elem_field(j & 1, e))) & 3u);
+        const int code = (int)w2_code(dv, j & 1, e);
         const float s = f16_bits_to_f32(sdev[((size_t)t * Gp + k / group) * 16 + c]);
         w[i] = (float)(code - 1) * s;
     }
 }
 
-__device__ __forceinline__ half2_t as_h2(uint32_t v) { return bitcast<half2_t>(v); }
-__device__ __forceinline__ uint32_t as_u(half2_t v) { return bitcast<uint32_t>(v); }
 
-// The two B operands (c - 1 in fp16, exact) of one dword: steps 2d and 2d + 1.
-__device__ __forceinline__ void dequant_w2_f16(uint32_t d, half8_t& b0, half8_t& b1) {
-    const uint32_t M = 0x64006400u;  // fp16 1024.0
-    const uint32_t t = d >> 8;
-    const half2_t q0 = as_h2((d & 0x00030003u) | M);  // 1024 + c
-    const half2_t q1 = as_h2((d & 0x000C000Cu) | M);  // 1024 + 4c
-    const half2_t q2 = as_h2((d & 0x00300030u) | M);  // 1024 + 16c
-    const half2_t q3 = as_h2((d & 0x00C000C0u) | M);  // 1024 + 64c
-    const half2_t q4 = as_h2((d & 0x03000300u) | M);  // 1024 + 256c
-    const half2_t q5 = as_h2((t & 0x000C000Cu) | M);  // 1024 + 4c
-    const half2_t q6 = as_h2((t & 0x00300030u) | M);  // 1024 + 16c
-    const half2_t q7 = as_h2((t & 0x00C000C0u) | M);  // 1024 + 64c
-    const half2_t n1025 = as_h2(0xE401E401u);
-    const half2_t r4 = as_h2(0x34003400u), n257 = as_h2(0xDC04DC04u);
-    const half2_t r16 = as_h2(0x2C002C00u), n65 = as_h2(0xD410D410u);
-    const half2_t r64 = as_h2(0x24002400u), n17 = as_h2(0xCC40CC40u);
-    const half2_t r256 = as_h2(0x1C001C00u), n5 = as_h2(0xC500C500u);
-    const u32x4_t v0 = {as_u(q0 + n1025), as_u(__builtin_elementwise_fma(q1, r4, n257)),
-                        as_u(__builtin_elementwise_fma(q2, r16, n65)),
-                        as_u(__builtin_elementwise_fma(q3, r64, n17))};
-    const u32x4_t v1 = {as_u(__builtin_elementwise_fma(q4, r256, n5)),
-                        as_u(__builtin_elementwise_fma(q5, r4, n257)),
-                        as_u(__builtin_elementwise_fma(q6, r16, n65)),
-                        as_u(__builtin_elementwise_fma(q7, r64, n17))};
-    b0 = bitcast<half8_t>(v0);
-    b1 = bitcast<half8_t>(v1);
-}
-
-// The two B operands (128 + c in bf16, exact) of one dword.
-__device__ __forceinline__ void biased_w2_bf16(uint32_t d, bf16x8_t& b0, bf16x8_t& b1) {
-    const uint32_t M = 0x43004300u;  // bf16 128.0
-    const u32x4_t v0 = {(d & 0x00030003u) | M, ((d >> 2) & 0x00030003u) | M,
-                        ((d >> 4) & 0x00030003u) | M, ((d >> 6) & 0x00030003u) | M};
-    const u32x4_t v1 = {((d >> 8) & 0x00030003u) | M, ((d >> 10) & 0x00030003u) | M,
-                        ((d >> 12) & 0x00030003u) | M, ((d >> 14) & 0x00030003u) | M};
-    b0 = bitcast<bf16x8_t>(v0);
-    b1 = bitcast<bf16x8_t>(v1);
+// The two B operands (the weights -1, 0, +1, exact) of one device dword:
+// steps 2d (nibbles of d & 0xAAAAAAAA) and 2d + 1 (of (d << 1) & 0xAAAAAAAA).
+template <bool BF16>
+__device__ __forceinline__ void w2_operands(uint32_t d, u32x4_t& b0, u32x4_t& b1) {
+    const uint32_t lo = d & 0xAAAAAAAAu, hi = (d << 1) & 0xAAAAAAAAu;
+    if constexpr (BF16) {
+        b0 = bitcast<u32x4_t>(fp4x8_to_bf16(lo, 1.0f));
+        b1 = bitcast<u32x4_t>(fp4x8_to_bf16(hi, 1.0f));
+    } else {
+        b0 = bitcast<u32x4_t>(fp4x8_to_f16(lo, 1.0f));
+        b1 = bitcast<u32x4_t>(fp4x8_to_f16(hi, 1.0f));
+    }
 }
 
 // One ring slot: a unit's 16 weight bytes for this lane plus the scales of
@@ -291,8 +271,6 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
     // 3) Dequantize and multiply, unit by unit, two 32-k steps per dword.
     const bool xrow = c < M;                                    // lane supplies x row c
     const uint8_t* xlane = (const uint8_t*)xs + (uint32_t)(c * a.xstride + 8 * kc) * 2u;
-    const bf16x8_t bias = bitcast<bf16x8_t>(
-        u32x4_t{0xC301C301u, 0xC301C301u, 0xC301C301u, 0xC301C301u});   // bf16 -129
     float4_t total = {0.f, 0.f, 0.f, 0.f};
     u32x4_t xa[2] = {};
 #pragma unroll
@@ -308,17 +286,7 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
                 }
                 // The dword's two steps as B operands.
                 u32x4_t bw[2];
-                if constexpr (!BF16) {
-                    half8_t b0, b1;
-                    dequant_w2_f16(sl.w[dd], b0, b1);
-                    bw[0] = bitcast<u32x4_t>(b0);
-                    bw[1] = bitcast<u32x4_t>(b1);
-                } else {
-                    bf16x8_t b0, b1;
-                    biased_w2_bf16(sl.w[dd], b0, b1);
-                    bw[0] = bitcast<u32x4_t>(b0);
-                    bw[1] = bitcast<u32x4_t>(b1);
-                }
+                w2_operands<BF16>(sl.w[dd], bw[0], bw[1]);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int st = 2 * dd + h;
@@ -326,10 +294,8 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
                         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                             bitcast<half8_t>(xa[h]), bitcast<half8_t>(bw[h]), acc, 0, 0, 0);
                     } else {
-                        const bf16x8_t av = bitcast<bf16x8_t>(xa[h]);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bitcast<bf16x8_t>(bw[h]),
-                                                                      acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bias, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            bitcast<bf16x8_t>(xa[h]), bitcast<bf16x8_t>(bw[h]), acc, 0, 0, 0);
                     }
                     if ((st + 1) % SPU == 0) {    // group complete: scale once, in fp32
                         const float sf = f16_bits_to_f32((uint16_t)sl.s[st / SPU]);
@@ -480,27 +446,20 @@ __global__ __launch_bounds__(512) void w2t_gemv_direct_kernel(const uint16_t* __
                 float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int st = 0; st < 8; st += 2) {
-                    const uint32_t dw = sl.w[st / 2];
+                    u32x4_t b0, b1;
+                    w2_operands<BF16>(sl.w[st / 2], b0, b1);
                     if constexpr (!BF16) {
-                        half8_t b0, b1;
-                        dequant_w2_f16(dw, b0, b1);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(xcur[st]), b0,
-                                                                     acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(xcur[st]),
+                                                                     bitcast<half8_t>(b0), acc, 0, 0, 0);
                         if ((st + 1) % SPU == 0) apply(acc, total, sl.s[st / SPU]);
                         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(xcur[st + 1]),
-                                                                     b1, acc, 0, 0, 0);
+                                                                     bitcast<half8_t>(b1), acc, 0, 0, 0);
                     } else {
-                        bf16x8_t b0, b1;
-                        biased_w2_bf16(dw, b0, b1);
-                        const bf16x8_t bias = bitcast<bf16x8_t>(
-                            u32x4_t{0xC301C301u, 0xC301C301u, 0xC301C301u, 0xC301C301u});  // -129
-                        const bf16x8_t a0 = bitcast<bf16x8_t>(xcur[st]);
-                        const bf16x8_t a1 = bitcast<bf16x8_t>(xcur[st + 1]);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bias, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(xcur[st]),
+                                                                      bitcast<bf16x8_t>(b0), acc, 0, 0, 0);
                         if ((st + 1) % SPU == 0) apply(acc, total, sl.s[st / SPU]);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bias, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(xcur[st + 1]),
+                                                                      bitcast<bf16x8_t>(b1), acc, 0, 0, 0);
                     }
                     if ((st + 2) % SPU == 0) apply(acc, total, sl.s[(st + 1) / SPU]);
                 }
