@@ -421,6 +421,66 @@ def test_repeat_calls_and_graph_replay_are_bitwise_identical():
         assert torch.equal(P.gemv(x, "bf16", M), y0)   # eager work between replays
 
 
+def _graph_replays_match(call, y, y0, eager):
+    """Capture call() (writing y) in a graph; every replay, with eager work
+    and synchronizations between them, must reproduce y0 bit for bit."""
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call(s)                                  # warm up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        call(s)
+    for r in range(4):
+        y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0), f"replay {r}"
+        assert torch.equal(eager(), y0)          # eager work between replays
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 5120, 17408), (64, 2064, 1280), (1, 4104, 5120)])
+def test_mxfp4_repeat_calls_and_graph_replay_are_bitwise_identical(M, N, K):
+    # GEMV with K slices, the M-tiled kernel, and a plain GEMV.
+    say(f"mxfp4 determinism M={M} N={N} K={K}")
+    w = synth.gen_mx((129, M), N, K)
+    P = PackedMX(w, N, K)
+    x = dev(synth.gen_x((129, M), M, K, "bf16", outlier_frac=0.01))
+    y0 = P.gemv(x, "bf16", M).clone()
+    for _ in range(10):
+        assert torch.equal(P.gemv(x, "bf16", M), y0)
+    y = torch.empty_like(y0)
+    wsb = L.mxfp4_workspace_bytes(M, N, K)
+    ws = workspace_bytes(wsb) if wsb else None
+    _graph_replays_match(
+        lambda s: L.mxfp4_gemv(x, "bf16", P.q, P.s, y, "f32", M, N, K, ws, wsb, stream=s),
+        y, y0, lambda: P.gemv(x, "bf16", M))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 5120, 5120), (24, 1032, 2048)])
+def test_w16a16_and_ternary_graph_replay_are_bitwise_identical(M, N, K):
+    say(f"w16 / ternary determinism M={M} N={N} K={K}")
+    w = dev(synth.gen_w16((130, M), N, K, "f16"))
+    x = dev(synth.gen_x((130, M), M, K, "f16"))
+    wsb = L.w16a16_workspace_bytes(M, N, K)
+    ws = workspace_bytes(wsb) if wsb else None
+
+    def w16(yy, s=None):
+        L.w16a16_gemv(x, w, "f16", yy, "f32", M, N, K, ws, wsb, stream=s)
+        return yy
+    y0 = w16(torch.empty((M, N), dtype=torch.float32, device=DEV)).clone()
+    torch.cuda.synchronize()
+    y = torch.empty_like(y0)
+    _graph_replays_match(lambda s: w16(y, s), y, y0,
+                         lambda: w16(torch.empty_like(y0)))
+    if M <= 16:
+        g = 128
+        P2 = PackedW2T(synth.gen_w2t((131,), N, K, g), N, K, g)
+        t0 = P2.gemv(x, "f16", M).clone()
+        for _ in range(5):
+            assert torch.equal(P2.gemv(x, "f16", M), t0)
+
+
 def test_split_k_narrow_shard_parity_and_poisoned_workspace():
     # One GPU's column share of down (N = 5120/8 = 640) splits K across
     # workgroups and merges fp32 partials from the workspace.
