@@ -780,6 +780,25 @@ def test_mxfp4_full_size_sampled_columns(name, K, N, M, xdt):
     assert_parity(y[:, cols], ref, "mxfp4 " + name)
 
 
+@pytest.mark.parametrize("name,K,N", [("qkv", 5120, 7168), ("gate_up", 5120, 34816),
+                                      ("down", 17408, 5120)])
+@pytest.mark.parametrize("M,dt", [(1, "f16"), (8, "bf16")])
+def test_w16a16_full_size_sampled_columns(name, K, N, M, dt):
+    # The W16A16 layer at the shapes and launch configuration the bench times.
+    say(f"w16 full {name} K={K} N={N} M={M} {dt}")
+    key = (132, K, N, M)
+    w = synth.gen_w16(key, N, K, dt)
+    x = synth.gen_x(key, M, K, dt)
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    wsb = L.w16a16_workspace_bytes(M, N, K)
+    ws = workspace_bytes(wsb) if wsb else None
+    L.w16a16_gemv(dev(x), dev(w), dt, y, "f32", M, N, K, ws, wsb)
+    torch.cuda.synchronize()
+    cols = sample_cols(N, np.random.default_rng(N + M + 11))
+    ref = oracle.w16_gemv(x, dt, w, M, N, K, cols=cols)
+    assert_parity(to_f64(y)[:, cols], ref, "w16 " + name)
+
+
 # ----------------------------------------------- full 27B-class shapes, sampled ---
 
 FULL = [("qkv", 5120, 7168), ("o_proj", 5120, 5120), ("gate_up", 5120, 34816),
