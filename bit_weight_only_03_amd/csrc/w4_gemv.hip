@@ -1,4 +1,8 @@
-// w4_gemv.hip -- y[M,N] = x[M,K] . ((q - z) * s)[K,N] on gfx950, M = 1..16.
+// w4_gemv.hip -- y[M,N] = x[M,K] . ((q - z) * s)[K,N] on gfx950: the GEMV
+// kernel for M = 1..16, the entry points (w4a16_gemv, w4a16_gemv_add,
+// mxfp4_gemv) that route larger M to the M-tiled kernel (w4_gemm.hip), and
+// the split-K merge.  The same kernel also runs MXFP4 weights (MX = true:
+// E2M1 elements with one E8M0 scale per 32 k, mxfp4.hip's layout).
 //
 // The layer is bound by HBM bandwidth: every call streams all packed weights
 // once (Ninfer V100 article, haowenji.com, section 三), so the kernel is built

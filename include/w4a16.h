@@ -174,12 +174,15 @@ int mxfp4_pack(const uint8_t* qweight_canon, const uint8_t* scales_canon, void* 
 int mxfp4_unpack(const void* qweight, const void* scales, uint8_t* qweight_canon,
                  uint8_t* scales_canon, int N, int K, w4a16_stream_t stream);
 
-/* y[M,N] = x[M,K] . w[N,K]^T from the packed device layout.  Each 32-k
- * block's product is summed in fp32 and then scaled by 2^(E - 127) (the MX
- * specification's block dot product), so every scale code is handled
- * exactly; products and sums fp32, deterministic.  Dtypes, alignment,
- * workspace and overlap rules as for w4a16_gemv; workspace size from
- * mxfp4_workspace_bytes. */
+/* y[M,N] = x[M,K] . w[N,K]^T from the packed device layout.  Every product
+ * is exact and every sum fp32, whatever the scale codes: where the four
+ * block scales of a 128-k span of a column lie within 2^36 of each other,
+ * they are folded into the exact element conversion (relative to the
+ * largest) and the span's fp32 sum takes the remaining power of two; wider
+ * spans take the MX specification's block dot product literally, each
+ * block's fp32 sum times its own 2^(E - 127).  Deterministic.  Dtypes,
+ * alignment, workspace and overlap rules as for w4a16_gemv; workspace size
+ * from mxfp4_workspace_bytes. */
 int mxfp4_workspace_bytes(int M, int N, int K, size_t* bytes);
 int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const void* scales, void* y,
                int y_dtype, int M, int N, int K, void* workspace, size_t workspace_bytes,
