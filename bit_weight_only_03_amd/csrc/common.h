@@ -248,6 +248,10 @@ inline int check_w2_shape(int N, int K, int group) {
     return W4A16_OK;
 }
 
+// Compute units of the current device (256 on MI355X; 256 if the query
+// fails), cached per device.  Host only.
+int cu_count();
+
 void set_last_variant(const char* fmt, ...);
 void set_last_error(const char* what);
 

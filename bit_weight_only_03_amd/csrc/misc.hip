@@ -3,6 +3,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+
 #include "common.h"
 
 using namespace w4k;
@@ -11,6 +13,9 @@ namespace {
 
 constexpr int kProbeBlocks = 4096;
 constexpr int kProbeThreads = 256;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not queried yet
 
 thread_local char g_last_variant[160] = "none";
 thread_local char g_last_error[96] = "none";
@@ -46,6 +51,19 @@ __global__ __launch_bounds__(kProbeThreads) void bw_probe_kernel(const u32x4_t* 
 }  // namespace
 
 namespace w4h {
+
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    hipDeviceProp_t prop;
+    n = (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
+            ? prop.multiProcessorCount
+            : 256;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);   // every racer stores the same value
+    return n;
+}
 void set_last_variant(const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);

@@ -175,18 +175,6 @@ w16_kernel_t pick_w16_rb(int rb) {
     }
 }
 
-int cu_count16() {
-    static int n = 0;
-    if (!n) {
-        int dev = 0;
-        hipDeviceProp_t prop;
-        n = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
-             prop.multiProcessorCount > 0)
-                ? prop.multiProcessorCount
-                : 256;
-    }
-    return n;
-}
 
 struct W16Plan {
     int rb, split;
@@ -205,7 +193,7 @@ W16Plan w16_plan(int M, int N, int K) {
     p.rb = (M + 15) / 16;
     p.workgroups = (T + kW16Waves - 1) / kW16Waves;
     p.split = 1;
-    while (p.workgroups * p.split < 8LL * cu_count16() && U / (2 * p.split) >= 6 &&
+    while (p.workgroups * p.split < 8LL * w4h::cu_count() && U / (2 * p.split) >= 6 &&
            p.split < kW16MaxSplit)
         p.split *= 2;
     if (const char* e = getenv("W16A16_SPLIT")) {

@@ -528,21 +528,6 @@ w2x_kernel_t pickx(int group) {
 
 // ------------------------------------------------------------------ dispatch
 
-// Compute units of the current device (queried once; 256 on MI355X).
-int cu_count2() {
-    static int n = 0;
-    static std::once_flag once;
-    std::call_once(once, [] {
-        int dev = 0;
-        hipDeviceProp_t prop;
-        if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
-            prop.multiProcessorCount > 0)
-            n = prop.multiProcessorCount;
-        else
-            n = 256;
-    });
-    return n;
-}
 
 constexpr size_t kLdsPerCu2 = 160 * 1024;      // gfx950
 constexpr int kUpwSet2[] = {1, 2, 3, 4, 5, 6, 8, 9, 12, 17};
@@ -753,7 +738,7 @@ extern "C" int w2t_workspace_bytes(int M, int N, int K, int group, size_t* bytes
     if (M < 1 || M > kMaxRows) return W4A16_ERR_SHAPE;
     int rc = w4h::check_w2_shape(N, K, group);
     if (rc) return rc;
-    const Plan2 p = make_plan2(M, N, K, cu_count2());
+    const Plan2 p = make_plan2(M, N, K, w4h::cu_count());
     if (use_staged(p)) {
         *bytes = 0;
     } else {
@@ -776,7 +761,7 @@ extern "C" int w2t_gemv(const void* x, int x_dtype, const void* qweight, const v
     if (!w4h::aligned16(x) || !w4h::aligned16(qweight) || !w4h::aligned16(scales) ||
         !w4h::aligned16(y))
         return W4A16_ERR_ALIGN;
-    Plan2 p = make_plan2(M, N, K, cu_count2());
+    Plan2 p = make_plan2(M, N, K, w4h::cu_count());
     if (!use_staged(p)) return launch_direct(x, x_dtype, qweight, scales, y, y_dtype, M, N, K, group,
                                              workspace, workspace_bytes, stream);
     const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;

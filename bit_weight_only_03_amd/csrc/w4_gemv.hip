@@ -483,21 +483,6 @@ const Tuning& tuning() {
     return t;
 }
 
-// Compute units of the current device (queried once; 256 on MI355X).
-int cu_count() {
-    static int n = 0;
-    static std::once_flag once;
-    std::call_once(once, [] {
-        int dev = 0;
-        hipDeviceProp_t prop;
-        if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
-            prop.multiProcessorCount > 0)
-            n = prop.multiProcessorCount;
-        else
-            n = 256;
-    });
-    return n;
-}
 
 constexpr size_t kLdsPerCu = 160 * 1024;      // gfx950
 constexpr int kWaves = 8;                     // waves per workgroup (two workgroups per CU)
@@ -701,7 +686,7 @@ bool use_gemm(int M, int N, int K, int group) {
     if (t >= 1) return M >= t;
     if (M > 12) return true;
     if (M < 8) return false;
-    const Plan p = make_plan(M, N, K, group, cu_count());
+    const Plan p = make_plan(M, N, K, group, w4h::cu_count());
     return p.tpw == 1 && p.lds > kLdsPerCu / 2;
 }
 
@@ -728,7 +713,7 @@ int check_gemv_args(const void* x, int x_dtype, const void* q, const void* s, co
 int launch_gemm(const void* x, int x_dtype, const void* qweight, const void* scales, const void* zeros,
                 void* y, int y_dtype, const void* res, int res_dtype, int M, int N, int K, int group,
                 void* workspace, size_t workspace_bytes, hipStream_t st) {
-    const w4h::GemmPlan p = w4h::gemm_plan(M, N, K, group, cu_count());
+    const w4h::GemmPlan p = w4h::gemm_plan(M, N, K, group, w4h::cu_count());
     const size_t need = gemm_workspace(p, M, N);
     if (need) {
         if (!workspace) return W4A16_ERR_NULL;
@@ -773,10 +758,10 @@ extern "C" int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* byt
     int rc = w4h::check_w4_shape(N, K, group);
     if (rc) return rc;
     if (use_gemm(M, N, K, group)) {
-        *bytes = gemm_workspace(w4h::gemm_plan(M, N, K, group, cu_count()), M, N);
+        *bytes = gemm_workspace(w4h::gemm_plan(M, N, K, group, w4h::cu_count()), M, N);
         return W4A16_OK;
     }
-    const Plan p = make_plan(M, N, K, group, cu_count());
+    const Plan p = make_plan(M, N, K, group, w4h::cu_count());
     *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     return W4A16_OK;
 }
@@ -791,7 +776,7 @@ int gemv_impl(const void* x, int x_dtype, const void* qweight, const void* scale
     if (use_gemm(M, N, K, group))
         return launch_gemm(x, x_dtype, qweight, scales, zeros, y, y_dtype, res, res_dtype, M, N, K,
                            group, workspace, workspace_bytes, (hipStream_t)stream);
-    Plan p = make_plan(M, N, K, group, cu_count());
+    Plan p = make_plan(M, N, K, group, w4h::cu_count());
     if (!p.upw) return W4A16_ERR_UNSUPPORTED;
     const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     if (need) {
@@ -869,10 +854,10 @@ extern "C" int mxfp4_workspace_bytes(int M, int N, int K, size_t* bytes) {
     if (M < 1 || M > w4h::kMaxRowsGemm) return W4A16_ERR_SHAPE;
     if (int rc = w4h::check_mx_shape(N, K)) return rc;
     if (use_gemm(M, N, K, kMxPlanGroup)) {
-        *bytes = gemm_workspace(w4h::gemm_plan(M, N, K, kMxPlanGroup, cu_count()), M, N);
+        *bytes = gemm_workspace(w4h::gemm_plan(M, N, K, kMxPlanGroup, w4h::cu_count()), M, N);
         return W4A16_OK;
     }
-    const Plan p = make_plan(M, N, K, kMxPlanGroup, cu_count());
+    const Plan p = make_plan(M, N, K, kMxPlanGroup, w4h::cu_count());
     *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     return W4A16_OK;
 }
@@ -883,7 +868,7 @@ extern "C" int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const
     if (int rc = check_mx_args(x, x_dtype, qweight, scales, y, y_dtype, M, N, K)) return rc;
     if (use_gemm(M, N, K, kMxPlanGroup)) {
         // Rows past the GEMV's crossover: the M-tiled kernel's MXFP4 mode.
-        const w4h::GemmPlan gp = w4h::gemm_plan(M, N, K, kMxPlanGroup, cu_count());
+        const w4h::GemmPlan gp = w4h::gemm_plan(M, N, K, kMxPlanGroup, w4h::cu_count());
         const size_t need = gemm_workspace(gp, M, N);
         if (need) {
             if (!workspace) return W4A16_ERR_NULL;
@@ -902,7 +887,7 @@ extern "C" int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const
                               pad_n(N) / kTileN, gp.split, gp.workgroups);
         return w4h::launch_status();
     }
-    Plan p = make_plan(M, N, K, kMxPlanGroup, cu_count());
+    Plan p = make_plan(M, N, K, kMxPlanGroup, w4h::cu_count());
     if (!p.upw) return W4A16_ERR_UNSUPPORTED;
     const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     if (need) {
