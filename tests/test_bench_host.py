@@ -1,0 +1,91 @@
+"""Host-side checks of bench.py: the one-GPU contract, the algorithmic byte
+counts the reported bandwidth divides by, and the folding of rocprofv3
+counter runs into the committed traffic summary.  No GPU needed."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_bytes_closed_forms():
+    # 4-bit: N K / 2 packed nibbles + G N fp16 scales + G N / 2 zero bytes + x + y.
+    M, N, K, g = 1, 7168, 5120, 128
+    G = K // g
+    assert bench.alg_bytes(M, N, K, g) == N * K // 2 + G * N * 2 + G * N // 2 + M * K * 2 + M * N * 4
+    # Bytes per weight: 0.5 + 2.5 / 128.
+    big = bench.alg_bytes(0, 1 << 12, 1 << 12, 128)
+    assert big / (1 << 24) == pytest.approx(0.5 + 2.5 / 128)
+    # Ternary: 2 bits per weight + fp16 scales; MXFP4: 4 bits + one byte per 32.
+    assert bench.w2t_bytes(0, 4096, 4096, 128) / (1 << 24) == pytest.approx(0.25 + 2 / 128)
+    assert bench.mx_bytes(0, 4096, 4096) / (1 << 24) == pytest.approx(0.5 + 1 / 32)
+    # The 64-layer sweep the headline divides by.
+    layer = sum(bench.alg_bytes(1, N_, K_, 128) for (_, K_, N_) in bench.SHAPES)
+    assert layer * 64 == pytest.approx(11.0e9, rel=0.01)
+
+
+def test_kernel_key_normalises_profiler_and_variant_names():
+    prof = "void (anonymous namespace)::w4_gemv_kernel<false, 4, 5, 3, false>(unsigned short const*, ...)"
+    var = "w4_mfma16 f16 g128 kernel=w4_gemv_kernel<false, 4, 5, 3> tiles=2176"
+    assert bench.kernel_key(prof) == bench.kernel_key(var) == "w4_gemv_kernel<false, 4, 5, 3>"
+    assert bench.kernel_key("w4_gemv_kernel<true, 4, 5, 1, true>") == "w4_gemv_kernel<true, 4, 5, 1, true>"
+    assert bench.kernel_key("w16_gemv_kernel<false, 1>") == "w16_gemv_kernel<false, 1>"
+    assert bench.kernel_key("__amd_rocclr_copyBuffer") is None
+
+
+def test_committed_traffic_summary_is_consistent():
+    with open(bench.TRAFFIC_FILE) as f:
+        t = json.load(f)
+    assert {"fetch", "write"} <= set(t["calibration"])
+    assert 1.9 < t["calibration"]["fetch"]["factor"] < 2.1      # FETCH_SIZE counts half
+    assert 0.95 < t["calibration"]["write"]["factor"] < 1.05
+    # Each instantiation of the sweep moves about its algorithmic bytes.
+    alg = {"w4_gemv_kernel<false, 4, 5, 3>": bench.alg_bytes(1, 34816, 5120, 128),
+           "w4_gemv_kernel<false, 4, 17, 1>": bench.alg_bytes(1, 5120, 17408, 128)}
+    for k, a in alg.items():
+        ratio = t["kernels"][k]["bytes_per_dispatch"] / a
+        assert 1.0 <= ratio < 1.03, (k, ratio)
+    # The bench reports it only while the kernel source is the profiled one.
+    got = bench.load_traffic("w4_gemv_kernel<false, 4, 5, 3>")
+    if t["kernel_source_sha256_16"] == bench.kernel_source_hash():
+        assert got == t["kernels"]["w4_gemv_kernel<false, 4, 5, 3>"]["bytes_per_dispatch"]
+    else:
+        assert got is None
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n")
+        for i, (name, kib) in enumerate(rows):
+            f.write(f'{i},"{name}",256,{counter},{kib}\n')
+
+
+def test_ingest_pmc_scales_by_the_calibration_copy(tmp_path, monkeypatch):
+    # The 1 GiB copy counted as 512 MiB fetched -> factor 2; writes count true.
+    gemv = "void (anonymous namespace)::w4_gemv_kernel<false, 4, 5, 3, false>(int)"
+    copy = "__amd_rocclr_copyBuffer"
+    f_csv, w_csv = tmp_path / "f.csv", tmp_path / "w.csv"
+    _counter_csv(f_csv, "FETCH_SIZE", [(copy, 512 * 1024), (gemv, 1000.0), (gemv, 1002.0)])
+    _counter_csv(w_csv, "WRITE_SIZE", [(copy, 1024 * 1024), (gemv, 10.0), (gemv, 10.0)])
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    bench.ingest_pmc(str(f_csv), str(w_csv), "test command")
+    t = json.loads(out.read_text())
+    k = t["kernels"]["w4_gemv_kernel<false, 4, 5, 3>"]
+    assert k["dispatches"] == [2, 2]
+    assert k["fetch_bytes_per_dispatch"] == round(1001.0 * 1024 * 2)
+    assert k["write_bytes_per_dispatch"] == 10 * 1024
+    assert k["bytes_per_dispatch"] == round(1001.0 * 1024 * 2 + 10 * 1024)
+    assert t["command"] == "test command"
