@@ -401,6 +401,7 @@ namespace w4h {
 // slices (so that the grid gives every CU at least two workgroups while each
 // slice keeps at least eight units).
 GemmPlan gemm_plan(int M, int N, int K, int group, int cus) {
+    (void)group;   // every group size has the same unit and register plan
     GemmPlan p;
     const int U = (K + kUnitK - 1) / kUnitK;
     const int T = pad_n(N) / kTileN;
