@@ -229,21 +229,29 @@ inline bool group_ok(int group) {
     return group == 32 || group == 64 || group == 128 || group == 256;
 }
 
+// Largest K: keeps every per-workgroup weight, scale and zero-point offset
+// (at most three tiles' columns) inside the 32-bit offsets of the kernels'
+// buffer resources.
+constexpr int kMaxK = 1 << 26;
+
+// x as one buffer resource (M * K * 2 bytes addressed by 32-bit offsets).
+inline bool x_fits(int M, int K) { return (long long)M * K * 2 <= 0xffffffffLL; }
+
 // Shape contract of the 4-bit functions (see w4a16.h).
 inline int check_w4_shape(int N, int K, int group) {
-    if (N < 1 || K < 1 || !group_ok(group)) return W4A16_ERR_SHAPE;
+    if (N < 1 || K < 1 || K > kMaxK || !group_ok(group)) return W4A16_ERR_SHAPE;
     if (N % 8 || K % 8 || K % group) return W4A16_ERR_SHAPE;
     return W4A16_OK;
 }
 
 // Shape contract of the MXFP4 functions (see w4a16.h).
 inline int check_mx_shape(int N, int K) {
-    if (N < 8 || K < 32 || N % 8 || K % 32) return W4A16_ERR_SHAPE;
+    if (N < 8 || K < 32 || K > kMaxK || N % 8 || K % 32) return W4A16_ERR_SHAPE;
     return W4A16_OK;
 }
 
 inline int check_w2_shape(int N, int K, int group) {
-    if (N < 1 || K < 1 || !group_ok(group)) return W4A16_ERR_SHAPE;
+    if (N < 1 || K < 1 || K > kMaxK || !group_ok(group)) return W4A16_ERR_SHAPE;
     if (K % 16 || K % group) return W4A16_ERR_SHAPE;
     return W4A16_OK;
 }

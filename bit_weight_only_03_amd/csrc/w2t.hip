@@ -735,7 +735,7 @@ extern "C" int w2t_dequant(const void* qweight, const void* scales, float* w, in
 
 extern "C" int w2t_workspace_bytes(int M, int N, int K, int group, size_t* bytes) {
     if (!bytes) return W4A16_ERR_NULL;
-    if (M < 1 || M > kMaxRows) return W4A16_ERR_SHAPE;
+    if (M < 1 || M > kMaxRows || !w4h::x_fits(M, K)) return W4A16_ERR_SHAPE;
     int rc = w4h::check_w2_shape(N, K, group);
     if (rc) return rc;
     const Plan2 p = make_plan2(M, N, K, w4h::cu_count());
@@ -755,7 +755,7 @@ extern "C" int w2t_gemv(const void* x, int x_dtype, const void* qweight, const v
     if (x_dtype != W4A16_F16 && x_dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
     if (y_dtype != W4A16_F32 && y_dtype != W4A16_F16 && y_dtype != W4A16_BF16)
         return W4A16_ERR_DTYPE;
-    if (M < 1 || M > kMaxRows) return W4A16_ERR_SHAPE;
+    if (M < 1 || M > kMaxRows || !w4h::x_fits(M, K)) return W4A16_ERR_SHAPE;
     int rc = w4h::check_w2_shape(N, K, group);
     if (rc) return rc;
     if (!w4h::aligned16(x) || !w4h::aligned16(qweight) || !w4h::aligned16(scales) ||

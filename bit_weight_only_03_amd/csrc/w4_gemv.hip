@@ -700,7 +700,7 @@ int check_gemv_args(const void* x, int x_dtype, const void* q, const void* s, co
     if (x_dtype != W4A16_F16 && x_dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
     if (y_dtype != W4A16_F32 && y_dtype != W4A16_F16 && y_dtype != W4A16_BF16)
         return W4A16_ERR_DTYPE;
-    if (M < 1 || M > w4h::kMaxRowsGemm) return W4A16_ERR_SHAPE;
+    if (M < 1 || M > w4h::kMaxRowsGemm || !w4h::x_fits(M, K)) return W4A16_ERR_SHAPE;
     int rc = w4h::check_w4_shape(N, K, group);
     if (rc) return rc;
     if (!w4h::aligned16(x) || !w4h::aligned16(q) || !w4h::aligned16(s) || !w4h::aligned16(z) ||
@@ -754,7 +754,7 @@ void launch_merge(const void* workspace, void* y, int y_dtype, const void* res, 
 
 extern "C" int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* bytes) {
     if (!bytes) return W4A16_ERR_NULL;
-    if (M < 1 || M > w4h::kMaxRowsGemm) return W4A16_ERR_SHAPE;
+    if (M < 1 || M > w4h::kMaxRowsGemm || !w4h::x_fits(M, K)) return W4A16_ERR_SHAPE;
     int rc = w4h::check_w4_shape(N, K, group);
     if (rc) return rc;
     if (use_gemm(M, N, K, group)) {
@@ -840,7 +840,7 @@ int check_mx_args(const void* x, int x_dtype, const void* q, const void* s, cons
     if (x_dtype != W4A16_F16 && x_dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
     if (y_dtype != W4A16_F32 && y_dtype != W4A16_F16 && y_dtype != W4A16_BF16)
         return W4A16_ERR_DTYPE;
-    if (M < 1 || M > w4h::kMaxRowsGemm) return W4A16_ERR_SHAPE;
+    if (M < 1 || M > w4h::kMaxRowsGemm || !w4h::x_fits(M, K)) return W4A16_ERR_SHAPE;
     if (int rc = w4h::check_mx_shape(N, K)) return rc;
     if (!w4h::aligned16(x) || !w4h::aligned16(q) || !w4h::aligned16(s) || !w4h::aligned16(y))
         return W4A16_ERR_ALIGN;
@@ -851,7 +851,7 @@ int check_mx_args(const void* x, int x_dtype, const void* q, const void* s, cons
 
 extern "C" int mxfp4_workspace_bytes(int M, int N, int K, size_t* bytes) {
     if (!bytes) return W4A16_ERR_NULL;
-    if (M < 1 || M > w4h::kMaxRowsGemm) return W4A16_ERR_SHAPE;
+    if (M < 1 || M > w4h::kMaxRowsGemm || !w4h::x_fits(M, K)) return W4A16_ERR_SHAPE;
     if (int rc = w4h::check_mx_shape(N, K)) return rc;
     if (use_gemm(M, N, K, kMxPlanGroup)) {
         *bytes = gemm_workspace(w4h::gemm_plan(M, N, K, kMxPlanGroup, w4h::cu_count()), M, N);

@@ -74,8 +74,10 @@ typedef enum {
 typedef enum { W4A16_F16 = 0, W4A16_BF16 = 1, W4A16_F32 = 2 } w4a16_dtype;
 
 /* Shape contract shared by the 4-bit functions:
- *   1 <= N, 1 <= K, N % 8 == 0, K % group == 0, K % 8 == 0,
- *   group in {32, 64, 128, 256}; for the GEMV also 1 <= M <= 64. */
+ *   1 <= N, 1 <= K <= 2^26, N % 8 == 0, K % group == 0, K % 8 == 0,
+ *   group in {32, 64, 128, 256}; for the GEMV also 1 <= M <= 64 and
+ *   M * K * 2 < 2^32 (x is addressed through 32-bit offsets).  The MXFP4 and
+ *   ternary functions take the same limits on K and M * K. */
 
 /* Bytes of the device layout for an N x K matrix with the given group.  Host
  * only.  Returns W4A16_OK or W4A16_ERR_SHAPE / W4A16_ERR_NULL. */

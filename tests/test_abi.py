@@ -179,3 +179,26 @@ def test_mxfp4_sizes_and_argument_checks():
     with pytest.raises(lib.W4A16Error) as e:
         lib.mxfp4_dequant(good, good, good + 8, 64, 64, stream=0)
     assert e.value.status == -3
+
+
+def test_offset_limits_are_rejected_before_launch():
+    # x is one 32-bit buffer resource (M * K * 2 < 2^32) and K <= 2^26 keeps
+    # the per-workgroup weight offsets in range: larger shapes are errors, not
+    # silent wrap-around.
+    good = 1 << 20
+    big_k = 1 << 26
+    for call in (lambda: lib.w4a16_workspace_bytes(64, 64, big_k, 128),   # M K 2 = 2^33
+                 lambda: lib.w4a16_workspace_bytes(1, 64, big_k + 128, 128),   # K > 2^26
+                 lambda: lib.mxfp4_workspace_bytes(64, 64, big_k),
+                 lambda: lib.w2t_workspace_bytes(64, 64, big_k, 128),
+                 lambda: lib.w4a16_packed_sizes(64, big_k + 128, 128),
+                 lambda: lib.mxfp4_packed_sizes(64, big_k + 32),
+                 lambda: lib.w4a16_gemv(good, 0, good, good, good, good, 2, 64, 64, big_k, 128,
+                                        stream=0),
+                 lambda: lib.mxfp4_gemv(good, 0, good, good, good, 2, 64, 64, big_k, stream=0)):
+        with pytest.raises(lib.W4A16Error) as e:
+            call()
+        assert e.value.status == -2
+    # The largest K at M = 1 is accepted (sizes only; nothing launches).
+    assert lib.w4a16_workspace_bytes(1, 64, big_k, 128) >= 0
+    assert lib.w4a16_packed_sizes(64, big_k, 128)[0] == 64 * big_k // 2
