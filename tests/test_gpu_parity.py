@@ -864,3 +864,75 @@ def test_gpu_rejects_bad_arguments_without_launching():
     with pytest.raises(L.W4A16Error) as e:
         L.w4a16_gemv(good.data_ptr() + 2, "f16", good, good, good, good, "f32", 1, 16, 128, 128)
     assert e.value.status == -3
+
+
+# ------------------------------------------------- seeded random shapes ---
+
+def _random_cases(seed, n, max_m, groups):
+    """n seeded (M, N, K, g, x dtype, y dtype) draws covering the planners'
+    choices: rows up to max_m, N up to ~2000 in steps of 8 (ragged tiles),
+    K a multiple of the group, often ragged against the 128-k unit."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        g = int(rng.choice(groups))
+        M = int(rng.integers(1, max_m + 1))
+        N = 8 * int(rng.integers(1, 250))
+        K = g * int(rng.integers(1, max(2, 3200 // g)))
+        out.append((M, N, K, g, str(rng.choice(["f16", "bf16"])), str(rng.choice(["f32", "f16", "bf16"]))))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K,g,xdt,ydt", _random_cases(2024, 16, 64, [32, 64, 128, 256]))
+def test_w4_random_shapes_match_oracle(M, N, K, g, xdt, ydt):
+    say(f"w4 random M={M} N={N} K={K} g={g} x={xdt} y={ydt}")
+    key = (140, M, N, K, g)
+    w = synth.gen_w4(key, N, K, g)
+    x = synth.gen_x(key, M, K, xdt)
+    y = PackedW4(w, N, K, g).gemv(dev(x), xdt, M, ydt)
+    torch.cuda.synchronize()
+    say("  variant: " + L.w4a16_last_variant())
+    ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g)
+    assert_parity(to_f64(y), ref, "w4 random", extra_rel=_ROUND[ydt])
+
+
+@pytest.mark.parametrize("M,N,K,g,xdt,ydt", _random_cases(2025, 10, 64, [32]))
+def test_mxfp4_random_shapes_match_oracle(M, N, K, g, xdt, ydt):
+    say(f"mxfp4 random M={M} N={N} K={K} x={xdt} y={ydt}")
+    key = (141, M, N, K)
+    w = synth.gen_mx(key, N, K)
+    x = synth.gen_x(key, M, K, xdt)
+    y = PackedMX(w, N, K).gemv(dev(x), xdt, M, ydt)
+    torch.cuda.synchronize()
+    say("  variant: " + L.w4a16_last_variant())
+    ref = oracle.mx_gemv(x, xdt, w["qweight"], w["scales"], M, N, K)
+    assert_parity(to_f64(y), ref, "mxfp4 random", extra_rel=_ROUND[ydt])
+
+
+@pytest.mark.parametrize("M,N,K,g,xdt,ydt", _random_cases(2026, 10, 64, [8]))
+def test_w16a16_random_shapes_match_oracle(M, N, K, g, xdt, ydt):
+    say(f"w16 random M={M} N={N} K={K} {xdt} y={ydt}")
+    key = (142, M, N, K)
+    w = synth.gen_w16(key, N, K, xdt)
+    x = synth.gen_x(key, M, K, xdt)
+    y = torch.empty((M, N), dtype=_TORCH_DT[ydt], device=DEV)
+    wsb = L.w16a16_workspace_bytes(M, N, K)
+    ws = workspace_bytes(wsb) if wsb else None
+    L.w16a16_gemv(dev(x), dev(w), xdt, y, ydt, M, N, K, ws, wsb)
+    torch.cuda.synchronize()
+    ref = oracle.w16_gemv(x, xdt, w, M, N, K)
+    assert_parity(to_f64(y), ref, "w16 random", extra_rel=_ROUND[ydt])
+
+
+@pytest.mark.parametrize("M,N,K,g,xdt,ydt", _random_cases(2027, 10, 16, [32, 64, 128, 256]))
+def test_w2t_random_shapes_match_oracle(M, N, K, g, xdt, ydt):
+    K = max(K, 16) // 16 * 16 if K % 16 else K          # the ternary contract: K % 16 == 0
+    say(f"w2t random M={M} N={N} K={K} g={g} x={xdt} y={ydt}")
+    key = (143, M, N, K, g)
+    w = synth.gen_w2t(key, N, K, g)
+    x = synth.gen_x(key, M, K, xdt)
+    y = PackedW2T(w, N, K, g).gemv(dev(x), xdt, M, ydt)
+    torch.cuda.synchronize()
+    say("  variant: " + L.w4a16_last_variant())
+    ref = oracle.w2t_gemv(x, xdt, w["codes"], w["scales"], M, N, K, g)
+    assert_parity(to_f64(y), ref, "w2t random", extra_rel=_ROUND[ydt])
