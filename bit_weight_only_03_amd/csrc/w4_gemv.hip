@@ -57,7 +57,7 @@ namespace {
 
 constexpr int kMaxWaves = 8;     // waves per workgroup (the kernel's 512-thread launch bound)
 constexpr int kMaxRows = 16;     // rows per MFMA
-constexpr int kMaxXLoads = 17;   // x load instructions per wave: M * (16 UPW + 1) <= 64 * 17
+constexpr int kMaxXLoads = 16;   // x load instructions per wave: M * 16 UPW <= 64 * 16
 
 // One ring slot: a unit's 16 weight bytes for this lane plus the scale and
 // zero-point words of the groups it touches.
@@ -159,34 +159,42 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     const int Gp = U * kUnitK / (SPG * 32);
     const int c = lane & 15, kc = lane >> 4;
 
-    // LDS: wave w's x range [M][xstride] halves at w * M * xstride, then the
-    // reduction buffer [W][M][16] floats.
-    uint16_t* xs = (uint16_t*)smem + (size_t)wave * M * a.xstride;
-    float* red = (float*)(smem + (size_t)W * M * a.xstride * 2);
+    // LDS: wave w's x range, [M][16 UPW chunks of 16 bytes] at byte
+    // 2 w M xstride (xstride = 128 UPW halves, no padding).  Inside each
+    // 128-k unit of row m, logical chunk p sits at position p ^ (m % 4): the
+    // rows are 256-byte multiples apart, so without the XOR the rows' copies
+    // of a chunk would share banks; with it, rows 0..3 use four distinct
+    // bank groups (rows m and m + 4 share one: a two-way conflict at M = 8).
+    // Only the low two bits are swizzled so that the MFMA step j keeps a
+    // lane-independent offset (64 j).  Once its products are
+    // done, each wave reuses its own region for its partial sums, so a
+    // workgroup needs exactly M x K x 2 bytes of LDS (two workgroups per CU
+    // up to M = 8 at K = 5120).
+    uint8_t* const xsb = smem + (size_t)wave * M * a.xstride * 2;
 
     // 1) x range -> this wave's LDS region, straight from memory into LDS
-    //    (no VGPRs, one round trip whatever M is).  Chunk ci of the padded
-    //    region [M][xstride / 8 chunks of 16 bytes] is row ci / cpr, chunk
-    //    ci % cpr; one load instruction fills 64 consecutive chunks (lane l ->
-    //    chunk 64 i + l).  Pad chunks are skipped; chunks past K (a ragged
-    //    last unit) are zeroed with ordinary LDS stores.  These are the
-    //    wave's first memory accesses; where its arithmetic is unconditional
-    //    the wave waits for them only after issuing its weight ring (below),
-    //    so the two round trips overlap.
+    //    (no VGPRs, one round trip whatever M is).  Position ci of the region
+    //    is row ci / cpr, position ci % cpr of that row; one load instruction
+    //    fills 64 consecutive positions (lane l -> position 64 i + l) with the
+    //    logical chunk the swizzle puts there.  Chunks past K (a ragged last
+    //    unit) are zeroed with ordinary LDS stores.  These are the wave's
+    //    first memory accesses; where its arithmetic is unconditional the
+    //    wave waits for them only after issuing its weight ring (below), so
+    //    the two round trips overlap.
     {
         const int cpr = a.xstride / 8;
-        const int live = nu * (kUnitK / 8);          // chunks of a row this wave reads
+        const int live = nu * (kUnitK / 8);          // positions of a row this wave reads
         const int xch = M * cpr;
         const uint32_t xbytes = (uint32_t)M * (uint32_t)K * 2u;
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xbytes);
-        uint8_t* xsb = (uint8_t*)xs;
 #pragma unroll
         for (int i = 0; i < kMaxXLoads; ++i) {
             if (i * 64 < xch) {                    // wave-uniform
                 const int ci = i * 64 + lane;
-                const int m = ci / cpr, kk = (ci % cpr) * 8;
-                const int kg = w0 * kUnitK + kk;
-                if (m < M && kk < live * 8) {
+                const int m = ci / cpr, pc = ci % cpr;
+                const int lc = pc ^ (m & 3);   // same unit and step as pc
+                const int kg = w0 * kUnitK + lc * 8;
+                if (m < M && pc < live) {
                     if (kg < K)
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(
                             rx, (__attribute__((address_space(3))) void*)(xsb + i * 1024), 16,
@@ -259,7 +267,8 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     const int zshift = 4 * (c & 7);
     const uint32_t magic = opaque_v(BF16 ? 0x43004300u : 0x64006400u);   // 128.0 / 1024.0 pairs
     const bool xrow = c < M;                                    // lane supplies x row c
-    const uint8_t* xlane = (const uint8_t*)xs + (uint32_t)(c * a.xstride + 8 * kc) * 2u;
+    // Step j of unit i: logical chunk 4 j + kc of row c, at position 4 j + (kc ^ c % 4).
+    const uint8_t* xlane = xsb + (uint32_t)(c * a.xstride + 8 * (kc ^ (c & 3))) * 2u;
     float4_t total[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) total[j] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -365,15 +374,21 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     }
 
     // 4) Wave partials (lane l holds rows 4*(l/16) + r of column l % 16) ->
-    //    LDS, then M x 16 threads add them in wave order and store.
+    //    [TPW][M][16] floats at the start of the wave's own x region (TPW M
+    //    64 <= M UPW 256 bytes; its last x reads were consumed above, and a
+    //    wave's LDS accesses complete in order), then M x 16 threads add
+    //    them in wave order and store.
+    float* const red = (float*)xsb;
+    const size_t rstride = (size_t)M * a.xstride / 2;         // floats between wave regions
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = 4 * kc + r;
-            if (m < M) red[((j * W + wave) * M + m) * kTileN + c] = total[j][r];
+            if (m < M) red[(j * M + m) * kTileN + c] = total[j][r];
         }
     __syncthreads();
+    const float* const red0 = (const float*)smem;
     for (int idx = threadIdx.x; idx < TPW * M * kTileN; idx += blockDim.x) {
         const int j = idx / (M * kTileN), rem = idx % (M * kTileN);
         const int m = rem >> 4, cc = rem & 15;
@@ -383,11 +398,11 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
         if (W == kMaxWaves) {
             float pw[kMaxWaves];
 #pragma unroll
-            for (int w = 0; w < kMaxWaves; ++w) pw[w] = red[((j * kMaxWaves + w) * M + m) * kTileN + cc];
+            for (int w = 0; w < kMaxWaves; ++w) pw[w] = red0[w * rstride + (j * M + m) * kTileN + cc];
 #pragma unroll
             for (int w = 0; w < kMaxWaves; ++w) v += pw[w];
         } else {
-            for (int w = 0; w < W; ++w) v += red[((j * W + w) * M + m) * kTileN + cc];
+            for (int w = 0; w < W; ++w) v += red0[w * rstride + (j * M + m) * kTileN + cc];
         }
         const int n = (t0 + j) * kTileN + cc;
         if (j < nt && n < a.N) {
@@ -515,15 +530,15 @@ Plan make_plan(int M, int N, int K, int group, int cus) {
     int W = kWaves;
     if (tu.waves >= 1 && tu.waves <= kMaxWaves) W = tu.waves;
     // K slices: a wave's range must fit a compiled UPW, its x range at most
-    // 16 chunks per lane (M * UPW <= 64), and the workgroup's x plus the
-    // reduction buffer the LDS of a CU.
+    // 16 chunks per lane (M * UPW <= 64), and the workgroup's x (whose regions the
+    // partial sums reuse) the LDS of a CU.
     auto fits = [&](int S, int& upw, size_t& lds, int& xstride) {
         const int RU = (U + S - 1) / S;
         const int w = W < RU ? W : RU;
         upw = pick_upw((RU + w - 1) / w);
         if (!upw || M * upw > 64) return false;
-        xstride = upw * kUnitK + 8;  // +16 bytes per row spreads rows over LDS banks
-        lds = (size_t)W * M * xstride * 2 + (size_t)W * M * kTileN * 4;
+        xstride = upw * kUnitK;      // the kernel swizzles chunks instead of padding rows
+        lds = (size_t)W * M * xstride * 2;   // the partial sums reuse the x regions
         return lds <= kLdsPerCu;
     };
     int S = 1, upw = 0, xstride = 0;
@@ -552,12 +567,8 @@ Plan make_plan(int M, int N, int K, int group, int cus) {
     p.tpw = 1;
     if (group_tpw_ok && upw <= 6 && S == 1 && T >= 6 * cus) p.tpw = 3;
     if (tu.tpw >= 1 && tu.tpw <= 4 && upw <= 6 && group_tpw_ok) p.tpw = tu.tpw;
-    // The reduction buffer holds one [W][M][16] block per tile.
-    const size_t red_more = (size_t)(p.tpw - 1) * W * M * kTileN * 4;
-    if (lds + red_more <= kLdsPerCu)
-        lds += red_more;
-    else
-        p.tpw = 1;
+    // The partial sums of all TPW tiles fit each wave's x region: TPW M 64
+    // bytes against M upw 256 (TPW <= 4).
     p.lds = lds;
     p.tiles = T;
     return p;
@@ -670,14 +681,14 @@ Plan make_plan(int M, int N, int K, int group, int cus);
 // Whether the M-tiled kernel (w4_gemm.hip) takes the call: every M above the
 // GEMV's 16, and below that from the measured crossover on.  Measured per
 // call on the 27B-class layers (us, GEMV / tiled):
-//   qkv      M = 6: 8.0 / 10.5   M = 8: 10.6 / 10.5   M = 12: 12.2 / 10.7
-//   o_proj   M = 8: 10.3 / 10.1  M = 12: 11.9 / 10.2
-//   gate_up  M = 8: 26.4 / 30.0  M = 12: 30.0 / 30.9  M = 16: 80.4 / 31.3
+//   qkv      M = 8: 8.6 / 10.2   M = 12: 12.2 / 10.7
+//   o_proj   M = 8: 8.3 / 9.9    M = 12: 11.9 / 10.2
+//   gate_up  M = 8: 23.5 / 30.0  M = 12: 30.0 / 30.9  M = 16: 80.4 / 31.3
 //   down     M = 6: 18.4 / 17.4  M = 8: 26.2 / 17.5
-//   K = N = 4096  M = 8: 5.6 / 8.2
+//   K = N = 4096  M = 8: 5.5 / 8.2
 // The GEMV falls off once its workgroup needs more than half a CU's LDS (one
-// workgroup per CU): 87 KB for qkv and o_proj at M = 8, 71 KB for
-// K = N = 4096.  So the tiled kernel takes M > 12, and M = 8..12 where the
+// workgroup per CU): its x takes M x K x 2 bytes, 80 KB (exactly half) for
+// K = 5120 at M = 8.  So the tiled kernel takes M > 12, and M = 8..12 where the
 // GEMV would run one tile per workgroup with more than half the LDS (on wide
 // layers the GEMV streams several tiles per workgroup and stays ahead).
 bool use_gemm(int M, int N, int K, int group) {

@@ -130,6 +130,29 @@ def test_w4_gemv_matches_oracle(M, N, K, g, xdt):
     assert_parity(to_f64(yb), ref, "bf16 out", extra_rel=2.0 ** -8)
 
 
+# The GEMV's x staging at its LDS edge: 5 to 8 rows (rows m and m + 4 share
+# a swizzle pattern), M = 8 at K = 5120 with one tile per workgroup fills
+# exactly half a CU's LDS, and a ragged last unit (K % 128 = 64) zeroes
+# chunks in every swizzled row.
+@pytest.mark.parametrize("M,N,K,g,xdt", [(8, 4104, 5120, 128, "bf16"), (8, 520, 5056, 64, "f16"),
+                                         (5, 264, 2240, 32, "f16"), (6, 136, 4032, 64, "bf16")])
+def test_w4_gemv_x_staging_rows_5_to_8(M, N, K, g, xdt):
+    say(f"w4 gemv x staging M={M} N={N} K={K} g={g} x={xdt}")
+    key = (131, M, N, K, g)
+    w = synth.gen_w4(key, N, K, g)
+    x = synth.gen_x(key, M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    P = PackedW4(w, N, K, g)
+    y = P.gemv(dev(x), xdt, M, "f32")
+    torch.cuda.synchronize()
+    variant = L.w4a16_last_variant()
+    say("  variant: " + variant)
+    assert "w4_gemv_kernel" in variant
+    if (M, K) == (8, 5120):
+        assert "slices=1 " in variant and "lds=81920" in variant
+    ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g)
+    assert_parity(to_f64(y), ref, f"M={M} N={N} K={K} g={g} {xdt}")
+
+
 # M-tiled kernel (more rows than one MFMA block): 2 to 4 row blocks, one or
 # two tiles per wave, every group size, ragged N (a last tile of 8 columns)
 # and ragged K (a last unit of 64 k), with and without K slices.
