@@ -16,6 +16,8 @@
 //   (2i, 2i + 1) of the MFMA B operand: -1, 0, +1 exactly, no bias term.
 //   scales_dev uint16 [Np/16][Kp/group][16]
 // Padding holds zero bits (weight 0) and scale +0.
+#include <stdlib.h>
+
 #include <mutex>
 
 #include "common.h"
@@ -26,7 +28,7 @@ namespace {
 
 constexpr int kMaxRows = 16;
 constexpr int kWaves2 = 8;       // waves per workgroup of the staged ternary kernel
-constexpr int kMaxXLoads2 = 17;  // x load instructions per wave: M * (32 UPW + 1) <= 64 * 17
+constexpr int kMaxXLoads2 = 16;  // x load instructions per wave: M * 32 UPW <= 64 * 16
 
 // Bits of the weight of step h (0, 1), element e (0..7) in its device dword.
 __host__ __device__ constexpr int nz_bit(int h, int e) { return 4 * e + 1 - h; }
@@ -153,7 +155,6 @@ struct W2Launch {
     int M, N, K;
     int U;        // 256-k units per column (K rounded up)
     int S;        // K slices: workgroups (t, s) cover units [s*U/S, (s+1)*U/S) of tile t
-    int xstride;  // LDS row stride of a wave's staged x, in halves
     int out_dtype;
 };
 
@@ -199,31 +200,37 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
     const int Gp = U * kUnitK2 / (SPG * 32);
     const int c = lane & 15, kc = lane >> 4;
 
-    // LDS: wave w's x range [M][xstride] halves at w * M * xstride, then the
-    // reduction buffer [W][M][16] floats.
-    uint16_t* xs = (uint16_t*)smem + (size_t)wave * M * a.xstride;
-    float* red = (float*)(smem + (size_t)W * M * a.xstride * 2);
+    // LDS: the slice's x, M x (r1 - r0) units of 512 bytes, split into one
+    // region per wave: wave w's [M][nu units] at M * 512 * (w0 - r0) bytes,
+    // rows nu * 512 bytes apart, so a workgroup takes exactly M x K-slice x
+    // 2 bytes.  Inside each unit of row m, the 16-byte chunk p sits at
+    // position p ^ (m % 4): rows a multiple of 256 bytes apart would
+    // otherwise share LDS banks (rows m and m + 4 still share one: a
+    // two-way conflict at M = 5..8), and the 32-k step keeps one offset
+    // for every lane.  Once its products are done, a wave with units reuses
+    // its own region for its partial sums (M x 16 floats <= M x 512 bytes).
+    const int xrow_bytes = nu * (kUnitK2 * 2);
+    uint8_t* const xsb = smem + (size_t)M * (kUnitK2 * 2) * (w0 - r0);
 
     // 1) x range -> this wave's LDS region, straight from memory into LDS in
     //    one round trip (the 4-bit kernel's scheme: lane l of load i fills
-    //    chunk 64 i + l of the padded region; pad chunks skipped, chunks past
-    //    K zeroed).  These are the wave's first memory accesses; where its
-    //    arithmetic is unconditional it waits for them after issuing its
-    //    weight ring, so the round trips overlap.
+    //    position 64 i + l of the region with the chunk the swizzle puts
+    //    there; chunks past K zeroed).  These are the wave's first memory
+    //    accesses; where its arithmetic is unconditional it waits for them
+    //    after issuing its weight ring, so the round trips overlap.
     {
-        const int cpr = a.xstride / 8;
-        const int live = nu * (kUnitK2 / 8);         // chunks of a row this wave reads
+        const int cpr = nu * (kUnitK2 / 8);          // chunks of a row
         const int xch = M * cpr;
         const uint32_t xbytes = (uint32_t)M * (uint32_t)K * 2u;
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xbytes);
-        uint8_t* xsb = (uint8_t*)xs;
 #pragma unroll
         for (int i = 0; i < kMaxXLoads2; ++i) {
-            if (i * 64 < xch) {                    // wave-uniform
+            if (i * 64 < xch) {                    // wave-uniform (false for a wave without units)
                 const int ci = i * 64 + lane;
-                const int m = ci / cpr, kk = (ci % cpr) * 8;
-                const int kg = w0 * kUnitK2 + kk;
-                if (m < M && kk < live * 8) {
+                const int m = ci / cpr, pc = ci % cpr;
+                const int lc = pc ^ (m & 3);       // same unit and step as pc
+                const int kg = w0 * kUnitK2 + lc * 8;
+                if (m < M) {
                     if (kg < K)
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(
                             rx, (__attribute__((address_space(3))) void*)(xsb + i * 1024), 16,
@@ -270,7 +277,8 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
 
     // 3) Dequantize and multiply, unit by unit, two 32-k steps per dword.
     const bool xrow = c < M;                                    // lane supplies x row c
-    const uint8_t* xlane = (const uint8_t*)xs + (uint32_t)(c * a.xstride + 8 * kc) * 2u;
+    // Step st of unit i: chunk 4 st + kc of row c, at position 4 st + (kc ^ c % 4).
+    const uint8_t* xlane = xsb + (uint32_t)(c * xrow_bytes) + 16u * (uint32_t)(kc ^ (c & 3));
     float4_t total = {0.f, 0.f, 0.f, 0.f};
     u32x4_t xa[2] = {};
 #pragma unroll
@@ -315,25 +323,41 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
         __builtin_amdgcn_sched_barrier(0);   // units in order: each waits for its own slot only
     }
 
-    // 4) Wave partials -> LDS, then M x 16 threads add them in wave order.
+    // 4) Wave partials -> the start of each wave's own x region (its last x
+    //    reads were consumed above, and a wave's LDS accesses complete in
+    //    order), then M x 16 threads add them in wave order.  A wave without
+    //    units has no region; its partial is exactly +0, and skipping it
+    //    leaves the sum unchanged (the sum starts at +0 and so is never -0).
+    float* const red = (float*)xsb;
+    if (nu > 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int m = 4 * kc + r;
-        if (m < M) red[(wave * M + m) * kTileN + c] = total[r];
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * kc + r;
+            if (m < M) red[m * kTileN + c] = total[r];
+        }
     }
     __syncthreads();
+    const int sl = r1 - r0;
     for (int idx = threadIdx.x; idx < M * kTileN; idx += blockDim.x) {
         const int m = idx >> 4, cc = idx & 15;
-        // All W partials are read before the first add, then added in wave order.
+        // All partials are read before the first add, then added in wave order.
         float v = 0.f;
         if (W == kWaves2) {
             float pw[kWaves2];
 #pragma unroll
-            for (int w = 0; w < kWaves2; ++w) pw[w] = red[(w * M + m) * kTileN + cc];
+            for (int w = 0; w < kWaves2; ++w) {
+                const int b = w * sl / kWaves2, e = (w + 1) * sl / kWaves2;
+                pw[w] = e > b ? ((const float*)(smem + (size_t)M * (kUnitK2 * 2) * b))[m * kTileN + cc]
+                              : 0.f;
+            }
 #pragma unroll
-            for (int w = 0; w < kWaves2; ++w) v += pw[w];
+            for (int w = 0; w < kWaves2; ++w)
+                if ((w + 1) * sl / kWaves2 > w * sl / kWaves2) v += pw[w];
         } else {
-            for (int w = 0; w < W; ++w) v += red[(w * M + m) * kTileN + cc];
+            for (int w = 0; w < W; ++w) {
+                const int b = w * sl / W, e = (w + 1) * sl / W;
+                if (e > b) v += ((const float*)(smem + (size_t)M * (kUnitK2 * 2) * b))[m * kTileN + cc];
+            }
         }
         const int n = t * kTileN + cc;
         if (n < a.N) {
@@ -365,10 +389,10 @@ __global__ void w2_merge_kernel(const float* __restrict__ ws, void* __restrict__
 // ------------------------------------------------- direct-x variant (larger M)
 //
 // The staged kernel above keeps M x (K slice) x 2 bytes of x in LDS per
-// workgroup, which for several rows and a long K leaves one workgroup per CU
-// or forces a K split.  This variant reads each unit's x fragment for the
-// lane's row straight from L2 into registers, double-buffered one unit ahead,
-// and keeps a four-deep weight ring; it needs no LDS for x.
+// workgroup, and past 8 rows its slices get too short to keep each wave's
+// ring busy.  This variant reads each unit's x fragment for the lane's row
+// straight from L2 into registers, double-buffered one unit ahead, and keeps
+// a four-deep weight ring; it needs no LDS for x.
 
 constexpr int kMaxWavesX = 8;
 
@@ -552,21 +576,25 @@ Plan2 make_plan2(int M, int N, int K, int cus) {
     const int U = (K + kUnitK2 - 1) / kUnitK2;
     const int T = pad_n(N) / kTileN;
     const int W = kWaves2;
-    auto fits = [&](int S, int& upw, size_t& lds, int& xstride) {
+    // The workgroup's x is exactly M x (its slice's units) x 512 bytes (the
+    // partial sums reuse it); slices differ by at most one unit.
+    auto fits = [&](int S, int& upw, size_t& lds) {
         const int RU = (U + S - 1) / S;
         const int w = W < RU ? W : RU;
         upw = pick_upw2((RU + w - 1) / w);
         if (!upw || M * upw > 32) return false;
-        xstride = upw * kUnitK2 + 8;   // +16 bytes per row spreads rows over LDS banks
-        lds = (size_t)W * M * xstride * 2 + (size_t)W * M * kTileN * 4;
+        lds = (size_t)M * RU * kUnitK2 * 2;
         return lds <= kLdsPerCu2;
     };
-    int S = 1, upw = 0, xstride = 0;
+    int S = 1, upw = 0;
     size_t lds = 0;
-    while (S < U && !fits(S, upw, lds, xstride)) S *= 2;
-    while ((long long)T * S < cus && U / (2 * S) >= 2 * W && fits(2 * S, upw, lds, xstride)) S *= 2;
-    if (!fits(S, upw, lds, xstride)) upw = 0;
-    p.l = W2Launch{M, N, K, U, S, xstride, W4A16_F32};
+    while (S < U && !fits(S, upw, lds)) S *= 2;
+    while ((long long)T * S < cus && U / (2 * S) >= 2 * W && fits(2 * S, upw, lds)) S *= 2;
+    // A workgroup with more than half a CU's LDS runs alone on its CU: more
+    // slices while each wave keeps at least two units.
+    while (lds > kLdsPerCu2 / 2 && U / (2 * S) >= 2 * W && fits(2 * S, upw, lds)) S *= 2;
+    if (!fits(S, upw, lds)) upw = 0;
+    p.l = W2Launch{M, N, K, U, S, W4A16_F32};
     p.waves = W;
     p.upw = upw;
     p.tiles = T;
@@ -606,11 +634,29 @@ w2_kernel_t pick2(bool bf16, int group, int upw) {
     return bf16 ? pick2_group<true>(group, upw) : pick2_group<false>(group, upw);
 }
 
-// The staged kernel when it runs unsplit with at most this much LDS per
-// workgroup (two or more workgroups per CU), the direct-x kernel otherwise.
-constexpr size_t kStagedLdsMax = 56 * 1024;
+// The staged kernel (split or not) up to 8 rows when its workgroup needs at
+// most half a CU's LDS (two or more workgroups per CU), the direct-x kernel
+// otherwise.  Measured, us per call, staged / direct-x:
+//   K 5120 N 7168    M = 1: 5.2 / 6.9    M = 8: 7.7 / 9.3    M = 12: 14.0 / 10.9
+//   K 5120 N 34816   M = 1: 15.1 / 22.4  M = 8: 28.0 / 33.3  M = 16: 52.7 / 45.9
+//   K 17408 N 5120   M = 4: 14.1 / 19.2  M = 8: 19.0 / 24.2  M = 16: 31.7 / 35.5
+// (above 8 rows a wave keeps at most two units per slice).
+constexpr size_t kStagedLdsMax = kLdsPerCu2 / 2;
+constexpr int kStagedMaxRows = 8;
 
-bool use_staged(const Plan2& p) { return p.upw && p.l.S == 1 && p.lds <= kStagedLdsMax; }
+size_t staged_lds_max() {
+    // Override for A/B measurement only, read once per process.
+    static size_t v = [] {
+        const char* e = getenv("W2T_STAGED_LDS_MAX");
+        const long long n = e ? atoll(e) : 0;
+        return n > 0 ? (size_t)n : kStagedLdsMax;
+    }();
+    return v;
+}
+
+bool use_staged(const Plan2& p) {
+    return p.upw && p.l.M <= kStagedMaxRows && p.lds <= staged_lds_max();
+}
 
 // Allow every ternary GEMV kernel the whole LDS of a CU, once per process.
 void allow_full_lds2() {
@@ -740,7 +786,7 @@ extern "C" int w2t_workspace_bytes(int M, int N, int K, int group, size_t* bytes
     if (rc) return rc;
     const Plan2 p = make_plan2(M, N, K, w4h::cu_count());
     if (use_staged(p)) {
-        *bytes = 0;
+        *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     } else {
         const PlanX px = make_planx(N, K);
         *bytes = px.split > 1 ? (size_t)px.split * M * N * sizeof(float) : 0;

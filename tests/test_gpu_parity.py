@@ -322,6 +322,11 @@ W2_GEMV_CASES = [
     (3, 264, 2304, 256, "f16"),
     (16, 520, 512, 32, "bf16"),
     (1, 7168, 5120, 128, "f16"),
+    # Staged kernel in two K slices with uneven units per wave and a ragged
+    # last unit, and one whose workgroup would need more than half a CU's
+    # LDS (the direct-x kernel).
+    (5, 1032, 8896, 64, "f16"),
+    (7, 4104, 6144, 128, "bf16"),
 ]
 
 
@@ -334,7 +339,12 @@ def test_w2t_gemv_matches_oracle(M, N, K, g, xdt):
     P = PackedW2T(w, N, K, g)
     y = P.gemv(dev(x), xdt, M)
     torch.cuda.synchronize()
-    say("  variant: " + L.w4a16_last_variant())
+    variant = L.w4a16_last_variant()
+    say("  variant: " + variant)
+    if (M, K) == (5, 8896):
+        assert "w2t_gemv_kernel" in variant and "slices=2 " in variant
+    if (M, K) == (7, 6144):
+        assert "w2t_gemv_direct_kernel" in variant
     ref = oracle.w2t_gemv(x, xdt, w["codes"], w["scales"], M, N, K, g)
     assert_parity(to_f64(y), ref, f"w2t M={M} N={N} K={K}")
 
