@@ -364,6 +364,15 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
                 total[tj][1] = __builtin_fmaf(sf, acc[1], total[tj][1]);
                 total[tj][2] = __builtin_fmaf(sf, acc[2], total[tj][2]);
                 total[tj][3] = __builtin_fmaf(sf, acc[3], total[tj][3]);
+                // g = 64 multi-tile chains: left alone, the compiler defers
+                // every group's scale FMA to the end of the chain and keeps
+                // all the group accumulators live (178 VGPRs for UPW = 5,
+                // TPW = 3: one workgroup per CU).  An empty asm statement that
+                // claims to change the running total makes each FMA happen
+                // here (94 VGPRs, two workgroups per CU).  It emits no
+                // instruction.  At g = 128 the same pin measured within noise
+                // (gate_up slower, lm_head faster), so it is left out there.
+                if constexpr (TPW > 1 && SPG == 2) asm volatile("" : "+v"(total[tj]));
             }
         }
         if (q + D < L) {                   // fixed refill schedule: position q + D into this slot
@@ -520,9 +529,11 @@ int pick_upw(int need) {
 }
 
 Plan make_plan(int M, int N, int K, int group, int cus) {
-    // Multi-tile kernels are compiled for g = 64 and 128; at g = 64 they pay
-    // off only with several rows (measured on lm_head-sized layers).
-    const bool group_tpw_ok = group == 128 || (group == 64 && M >= 2);
+    // Multi-tile kernels are compiled for g = 64 and 128.  At g = 64, M = 1,
+    // they measured 83.8 us on the lm_head shape (N = 152064, K = 5120)
+    // against 96.4 us with one tile per workgroup, and 21.2 against 23.5 us
+    // on gate_up.
+    const bool group_tpw_ok = group == 128 || group == 64;
     Plan p;
     const Tuning& tu = tuning();
     const int U = (K + kUnitK - 1) / kUnitK;

@@ -598,7 +598,8 @@ def test_split_k_workspace_reused_across_shapes_and_graph_replays():
 
 @pytest.mark.parametrize("M,K,g,xdt", [(1, 1152, 128, "f16"), (8, 1152, 128, "bf16"),
                                          (3, 640, 128, "f16"), (12, 256, 128, "bf16"),
-                                         (2, 1152, 64, "f16"), (4, 640, 64, "bf16")])
+                                         (2, 1152, 64, "f16"), (4, 640, 64, "bf16"),
+                                         (1, 896, 64, "f16"), (8, 1152, 64, "bf16")])
 def test_multi_tile_workgroups_ragged(M, K, g, xdt):
     # Many more tiles than the GPU holds at once: each workgroup takes three
     # tiles, and 1537 tiles leave a last workgroup with a single one.
