@@ -22,6 +22,8 @@
 // 5-25% slower.
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "common.h"
 
 using namespace w4k;
@@ -163,6 +165,157 @@ __global__ __launch_bounds__(256) void w16_gemv_kernel(const uint16_t* __restric
         }
 }
 
+// Layers with few tiles, up to 16 rows: the GEMV kernel's shape instead.
+// One workgroup of 8 waves per 16-column tile, the waves splitting the K
+// units, so a layer of a few hundred tiles fills the GPU without K slices and
+// their merge launch.  Each wave
+//   1. stages its own units of x (all M rows) in LDS straight from memory
+//      (the 4-bit GEMV's scheme: exact per-wave regions [M][nu units of 256
+//      bytes], 16-byte chunk p of a unit in row m at position p ^ (m % 4);
+//      chunks past K zeroed);
+//   2. streams its units' weights, four 16-byte loads per lane and unit
+//      (the coalesced per-step layout above), kW16KRing units ahead;
+//   3. multiplies unit by unit: x rows from LDS as A, the weight chunks as B.
+// The waves' partial sums go through LDS (each wave's own x region) and are
+// added in wave order.  A wave past the units of a short K has no region and
+// adds nothing (its partial would be +0, and the sum starts at +0).
+constexpr int kW16KWaves = 8;
+constexpr size_t kW16KLdsMax = 80 * 1024;   // half of a CU's 160 KB
+// Units of weight loads in flight per wave.  Four (92 VGPRs against 58)
+// measured 7-15% slower on every shape.
+constexpr int kW16KRing = 2;
+// Units per wave it takes at most: the down shape (K = 17408, 17 units per
+// wave) ran 44.2 us against 36.7 us for the tiled kernel in 16 K slices.
+constexpr int kW16KMaxUnits = 8;
+constexpr int kW16KMaxXLoads = 16;   // x load instructions per wave: M * 16 * units <= 64 * 16
+
+template <bool BF16>
+__global__ __launch_bounds__(512) void w16_ksplit_kernel(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ w, void* out,
+                                                         W16Launch a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int M = a.M, N = a.N, K = a.K, U = a.U;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15, kc = lane >> 4;
+    const int t = blockIdx.x;
+    const int w0 = wave * U / kW16KWaves, w1 = (wave + 1) * U / kW16KWaves;
+    const int nu = w1 - w0;
+    const int rows = N - 16 * t < 16 ? N - 16 * t : 16;
+    constexpr int kUnitBytes = kUnitK * 2;                  // one row of one unit of x
+    uint8_t* const xsb = smem + (size_t)M * kUnitBytes * w0;
+    const int rowb = nu * kUnitBytes;
+
+    // 1) x units of this wave -> LDS (lane l of load i fills position 64 i + l).
+    {
+        const int cpr = nu * (kUnitK / 8);
+        const int xch = M * cpr;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+#pragma unroll
+        for (int i = 0; i < kW16KMaxXLoads; ++i) {
+            if (i * 64 < xch) {                      // wave-uniform (false without units)
+                const int ci = i * 64 + lane;
+                const int m = ci / cpr, pc = ci % cpr;
+                const int kg = w0 * kUnitK + (pc ^ (m & 3)) * 8;
+                if (m < M) {
+                    if (kg < K)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rx, (__attribute__((address_space(3))) void*)(xsb + i * 1024), 16,
+                            (uint32_t)(m * K + kg) * 2u, 0, 0, 0);
+                    else
+                        *(u32x4_t*)(xsb + (uint32_t)ci * 16u) = u32x4_t{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2) The tile's rows as one resource (rows past N read zeros; the tail of
+    //    a ragged last unit reads the next row, which meets zero x).
+    const uint32_t wend = (uint32_t)rows * (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)16 * t * K, wend);
+    const uint32_t wlane = (uint32_t)c * (uint32_t)K * 2u + 16u * kc;
+    auto load_unit = [&](int i, u32x4_t (&r)[4]) {
+        const uint32_t off = i < nu ? wlane + (uint32_t)(w0 + i) * kUnitBytes : wend;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            r[j] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rw, off + 64u * j, 0, 0));
+    };
+    constexpr int R = kW16KRing;
+    u32x4_t ring[R][4];
+#pragma unroll
+    for (int d = 0; d < R; ++d) {
+        load_unit(d, ring[d]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // Loads complete in issue order: with the ring's 4 R loads outstanding
+    // the x loads issued before them have landed in LDS.  This needs the
+    // ring loads issued here, before the wait: the loop below runs at least
+    // once for every wave, so no use of them sits in a conditional block the
+    // compiler could sink them into (a host-side test checks the assembly).
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * R) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3) Products.  Step j of unit i: chunk 4 j + kc of row c, at position
+    //    4 j + (kc ^ c % 4).  Units past the range load zero weights and keep
+    //    the last x fragments, so they add exactly 0.
+    const bool xrow = c < M;
+    const uint8_t* xl = xsb + (uint32_t)(c * rowb) + 16u * (uint32_t)(kc ^ (c & 3));
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    u32x4_t xa[4] = {};
+    const int upw = (U + kW16KWaves - 1) / kW16KWaves;   // >= 1, the same for every wave
+    int i = 0;
+    do {
+#pragma unroll
+        for (int d = 0; d < R; ++d) {
+            if (xrow && i + d < nu) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xa[j] = *(const u32x4_t*)(xl + (uint32_t)(i + d) * kUnitBytes + 64 * j);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (BF16)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(xa[j]),
+                                                                  bitcast<bf16x8_t>(ring[d][j]), acc,
+                                                                  0, 0, 0);
+                else
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(xa[j]),
+                                                                 bitcast<half8_t>(ring[d][j]), acc,
+                                                                 0, 0, 0);
+            }
+            load_unit(i + d + R, ring[d]);
+        }
+        i += R;
+    } while (i < upw);
+
+    // 4) Partials -> the wave's own x region, then the wave-order sum.
+    if (nu > 0) {
+        float* const red = (float*)xsb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * kc + r;
+            if (m < M) red[m * kTileN + c] = acc[r];
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < M * kTileN; idx += blockDim.x) {
+        const int m = idx >> 4, cc = idx & 15;
+        float pw[kW16KWaves];
+#pragma unroll
+        for (int wv = 0; wv < kW16KWaves; ++wv) {
+            const int b = wv * U / kW16KWaves, e = (wv + 1) * U / kW16KWaves;
+            pw[wv] = e > b ? ((const float*)(smem + (size_t)M * kUnitBytes * b))[m * kTileN + cc] : 0.f;
+        }
+        float v = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < kW16KWaves; ++wv)
+            if ((wv + 1) * U / kW16KWaves > wv * U / kW16KWaves) v += pw[wv];
+        const int n = 16 * t + cc;
+        if (n < N) store_out(out, a.out_dtype, (size_t)m * N + n, v);
+    }
+}
+
 typedef void (*w16_kernel_t)(const uint16_t*, const uint16_t*, void*, W16Launch);
 
 template <bool BF16>
@@ -179,6 +332,8 @@ w16_kernel_t pick_w16_rb(int rb) {
 struct W16Plan {
     int rb, split;
     long long workgroups;
+    bool ksplit;    // the K-split kernel (one tile per workgroup)
+    size_t lds;     // its dynamic LDS bytes
 };
 
 // K slices double while each keeps at least six units (4 KB of weights per
@@ -190,6 +345,13 @@ W16Plan w16_plan(int M, int N, int K) {
     W16Plan p;
     const int U = (K + kUnitK - 1) / kUnitK;
     const int T = pad_n(N) / kTileN;
+    // The K-split kernel up to 16 rows, when a wave's x fits its 16 load
+    // instructions and the workgroup's x half a CU's LDS (two per CU).
+    const int upw = (U + kW16KWaves - 1) / kW16KWaves;
+    p.lds = (size_t)M * U * kUnitK * 2;
+    p.ksplit = M <= 16 && upw <= kW16KMaxUnits && M * upw <= 64 && p.lds <= kW16KLdsMax;
+    // Override for A/B measurement only: 0 turns the K-split kernel off.
+    if (const char* e = getenv("W16A16_KSPLIT")) p.ksplit = p.ksplit && atoi(e) != 0;
     p.rb = (M + 15) / 16;
     p.workgroups = (T + kW16Waves - 1) / kW16Waves;
     p.split = 1;
@@ -210,7 +372,17 @@ int check_w16(int M, int N, int K) {
 }
 
 size_t w16_workspace(const W16Plan& p, int M, int N) {
-    return p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0;
+    return !p.ksplit && p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0;
+}
+
+void allow_w16_lds() {
+    static std::once_flag once;
+    std::call_once(once, [] {
+        for (const void* k : {(const void*)w16_ksplit_kernel<false>,
+                              (const void*)w16_ksplit_kernel<true>})
+            (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kW16KLdsMax);
+        (void)hipGetLastError();
+    });
 }
 
 }  // namespace
@@ -243,6 +415,16 @@ extern "C" int w16a16_gemv(const void* x, const void* w, int dtype, void* y, int
     const int T = pad_n(N) / kTileN;
     W16Launch l{M, N, K, U, p.split, T, y_dtype};
     hipStream_t st = (hipStream_t)stream;
+    if (p.ksplit) {
+        allow_w16_lds();
+        w4h::begin_launches();
+        hipLaunchKernelGGL(bf16 ? w16_ksplit_kernel<true> : w16_ksplit_kernel<false>, dim3(T),
+                           dim3(64 * kW16KWaves), p.lds, st, (const uint16_t*)x, (const uint16_t*)w,
+                           y, l);
+        w4h::set_last_variant("w16_mfma16 %s kernel=w16_ksplit_kernel<%s> tiles=%d slices=1 lds=%zu",
+                              bf16 ? "bf16" : "f16", bf16 ? "true" : "false", T, p.lds);
+        return w4h::launch_status();
+    }
     w4h::begin_launches();
     hipLaunchKernelGGL(bf16 ? pick_w16_rb<true>(p.rb) : pick_w16_rb<false>(p.rb),
                        dim3((unsigned)p.workgroups, p.split), dim3(64 * kW16Waves), 0, st,

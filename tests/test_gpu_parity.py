@@ -286,7 +286,24 @@ W16_CASES = [
     (24, 40, 8, "bf16"),
     (64, 264, 1536, "f16"),
     (3, 12296, 512, "bf16"),
+    # The K-split kernel at its limits: 16 rows filling half a CU's LDS, a
+    # single unit (seven waves without units), 8 units per wave with a
+    # ragged last one; a shape whose x is too large for it and one with
+    # more units per wave than it takes.
+    (16, 264, 2560, "bf16"),
+    (2, 40, 8, "f16"),
+    (1, 520, 8168, "f16"),
+    (6, 264, 8192, "bf16"),
+    (1, 520, 17400, "f16"),
 ]
+
+
+def w16_expects_ksplit(M, K):
+    # One workgroup per tile up to 8 units per wave, when a wave's x fits 16
+    # loads and the workgroup's x half of a CU's LDS.
+    U = -(-K // 128)
+    upw = -(-U // 8)
+    return M <= 16 and upw <= 8 and M * upw <= 64 and M * U * 256 <= 80 * 1024
 
 
 @pytest.mark.parametrize("M,N,K,dt", W16_CASES)
@@ -305,8 +322,10 @@ def test_w16a16_gemv_matches_oracle(M, N, K, dt):
         L.w16a16_gemv(xd, wd, dt, y, ydt, M, N, K, ws, wsb)
         torch.cuda.synchronize()
         if ydt == "f32":
-            say("  variant: " + L.w4a16_last_variant())
-            assert "w16_gemv_kernel" in L.w4a16_last_variant()
+            variant = L.w4a16_last_variant()
+            say("  variant: " + variant)
+            kern = "w16_ksplit_kernel" if w16_expects_ksplit(M, K) else "w16_gemv_kernel"
+            assert kern in variant
             y0 = y.clone()
         assert_parity(to_f64(y)[:, cols], ref, f"w16 M={M} N={N} K={K} {dt} y={ydt}", extra_rel=extra)
     y1 = torch.empty_like(y0)
