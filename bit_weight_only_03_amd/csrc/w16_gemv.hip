@@ -8,7 +8,10 @@
 // same stream without the dequantization: each wave owns one 16-column tile
 // over its workgroup's K slice, the workgroup streams x through LDS one
 // 128-k unit at a time (double-buffered, shared by its waves), and every
-// 16-byte chunk a lane loads is directly the MFMA B operand.
+// 16-byte chunk a lane loads is directly the MFMA B operand.  Layers of a
+// few hundred tiles (up to 16 rows and 8 units per wave) take a second,
+// GEMV-shaped kernel instead: one tile per workgroup, its waves splitting K,
+// so they fill the GPU without K slices and a merge launch.
 //
 // Layout of one unit for one tile: lane l serves column n = 16 t + l % 16;
 // its j-th 16-byte load (j = 0..3) is w[n][128 u + 32 j + 8 (l / 16) .. + 8],
