@@ -42,6 +42,8 @@ def test_kernel_key_normalises_profiler_and_variant_names():
     assert bench.kernel_key(prof) == bench.kernel_key(var) == "w4_gemv_kernel<false, 4, 5, 3>"
     assert bench.kernel_key("w4_gemv_kernel<true, 4, 5, 1, true>") == "w4_gemv_kernel<true, 4, 5, 1, true>"
     assert bench.kernel_key("w16_gemv_kernel<false, 1>") == "w16_gemv_kernel<false, 1>"
+    assert bench.kernel_key("w16_mfma16 f16 kernel=w16_ksplit_kernel<false> tiles=448") == \
+        "w16_ksplit_kernel<false>"
     assert bench.kernel_key("__amd_rocclr_copyBuffer") is None
 
 
