@@ -202,3 +202,22 @@ def test_offset_limits_are_rejected_before_launch():
     # The largest K at M = 1 is accepted (sizes only; nothing launches).
     assert lib.w4a16_workspace_bytes(1, 64, big_k, 128) >= 0
     assert lib.w4a16_packed_sizes(64, big_k, 128)[0] == 64 * big_k // 2
+
+
+def test_workspace_queries_follow_the_dispatch():
+    # The size queries run the same host planner as the launches (no GPU
+    # work; without a device the planner assumes 256 CUs), so they show
+    # which kernel a shape gets.  fp32 partials are S x M x N x 4 bytes.
+    # W16A16: few-tile layers run the K-split kernel (no slices); the
+    # 17-units-per-wave down shape keeps the tiled kernel in 16 slices.
+    assert lib.w16a16_workspace_bytes(1, 7168, 5120) == 0
+    assert lib.w16a16_workspace_bytes(8, 5120, 5120) == 0
+    assert lib.w16a16_workspace_bytes(1, 5120, 17408) == 16 * 1 * 5120 * 4
+    # Ternary: the staged kernel unsplit at K = 5120 up to 8 rows, and in 2
+    # and 4 slices for the down shape at 4 and 8 rows.
+    assert lib.w2t_workspace_bytes(8, 7168, 5120, 128) == 0
+    assert lib.w2t_workspace_bytes(4, 5120, 17408, 128) == 2 * 4 * 5120 * 4
+    assert lib.w2t_workspace_bytes(8, 5120, 17408, 128) == 4 * 8 * 5120 * 4
+    # 4-bit: down at M = 4 in 4 slices; M = 8 at K = 5120 unsplit on the GEMV.
+    assert lib.w4a16_workspace_bytes(4, 5120, 17408, 128) == 4 * 4 * 5120 * 4
+    assert lib.w4a16_workspace_bytes(8, 5120, 5120, 128) == 0
