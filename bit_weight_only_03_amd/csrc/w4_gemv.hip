@@ -577,6 +577,13 @@ Plan make_plan(int M, int N, int K, int group, int cus) {
     // workgroup stages x once for all its tiles.
     p.tpw = 1;
     if (group_tpw_ok && upw <= 6 && S == 1 && T >= 6 * cus) p.tpw = 3;
+    // A one-tile workgroup that needs more than half a CU's LDS runs alone
+    // on its CU, and a grid of more tiles than CUs then takes two rounds.
+    // Two tiles per workgroup (x staged once for both) make it one round:
+    // K = N = 8192 at M = 6 went from 14.0 to 10.5 us, at M = 8 from 13.9 us
+    // (the M-tiled kernel) to 11.2 us (g = 64: 15.3 -> 12.2, 14.9 -> 13.0).
+    if (group_tpw_ok && p.tpw == 1 && upw == 8 && S == 1 && lds > kLdsPerCu / 2 && T >= 2 * cus)
+        p.tpw = 2;
     if (tu.tpw >= 1 && tu.tpw <= 4 && upw <= 6 && group_tpw_ok) p.tpw = tu.tpw;
     // The partial sums of all TPW tiles fit each wave's x region: TPW M 64
     // bytes against M upw 256 (TPW <= 4).
@@ -611,7 +618,10 @@ w4_kernel_t pick_upw_kernel(int upw, int tpw) {
         return pick_small_upw<BF16, SPG, 1>(upw);
     }
     switch (upw) {
-        case 8: return w4_gemv_kernel<BF16, SPG, 8, 1>;
+        case 8:
+            if constexpr (SPG == 2 || SPG == 4)
+                if (tpw == 2) return w4_gemv_kernel<BF16, SPG, 8, 2>;
+            return w4_gemv_kernel<BF16, SPG, 8, 1>;
         case 9: return w4_gemv_kernel<BF16, SPG, 9, 1>;
         case 12: return w4_gemv_kernel<BF16, SPG, 12, 1>;
         default: return w4_gemv_kernel<BF16, SPG, 17, 1>;
@@ -654,7 +664,7 @@ w4_kernel_t pick_mx_upw(int upw, int tpw) {
         return pick_mx_small_upw<BF16, 1>(upw);
     }
     switch (upw) {
-        case 8: return w4_gemv_kernel<BF16, 4, 8, 1, true>;
+        case 8: return tpw == 2 ? w4_gemv_kernel<BF16, 4, 8, 2, true> : w4_gemv_kernel<BF16, 4, 8, 1, true>;
         case 9: return w4_gemv_kernel<BF16, 4, 9, 1, true>;
         case 12: return w4_gemv_kernel<BF16, 4, 12, 1, true>;
         default: return w4_gemv_kernel<BF16, 4, 17, 1, true>;
@@ -701,7 +711,8 @@ Plan make_plan(int M, int N, int K, int group, int cus);
 // workgroup per CU): its x takes M x K x 2 bytes, 80 KB (exactly half) for
 // K = 5120 at M = 8.  So the tiled kernel takes M > 12, and M = 8..12 where the
 // GEMV would run one tile per workgroup with more than half the LDS (on wide
-// layers the GEMV streams several tiles per workgroup and stays ahead).
+// layers the GEMV streams two or three tiles per workgroup and stays ahead:
+// K = N = 8192 at M = 8 takes 11.1 us with two, against 13.9 us tiled).
 bool use_gemm(int M, int N, int K, int group) {
     const int t = tuning().gemm_min_m;
     if (M > kMaxRows) return true;

@@ -153,6 +153,43 @@ def test_w4_gemv_x_staging_rows_5_to_8(M, N, K, g, xdt):
     assert_parity(to_f64(y), ref, f"M={M} N={N} K={K} g={g} {xdt}")
 
 
+# Two tiles per workgroup where one tile's x would take more than half a
+# CU's LDS (8 units per wave): 513 tiles leave a last workgroup with one.
+@pytest.mark.parametrize("M,g,xdt", [(8, 128, "bf16"), (6, 64, "f16"), (7, 128, "f16")])
+def test_w4_gemv_two_tiles_at_long_k(M, g, xdt):
+    N, K = 8208, 8192
+    say(f"w4 gemv two tiles M={M} N={N} K={K} g={g} x={xdt}")
+    key = (133, M, g)
+    w = synth.gen_w4(key, N, K, g)
+    x = synth.gen_x(key, M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    P = PackedW4(w, N, K, g)
+    y = to_f64(P.gemv(dev(x), xdt, M, "f32"))
+    torch.cuda.synchronize()
+    variant = L.w4a16_last_variant()
+    say("  variant: " + variant)
+    assert "w4_gemv_kernel" in variant and "tpw=2 " in variant
+    cols = sample_cols(N, np.random.default_rng(M))
+    ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g, cols=cols)
+    assert_parity(y[:, cols], ref, f"two tiles M={M} g={g}")
+
+
+def test_mxfp4_gemv_two_tiles_at_long_k():
+    M, N, K = 8, 8208, 8192
+    say(f"mxfp4 gemv two tiles M={M} N={N} K={K}")
+    key = (134, M)
+    w = synth.gen_mx(key, N, K)
+    x = synth.gen_x(key, M, K, "f16")
+    P = PackedMX(w, N, K)
+    y = to_f64(P.gemv(dev(x), "f16", M, "f32"))
+    torch.cuda.synchronize()
+    variant = L.w4a16_last_variant()
+    say("  variant: " + variant)
+    assert "tpw=2 " in variant
+    cols = sample_cols(N, np.random.default_rng(M + 1))
+    ref = oracle.mx_gemv(x, "f16", w["qweight"], w["scales"], M, N, K, cols=cols)
+    assert_parity(y[:, cols], ref, "mx two tiles")
+
+
 # M-tiled kernel (more rows than one MFMA block): 2 to 4 row blocks, one or
 # two tiles per wave, every group size, ragged N (a last tile of 8 columns)
 # and ragged K (a last unit of 64 k), with and without K slices.
