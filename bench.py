@@ -89,10 +89,14 @@ def kernel_key(name):
     if not m:
         return None
     k = re.sub(r"\s+", " ", m.group(0))
-    # The 4-bit GEMV's fifth template argument (MXFP4 mode) defaults to false
-    # and the variant strings leave it out; profiler names spell it.
-    if k.startswith("w4_gemv_kernel<") and k.count(",") == 4 and k.endswith(", false>"):
-        k = k[: -len(", false>")] + ">"
+    # The 4-bit GEMV's fifth and sixth template arguments (MXFP4 mode,
+    # per-unit x staging) default to false and the variant strings leave
+    # them out; profiler names spell them.
+    if k.startswith("w4_gemv_kernel<"):
+        if k.count(",") == 5 and k.endswith(", false, false>"):
+            k = k[: -len(", false, false>")] + ">"
+        elif k.count(",") == 4 and k.endswith(", false>"):
+            k = k[: -len(", false>")] + ">"
     return k
 
 

@@ -132,7 +132,12 @@ constexpr int min_waves() { return (SPG >= 4 && UPW <= 5) || (SPG == 2 && UPW <=
 // apply step by step otherwise (mx_unit in common.h).  Its slot (5 VGPRs) is
 // the size of a g = 128 slot, so it is instantiated with SPG = 4 for the
 // register plan.
-template <bool BF16, int SPG, int UPW, int TPW, bool MX = false>
+// PX = true stages x unit by unit instead (up to 4 rows, K a multiple of
+// 128, unconditional arithmetic): each unit's x is one load of [4 rows][256
+// bytes] straight into LDS, issued with the unit's first ring slot, and the
+// wave waits for it just before the unit's products.  The first unit then
+// waits for its own 1 KB of x and not for the wave's whole range.
+template <bool BF16, int SPG, int UPW, int TPW, bool MX = false, bool PX = false>
 __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4_gemv_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ qdev,
     const uint16_t* __restrict__ sdev, const uint32_t* __restrict__ zdev, void* out,
@@ -145,6 +150,7 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     constexpr bool kUncond = SPG >= 4 || (SPG == 2 && UPW <= 6) || UPW <= 2;
     constexpr int LPS = MX ? 2 : 1 + 2 * NG;              // loads per ring slot
     using SlotT = typename SlotSel<NG, MX>::type;
+    static_assert(!PX || (kUncond && !MX && D <= 9), "per-unit x staging needs a straight-line ring");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int M = a.M, K = a.K, U = a.U;
@@ -170,7 +176,11 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     // done, each wave reuses its own region for its partial sums, so a
     // workgroup needs exactly M x K x 2 bytes of LDS (two workgroups per CU
     // up to M = 8 at K = 5120).
-    uint8_t* const xsb = smem + (size_t)wave * M * a.xstride * 2;
+    // PX: wave w's region is [UPW units][4 rows][256 bytes] at w UPW 1024
+    // bytes, the same chunk swizzle inside each row.
+    uint8_t* const xsb = smem + (PX ? (size_t)wave * UPW * 1024 : (size_t)wave * M * a.xstride * 2);
+    const uint32_t xbytes = (uint32_t)M * (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xbytes);
 
     // 1) x range -> this wave's LDS region, straight from memory into LDS
     //    (no VGPRs, one round trip whatever M is).  Position ci of the region
@@ -181,12 +191,10 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     //    first memory accesses; where its arithmetic is unconditional the
     //    wave waits for them only after issuing its weight ring (below), so
     //    the two round trips overlap.
-    {
+    if constexpr (!PX) {
         const int cpr = a.xstride / 8;
         const int live = nu * (kUnitK / 8);          // positions of a row this wave reads
         const int xch = M * cpr;
-        const uint32_t xbytes = (uint32_t)M * (uint32_t)K * 2u;
-        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xbytes);
 #pragma unroll
         for (int i = 0; i < kMaxXLoads; ++i) {
             if (i * 64 < xch) {                    // wave-uniform
@@ -231,6 +239,16 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
         const int i = q / TPW, j = q % TPW;
         const bool valid = i < nu && j < nt;
         const int u = w0 + i;
+        if constexpr (PX) {
+            if (j == 0) {   // the unit's x: lane l -> row l / 16, position l % 16
+                const int m = lane >> 4, pc = lane & 15;
+                const int k = u * kUnitK + 8 * (pc ^ (m & 3));
+                const uint32_t off = (i < nu && m < M) ? (uint32_t)(m * K + k) * 2u : xbytes;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (__attribute__((address_space(3))) void*)(xsb + i * 1024), 16, off, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);   // before the slot's own loads
+            }
+        }
         r.w = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
             rw, valid ? wlane + (uint32_t)(j * U + u) * 1024u : wend, 0, kAuxNT));
         if constexpr (MX) {
@@ -260,7 +278,7 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     // the wait falls short.  Hence the overlap only where the arithmetic is
     // unconditional (elsewhere the wait above, after the x loads, covers
     // them); a host-side test checks the compiled kernels for this.
-    if constexpr (kUncond) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D * LPS) : "memory");
+    if constexpr (kUncond && !PX) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D * LPS) : "memory");
     __builtin_amdgcn_sched_barrier(0);
 
     // 3) Dequantize and multiply, unit by unit.
@@ -268,7 +286,10 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     const uint32_t magic = opaque_v(BF16 ? 0x43004300u : 0x64006400u);   // 128.0 / 1024.0 pairs
     const bool xrow = c < M;                                    // lane supplies x row c
     // Step j of unit i: logical chunk 4 j + kc of row c, at position 4 j + (kc ^ c % 4).
-    const uint8_t* xlane = xsb + (uint32_t)(c * a.xstride + 8 * (kc ^ (c & 3))) * 2u;
+    const uint8_t* xlane =
+        xsb + (PX ? (uint32_t)(c * 256 + 16 * (kc ^ (c & 3)))
+                  : (uint32_t)(c * a.xstride + 8 * (kc ^ (c & 3))) * 2u);
+    constexpr uint32_t kXUnit = PX ? 1024u : (uint32_t)kUnitK * 2;   // bytes between units of a row
     float4_t total[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) total[j] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -277,10 +298,28 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     for (int q = 0; q < L; ++q) {
         const int i = q / TPW, tj = q % TPW;
         SlotT& sl = ring[q % D];
+        if constexpr (PX) {
+            if (tj == 0) {
+                // Wait for this unit's x: loads complete in issue order, and
+                // after it went out came its slot's LPS loads and, for each
+                // later slot already issued, LPS loads plus an x load at every
+                // TPW-th one.  rem = later slots issued (0 .. D - 1).
+                const int rem = (q + D - 1 < L - 1 ? q + D - 1 : L - 1) - q;
+#define W4_PX_WAIT(R) \
+    case R: asm volatile("s_waitcnt vmcnt(%0)" ::"n"((R + 1) * LPS + R / TPW) : "memory"); break;
+                switch (rem) {
+                    W4_PX_WAIT(0) W4_PX_WAIT(1) W4_PX_WAIT(2) W4_PX_WAIT(3) W4_PX_WAIT(4)
+                    W4_PX_WAIT(5) W4_PX_WAIT(6) W4_PX_WAIT(7) W4_PX_WAIT(8)
+                    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+#undef W4_PX_WAIT
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
         if (tj == 0 && i < nu && xrow) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                xa[j] = *(const u32x4_t*)(xlane + (uint32_t)i * (kUnitK * 2) + 64 * j);
+                xa[j] = *(const u32x4_t*)(xlane + (uint32_t)i * kXUnit + 64 * j);
         }
         // Units past this wave's range arrived as zeros (q = z = 0, s = +0) and
         // add exactly 0 with the finite x the lane still holds, so where the
@@ -388,7 +427,7 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     //    wave's LDS accesses complete in order), then M x 16 threads add
     //    them in wave order and store.
     float* const red = (float*)xsb;
-    const size_t rstride = (size_t)M * a.xstride / 2;         // floats between wave regions
+    const size_t rstride = PX ? (size_t)UPW * 1024 / 4 : (size_t)M * a.xstride / 2;   // floats between wave regions
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
 #pragma unroll
@@ -517,6 +556,7 @@ struct Plan {
     int waves;
     int upw;
     int tpw;
+    bool px;     // x staged unit by unit (PX kernels)
     size_t lds;
     int tiles;
 };
@@ -528,7 +568,17 @@ int pick_upw(int need) {
     return 0;
 }
 
-Plan make_plan(int M, int N, int K, int group, int cus) {
+// Instantiations with per-unit x staging: g = 64 and 128 at 3 to 6 units
+// per wave with one or three tiles, and g = 128 at 8 units with one tile.
+// (With one or two units the compiler moved the lone slot's loads past the
+// unit's x wait, which the assembly test caught; short chains keep the
+// whole-range staging.)
+bool px_compiled(int group, int upw, int tpw) {
+    if (group == 128 && upw == 8 && tpw == 1) return true;
+    return (group == 64 || group == 128) && upw >= 3 && upw <= 6 && (tpw == 1 || tpw == 3);
+}
+
+Plan make_plan(int M, int N, int K, int group, int cus, bool allow_px) {
     // Multi-tile kernels are compiled for g = 64 and 128.  At g = 64, M = 1,
     // they measured 83.8 us on the lm_head shape (N = 152064, K = 5120)
     // against 96.4 us with one tile per workgroup, and 21.2 against 23.5 us
@@ -588,6 +638,16 @@ Plan make_plan(int M, int N, int K, int group, int cus) {
     // The partial sums of all TPW tiles fit each wave's x region: TPW M 64
     // bytes against M upw 256 (TPW <= 4).
     p.lds = lds;
+    // Per-unit x staging up to 4 rows (one [4][256-byte] load per unit) with
+    // no ragged unit.  Measured on the 27B-class layers (us, whole-range
+    // staging / per-unit): M = 1 qkv 6.33 / 5.96, o_proj 6.15 / 5.76,
+    // gate_up 18.1 / 17.6-18.0; M = 4 (bf16) qkv 7.15 / 6.57, o_proj 7.14 /
+    // 6.31, gate_up 21.0 / 19.6-19.7, down (4 slices) 15.1 / 13.4.  Down at
+    // M = 1 (17 units per wave) keeps the whole-range staging: a quarter-full
+    // load per unit ran 15.8 against 14.2 us there.
+    p.px = allow_px && M <= 4 && K % kUnitK == 0 && px_compiled(group, upw, p.tpw);
+    if (const char* e = getenv("W4A16_PX")) p.px = p.px && atoi(e) != 0;   // A/B only
+    if (p.px) p.lds = (size_t)W * upw * 1024;
     p.tiles = T;
     return p;
 }
@@ -605,6 +665,26 @@ w4_kernel_t pick_small_upw(int upw) {
         case 5: return w4_gemv_kernel<BF16, SPG, 5, TPW>;
         default: return w4_gemv_kernel<BF16, SPG, 6, TPW>;
     }
+}
+
+template <bool BF16, int SPG, int TPW>
+w4_kernel_t pick_px_upw(int upw) {
+    switch (upw) {
+        case 3: return w4_gemv_kernel<BF16, SPG, 3, TPW, false, true>;
+        case 4: return w4_gemv_kernel<BF16, SPG, 4, TPW, false, true>;
+        case 5: return w4_gemv_kernel<BF16, SPG, 5, TPW, false, true>;
+        default: return w4_gemv_kernel<BF16, SPG, 6, TPW, false, true>;
+    }
+}
+
+// The per-unit staging kernels (px_compiled says which exist).
+template <bool BF16>
+w4_kernel_t pick_px(int group, int upw, int tpw) {
+    if (group == 128) {
+        if (upw == 8) return w4_gemv_kernel<BF16, 4, 8, 1, false, true>;
+        return tpw == 3 ? pick_px_upw<BF16, 4, 3>(upw) : pick_px_upw<BF16, 4, 1>(upw);
+    }
+    return tpw == 3 ? pick_px_upw<BF16, 2, 3>(upw) : pick_px_upw<BF16, 2, 1>(upw);
 }
 
 template <bool BF16, int SPG>
@@ -638,7 +718,8 @@ w4_kernel_t pick_group(int group, int upw, int tpw) {
     }
 }
 
-w4_kernel_t pick_kernel(bool bf16, int group, int upw, int tpw) {
+w4_kernel_t pick_kernel(bool bf16, int group, int upw, int tpw, bool px = false) {
+    if (px) return bf16 ? pick_px<true>(group, upw, tpw) : pick_px<false>(group, upw, tpw);
     return bf16 ? pick_group<true>(group, upw, tpw) : pick_group<false>(group, upw, tpw);
 }
 
@@ -688,6 +769,14 @@ void allow_full_lds() {
                                               hipFuncAttributeMaxDynamicSharedMemorySize,
                                               (int)kLdsPerCu);
         for (int bf = 0; bf < 2; ++bf)
+            for (int g : {64, 128})
+                for (int u : kUpwSet)
+                    for (int tp = 1; tp <= 4; ++tp)
+                        if (px_compiled(g, u, tp))
+                            (void)hipFuncSetAttribute((const void*)pick_kernel(bf, g, u, tp, true),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                      (int)kLdsPerCu);
+        for (int bf = 0; bf < 2; ++bf)
             for (int u : kUpwSet)
                 for (int tp = 1; tp <= 4; ++tp)
                     (void)hipFuncSetAttribute((const void*)pick_mx_kernel(bf, u, tp),
@@ -697,7 +786,7 @@ void allow_full_lds() {
     });
 }
 
-Plan make_plan(int M, int N, int K, int group, int cus);
+Plan make_plan(int M, int N, int K, int group, int cus, bool allow_px);
 
 // Whether the M-tiled kernel (w4_gemm.hip) takes the call: every M above the
 // GEMV's 16, and below that from the measured crossover on.  Measured per
@@ -719,7 +808,7 @@ bool use_gemm(int M, int N, int K, int group) {
     if (t >= 1) return M >= t;
     if (M > 12) return true;
     if (M < 8) return false;
-    const Plan p = make_plan(M, N, K, group, w4h::cu_count());
+    const Plan p = make_plan(M, N, K, group, w4h::cu_count(), false);
     return p.tpw == 1 && p.lds > kLdsPerCu / 2;
 }
 
@@ -794,7 +883,7 @@ extern "C" int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* byt
         *bytes = gemm_workspace(w4h::gemm_plan(M, N, K, group, w4h::cu_count()), M, N);
         return W4A16_OK;
     }
-    const Plan p = make_plan(M, N, K, group, w4h::cu_count());
+    const Plan p = make_plan(M, N, K, group, w4h::cu_count(), true);
     *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     return W4A16_OK;
 }
@@ -809,7 +898,7 @@ int gemv_impl(const void* x, int x_dtype, const void* qweight, const void* scale
     if (use_gemm(M, N, K, group))
         return launch_gemm(x, x_dtype, qweight, scales, zeros, y, y_dtype, res, res_dtype, M, N, K,
                            group, workspace, workspace_bytes, (hipStream_t)stream);
-    Plan p = make_plan(M, N, K, group, w4h::cu_count());
+    Plan p = make_plan(M, N, K, group, w4h::cu_count(), true);
     if (!p.upw) return W4A16_ERR_UNSUPPORTED;
     const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     if (need) {
@@ -820,7 +909,7 @@ int gemv_impl(const void* x, int x_dtype, const void* qweight, const void* scale
     allow_full_lds();
     hipStream_t st = (hipStream_t)stream;
     const bool bf16 = x_dtype == W4A16_BF16;
-    w4_kernel_t k = pick_kernel(bf16, group, p.upw, p.tpw);
+    w4_kernel_t k = pick_kernel(bf16, group, p.upw, p.tpw, p.px);
     void* out = p.l.S > 1 ? workspace : y;
     p.l.out_dtype = p.l.S > 1 ? W4A16_F32 : y_dtype;
     p.l.res = res;
@@ -831,10 +920,11 @@ int gemv_impl(const void* x, int x_dtype, const void* qweight, const void* scale
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros,
                        out, p.l);
     if (p.l.S > 1) w4h::launch_merge(workspace, y, y_dtype, res, res_dtype, M, N, p.l.S, st);
-    w4h::set_last_variant("w4_mfma16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, %d> tiles=%d slices=%d "
-                          "waves=%d upw=%d tpw=%d lds=%zu",
+    w4h::set_last_variant("w4_mfma16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, %d%s> tiles=%d slices=%d "
+                          "waves=%d upw=%d tpw=%d lds=%zu px=%d",
                           bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.upw,
-                          p.tpw, p.tiles, p.l.S, p.waves, p.upw, p.tpw, p.lds);
+                          p.tpw, p.px ? ", false, true" : "", p.tiles, p.l.S, p.waves, p.upw, p.tpw,
+                          p.lds, (int)p.px);
     return w4h::launch_status();
 }
 
@@ -890,7 +980,7 @@ extern "C" int mxfp4_workspace_bytes(int M, int N, int K, size_t* bytes) {
         *bytes = gemm_workspace(w4h::gemm_plan(M, N, K, kMxPlanGroup, w4h::cu_count()), M, N);
         return W4A16_OK;
     }
-    const Plan p = make_plan(M, N, K, kMxPlanGroup, w4h::cu_count());
+    const Plan p = make_plan(M, N, K, kMxPlanGroup, w4h::cu_count(), false);
     *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     return W4A16_OK;
 }
@@ -920,7 +1010,7 @@ extern "C" int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const
                               pad_n(N) / kTileN, gp.split, gp.workgroups);
         return w4h::launch_status();
     }
-    Plan p = make_plan(M, N, K, kMxPlanGroup, w4h::cu_count());
+    Plan p = make_plan(M, N, K, kMxPlanGroup, w4h::cu_count(), false);
     if (!p.upw) return W4A16_ERR_UNSUPPORTED;
     const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     if (need) {

@@ -41,10 +41,20 @@ def test_kernel_key_normalises_profiler_and_variant_names():
     var = "w4_mfma16 f16 g128 kernel=w4_gemv_kernel<false, 4, 5, 3> tiles=2176"
     assert bench.kernel_key(prof) == bench.kernel_key(var) == "w4_gemv_kernel<false, 4, 5, 3>"
     assert bench.kernel_key("w4_gemv_kernel<true, 4, 5, 1, true>") == "w4_gemv_kernel<true, 4, 5, 1, true>"
+    # Six arguments: MXFP4 mode and per-unit x staging.
+    assert bench.kernel_key("void (anonymous namespace)::w4_gemv_kernel<false, 4, 17, 1, false, false>(int)") \
+        == "w4_gemv_kernel<false, 4, 17, 1>"
+    px = "w4_gemv_kernel<false, 4, 5, 3, false, true>"
+    assert bench.kernel_key("void (anonymous namespace)::" + px + "(int)") == px
+    assert bench.kernel_key("w4_mfma16 f16 g128 kernel=" + px + " tiles=2176") == px
     assert bench.kernel_key("w16_gemv_kernel<false, 1>") == "w16_gemv_kernel<false, 1>"
     assert bench.kernel_key("w16_mfma16 f16 kernel=w16_ksplit_kernel<false> tiles=448") == \
         "w16_ksplit_kernel<false>"
     assert bench.kernel_key("__amd_rocclr_copyBuffer") is None
+
+
+# gate_up's instantiation at M = 1: three tiles per workgroup, x staged unit by unit.
+GATE_UP = "w4_gemv_kernel<false, 4, 5, 3, false, true>"
 
 
 def test_committed_traffic_summary_is_consistent():
@@ -54,15 +64,15 @@ def test_committed_traffic_summary_is_consistent():
     assert 1.9 < t["calibration"]["fetch"]["factor"] < 2.1      # FETCH_SIZE counts half
     assert 0.95 < t["calibration"]["write"]["factor"] < 1.05
     # Each instantiation of the sweep moves about its algorithmic bytes.
-    alg = {"w4_gemv_kernel<false, 4, 5, 3>": bench.alg_bytes(1, 34816, 5120, 128),
+    alg = {GATE_UP: bench.alg_bytes(1, 34816, 5120, 128),
            "w4_gemv_kernel<false, 4, 17, 1>": bench.alg_bytes(1, 5120, 17408, 128)}
     for k, a in alg.items():
         ratio = t["kernels"][k]["bytes_per_dispatch"] / a
         assert 1.0 <= ratio < 1.03, (k, ratio)
     # The bench reports it only while the kernel source is the profiled one.
-    got = bench.load_traffic("w4_gemv_kernel<false, 4, 5, 3>")
+    got = bench.load_traffic(GATE_UP)
     if t["kernel_source_sha256_16"] == bench.kernel_source_hash():
-        assert got == t["kernels"]["w4_gemv_kernel<false, 4, 5, 3>"]["bytes_per_dispatch"]
+        assert got == t["kernels"][GATE_UP]["bytes_per_dispatch"]
     else:
         assert got is None
 

@@ -3,7 +3,10 @@
 The staging kernels load their x range straight into LDS and only then issue
 their weight ring; one explicit `s_waitcnt vmcnt(N)` (N = the ring's load
 count) then waits for the x loads alone, relying on vector memory loads
-completing in issue order.  The compiler does not track LDS writes made by
+completing in issue order.  The GEMV's per-unit staging kernels issue one x
+load with each unit's first ring slot and wait for it just before the unit's
+products; each of those waits is checked against the loads issued after its
+x load.  The compiler does not track LDS writes made by
 such loads, so nothing else guards that wait: it is only correct if at least
 N vector memory loads are issued, in straight-line code, between the last x
 load and the wait, and if no LDS read comes before it.  This test compiles
@@ -90,6 +93,35 @@ def check_x_wait(lines):
     return None
 
 
+def check_unit_x_waits(lines):
+    """Per-unit x staging (the GEMV's PX kernels): the i-th explicit wait
+    guards the i-th x load.  With loads completing in issue order, vmcnt(n)
+    covers that load only if at least n vector memory loads were issued
+    after it (and before the wait).  The loads and waits sit in straight-line
+    code (only the LDS reads are under branches), so program order is issue
+    order.  Returns None if every wait is safe, else a reason."""
+    issued = []          # "x" or "w" per vector memory load, in program order
+    xs = []              # positions of the x loads in `issued`
+    w = 0
+    for i, line in enumerate(lines):
+        if is_vmem_load(line):
+            if " lds" in line:
+                xs.append(len(issued))
+            issued.append("x" if " lds" in line else "w")
+        m = re.fullmatch(r"s_waitcnt vmcnt\((\d+)\)", line)
+        if m and lines[i - 1].startswith(";;#ASMSTART"):
+            n = int(m.group(1))
+            if w >= len(xs):
+                return f"wait {w} before its x load"
+            after = len(issued) - xs[w] - 1
+            if after < n:
+                return f"wait {w}: vmcnt({n}) with only {after} loads after its x load"
+            w += 1
+    if w != len(xs):
+        return f"{len(xs)} x loads but {w} waits"
+    return None
+
+
 def test_x_wait_covers_the_x_loads(asm_files):
     checked = 0
     bad = []
@@ -98,7 +130,10 @@ def test_x_wait_covers_the_x_loads(asm_files):
             if not any(is_vmem_load(l) and " lds" in l for l in lines):
                 continue            # no LDS-direct x staging in this kernel
             checked += 1
-            why = check_x_wait(lines)
+            # The GEMV's per-unit x staging (template argument PX = true)
+            # has one wait per x load; every other kernel one wait in all.
+            px = "ELb0ELb1EE" in name
+            why = check_unit_x_waits(lines) if px else check_x_wait(lines)
             if why:
                 bad.append(f"{src} {name}: {why}")
     # every 4-bit and staged ternary instantiation stages x this way
