@@ -190,6 +190,32 @@ def test_mxfp4_gemv_two_tiles_at_long_k():
     assert_parity(y[:, cols], ref, "mx two tiles")
 
 
+# Per-unit x staging (up to 4 rows, K a multiple of 128, 3 to 6 units per
+# wave with one or three tiles, or 8 with one) and its fallbacks: a ragged
+# last unit, and chains of one or two units per wave.
+@pytest.mark.parametrize("M,N,K,g,xdt,px", [
+    (3, 1032, 5120, 128, "bf16", True),    # two K slices, 3 units per wave
+    (4, 24592, 3072, 64, "f16", True),     # three tiles per workgroup, a last one alone
+    (2, 4104, 8192, 128, "f16", True),     # 8 units per wave
+    (4, 520, 5056, 64, "bf16", False),     # ragged last unit
+    (1, 264, 1024, 128, "f16", False),     # one unit per wave
+])
+def test_w4_gemv_per_unit_x_staging(M, N, K, g, xdt, px):
+    say(f"w4 gemv per-unit x M={M} N={N} K={K} g={g} x={xdt}")
+    key = (135, M, N, K, g)
+    w = synth.gen_w4(key, N, K, g)
+    x = synth.gen_x(key, M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    P = PackedW4(w, N, K, g)
+    y = to_f64(P.gemv(dev(x), xdt, M, "f32"))
+    torch.cuda.synchronize()
+    variant = L.w4a16_last_variant()
+    say("  variant: " + variant)
+    assert ("px=1" in variant) == px
+    cols = sample_cols(N, np.random.default_rng(M + K)) if N > 4200 else np.arange(N)
+    ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g, cols=cols)
+    assert_parity(y[:, cols], ref, f"per-unit x M={M} K={K}")
+
+
 # M-tiled kernel (more rows than one MFMA block): 2 to 4 row blocks, one or
 # two tiles per wave, every group size, ragged N (a last tile of 8 columns)
 # and ragged K (a last unit of 64 k), with and without K slices.
