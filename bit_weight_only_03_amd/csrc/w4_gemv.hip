@@ -150,7 +150,7 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     constexpr bool kUncond = SPG >= 4 || (SPG == 2 && UPW <= 6) || UPW <= 2;
     constexpr int LPS = MX ? 2 : 1 + 2 * NG;              // loads per ring slot
     using SlotT = typename SlotSel<NG, MX>::type;
-    static_assert(!PX || (kUncond && !MX && D <= 9), "per-unit x staging needs a straight-line ring");
+    static_assert(!PX || (kUncond && D <= 9), "per-unit x staging needs a straight-line ring");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int M = a.M, K = a.K, U = a.U;
@@ -752,7 +752,25 @@ w4_kernel_t pick_mx_upw(int upw, int tpw) {
     }
 }
 
-w4_kernel_t pick_mx_kernel(bool bf16, int upw, int tpw) {
+template <bool BF16, int TPW>
+w4_kernel_t pick_mx_px_upw(int upw) {
+    switch (upw) {
+        case 3: return w4_gemv_kernel<BF16, 4, 3, TPW, true, true>;
+        case 4: return w4_gemv_kernel<BF16, 4, 4, TPW, true, true>;
+        case 5: return w4_gemv_kernel<BF16, 4, 5, TPW, true, true>;
+        default: return w4_gemv_kernel<BF16, 4, 6, TPW, true, true>;
+    }
+}
+
+// MXFP4 with per-unit x staging (px_compiled(128, upw, tpw) says which).
+template <bool BF16>
+w4_kernel_t pick_mx_px(int upw, int tpw) {
+    if (upw == 8) return w4_gemv_kernel<BF16, 4, 8, 1, true, true>;
+    return tpw == 3 ? pick_mx_px_upw<BF16, 3>(upw) : pick_mx_px_upw<BF16, 1>(upw);
+}
+
+w4_kernel_t pick_mx_kernel(bool bf16, int upw, int tpw, bool px = false) {
+    if (px) return bf16 ? pick_mx_px<true>(upw, tpw) : pick_mx_px<false>(upw, tpw);
     return bf16 ? pick_mx_upw<true>(upw, tpw) : pick_mx_upw<false>(upw, tpw);
 }
 
@@ -776,6 +794,13 @@ void allow_full_lds() {
                             (void)hipFuncSetAttribute((const void*)pick_kernel(bf, g, u, tp, true),
                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
                                                       (int)kLdsPerCu);
+        for (int bf = 0; bf < 2; ++bf)
+            for (int u : kUpwSet)
+                for (int tp = 1; tp <= 4; ++tp)
+                    if (px_compiled(128, u, tp))
+                        (void)hipFuncSetAttribute((const void*)pick_mx_kernel(bf, u, tp, true),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  (int)kLdsPerCu);
         for (int bf = 0; bf < 2; ++bf)
             for (int u : kUpwSet)
                 for (int tp = 1; tp <= 4; ++tp)
@@ -980,7 +1005,7 @@ extern "C" int mxfp4_workspace_bytes(int M, int N, int K, size_t* bytes) {
         *bytes = gemm_workspace(w4h::gemm_plan(M, N, K, kMxPlanGroup, w4h::cu_count()), M, N);
         return W4A16_OK;
     }
-    const Plan p = make_plan(M, N, K, kMxPlanGroup, w4h::cu_count(), false);
+    const Plan p = make_plan(M, N, K, kMxPlanGroup, w4h::cu_count(), true);
     *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     return W4A16_OK;
 }
@@ -1010,7 +1035,7 @@ extern "C" int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const
                               pad_n(N) / kTileN, gp.split, gp.workgroups);
         return w4h::launch_status();
     }
-    Plan p = make_plan(M, N, K, kMxPlanGroup, w4h::cu_count(), false);
+    Plan p = make_plan(M, N, K, kMxPlanGroup, w4h::cu_count(), true);
     if (!p.upw) return W4A16_ERR_UNSUPPORTED;
     const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     if (need) {
@@ -1021,7 +1046,7 @@ extern "C" int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const
     allow_full_lds();
     hipStream_t st = (hipStream_t)stream;
     const bool bf16 = x_dtype == W4A16_BF16;
-    w4_kernel_t k = pick_mx_kernel(bf16, p.upw, p.tpw);
+    w4_kernel_t k = pick_mx_kernel(bf16, p.upw, p.tpw, p.px);
     void* out = p.l.S > 1 ? workspace : y;
     p.l.out_dtype = p.l.S > 1 ? W4A16_F32 : y_dtype;
     w4h::begin_launches();
@@ -1029,9 +1054,9 @@ extern "C" int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const
                        (const uint16_t*)x, (const u32x4_t*)qweight, (const uint16_t*)scales,
                        (const uint32_t*)nullptr, out, p.l);
     if (p.l.S > 1) w4h::launch_merge(workspace, y, y_dtype, nullptr, W4A16_F32, M, N, p.l.S, st);
-    w4h::set_last_variant("mxfp4_mfma16 %s kernel=w4_gemv_kernel<%s, 4, %d, %d, true> tiles=%d "
-                          "slices=%d waves=%d upw=%d tpw=%d lds=%zu",
-                          bf16 ? "bf16" : "f16", bf16 ? "true" : "false", p.upw, p.tpw, p.tiles, p.l.S,
-                          p.waves, p.upw, p.tpw, p.lds);
+    w4h::set_last_variant("mxfp4_mfma16 %s kernel=w4_gemv_kernel<%s, 4, %d, %d, true%s> tiles=%d "
+                          "slices=%d waves=%d upw=%d tpw=%d lds=%zu px=%d",
+                          bf16 ? "bf16" : "f16", bf16 ? "true" : "false", p.upw, p.tpw,
+                          p.px ? ", true" : "", p.tiles, p.l.S, p.waves, p.upw, p.tpw, p.lds, (int)p.px);
     return w4h::launch_status();
 }

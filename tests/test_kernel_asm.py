@@ -132,7 +132,7 @@ def test_x_wait_covers_the_x_loads(asm_files):
             checked += 1
             # The GEMV's per-unit x staging (template argument PX = true)
             # has one wait per x load; every other kernel one wait in all.
-            px = "ELb0ELb1EE" in name
+            px = re.search(r"ELb[01]ELb1EEEv", name) is not None   # <..., MX, PX = true>
             why = check_unit_x_waits(lines) if px else check_x_wait(lines)
             if why:
                 bad.append(f"{src} {name}: {why}")
