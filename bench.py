@@ -186,7 +186,7 @@ class Sweep:
         self.bytes = sum(alg_bytes(M, N, K, GROUP) for (_, _, K, N, _) in self.mats_meta)
         # One workspace serves every call: calls on one stream run one after another.
         self.ws_bytes = max(L.w4a16_workspace_bytes(M, N, K, GROUP) for (_, _, K, N, _) in self.mats)
-        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device="cuda") if self.ws_bytes else None
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda") if self.ws_bytes else None
 
     @property
     def mats_meta(self):
@@ -364,7 +364,7 @@ def residual_fusion(L, torch, synth, oracle_mod, K, N, g, steps, warmup, stream,
     h = h0.clone()
     t = torch.empty((M, N), dtype=torch.float16, device="cuda")
     wsb = L.w4a16_workspace_bytes(M, N, K, g)
-    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
 
     def fused(bufs):
         L.w4a16_gemv_add(x, "f16", *bufs, h, "f16", h, "f16", M, N, K, g, ws, wsb, stream)
@@ -424,7 +424,7 @@ def w16_sweep(L, torch, synth, oracle_mod, K, N, Ms, steps, warmup, stream, key)
         x = synth.gen_x_torch(key + (M,), M, K, "f16")
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         wsb = L.w16a16_workspace_bytes(M, N, K)
-        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
 
         def call(wm):
             L.w16a16_gemv(x, wm, "f16", y, "f32", M, N, K, ws, wsb, stream)
@@ -499,7 +499,7 @@ def rotation_sweep(L, torch, synth, oracle_mod, kind, K, N, g, Ms, steps, warmup
             wsb = L.mxfp4_workspace_bytes(M, N, K)
         else:
             wsb = L.w2t_workspace_bytes(M, N, K, g)
-        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
 
         def call(bufs):
             if kind == "w4":
@@ -608,6 +608,8 @@ def main():
                     help="fold two rocprofv3 counter runs of this script into "
                          "profiles/w4_gemv_traffic.json and exit (no GPU work)")
     ap.add_argument("--pmc-command", default="", help="the command the counter runs used")
+    ap.add_argument("--extra-json", default=None,
+                    help="also write the detailed measurements (`extra`) to this JSON file")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.pmc_command)
@@ -778,9 +780,45 @@ def main():
                      "per_launch_alg_bytes": round(kbytes), "per_launch_us": round(ktime * 1e6, 3),
                      "timing": "HIP events around replays of a graph of the shape's 64 calls"},
         "cpu_baseline": cpu,
-        "extra": extra,
     }
-    print(json.dumps(result), flush=True)
+    emit(result, extra, args.extra_json)
+
+
+HEADLINE_MAX_BYTES = 4096
+
+
+def summary(extra):
+    """The few figures of `extra` that belong on the headline line: the
+    sweep's share of peak and of the read probe, µs per call of each shape at
+    M = 1 and M = 4, and the M = 4 sweep."""
+    out = {"pct_of_peak": extra.get("pct_of_peak"), "bw_probe_GBps": extra.get("bw_probe_GBps"),
+           "value_pct_of_probe": extra.get("value_pct_of_probe"),
+           "m1_us": {k: d["us"] for k, d in extra.get("m1_per_shape", {}).items()}}
+    m4 = extra.get("m4_sweep")
+    if m4:
+        out["m4_ms_per_token"] = m4["ms_per_token"]
+        out["m4_pct_of_peak"] = m4["pct_of_peak"]
+        out["m4_us"] = {k: d["us"] for k, d in m4["per_shape"].items()}
+    return out
+
+
+def emit(result, extra, extra_json=None):
+    """Print the detail (`extra`) as one stderr line (and to a file when
+    asked), then the headline as the last stdout line: one JSON object of at
+    most HEADLINE_MAX_BYTES bytes."""
+    log("extra " + json.dumps(extra))
+    if extra_json:
+        with open(extra_json, "w") as f:
+            json.dump(extra, f, indent=1)
+            f.write("\n")
+    head = dict(result)
+    head["summary"] = summary(extra)
+    line = json.dumps(head)
+    if len(line.encode()) > HEADLINE_MAX_BYTES:
+        head.pop("summary")
+        line = json.dumps(head)
+    print(line, flush=True)
+    return line
 
 
 if __name__ == "__main__":

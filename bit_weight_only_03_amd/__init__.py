@@ -59,6 +59,7 @@ _SIGS = {
     "w4a16_bw_probe_sink_floats": [],
     "w4a16_status_string": [_I],
     "w4a16_last_variant": [],
+    "w4a16_plan_variant": [_I, _I, _I, _I, _I, ctypes.c_char_p, _SZ],
     "w4a16_last_error": [],
 }
 _STR_RESULT = ("w4a16_status_string", "w4a16_last_variant", "w4a16_last_error")
@@ -125,6 +126,13 @@ def w4a16_status_string(status: int) -> str:
 
 def w4a16_last_variant() -> str:
     return _lib.w4a16_last_variant().decode()
+
+
+def w4a16_plan_variant(M: int, N: int, K: int, group: int, x_dtype="f16") -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check("w4a16_plan_variant", _lib.w4a16_plan_variant(M, N, K, group, _dt(x_dtype), buf,
+                                                         len(buf)))
+    return buf.value.decode()
 
 
 def w4a16_last_error() -> str:

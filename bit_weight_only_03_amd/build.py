@@ -8,6 +8,7 @@ harmless warning that it does not know that feature.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import subprocess
@@ -24,25 +25,31 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(HERE, "_build", os.path.basename(src) + ".o")
+    cmd = [HIPCC, "-c", "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wall", "-Wno-unused-function", "-o", obj, src]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                     if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{errs}")
+    if errs.strip() and verbose:
+        print(errs, flush=True)
+    return obj
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; always rebuilds."""
+    """Compile every source (in parallel) and link the shared library; always
+    rebuilds."""
     os.makedirs(os.path.join(HERE, "_build"), exist_ok=True)
-    objs = []
-    for src in sources():
-        obj = os.path.join(HERE, "_build", os.path.basename(src) + ".o")
-        cmd = [HIPCC, "-c", "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-               "-Wall", "-Wno-unused-function", "-o", obj, src]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        errs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                         if "packed-fp32-ops" not in l)
-        if res.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{errs}")
-        if errs.strip() and verbose:
-            print(errs, flush=True)
-        objs.append(obj)
+    srcs = sources()
+    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", "0")) or os.cpu_count() or 1, 8))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+        objs = list(pool.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -260,6 +260,26 @@ inline int check_w2_shape(int N, int K, int group) {
 // fails), cached per device.  Host only.
 int cu_count();
 
+// Planner overrides for A/B measurement, read from the environment once per
+// process, at the first planner call; later changes to the environment are
+// not seen, so a shape's plan -- and the workspace size it implies -- stays
+// the same for the life of the process (NINFER tuning page, section 七:
+// decode-path choices stay frozen; section 五: workspace capacity is declared
+// up front).  0 (or -1 where 0 is meaningful) means automatic.
+struct Overrides {
+    int w4_waves = 0;          // W4A16_WAVES: waves per GEMV workgroup
+    int w4_split = 0;          // W4A16_SPLIT: GEMV K slices
+    int w4_tpw = 0;            // W4A16_TPW: GEMV tiles per workgroup
+    int w4_gemm_min_m = 0;     // W4A16_GEMM_MIN_M: rows from which the M-tiled kernel runs
+    int w4_px = -1;            // W4A16_PX: 0 turns per-unit x staging off
+    int gemm_tn = 0;           // W4A16_GEMM_TN: tiles per wave of the M-tiled kernel
+    int gemm_split = 0;        // W4A16_GEMM_SPLIT: K slices of the M-tiled kernel
+    int w16_ksplit = -1;       // W16A16_KSPLIT: 0 turns the W16 K-split kernel off
+    int w16_split = 0;         // W16A16_SPLIT: K slices of the W16 tiled kernel
+    long long w2t_staged_lds_max = 0;   // W2T_STAGED_LDS_MAX: LDS limit of the staged ternary kernel
+};
+const Overrides& overrides();
+
 void set_last_variant(const char* fmt, ...);
 void set_last_error(const char* what);
 

@@ -2,8 +2,10 @@
 // HBM bandwidth probe.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "common.h"
 
@@ -64,6 +66,28 @@ int cu_count() {
     g_cu_count[dev].store(n, std::memory_order_relaxed);   // every racer stores the same value
     return n;
 }
+
+const Overrides& overrides() {
+    static Overrides o;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        auto geti = [](const char* name, int& v) {
+            if (const char* e = getenv(name)) v = atoi(e);
+        };
+        geti("W4A16_WAVES", o.w4_waves);
+        geti("W4A16_SPLIT", o.w4_split);
+        geti("W4A16_TPW", o.w4_tpw);
+        geti("W4A16_GEMM_MIN_M", o.w4_gemm_min_m);
+        geti("W4A16_PX", o.w4_px);
+        geti("W4A16_GEMM_TN", o.gemm_tn);
+        geti("W4A16_GEMM_SPLIT", o.gemm_split);
+        geti("W16A16_KSPLIT", o.w16_ksplit);
+        geti("W16A16_SPLIT", o.w16_split);
+        if (const char* e = getenv("W2T_STAGED_LDS_MAX")) o.w2t_staged_lds_max = atoll(e);
+    });
+    return o;
+}
+
 void set_last_variant(const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);

@@ -354,17 +354,14 @@ W16Plan w16_plan(int M, int N, int K) {
     p.lds = (size_t)M * U * kUnitK * 2;
     p.ksplit = M <= 16 && upw <= kW16KMaxUnits && M * upw <= 64 && p.lds <= kW16KLdsMax;
     // Override for A/B measurement only: 0 turns the K-split kernel off.
-    if (const char* e = getenv("W16A16_KSPLIT")) p.ksplit = p.ksplit && atoi(e) != 0;
+    if (w4h::overrides().w16_ksplit == 0) p.ksplit = false;
     p.rb = (M + 15) / 16;
     p.workgroups = (T + kW16Waves - 1) / kW16Waves;
     p.split = 1;
     while (p.workgroups * p.split < 8LL * w4h::cu_count() && U / (2 * p.split) >= 6 &&
            p.split < kW16MaxSplit)
         p.split *= 2;
-    if (const char* e = getenv("W16A16_SPLIT")) {
-        const int s = atoi(e);
-        if (s >= 1 && s <= U && s <= kW16MaxSplit) p.split = s;
-    }
+    if (const int s = w4h::overrides().w16_split; s >= 1 && s <= U && s <= kW16MaxSplit) p.split = s;
     return p;
 }
 

@@ -645,13 +645,9 @@ constexpr size_t kStagedLdsMax = kLdsPerCu2 / 2;
 constexpr int kStagedMaxRows = 8;
 
 size_t staged_lds_max() {
-    // Override for A/B measurement only, read once per process.
-    static size_t v = [] {
-        const char* e = getenv("W2T_STAGED_LDS_MAX");
-        const long long n = e ? atoll(e) : 0;
-        return n > 0 ? (size_t)n : kStagedLdsMax;
-    }();
-    return v;
+    // Override for A/B measurement only (read once per process: common.h).
+    const long long n = w4h::overrides().w2t_staged_lds_max;
+    return n > 0 ? (size_t)n : kStagedLdsMax;
 }
 
 bool use_staged(const Plan2& p) {

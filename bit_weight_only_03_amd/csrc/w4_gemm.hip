@@ -409,17 +409,11 @@ GemmPlan gemm_plan(int M, int N, int K, int group, int cus) {
     // One tile per wave: the two-tile build needs 212 VGPRs (two waves per
     // SIMD) and measured slower (gate_up at M = 64: 64.9 us against 57.6 us).
     p.tn = 1;
-    if (const char* e = getenv("W4A16_GEMM_TN")) {
-        const int t = atoi(e);
-        if (t == 1 || t == 2) p.tn = t;
-    }
+    if (const int t = overrides().gemm_tn; t == 1 || t == 2) p.tn = t;
     const long long cols = (T + kGemmWaves * p.tn - 1) / (kGemmWaves * p.tn);
     p.split = 1;
     while (cols * p.split < 2LL * cus && U / (2 * p.split) >= 8 && p.split < kMaxSplitGemm) p.split *= 2;
-    if (const char* e = getenv("W4A16_GEMM_SPLIT")) {
-        const int s = atoi(e);
-        if (s >= 1 && s <= U && s <= kMaxSplitGemm) p.split = s;
-    }
+    if (const int s = overrides().gemm_split; s >= 1 && s <= U && s <= kMaxSplitGemm) p.split = s;
     p.workgroups = cols;
     return p;
 }

@@ -527,25 +527,8 @@ merge_kernel_t pick_merge(int S) {
 
 // ------------------------------------------------------------------ dispatch
 
-struct Tuning {
-    int waves = 0, split = 0, tpw = 0;  // 0 = automatic
-    int gemm_min_m = 0;                 // rows from which the M-tiled kernel runs (0 = automatic)
-};
-
-const Tuning& tuning() {
-    // Overrides for A/B measurement only, read once per process (decode-path
-    // choices are frozen: NINFER tuning page, section 七).
-    static Tuning t;
-    static std::once_flag once;
-    std::call_once(once, [] {
-        if (const char* e = getenv("W4A16_WAVES")) t.waves = atoi(e);
-        if (const char* e = getenv("W4A16_SPLIT")) t.split = atoi(e);
-        if (const char* e = getenv("W4A16_TPW")) t.tpw = atoi(e);
-        if (const char* e = getenv("W4A16_GEMM_MIN_M")) t.gemm_min_m = atoi(e);
-    });
-    return t;
-}
-
+// Planner overrides (A/B measurement only), read once per process: common.h.
+using w4h::overrides;
 
 constexpr size_t kLdsPerCu = 160 * 1024;      // gfx950
 constexpr int kWaves = 8;                     // waves per workgroup (two workgroups per CU)
@@ -585,11 +568,11 @@ Plan make_plan(int M, int N, int K, int group, int cus, bool allow_px) {
     // on gate_up.
     const bool group_tpw_ok = group == 128 || group == 64;
     Plan p;
-    const Tuning& tu = tuning();
+    const w4h::Overrides& tu = overrides();
     const int U = (K + kUnitK - 1) / kUnitK;
     const int T = pad_n(N) / kTileN;
     int W = kWaves;
-    if (tu.waves >= 1 && tu.waves <= kMaxWaves) W = tu.waves;
+    if (tu.w4_waves >= 1 && tu.w4_waves <= kMaxWaves) W = tu.w4_waves;
     // K slices: a wave's range must fit a compiled UPW, its x range at most
     // 16 chunks per lane (M * UPW <= 64), and the workgroup's x (whose regions the
     // partial sums reuse) the LDS of a CU.
@@ -616,7 +599,7 @@ Plan make_plan(int M, int N, int K, int group, int cus, bool allow_px) {
     // 17.9 us at two slices and 17.0 us at four.
     if (S > 1 && (long long)T * S < 4LL * cus && U / (2 * S) >= 4 * W && fits(2 * S, upw, lds, xstride))
         S *= 2;
-    if (tu.split >= 1 && tu.split <= U) S = tu.split;
+    if (tu.w4_split >= 1 && tu.w4_split <= U) S = tu.w4_split;
     if (!fits(S, upw, lds, xstride)) upw = 0;   // an override that cannot run is refused
     p.l = GemvLaunch{M, N, K, U, S, T, xstride, W4A16_F32, nullptr, W4A16_F32};
     p.waves = W;
@@ -634,7 +617,7 @@ Plan make_plan(int M, int N, int K, int group, int cus, bool allow_px) {
     // (the M-tiled kernel) to 11.2 us (g = 64: 15.3 -> 12.2, 14.9 -> 13.0).
     if (group_tpw_ok && p.tpw == 1 && upw == 8 && S == 1 && lds > kLdsPerCu / 2 && T >= 2 * cus)
         p.tpw = 2;
-    if (tu.tpw >= 1 && tu.tpw <= 4 && upw <= 6 && group_tpw_ok) p.tpw = tu.tpw;
+    if (tu.w4_tpw >= 1 && tu.w4_tpw <= 4 && upw <= 6 && group_tpw_ok) p.tpw = tu.w4_tpw;
     // The partial sums of all TPW tiles fit each wave's x region: TPW M 64
     // bytes against M upw 256 (TPW <= 4).
     p.lds = lds;
@@ -646,7 +629,7 @@ Plan make_plan(int M, int N, int K, int group, int cus, bool allow_px) {
     // M = 1 (17 units per wave) keeps the whole-range staging: a quarter-full
     // load per unit ran 15.8 against 14.2 us there.
     p.px = allow_px && M <= 4 && K % kUnitK == 0 && px_compiled(group, upw, p.tpw);
-    if (const char* e = getenv("W4A16_PX")) p.px = p.px && atoi(e) != 0;   // A/B only
+    if (tu.w4_px == 0) p.px = false;   // A/B only
     if (p.px) p.lds = (size_t)W * upw * 1024;
     p.tiles = T;
     return p;
@@ -828,7 +811,7 @@ Plan make_plan(int M, int N, int K, int group, int cus, bool allow_px);
 // layers the GEMV streams two or three tiles per workgroup and stays ahead:
 // K = N = 8192 at M = 8 takes 11.1 us with two, against 13.9 us tiled).
 bool use_gemm(int M, int N, int K, int group) {
-    const int t = tuning().gemm_min_m;
+    const int t = overrides().w4_gemm_min_m;
     if (M > kMaxRows) return true;
     if (t >= 1) return M >= t;
     if (M > 12) return true;
@@ -856,6 +839,24 @@ int check_gemv_args(const void* x, int x_dtype, const void* q, const void* s, co
     return W4A16_OK;
 }
 
+// The dispatch probe's text for a plan (NINFER tuning page, section 二: every
+// dispatch branch names itself): the kernel instantiation and launch shape.
+void format_gemv(char* b, size_t n, bool bf16, int group, const Plan& p) {
+    snprintf(b, n,
+             "w4_mfma16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, %d%s> tiles=%d slices=%d "
+             "waves=%d upw=%d tpw=%d lds=%zu px=%d",
+             bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.upw, p.tpw,
+             p.px ? ", false, true" : "", p.tiles, p.l.S, p.waves, p.upw, p.tpw, p.lds, (int)p.px);
+}
+
+void format_gemm(char* b, size_t n, bool bf16, int group, int N, const w4h::GemmPlan& p) {
+    snprintf(b, n,
+             "w4_gemm16 %s g%d kernel=w4_gemm_kernel<%s, %d, %d, %d> tiles=%d slices=%d "
+             "workgroups=%lld",
+             bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.rb, p.tn,
+             pad_n(N) / kTileN, p.split, p.workgroups);
+}
+
 // y = the slice-order sum of S fp32 partials [S][M][N] in the workspace.
 int launch_gemm(const void* x, int x_dtype, const void* qweight, const void* scales, const void* zeros,
                 void* y, int y_dtype, const void* res, int res_dtype, int M, int N, int K, int group,
@@ -872,10 +873,9 @@ int launch_gemm(const void* x, int x_dtype, const void* qweight, const void* sca
     w4h::gemm_launch(p, x, bf16, qweight, scales, zeros, y, y_dtype, res, res_dtype, M, N, K, group,
                      workspace, st);
     if (p.split > 1) w4h::launch_merge(workspace, y, y_dtype, res, res_dtype, M, N, p.split, st);
-    w4h::set_last_variant("w4_gemm16 %s g%d kernel=w4_gemm_kernel<%s, %d, %d, %d> tiles=%d slices=%d "
-                          "workgroups=%lld",
-                          bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.rb, p.tn,
-                          pad_n(N) / kTileN, p.split, p.workgroups);
+    char v[160];
+    format_gemm(v, sizeof v, bf16, group, N, p);
+    w4h::set_last_variant("%s", v);
     return w4h::launch_status();
 }
 
@@ -945,15 +945,30 @@ int gemv_impl(const void* x, int x_dtype, const void* qweight, const void* scale
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros,
                        out, p.l);
     if (p.l.S > 1) w4h::launch_merge(workspace, y, y_dtype, res, res_dtype, M, N, p.l.S, st);
-    w4h::set_last_variant("w4_mfma16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, %d%s> tiles=%d slices=%d "
-                          "waves=%d upw=%d tpw=%d lds=%zu px=%d",
-                          bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.upw,
-                          p.tpw, p.px ? ", false, true" : "", p.tiles, p.l.S, p.waves, p.upw, p.tpw,
-                          p.lds, (int)p.px);
+    char v[160];
+    format_gemv(v, sizeof v, bf16, group, p);
+    w4h::set_last_variant("%s", v);
     return w4h::launch_status();
 }
 
 }  // namespace
+
+extern "C" int w4a16_plan_variant(int M, int N, int K, int group, int x_dtype, char* text,
+                                  size_t text_bytes) {
+    if (!text || text_bytes == 0) return W4A16_ERR_NULL;
+    if (x_dtype != W4A16_F16 && x_dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (M < 1 || M > w4h::kMaxRowsGemm || !w4h::x_fits(M, K)) return W4A16_ERR_SHAPE;
+    if (int rc = w4h::check_w4_shape(N, K, group)) return rc;
+    const bool bf16 = x_dtype == W4A16_BF16;
+    if (use_gemm(M, N, K, group)) {
+        format_gemm(text, text_bytes, bf16, group, N, w4h::gemm_plan(M, N, K, group, w4h::cu_count()));
+        return W4A16_OK;
+    }
+    const Plan p = make_plan(M, N, K, group, w4h::cu_count(), true);
+    if (!p.upw) return W4A16_ERR_UNSUPPORTED;
+    format_gemv(text, text_bytes, bf16, group, p);
+    return W4A16_OK;
+}
 
 extern "C" int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const void* scales,
                           const void* zeros, void* y, int y_dtype, int M, int N, int K, int group,

@@ -79,8 +79,11 @@ typedef enum { W4A16_F16 = 0, W4A16_BF16 = 1, W4A16_F32 = 2 } w4a16_dtype;
  *   M * K * 2 < 2^32 (x is addressed through 32-bit offsets).  The MXFP4 and
  *   ternary functions take the same limits on K and M * K. */
 
-/* Bytes of the device layout for an N x K matrix with the given group.  Host
- * only.  Returns W4A16_OK or W4A16_ERR_SHAPE / W4A16_ERR_NULL. */
+/* Bytes of the device layout for an N x K matrix with the given group, so a
+ * caller can allocate the repacked weights once, at load time, before any
+ * capture (Z100 article, section 四: repack once after loading; NINFER tuning
+ * page, section 五: sizes declared up front).  Host only.  Returns W4A16_OK or
+ * W4A16_ERR_SHAPE / W4A16_ERR_NULL. */
 int w4a16_packed_sizes(int N, int K, int group, size_t* q_bytes, size_t* s_bytes,
                        size_t* z_bytes);
 
@@ -93,7 +96,13 @@ int w4a16_pack(const int32_t* qweight_canon, const uint16_t* scales_canon,
                const int32_t* zeros_canon, void* qweight, void* scales, void* zeros, int N,
                int K, int group, w4a16_stream_t stream);
 
-/* Device layout -> canonical, the exact inverse of w4a16_pack. */
+/* Device layout -> canonical, the exact inverse of w4a16_pack: every byte of
+ * the canonical arrays comes back as it went in.  A conversion of the weight
+ * files must be checkable bit for bit against the original (Ninfer V100
+ * article, section 十三: the 452 weight blocks of the split files were
+ * compared with the source file bit by bit).  Same arguments, sizes and
+ * errors as w4a16_pack, with the roles of the two sides swapped; the
+ * buffers must not overlap. */
 int w4a16_unpack(const void* qweight, const void* scales, const void* zeros,
                  int32_t* qweight_canon, uint16_t* scales_canon, int32_t* zeros_canon, int N,
                  int K, int group, w4a16_stream_t stream);
@@ -103,6 +112,8 @@ int w4a16_unpack(const void* qweight, const void* scales, const void* zeros,
  * process, so a workspace sized once may be reused inside a captured graph
  * (NINFER tuning page, section 五: declare workspace capacity up front). */
 int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* bytes);
+/* (The A/B overrides the planners honour are read from the environment once,
+ * at the first size query or call of the process; see w4a16_plan_variant.) */
 
 /* y[M,N] = x[M,K] . ((q - z) * s)[K,N] from the packed device layout, for
  * 1 <= M <= 64 (the Z100 article, section 五: the weights are read and
@@ -135,7 +146,11 @@ int w4a16_gemv_add(const void* x, int x_dtype, const void* qweight, const void* 
                    w4a16_stream_t stream);
 
 /* Debug / parity: the dequantized matrix w[K][N] = (q - z) * s as fp32 from the
- * packed layout.  Exact, since |q - z| <= 15 times an fp16 scale fits in fp32. */
+ * packed layout -- the integer restored with its group's zero point and
+ * multiplied back by the group's scale (Ninfer V100 article, section 十一,
+ * groupwise-int; Z100 article, section 四).  Exact, since |q - z| <= 15 times
+ * an fp16 scale fits in fp32.  w is a device buffer of K * N floats, 16-byte
+ * aligned, written in full; shape and pointer errors as w4a16_pack. */
 int w4a16_dequant(const void* qweight, const void* scales, const void* zeros, float* w, int N,
                   int K, int group, w4a16_stream_t stream);
 
@@ -197,10 +212,22 @@ int mxfp4_dequant(const void* qweight, const void* scales, float* w, int N, int 
                   w4a16_stream_t stream);
 
 /* ---- ternary 2-bit variant: w = (c - 1) * s, one fp16 scale per group ----
- * Shape contract: 1 <= N, 1 <= K, K % group == 0, K % 16 == 0,
- * group in {32, 64, 128, 256}; for the GEMV also 1 <= M <= 16.
- * A code of 3 is invalid input: the output for such weights is unspecified
- * (no error is reported; the GPU path does not scan for it). */
+ * Weights in {-1, 0, +1} times a per-group scale, streamed at two bits each
+ * ("NINFER 三元引擎性能调优", sections 五 and 六: the ternary decode path is
+ * bound by the bytes it reads plus its decode arithmetic).  Shape contract:
+ * 1 <= N, 1 <= K, K % group == 0, K % 16 == 0, group in {32, 64, 128, 256};
+ * for the GEMV also 1 <= M <= 16.  A code of 3 is invalid input: the output
+ * for such weights is unspecified (no error is reported; the GPU path does
+ * not scan for it).
+ * w2t_packed_sizes: device bytes of the packed codes and scales (host only).
+ * w2t_pack / w2t_unpack: canonical codes_canon [N][K/16] and scales_canon
+ *   [K/group][N] <-> the device layout, exact inverses of each other (as for
+ *   w4a16_pack / w4a16_unpack: repacked once after loading, Z100 article,
+ *   section 四; checkable bit for bit, Ninfer V100 article, section 十三).
+ * w2t_workspace_bytes / w2t_gemv: y[M,N] = x[M,K] . ((c - 1) * s)[K,N], with
+ *   the dtypes, alignment, determinism, workspace and overlap rules of
+ *   w4a16_gemv.
+ * w2t_dequant: debug / parity, w[K][N] = (c - 1) * s as fp32, exact. */
 int w2t_packed_sizes(int N, int K, int group, size_t* q_bytes, size_t* s_bytes);
 int w2t_pack(const int32_t* codes_canon, const uint16_t* scales_canon, void* qweight,
              void* scales, int N, int K, int group, w4a16_stream_t stream);
@@ -233,6 +260,15 @@ const char* w4a16_status_string(int status);
  * (every dispatch branch reports itself: NINFER tuning page, section 二).
  * Host string owned by the library, valid until the next call on the thread. */
 const char* w4a16_last_variant(void);
+
+/* The same text for the kernel a w4a16_gemv (or w4a16_gemv_add) call of this
+ * shape and x dtype would launch, without launching anything: a host-only
+ * query of the frozen dispatch (NINFER tuning page, sections 二 and 七: ask
+ * which tier runs, and keep that choice fixed).  Writes a NUL-terminated
+ * string of at most text_bytes bytes (truncated if longer) into the host
+ * buffer text.  Returns W4A16_OK, or W4A16_ERR_NULL / _DTYPE / _SHAPE /
+ * _UNSUPPORTED for the arguments w4a16_gemv would refuse. */
+int w4a16_plan_variant(int M, int N, int K, int group, int x_dtype, char* text, size_t text_bytes);
 
 /* HIP error name behind the most recent W4A16_ERR_HIP on this host thread
  * ("none" if there was none).  Static host string. */

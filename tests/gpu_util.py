@@ -34,8 +34,10 @@ def empty_bytes(n: int) -> torch.Tensor:
 
 
 def workspace_bytes(n: int) -> torch.Tensor:
-    """A GEMV workspace: zero-filled before first use, as the library requires."""
-    return torch.zeros(max(n, 16), dtype=torch.uint8, device=DEV)
+    """A GEMV workspace.  The library needs no zeroing (every byte it reads
+    was written earlier in the same call; the poisoned-workspace tests fill it
+    with NaN to show this), so it is left uninitialised."""
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=DEV)
 
 
 class PackedW4:

@@ -101,3 +101,32 @@ def test_ingest_pmc_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     assert k["write_bytes_per_dispatch"] == 10 * 1024
     assert k["bytes_per_dispatch"] == round(1001.0 * 1024 * 2 + 10 * 1024)
     assert t["command"] == "test command"
+
+
+def test_headline_is_the_last_line_and_small(capsys):
+    # A result shaped like a real run, with a large `extra` block: the last
+    # stdout line is the compact headline, which parses and stays small; the
+    # detail goes to stderr.
+    shape = {"us": 17.8, "GBps": 5206.6, "bytes": 92760064, "kernel": "k", "variant": "v" * 150}
+    extra = {"pct_of_peak": 50.5, "bw_probe_GBps": 6331.0, "value_pct_of_probe": 63.8,
+             "m1_per_shape": {n: dict(shape) for n in ("qkv", "o_proj", "gate_up", "down")},
+             "m4_sweep": {"ms_per_token": 2.9, "pct_of_peak": 47.4,
+                          "per_shape": {n: dict(shape) for n in ("qkv", "o_proj", "gate_up", "down")}},
+             "skinny_sweep": [dict(shape, M=m) for m in range(200)]}
+    result = {"metric": "m", "value": 4039.0, "unit": "GB/s", "n_gpus": 1, "steps": 20, "warmup": 3,
+              "ms_per_step": 2.72, "dtype": "f16", "config": {"workload": "w"},
+              "roofline": {"bound": "hbm", "achieved": 5206.6, "peak": 8000.0, "unit": "GB/s",
+                           "frac": 0.6508, "traffic": 93053843},
+              "cpu_baseline": {"value": 0.7, "unit": "GB/s", "cores": 16, "kind": "oracle",
+                               "sample": "s"}}
+    bench.emit(result, extra)
+    cap = capsys.readouterr()
+    last = cap.out.strip().splitlines()[-1]
+    assert len(last.encode()) <= bench.HEADLINE_MAX_BYTES
+    head = json.loads(last)
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "ms_per_step", "dtype", "config",
+                "roofline", "cpu_baseline"):
+        assert key in head
+    assert "extra" not in head
+    assert head["summary"]["m4_us"]["gate_up"] == 17.8
+    assert "skinny_sweep" in cap.err
