@@ -314,7 +314,7 @@ def cpu_baseline(torch, synth, oracle_mod, budget_s=12.0):
             t_total += time.perf_counter() - t0
             nbytes += alg_bytes(1, N, K, GROUP)
         layers += 1
-        if layers % 4 == 0:
+        if layers % 16 == 0:
             log(f"cpu oracle: {layers} layer(s), {t_total:.1f} s")
     return {"value": round(gbps(nbytes, t_total), 4), "unit": "GB/s",
             "cores": oracle_mod.num_threads(), "kind": "oracle",
@@ -608,8 +608,8 @@ def main():
                     help="fold two rocprofv3 counter runs of this script into "
                          "profiles/w4_gemv_traffic.json and exit (no GPU work)")
     ap.add_argument("--pmc-command", default="", help="the command the counter runs used")
-    ap.add_argument("--extra-json", default=None,
-                    help="also write the detailed measurements (`extra`) to this JSON file")
+    ap.add_argument("--extra-json", default=EXTRA_JSON,
+                    help="where to write the detailed measurements (`extra`) as JSON")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.pmc_command)
@@ -646,7 +646,7 @@ def main():
     te1 = s1.time_eager(stream, max(2, args.steps // 4))
     shapes1 = s1.per_shape(stream, args.steps, args.warmup)
     for name, d in shapes1.items():
-        log(f"  {name}: {d['us']:.2f} us/call, {d['GBps']:.0f} GB/s  [{d['variant']}]")
+        log(f"  {name}: {d['us']:.2f} us/call, {d['GBps']:.0f} GB/s  [{d['kernel']}]")
     kern, kshapes, kbytes, ktime = dominant(shapes1)
     achieved = gbps(kbytes, ktime)
     traffic = load_traffic(kern)
@@ -670,7 +670,7 @@ def main():
                              "bytes": s4.bytes, "parity_worst_rel": w4, "per_shape": shapes4}
         log(f"M=4 sweep: {t4 * 1e3:.4f} ms/token, {gbps(s4.bytes, t4):.1f} GB/s")
         for name, d in shapes4.items():
-            log(f"  {name}: {d['us']:.2f} us/call, {d['GBps']:.0f} GB/s  [{d['variant']}]")
+            log(f"  {name}: {d['us']:.2f} us/call, {d['GBps']:.0f} GB/s  [{d['kernel']}]")
         del s4
 
     if not args.no_extra:
@@ -784,7 +784,8 @@ def main():
     emit(result, extra, args.extra_json)
 
 
-HEADLINE_MAX_BYTES = 4096
+HEADLINE_MAX_BYTES = 3072
+EXTRA_JSON = os.path.join(ROOT, "gpurun_out", "bench_extra.json")
 
 
 def summary(extra):
@@ -803,14 +804,16 @@ def summary(extra):
 
 
 def emit(result, extra, extra_json=None):
-    """Print the detail (`extra`) as one stderr line (and to a file when
-    asked), then the headline as the last stdout line: one JSON object of at
-    most HEADLINE_MAX_BYTES bytes."""
-    log("extra " + json.dumps(extra))
+    """Write the detail (`extra`) to a JSON file, then print the headline as
+    the last stdout line: one JSON object of at most HEADLINE_MAX_BYTES
+    bytes (a reader that keeps only the tail of the output still gets it
+    whole)."""
     if extra_json:
+        os.makedirs(os.path.dirname(os.path.abspath(extra_json)), exist_ok=True)
         with open(extra_json, "w") as f:
             json.dump(extra, f, indent=1)
             f.write("\n")
+        log(f"detailed measurements written to {extra_json}")
     head = dict(result)
     head["summary"] = summary(extra)
     line = json.dumps(head)

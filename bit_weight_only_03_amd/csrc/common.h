@@ -136,11 +136,25 @@ __device__ __forceinline__ half8_t dequant_f16(uint32_t d, uint32_t magic, uint3
     return bitcast<half8_t>(v);
 }
 
-// B operand (8 bf16 = 128 + q, exact) for the 8 weights of one device dword.
-__device__ __forceinline__ bf16x8_t biased_bf16(uint32_t d, uint32_t magic) {
-    u32x4_t v = {bfi(0x000F000Fu, d, magic), bfi(0x000F000Fu, d >> 4, magic),
-                 bfi(0x000F000Fu, d >> 8, magic), bfi(0x000F000Fu, d >> 12, magic)};
-    return bitcast<bf16x8_t>(v);
+// bf16 activations for the 4-bit kernels: the staged x is rewritten in place
+// as fp16, so the products take the exact fp16 q - z above (gfx950 has no
+// packed bf16 add to form q - z in bf16, and a biased bf16 operand with a
+// separate zero-point product leaves q = z as a rounding residue instead of
+// an exact 0).  One 16-byte chunk, 8 values: bf16 -> fp32 is a shift or a
+// mask, fp32 -> fp16 one v_cvt_pk_f16_f32 per pair, round to nearest even.
+// Exact for every bf16 value of magnitude in [2^-17, 65280] and for zeros;
+// smaller magnitudes land on fp16's 2^-24 subnormal grid (a change below
+// 2^-25), and magnitudes of 65536 or more (past fp16's range) become
+// infinite -- outside the library's contract for bf16 x.
+__device__ __forceinline__ u32x4_t bf16x8_to_f16x8(u32x4_t v) {
+    u32x4_t r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float lo = bitcast<float>(v[j] << 16);
+        const float hi = bitcast<float>(v[j] & 0xffff0000u);
+        r[j] = as_u(half2_t{(_Float16)lo, (_Float16)hi});
+    }
+    return r;
 }
 
 // MXFP4 (OCP MX v1.0: E2M1 elements, one E8M0 scale per 32 elements along K).

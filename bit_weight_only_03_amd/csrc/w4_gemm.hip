@@ -169,16 +169,21 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
                 rx, in ? (uint32_t)(m * K + k) * 2u : xend, 0, 0));
         }
     };
+    // bf16 x with 4-bit weights is stored as fp16 (exact over fp16's range,
+    // common.h), so the products take the exact fp16 q - z.
     auto store_x = [&](int b, int slot) {
 #pragma unroll
         for (int p = 0; p < XPT; ++p) {
             const int ch = threadIdx.x + 256 * p;
-            *(u32x4_t*)&xs[b][ch >> 4][8 * (ch & 15)] = xr[slot][p];
+            if constexpr (BF16 && !MX)
+                *(u32x4_t*)&xs[b][ch >> 4][8 * (ch & 15)] = bf16x8_to_f16x8(xr[slot][p]);
+            else
+                *(u32x4_t*)&xs[b][ch >> 4][8 * (ch & 15)] = xr[slot][p];
         }
     };
 
     const int zshift = 4 * (c & 7);
-    const uint32_t magic = opaque_v(BF16 ? 0x43004300u : 0x64006400u);   // 128.0 / 1024.0 pairs
+    const uint32_t magic = opaque_v(0x64006400u);   // fp16 1024.0 pairs
     float4_t total[TN][RB];
 #pragma unroll
     for (int j = 0; j < TN; ++j)
@@ -284,28 +289,15 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const uint32_t zq = (r[j].z[gi] >> zshift) & 15u;
-                    if constexpr (!BF16) {
-                        uint32_t nz1024 = 0xE400u + zq;          // fp16 -(1024 + z)
-                        nz1024 |= nz1024 << 16;
-                        uint32_t nz64 = 0xD400u + (zq << 4);     // fp16 -(64 + z)
-                        nz64 |= nz64 << 16;
-                        const half8_t bq = dequant_f16(r[j].w[st], magic, nz1024, nz64);
+                    uint32_t nz1024 = 0xE400u + zq;          // fp16 -(1024 + z)
+                    nz1024 |= nz1024 << 16;
+                    uint32_t nz64 = 0xD400u + (zq << 4);     // fp16 -(64 + z)
+                    nz64 |= nz64 << 16;
+                    const half8_t bq = dequant_f16(r[j].w[st], magic, nz1024, nz64);
 #pragma unroll
-                        for (int rb = 0; rb < RB; ++rb)
-                            acc[j][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                bitcast<half8_t>(av[rb]), bq, acc[j][rb], 0, 0, 0);
-                    } else {
-                        uint32_t nb = 0xC300u + zq;              // bf16 -(128 + z)
-                        nb |= nb << 16;
-                        const bf16x8_t bias = bitcast<bf16x8_t>(u32x4_t{nb, nb, nb, nb});
-                        const bf16x8_t bq = biased_bf16(r[j].w[st], magic);
-#pragma unroll
-                        for (int rb = 0; rb < RB; ++rb) {
-                            const bf16x8_t ax = bitcast<bf16x8_t>(av[rb]);
-                            acc[j][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bq, acc[j][rb], 0, 0, 0);
-                            acc[j][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bias, acc[j][rb], 0, 0, 0);
-                        }
-                    }
+                    for (int rb = 0; rb < RB; ++rb)
+                        acc[j][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            bitcast<half8_t>(av[rb]), bq, acc[j][rb], 0, 0, 0);
                 }
             }
 #pragma unroll

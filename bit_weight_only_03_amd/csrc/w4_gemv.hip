@@ -25,9 +25,9 @@
 // in a 16-bit float's mantissa and subtract a constant" trick of the Ninfer
 // V100 article, section 十), then one packed add of -(1024 + z) (or a packed
 // fma by 1/16 and -(64 + z) for the nibbles in the high half of a byte), which
-// gives q - z exactly.  For bf16 activations the pairs are 128 + q and the
-// zero point enters through a second MFMA against the constant operand
-// -(128 + z), which also keeps every product exact.
+// gives q - z exactly.  bf16 activations are rewritten as fp16 in LDS right
+// after they are staged (exact over fp16's range, common.h), so they meet the
+// same exact fp16 q - z: q = z gives exactly 0 for either activation type.
 //
 // Products.  The dequantized pairs are the B operand of v_mfma_f32_16x16x32
 // (lane l supplies column l % 16 and the k-block l / 16) and the x rows are
@@ -151,6 +151,7 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     constexpr int LPS = MX ? 2 : 1 + 2 * NG;              // loads per ring slot
     using SlotT = typename SlotSel<NG, MX>::type;
     static_assert(!PX || (kUncond && D <= 9), "per-unit x staging needs a straight-line ring");
+    constexpr bool kCvtX = BF16 && !MX;   // bf16 x taken to fp16 in LDS for the 4-bit products
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int M = a.M, K = a.K, U = a.U;
@@ -280,10 +281,24 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     // them); a host-side test checks the compiled kernels for this.
     if constexpr (kUncond && !PX) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D * LPS) : "memory");
     __builtin_amdgcn_sched_barrier(0);
+    // bf16 x: each lane rewrites the chunks its own x loads filled as fp16.
+    if constexpr (kCvtX && !PX) {
+        const int cpr = a.xstride / 8, live = nu * (kUnitK / 8), xch = M * cpr;
+#pragma unroll
+        for (int i = 0; i < kMaxXLoads; ++i) {
+            if (i * 64 < xch) {
+                const int ci = i * 64 + lane;
+                if (ci / cpr < M && ci % cpr < live) {
+                    u32x4_t* const p = (u32x4_t*)(xsb + (uint32_t)ci * 16u);
+                    *p = bf16x8_to_f16x8(*p);
+                }
+            }
+        }
+    }
 
     // 3) Dequantize and multiply, unit by unit.
     const int zshift = 4 * (c & 7);
-    const uint32_t magic = opaque_v(BF16 ? 0x43004300u : 0x64006400u);   // 128.0 / 1024.0 pairs
+    const uint32_t magic = opaque_v(0x64006400u);   // fp16 1024.0 pairs
     const bool xrow = c < M;                                    // lane supplies x row c
     // Step j of unit i: logical chunk 4 j + kc of row c, at position 4 j + (kc ^ c % 4).
     const uint8_t* xlane =
@@ -314,6 +329,10 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
                 }
 #undef W4_PX_WAIT
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (kCvtX) {   // the 16 bytes this lane's x load wrote, as fp16
+                    u32x4_t* const p = (u32x4_t*)(xsb + (uint32_t)i * 1024u + (uint32_t)lane * 16u);
+                    *p = bf16x8_to_f16x8(*p);
+                }
             }
         }
         if (tj == 0 && i < nu && xrow) {
@@ -373,30 +392,15 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
             for (int gi = 0; gi < NG; ++gi) {
                 const uint32_t zq = (sl.z[gi] >> zshift) & 15u;
                 float4_t acc = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (!BF16) {
-                    uint32_t nz1024 = 0xE400u + zq;          // fp16 -(1024 + z)
-                    nz1024 |= nz1024 << 16;
-                    uint32_t nz64 = 0xD400u + (zq << 4);     // fp16 -(64 + z)
-                    nz64 |= nz64 << 16;
+                uint32_t nz1024 = 0xE400u + zq;          // fp16 -(1024 + z)
+                nz1024 |= nz1024 << 16;
+                uint32_t nz64 = 0xD400u + (zq << 4);     // fp16 -(64 + z)
+                nz64 |= nz64 << 16;
 #pragma unroll
-                    for (int js = 0; js < SPU; ++js) {
-                        const int j = gi * SPU + js;
-                        const half8_t b = dequant_f16(sl.w[j], magic, nz1024, nz64);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(xa[j]), b, acc,
-                                                                     0, 0, 0);
-                    }
-                } else {
-                    uint32_t nb = 0xC300u + zq;              // bf16 -(128 + z)
-                    nb |= nb << 16;
-                    const bf16x8_t bias = bitcast<bf16x8_t>(u32x4_t{nb, nb, nb, nb});
-#pragma unroll
-                    for (int js = 0; js < SPU; ++js) {
-                        const int j = gi * SPU + js;
-                        const bf16x8_t av = bitcast<bf16x8_t>(xa[j]);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, biased_bf16(sl.w[j], magic),
-                                                                      acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bias, acc, 0, 0, 0);
-                    }
+                for (int js = 0; js < SPU; ++js) {
+                    const int j = gi * SPU + js;
+                    const half8_t b = dequant_f16(sl.w[j], magic, nz1024, nz64);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(xa[j]), b, acc, 0, 0, 0);
                 }
                 const float sf = f16_bits_to_f32((uint16_t)sl.s[gi]);
                 total[tj][0] = __builtin_fmaf(sf, acc[0], total[tj][0]);

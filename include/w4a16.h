@@ -122,9 +122,17 @@ int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* bytes);
  * 16) runs an M-tiled kernel whose waves split N and share x through LDS.
  * w4a16_last_variant() names the kernel that ran.
  * x_dtype: W4A16_F16 or W4A16_BF16.  y_dtype: W4A16_F32, W4A16_F16 or
- * W4A16_BF16 (rounded to nearest even from the fp32 result).  Products and
- * sums are fp32; the result is deterministic: the same inputs give the same
- * bits on every call and every graph replay.  workspace may be NULL when
+ * W4A16_BF16 (rounded to nearest even from the fp32 result).  q - z is formed
+ * exactly before any product (the integer placed in a 16-bit float's mantissa
+ * and a constant subtracted: Ninfer V100 article, section 十), so q = z gives
+ * exactly 0 and s -> 2s exactly 2y.  bf16 x is taken to fp16 on chip before
+ * the products: exact for every magnitude in [2^-17, 65280] and for zeros,
+ * rounded to fp16's 2^-24 grid below 2^-17 (a change under 2^-25 per
+ * element); magnitudes of 65536 and above are outside the contract (they
+ * overflow fp16).  A bf16 x therefore gives bit for bit the result of the
+ * fp16 x holding the same values.  Products and sums are fp32; the result is
+ * deterministic: the same inputs give the same bits on every call and every
+ * graph replay.  workspace may be NULL when
  * w4a16_workspace_bytes reports 0; otherwise it must hold that many bytes and
  * is scratch owned by the call while it runs (no zeroing needed).  x and y
  * must not overlap the weights or each other. */

@@ -103,10 +103,10 @@ def test_ingest_pmc_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     assert t["command"] == "test command"
 
 
-def test_headline_is_the_last_line_and_small(capsys):
+def test_headline_is_the_last_line_and_small(capsys, tmp_path):
     # A result shaped like a real run, with a large `extra` block: the last
     # stdout line is the compact headline, which parses and stays small; the
-    # detail goes to stderr.
+    # detail goes to a file.
     shape = {"us": 17.8, "GBps": 5206.6, "bytes": 92760064, "kernel": "k", "variant": "v" * 150}
     extra = {"pct_of_peak": 50.5, "bw_probe_GBps": 6331.0, "value_pct_of_probe": 63.8,
              "m1_per_shape": {n: dict(shape) for n in ("qkv", "o_proj", "gate_up", "down")},
@@ -119,7 +119,8 @@ def test_headline_is_the_last_line_and_small(capsys):
                            "frac": 0.6508, "traffic": 93053843},
               "cpu_baseline": {"value": 0.7, "unit": "GB/s", "cores": 16, "kind": "oracle",
                                "sample": "s"}}
-    bench.emit(result, extra)
+    out = tmp_path / "sub" / "extra.json"
+    bench.emit(result, extra, str(out))
     cap = capsys.readouterr()
     last = cap.out.strip().splitlines()[-1]
     assert len(last.encode()) <= bench.HEADLINE_MAX_BYTES
@@ -129,4 +130,5 @@ def test_headline_is_the_last_line_and_small(capsys):
         assert key in head
     assert "extra" not in head
     assert head["summary"]["m4_us"]["gate_up"] == 17.8
-    assert "skinny_sweep" in cap.err
+    assert json.loads(out.read_text())["skinny_sweep"][199]["M"] == 199
+    assert len(cap.err) < 200

@@ -433,47 +433,85 @@ def test_w2t_gemv_matches_oracle(M, N, K, g, xdt):
 
 # ----------------------------------------------------------- bitwise identities ---
 
-def test_w4_zero_point_identity_gives_exact_zero():
-    say("w4 q = z identity")
-    M, N, K, g = 4, 264, 1024, 128
-    rng = np.random.default_rng(7)
-    G = K // g
-    z = rng.integers(0, 16, size=(G, N))
+def _w4_constant_q(z, g, N, rng):
+    """Canonical arrays whose every weight equals its group's zero point."""
+    G = z.shape[0]
     q = np.repeat(z, g, axis=0)  # [K][N]
-    qweight = np.zeros((N, K // 8), dtype=np.uint32)
+    qweight = np.zeros((N, G * g // 8), dtype=np.uint32)
     for i in range(8):
         qweight |= (q[i::8].T.astype(np.uint32) << np.uint32(4 * i))
     zeros = np.zeros((G, N // 8), dtype=np.uint32)
     for i in range(8):
         zeros |= (z[:, i::8].astype(np.uint32) << np.uint32(4 * i))
-    w = {"qweight": qweight.view(np.int32), "zeros": zeros.view(np.int32),
-         "scales": synth.f64_to_f16_bits(rng.uniform(0.002, 0.02, size=(G, N)))}
-    assert np.all(oracle.w4_gemv(synth.gen_x((1,), M, K), "f16", w["qweight"], w["scales"],
-                                 w["zeros"], M, N, K, g) == 0)
-    P = PackedW4(w, N, K, g)
-    # fp16 activations: q - z is formed exactly in fp16, every product is 0.
-    y = P.gemv(dev(synth.gen_x((1,), M, K, "f16")), "f16", M)
+    return {"qweight": qweight.view(np.int32), "zeros": zeros.view(np.int32),
+            "scales": synth.f64_to_f16_bits(rng.uniform(0.002, 0.02, size=(G, N)))}
+
+
+# Kernels covered: the GEMV with x staged unit by unit (M <= 4, 3 units per
+# wave), with the whole range staged (M = 8), in K slices (narrow N, long K),
+# the M-tiled kernel (M = 32) and its K slices (M = 64, narrow N).
+IDENTITY_CASES = [(4, 264, 3072, 128), (1, 264, 3072, 64), (8, 264, 1024, 128),
+                  (4, 264, 17408, 128), (32, 520, 1024, 64), (64, 136, 4096, 128)]
+
+
+@pytest.mark.parametrize("M,N,K,g", IDENTITY_CASES)
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_w4_zero_point_identity_gives_exact_zero(M, N, K, g, xdt):
+    # q = z everywhere: every weight (q - z) * s is 0, so y is exactly 0 for
+    # either activation type -- q - z is formed exactly before any product.
+    say(f"w4 q = z identity M={M} N={N} K={K} g={g} x={xdt}")
+    rng = np.random.default_rng(7 + M + K)
+    w = _w4_constant_q(rng.integers(0, 16, size=(K // g, N)), g, N, rng)
+    x = synth.gen_x((1, M, K), M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    assert np.all(oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g) == 0)
+    y = PackedW4(w, N, K, g).gemv(dev(x), xdt, M)
+    torch.cuda.synchronize()
+    say("  variant: " + L.w4a16_last_variant())
     assert torch.count_nonzero(y).item() == 0
-    # bf16 activations: the zero point enters as a second MFMA against
-    # -(128 + z), so q = z cancels up to the fp32 rounding of the running sum
-    # of x * (128 + q): at most a few ulps of 143 * sum|x| per group, times s.
-    xb = synth.gen_x((1,), M, K, "bf16")
-    y = to_f64(P.gemv(dev(xb), "bf16", M))
-    xf = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    smax = w["scales"].view(np.float16).astype(np.float64).max()
-    bound = 2.0 ** -20 * 143 * np.abs(xf).sum(axis=1, keepdims=True) * smax
-    assert np.all(np.abs(y) <= bound)
 
 
-def test_w4_scale_doubling_is_bitwise():
-    say("w4 s -> 2s")
-    M, N, K, g = 4, 520, 2048, 128
-    w = synth.gen_w4((107,), N, K, g)
+@pytest.mark.parametrize("M,N,K,g", [(4, 520, 2048, 128), (8, 520, 2048, 64), (32, 264, 1024, 128)])
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_w4_scale_doubling_is_bitwise(M, N, K, g, xdt):
+    # s -> 2s doubles every weight exactly, and with it every fp32 partial
+    # sum: y doubles bit for bit.
+    say(f"w4 s -> 2s M={M} x={xdt}")
+    w = synth.gen_w4((107, M), N, K, g)
     w2 = dict(w, scales=(w["scales"].view(np.float16) * np.float16(2)).view(np.uint16))
-    x = dev(synth.gen_x((107,), M, K))
-    y1 = PackedW4(w, N, K, g).gemv(x, "f16", M)
-    y2 = PackedW4(w2, N, K, g).gemv(x, "f16", M)
+    x = dev(synth.gen_x((107, M), M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0))
+    y1 = PackedW4(w, N, K, g).gemv(x, xdt, M)
+    y2 = PackedW4(w2, N, K, g).gemv(x, xdt, M)
     assert torch.equal(y2, 2 * y1)
+
+
+@pytest.mark.parametrize("M,N,K,g", [(4, 520, 3072, 128), (8, 264, 2048, 64), (2, 136, 17408, 128),
+                                     (32, 264, 1024, 128)])
+def test_w4_bf16_x_equals_f16_x_bitwise(M, N, K, g):
+    # bf16 activations are taken to fp16 on chip (exact over fp16's range,
+    # round to nearest even below it), so a bf16 x gives bit for bit the
+    # result of the fp16 x holding the same values.  The x here spans the
+    # contract: N(0,1) with outliers, values at the largest bf16 below
+    # fp16's overflow (65280), at 2^-17 (the smallest exact magnitude) and
+    # below it, where both sides round to fp16's 2^-24 grid the same way.
+    say(f"w4 bf16 x = f16 x M={M} N={N} K={K} g={g}")
+    xb = synth.gen_x((108, M, K), M, K, "bf16", outlier_frac=0.01)
+    rng = np.random.default_rng(M + K)
+    special = np.array([65280.0, -65280.0, 2.0 ** -17, -(2.0 ** -17), 3 * 2.0 ** -20,
+                        2.0 ** -24 * 1.5, 2.0 ** -26], dtype=np.float32)
+    pos = rng.choice(M * K, size=special.size, replace=False)
+    xb = xb.copy().reshape(-1)
+    xb[pos] = (special.view(np.uint32) >> 16).astype(np.uint16)
+    xb = xb.reshape(M, K)
+    xf32 = (xb.astype(np.uint32) << 16).view(np.float32)
+    xh = xf32.astype(np.float16).view(np.uint16)
+    w = synth.gen_w4((108, N, K), N, K, g)
+    P = PackedW4(w, N, K, g)
+    yb = P.gemv(dev(xb), "bf16", M)
+    yh = P.gemv(dev(xh), "f16", M)
+    torch.cuda.synchronize()
+    assert torch.equal(yb, yh)
+    ref = oracle.w4_gemv(xb, "bf16", w["qweight"], w["scales"], w["zeros"], M, N, K, g)
+    assert_parity(to_f64(yb), ref, "bf16 range edges")
 
 
 def test_w4_one_hot_rows_are_exact():
@@ -940,6 +978,43 @@ def test_full_size_sampled_columns(name, K, N, M, xdt):
     cols = sample_cols(N, np.random.default_rng(N + M))
     ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g, cols=cols)
     assert_parity(y[:, cols], ref, name)
+
+
+_LM_HEAD = {}
+
+
+def _lm_head(g):
+    """The lm_head-like matrix (N = 152064, K = 5120) at group g, generated
+    and packed once per test module."""
+    if g not in _LM_HEAD:
+        _LM_HEAD.clear()
+        N, K = 152064, 5120
+        w = synth.gen_w4((115, g), N, K, g)
+        _LM_HEAD[g] = (w, PackedW4(w, N, K, g))
+    return _LM_HEAD[g]
+
+
+@pytest.mark.parametrize("g,M", [(64, m) for m in (1, 2, 3, 4, 6, 8)] +
+                         [(128, m) for m in (2, 3, 6)])
+def test_lm_head_sampled_columns(g, M):
+    # The skinny sweep's lm_head-like shape at every row count it measures:
+    # three 16-column tiles per workgroup (9504 tiles), x staged unit by unit
+    # up to 4 rows.  Columns include the tile and workgroup edges at both ends.
+    N, K = 152064, 5120
+    say(f"lm_head g={g} M={M}")
+    w, P = _lm_head(g)
+    x = synth.gen_x((115, g, M), M, K, "f16")
+    y = to_f64(P.gemv(dev(x), "f16", M))
+    variant = L.w4a16_last_variant()
+    say("  variant: " + variant)
+    assert "w4_gemv_kernel" in variant and "tpw=3" in variant and "slices=1 " in variant
+    assert ("px=1" in variant) == (M <= 4)
+    rng = np.random.default_rng(g + M)
+    cols = set(sample_cols(N, rng, n=160).tolist())
+    cols |= {31, 32, 47, 48, 49, 95, 96, N - 49, N - 48, N - 47, N - 33, N - 32}
+    cols = np.array(sorted(cols), dtype=np.int64)
+    ref = oracle.w4_gemv(x, "f16", w["qweight"], w["scales"], w["zeros"], M, N, K, g, cols=cols)
+    assert_parity(y[:, cols], ref, f"lm_head g{g} M{M}")
 
 
 @pytest.mark.parametrize("K,N", [(5120, 7168), (5120, 34816), (17408, 5120)])
