@@ -39,6 +39,7 @@ _SIGS = {
     "w4a16_unpack": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "w4a16_workspace_bytes": [_I, _I, _I, _I, _PSZ],
     "w4a16_gemv": [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P],
+    "w4a16_gemv_noalloc": [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P],
     "w4a16_gemv_add": [_P, _I, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _SZ, _P],
     "w16a16_workspace_bytes": [_I, _I, _I, _PSZ],
     "w16a16_gemv": [_P, _P, _I, _P, _I, _I, _I, _I, _P, _SZ, _P],
@@ -171,6 +172,16 @@ def w4a16_gemv(x, x_dtype, qweight, scales, zeros, y, y_dtype, M, N, K, group, w
     _check("w4a16_gemv", _lib.w4a16_gemv(_ptr(x), _dt(x_dtype), _ptr(qweight), _ptr(scales),
                                          _ptr(zeros), _ptr(y), _dt(y_dtype), M, N, K, group,
                                          _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def w4a16_gemv_noalloc(x, x_dtype, qweight, scales, zeros, y, y_dtype, M, N, K, group,
+                       stream=None):
+    _check("w4a16_gemv_noalloc", _lib.w4a16_gemv_noalloc(
+        _ptr(x), _dt(x_dtype), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(y), _dt(y_dtype),
+        M, N, K, group, _stream(stream)))
+
+
+W4A16_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def w4a16_gemv_add(x, x_dtype, qweight, scales, zeros, residual, residual_dtype, y, y_dtype, M, N, K,

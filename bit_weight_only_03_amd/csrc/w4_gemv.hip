@@ -993,6 +993,69 @@ extern "C" int w4a16_gemv_add(const void* x, int x_dtype, const void* qweight, c
                      group, workspace, workspace_bytes, stream);
 }
 
+// ---------------------------------------------------- no-allocation variant
+
+// The split-K workspace of w4a16_gemv_noalloc: a library-owned device array,
+// one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = W4A16_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+void* g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+
+// The device address of `scratch` on the current device, looked up the first
+// time this device is used (with that device current) and kept.
+int scratch_for_current_device(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) {
+        w4h::set_last_error("no usable current HIP device for the static scratch");
+        return W4A16_ERR_HIP;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) {
+        w4h::set_last_error(hipGetErrorName(g_scratch_err[dev]));
+        return W4A16_ERR_HIP;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" int w4a16_gemv_noalloc(const void* x, int x_dtype, const void* qweight, const void* scales,
+                                  const void* zeros, void* y, int y_dtype, int M, int N, int K,
+                                  int group, w4a16_stream_t stream) {
+    // Everything w4a16_gemv checks, then the workspace this shape needs
+    // against the static array -- all on the host, before any device work.
+    if (int rc = check_gemv_args(x, x_dtype, qweight, scales, zeros, y, y_dtype, M, N, K, group))
+        return rc;
+    size_t need = 0;
+    if (int rc = w4a16_workspace_bytes(M, N, K, group, &need)) return rc;
+    if (need > kNoAllocScratchBytes) {
+        char msg[96];
+        snprintf(msg, sizeof msg, "workspace of %zu bytes exceeds the %zu-byte static scratch", need,
+                 kNoAllocScratchBytes);
+        w4h::set_last_error(msg);
+        return W4A16_ERR_WORKSPACE;
+    }
+    void* ws = nullptr;
+    if (need) {
+        if (int rc = scratch_for_current_device(&ws)) return rc;
+    }
+    return gemv_impl(x, x_dtype, qweight, scales, zeros, nullptr, W4A16_F32, y, y_dtype, M, N, K, group,
+                     ws, need ? kNoAllocScratchBytes : 0, stream);
+}
+
 // ------------------------------------------------------------------ MXFP4
 
 namespace {

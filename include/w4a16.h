@@ -153,7 +153,27 @@ int w4a16_gemv_add(const void* x, int x_dtype, const void* qweight, const void* 
                    int M, int N, int K, int group, void* workspace, size_t workspace_bytes,
                    w4a16_stream_t stream);
 
-/* Debug / parity: the dequantized matrix w[K][N] = (q - z) * s as fp32 from the
+/* For callers that cannot allocate device memory -- code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc: w4a16_gemv with the
+ * same arguments, kernels and results (bit for bit), except that the split-K
+ * workspace is a library-owned static device array of
+ * W4A16_NOALLOC_SCRATCH_BYTES per GPU instead of a caller buffer.  The call
+ * allocates nothing (no hipMalloc, no library allocation).  Each GPU holds its
+ * array from its first use until the process ends; its address is looked up
+ * once per device, on the first call that needs it with that device current.
+ * The array needs no clearing: every byte a call reads was written earlier
+ * in the same call.  All calls on one GPU share that GPU's array, so calls
+ * that overlap in time on one GPU (for example on two streams) race and must
+ * be serialized by the caller.  Returns W4A16_ERR_WORKSPACE, before any GPU
+ * work, when the shape's workspace (w4a16_workspace_bytes) exceeds the array
+ * (w4a16_last_error() then says by how much), and the errors of w4a16_gemv
+ * otherwise. */
+#define W4A16_NOALLOC_SCRATCH_BYTES (16u << 20)
+int w4a16_gemv_noalloc(const void* x, int x_dtype, const void* qweight, const void* scales,
+                       const void* zeros, void* y, int y_dtype, int M, int N, int K, int group,
+                       w4a16_stream_t stream);
+
+/* Debug / parity: the dequantized matrix w[K][N] = (q - z) * s as fp32 from the/* Debug / parity: the dequantized matrix w[K][N] = (q - z) * s as fp32 from the
  * packed layout -- the integer restored with its group's zero point and
  * multiplied back by the group's scale (Ninfer V100 article, section 十一,
  * groupwise-int; Z100 article, section 四).  Exact, since |q - z| <= 15 times

@@ -221,3 +221,27 @@ def test_workspace_queries_follow_the_dispatch():
     # 4-bit: down at M = 4 in 4 slices; M = 8 at K = 5120 unsplit on the GEMV.
     assert lib.w4a16_workspace_bytes(4, 5120, 17408, 128) == 4 * 4 * 5120 * 4
     assert lib.w4a16_workspace_bytes(8, 5120, 5120, 128) == 0
+
+
+def test_noalloc_checks_return_before_any_device_work():
+    # The no-allocation GEMV refuses, on the host, a shape whose split-K
+    # workspace exceeds its static array (K = 2^24 at N = 8192: 1024 slices,
+    # 32 MiB of partials), naming the reason; the ordinary argument checks
+    # come first.  No GPU is touched (stream 0, fake aligned pointers).
+    M, N, K, g = 1, 8192, 1 << 24, 128
+    assert lib.w4a16_workspace_bytes(M, N, K, g) > lib.W4A16_NOALLOC_SCRATCH_BYTES
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.w4a16_gemv_noalloc(256, "f16", 256, 256, 256, 256, "f32", M, N, K, g, stream=0)
+    assert e.value.status == -5
+    assert "static scratch" in lib.w4a16_last_error()
+    for args, status in (((256, "f16", 256, 256, 256, None, "f32", 1, 64, 128, 128), -1),
+                         ((256, "f32", 256, 256, 256, 256, "f32", 1, 64, 128, 128), -4),
+                         ((256, "f16", 256, 256, 256, 256, "f32", 65, 64, 128, 128), -2),
+                         ((264, "f16", 256, 256, 256, 256, "f32", 1, 64, 128, 128), -3)):
+        with pytest.raises(lib.W4A16Error) as e:
+            lib.w4a16_gemv_noalloc(*args, stream=0)
+        assert e.value.status == status
+    # The header's array size and the binding's agree.
+    text = open(HEADER).read()
+    assert "#define W4A16_NOALLOC_SCRATCH_BYTES (16u << 20)" in text
+    assert lib.W4A16_NOALLOC_SCRATCH_BYTES == 16 << 20
