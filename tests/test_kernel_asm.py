@@ -55,7 +55,9 @@ def asm_files():
 
 
 def functions(text):
-    for m in re.finditer(r"^(_Z\w+):", text, re.M):
+    # Kernel symbols only (each ends at its .Lfunc_end label); data symbols
+    # such as a file-scope device array have no function body.
+    for m in re.finditer(r"^(_Z\w+):[ \t]*; @", text, re.M):
         end = text.index(".Lfunc_end", m.start())
         yield m.group(1), [l.strip() for l in text[m.start():end].split("\n") if l.strip()]
 
