@@ -173,7 +173,7 @@ int w4a16_gemv_noalloc(const void* x, int x_dtype, const void* qweight, const vo
                        const void* zeros, void* y, int y_dtype, int M, int N, int K, int group,
                        w4a16_stream_t stream);
 
-/* Debug / parity: the dequantized matrix w[K][N] = (q - z) * s as fp32 from the/* Debug / parity: the dequantized matrix w[K][N] = (q - z) * s as fp32 from the
+/* Debug / parity: the dequantized matrix w[K][N] = (q - z) * s as fp32 from the
  * packed layout -- the integer restored with its group's zero point and
  * multiplied back by the group's scale (Ninfer V100 article, section 十一,
  * groupwise-int; Z100 article, section 四).  Exact, since |q - z| <= 15 times

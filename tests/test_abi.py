@@ -245,3 +245,18 @@ def test_noalloc_checks_return_before_any_device_work():
     text = open(HEADER).read()
     assert "#define W4A16_NOALLOC_SCRATCH_BYTES (16u << 20)" in text
     assert lib.W4A16_NOALLOC_SCRATCH_BYTES == 16 << 20
+
+
+def test_header_compiles_cleanly_as_c_and_cpp(tmp_path):
+    # The header is the boundary's contract: it must compile warning-free on
+    # its own for C and C++ callers (no nested comments, no missing types).
+    import shutil
+    import subprocess
+    for cc, lang in (("gcc", "c"), ("g++", "c++")):
+        if not shutil.which(cc):
+            continue
+        src = tmp_path / f"use.{ 'c' if lang == 'c' else 'cpp'}"
+        src.write_text('#include "w4a16.h"\nint main(void) { return w4a16_status_string(0) ? 0 : 1; }\n')
+        res = subprocess.run([cc, "-fsyntax-only", "-Wall", "-Wextra", "-Werror", "-x", lang,
+                              f"-I{os.path.dirname(HEADER)}", str(src)], capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr
