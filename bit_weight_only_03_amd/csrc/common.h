@@ -222,7 +222,9 @@ __device__ __forceinline__ float mx_unit_scale(uint32_t emax) {
 // Raw buffer resources: a wave-uniform 128-bit descriptor (base, byte size)
 // lets every load take its lane offset from one VGPR and its unit offset from
 // an SGPR, with no per-load 64-bit address arithmetic.  Lanes whose
-// VGPR + immediate offset falls outside the byte size read zeros.
+// VGPR + immediate offset falls outside the byte size read zeros, and a
+// descriptor of byte size 0 reads zeros for every lane: the GEMV selects one
+// (on the scalar side) for a unit or tile that does not exist.
 constexpr int kRsrcFlags = 0x00020000;   // raw (untyped) 32-bit data, gfx9 family
 constexpr int kAuxNT = 2;                // non-temporal cache policy
 
@@ -286,6 +288,7 @@ struct Overrides {
     int w4_tpw = 0;            // W4A16_TPW: GEMV tiles per workgroup
     int w4_gemm_min_m = 0;     // W4A16_GEMM_MIN_M: rows from which the M-tiled kernel runs
     int w4_px = -1;            // W4A16_PX: 0 turns per-unit x staging off
+    int w4_valu = 0;           // W4A16_VALU: 1 runs the MFMA-free GEMV (up to 8 rows)
     int gemm_tn = 0;           // W4A16_GEMM_TN: tiles per wave of the M-tiled kernel
     int gemm_split = 0;        // W4A16_GEMM_SPLIT: K slices of the M-tiled kernel
     int w16_ksplit = -1;       // W16A16_KSPLIT: 0 turns the W16 K-split kernel off
@@ -313,6 +316,12 @@ inline int launch_status() {
 // y = the slice-order sum of S fp32 partials [S][M][N] (+ residual); N % 8 == 0.
 void launch_merge(const void* workspace, void* y, int y_dtype, const void* res, int res_dtype, int M,
                   int N, int S, hipStream_t st);
+
+// The MFMA-free GEMV (w4_gemv_valu.hip), an A/B alternative selected only by
+// the W4A16_VALU override.
+int valu_launch(const void* x, bool bf16, const void* qweight, const void* scales, const void* zeros,
+                void* out, int out_dtype, int M, int N, int K, int group, int upw, int S, size_t lds,
+                hipStream_t st);
 
 // The M-tiled path (w4_gemm.hip) for rows the GEMV does not take.
 constexpr int kMaxRowsGemm = 64;

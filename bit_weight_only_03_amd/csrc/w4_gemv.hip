@@ -193,7 +193,7 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     //    wave waits for them only after issuing its weight ring (below), so
     //    the two round trips overlap.
     if constexpr (!PX) {
-        const int cpr = a.xstride / 8;
+        constexpr int cpr = UPW * (kUnitK / 8);      // chunks per staged row (xstride = 128 UPW)
         const int live = nu * (kUnitK / 8);          // positions of a row this wave reads
         const int xch = M * cpr;
 #pragma unroll
@@ -230,9 +230,20 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
                   send);
     const __amdgpu_buffer_rsrc_t rz =
         make_rsrc(MX ? (const void*)qdev : (const void*)(zdev + (size_t)t0 * Gp * 2), zend);
+    // The same resources with no records: every load through them returns
+    // zeros.  A missing unit or tile selects these (a wave-uniform choice made
+    // on the scalar side), so each load's per-lane offset stays fixed and its
+    // unit offset is an SGPR: no vector instruction per load.
+    const __amdgpu_buffer_rsrc_t rw0 = make_rsrc(qdev, 0), rs0 = make_rsrc(sdev, 0),
+                                 rz0 = make_rsrc(qdev, 0), rx0 = make_rsrc(x, 0);
     const uint32_t wlane = (uint32_t)lane * 16u;
     const uint32_t slane = (uint32_t)c * 2u;
     const uint32_t zlane = (uint32_t)(c >> 3) * 4u;
+    // PX: this lane's x chunk of a unit is row lane / 16, position lane % 16;
+    // rows past M read past the end of x, i.e. zeros.
+    const uint32_t xlane_off = (lane >> 4) < M
+                                   ? (uint32_t)((lane >> 4) * K + 8 * ((lane & 15) ^ ((lane >> 4) & 3))) * 2u
+                                   : xbytes;
 
     // Chain position q = unit i (of this wave's range) x tile j, unit-major,
     // so one x fragment serves the workgroup's TPW tiles back to back.
@@ -241,26 +252,24 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
         const bool valid = i < nu && j < nt;
         const int u = w0 + i;
         if constexpr (PX) {
-            if (j == 0) {   // the unit's x: lane l -> row l / 16, position l % 16
-                const int m = lane >> 4, pc = lane & 15;
-                const int k = u * kUnitK + 8 * (pc ^ (m & 3));
-                const uint32_t off = (i < nu && m < M) ? (uint32_t)(m * K + k) * 2u : xbytes;
+            if (j == 0) {   // the unit's x: [4 rows][256 bytes] straight into LDS
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rx, (__attribute__((address_space(3))) void*)(xsb + i * 1024), 16, off, 0, 0, 0);
+                    i < nu ? rx : rx0, (__attribute__((address_space(3))) void*)(xsb + i * 1024), 16,
+                    xlane_off, (uint32_t)u * (kUnitK * 2u), 0, 0);
                 __builtin_amdgcn_sched_barrier(0);   // before the slot's own loads
             }
         }
         r.w = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
-            rw, valid ? wlane + (uint32_t)(j * U + u) * 1024u : wend, 0, kAuxNT));
+            valid ? rw : rw0, wlane, (uint32_t)(j * U + u) * 1024u, kAuxNT));
         if constexpr (MX) {
-            r.s = __builtin_amdgcn_raw_buffer_load_b32(
-                rs, valid ? (uint32_t)c * 4u + (uint32_t)(j * U + u) * 64u : send, 0, 0);
+            r.s = __builtin_amdgcn_raw_buffer_load_b32(valid ? rs : rs0, (uint32_t)c * 4u,
+                                                       (uint32_t)(j * U + u) * 64u, 0);
         } else {
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const int g = j * Gp + (u * 4) / SPG + gi;
-                r.s[gi] = __builtin_amdgcn_raw_buffer_load_b16(rs, valid ? slane + (uint32_t)g * 32u : send, 0, 0);
-                r.z[gi] = __builtin_amdgcn_raw_buffer_load_b32(rz, valid ? zlane + (uint32_t)g * 8u : zend, 0, 0);
+                r.s[gi] = __builtin_amdgcn_raw_buffer_load_b16(valid ? rs : rs0, slane, (uint32_t)g * 32u, 0);
+                r.z[gi] = __builtin_amdgcn_raw_buffer_load_b32(valid ? rz : rz0, zlane, (uint32_t)g * 8u, 0);
             }
         }
     };
@@ -799,6 +808,7 @@ void allow_full_lds() {
 }
 
 Plan make_plan(int M, int N, int K, int group, int cus, bool allow_px);
+Plan valu_plan(int M, int N, int K, int group);
 
 // Whether the M-tiled kernel (w4_gemm.hip) takes the call: every M above the
 // GEMV's 16, and below that from the measured crossover on.  Measured per
@@ -908,6 +918,11 @@ extern "C" int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* byt
     if (M < 1 || M > w4h::kMaxRowsGemm || !w4h::x_fits(M, K)) return W4A16_ERR_SHAPE;
     int rc = w4h::check_w4_shape(N, K, group);
     if (rc) return rc;
+    if (overrides().w4_valu == 1 && M <= 8) {
+        const Plan p = valu_plan(M, N, K, group);
+        *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
+        return W4A16_OK;
+    }
     if (use_gemm(M, N, K, group)) {
         *bytes = gemm_workspace(w4h::gemm_plan(M, N, K, group, w4h::cu_count()), M, N);
         return W4A16_OK;
@@ -919,16 +934,52 @@ extern "C" int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* byt
 
 namespace {
 
+// The MFMA-free GEMV (A/B only, W4A16_VALU=1): the GEMV planner's split and
+// x staging with one tile per workgroup.
+Plan valu_plan(int M, int N, int K, int group) {
+    Plan p = make_plan(M, N, K, group, w4h::cu_count(), false);
+    p.tpw = 1;
+    return p;
+}
+
+int launch_valu(const void* x, int x_dtype, const void* qweight, const void* scales, const void* zeros,
+                void* y, int y_dtype, int M, int N, int K, int group, void* workspace,
+                size_t workspace_bytes, hipStream_t st) {
+    const Plan p = valu_plan(M, N, K, group);
+    if (!p.upw || p.l.xstride != p.upw * kUnitK) return W4A16_ERR_UNSUPPORTED;
+    const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
+    if (need) {
+        if (!workspace) return W4A16_ERR_NULL;
+        if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
+        if (!w4h::aligned16(workspace)) return W4A16_ERR_ALIGN;
+    }
+    const bool bf16 = x_dtype == W4A16_BF16;
+    w4h::begin_launches();
+    int rc = w4h::valu_launch(x, bf16, qweight, scales, zeros, p.l.S > 1 ? workspace : y,
+                              p.l.S > 1 ? W4A16_F32 : y_dtype, M, N, K, group, p.upw, p.l.S, p.lds, st);
+    if (rc) return rc;
+    if (p.l.S > 1) w4h::launch_merge(workspace, y, y_dtype, nullptr, W4A16_F32, M, N, p.l.S, st);
+    w4h::set_last_variant("w4_valu %s g%d kernel=w4_gemv_valu_kernel<%s, %d, %d, %d> tiles=%d slices=%d "
+                          "waves=8 upw=%d lds=%zu",
+                          bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.upw,
+                          M == 1 ? 1 : 8, p.tiles, p.l.S, p.upw, p.lds);
+    return w4h::launch_status();
+}
+
 int gemv_impl(const void* x, int x_dtype, const void* qweight, const void* scales, const void* zeros,
               const void* res, int res_dtype, void* y, int y_dtype, int M, int N, int K, int group,
               void* workspace, size_t workspace_bytes, w4a16_stream_t stream) {
     int rc = check_gemv_args(x, x_dtype, qweight, scales, zeros, y, y_dtype, M, N, K, group);
     if (rc) return rc;
+    if (overrides().w4_valu == 1 && M <= 8 && !res)
+        return launch_valu(x, x_dtype, qweight, scales, zeros, y, y_dtype, M, N, K, group, workspace,
+                           workspace_bytes, (hipStream_t)stream);
     if (use_gemm(M, N, K, group))
         return launch_gemm(x, x_dtype, qweight, scales, zeros, y, y_dtype, res, res_dtype, M, N, K,
                            group, workspace, workspace_bytes, (hipStream_t)stream);
     Plan p = make_plan(M, N, K, group, w4h::cu_count(), true);
-    if (!p.upw) return W4A16_ERR_UNSUPPORTED;
+    // (The kernels stage x rows of exactly upw units: xstride = 128 upw.)
+    if (!p.upw || p.l.xstride != p.upw * kUnitK) return W4A16_ERR_UNSUPPORTED;
     const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     if (need) {
         if (!workspace) return W4A16_ERR_NULL;
@@ -1118,7 +1169,7 @@ extern "C" int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const
         return w4h::launch_status();
     }
     Plan p = make_plan(M, N, K, kMxPlanGroup, w4h::cu_count(), true);
-    if (!p.upw) return W4A16_ERR_UNSUPPORTED;
+    if (!p.upw || p.l.xstride != p.upw * kUnitK) return W4A16_ERR_UNSUPPORTED;
     const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
     if (need) {
         if (!workspace) return W4A16_ERR_NULL;

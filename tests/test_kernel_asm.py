@@ -29,7 +29,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "bit_weight_only_03_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["w4_gemv.hip", "w2t.hip", "w4_gemm.hip", "w16_gemv.hip"]
+SOURCES = ["w4_gemv.hip", "w2t.hip", "w4_gemm.hip", "w16_gemv.hip", "w4_gemv_valu.hip"]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
 
