@@ -186,7 +186,7 @@ class Sweep:
         self.bytes = sum(alg_bytes(M, N, K, GROUP) for (_, _, K, N, _) in self.mats_meta)
         # One workspace serves every call: calls on one stream run one after another.
         self.ws_bytes = max(L.w4a16_workspace_bytes(M, N, K, GROUP) for (_, _, K, N, _) in self.mats)
-        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda") if self.ws_bytes else None
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device="cuda") if self.ws_bytes else None
 
     @property
     def mats_meta(self):
@@ -364,7 +364,7 @@ def residual_fusion(L, torch, synth, oracle_mod, K, N, g, steps, warmup, stream,
     h = h0.clone()
     t = torch.empty((M, N), dtype=torch.float16, device="cuda")
     wsb = L.w4a16_workspace_bytes(M, N, K, g)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
 
     def fused(bufs):
         L.w4a16_gemv_add(x, "f16", *bufs, h, "f16", h, "f16", M, N, K, g, ws, wsb, stream)
@@ -424,7 +424,7 @@ def w16_sweep(L, torch, synth, oracle_mod, K, N, Ms, steps, warmup, stream, key)
         x = synth.gen_x_torch(key + (M,), M, K, "f16")
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         wsb = L.w16a16_workspace_bytes(M, N, K)
-        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
 
         def call(wm):
             L.w16a16_gemv(x, wm, "f16", y, "f32", M, N, K, ws, wsb, stream)
@@ -499,7 +499,7 @@ def rotation_sweep(L, torch, synth, oracle_mod, kind, K, N, g, Ms, steps, warmup
             wsb = L.mxfp4_workspace_bytes(M, N, K)
         else:
             wsb = L.w2t_workspace_bytes(M, N, K, g)
-        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
 
         def call(bufs):
             if kind == "w4":
