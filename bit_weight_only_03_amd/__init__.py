@@ -182,6 +182,8 @@ def w4a16_gemv_noalloc(x, x_dtype, qweight, scales, zeros, y, y_dtype, M, N, K, 
 
 
 W4A16_NOALLOC_SCRATCH_BYTES = 16 << 20
+# Arrival counters at the start of every workspace: zero before its first use.
+W4A16_WORKSPACE_HEAD_BYTES = 64 << 10
 
 
 def w4a16_gemv_add(x, x_dtype, qweight, scales, zeros, residual, residual_dtype, y, y_dtype, M, N, K,

@@ -241,6 +241,14 @@ namespace w4h {
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Every workspace begins with kWsHead bytes of arrival counters, zero before
+// the workspace's first use and left zero by every call; a call's fp32
+// partial sums follow them.  ws_bytes gives the workspace a call needs for
+// `partials` bytes of partial sums (0: none at all).
+constexpr size_t kWsHead = 64 * 1024;
+inline size_t ws_bytes(size_t partials) { return partials ? kWsHead + partials : 0; }
+inline void* ws_part(void* ws) { return ws ? (uint8_t*)ws + kWsHead : nullptr; }
+
 inline bool group_ok(int group) {
     return group == 32 || group == 64 || group == 128 || group == 256;
 }
@@ -289,6 +297,7 @@ struct Overrides {
     int w4_gemm_min_m = 0;     // W4A16_GEMM_MIN_M: rows from which the M-tiled kernel runs
     int w4_px = -1;            // W4A16_PX: 0 turns per-unit x staging off
     int w4_valu = 0;           // W4A16_VALU: 1 runs the MFMA-free GEMV (up to 8 rows)
+    int w4_bal = -1;           // W4A16_BAL: 0 turns the balanced GEMV plan off
     int gemm_tn = 0;           // W4A16_GEMM_TN: tiles per wave of the M-tiled kernel
     int gemm_split = 0;        // W4A16_GEMM_SPLIT: K slices of the M-tiled kernel
     int w16_ksplit = -1;       // W16A16_KSPLIT: 0 turns the W16 K-split kernel off

@@ -80,6 +80,7 @@ const Overrides& overrides() {
         geti("W4A16_GEMM_MIN_M", o.w4_gemm_min_m);
         geti("W4A16_PX", o.w4_px);
         geti("W4A16_VALU", o.w4_valu);
+        geti("W4A16_BAL", o.w4_bal);
         geti("W4A16_GEMM_TN", o.gemm_tn);
         geti("W4A16_GEMM_SPLIT", o.gemm_split);
         geti("W16A16_KSPLIT", o.w16_ksplit);

@@ -372,7 +372,7 @@ int check_w16(int M, int N, int K) {
 }
 
 size_t w16_workspace(const W16Plan& p, int M, int N) {
-    return !p.ksplit && p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0;
+    return w4h::ws_bytes(!p.ksplit && p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0);
 }
 
 void allow_w16_lds() {
@@ -428,8 +428,8 @@ extern "C" int w16a16_gemv(const void* x, const void* w, int dtype, void* y, int
     w4h::begin_launches();
     hipLaunchKernelGGL(bf16 ? pick_w16_rb<true>(p.rb) : pick_w16_rb<false>(p.rb),
                        dim3((unsigned)p.workgroups, p.split), dim3(64 * kW16Waves), 0, st,
-                       (const uint16_t*)x, (const uint16_t*)w, p.split > 1 ? workspace : y, l);
-    if (p.split > 1) w4h::launch_merge(workspace, y, y_dtype, nullptr, W4A16_F32, M, N, p.split, st);
+                       (const uint16_t*)x, (const uint16_t*)w, p.split > 1 ? w4h::ws_part(workspace) : y, l);
+    if (p.split > 1) w4h::launch_merge(w4h::ws_part(workspace), y, y_dtype, nullptr, W4A16_F32, M, N, p.split, st);
     w4h::set_last_variant("w16_mfma16 %s kernel=w16_gemv_kernel<%s, %d> tiles=%d slices=%d "
                           "workgroups=%lld",
                           bf16 ? "bf16" : "f16", bf16 ? "true" : "false", p.rb, T, p.split,

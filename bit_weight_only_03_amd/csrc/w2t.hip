@@ -683,7 +683,7 @@ int launch_direct(const void* x, int x_dtype, const void* qweight, const void* s
                   int y_dtype, int M, int N, int K, int group, void* workspace,
                   size_t workspace_bytes, w4a16_stream_t stream) {
     const PlanX p = make_planx(N, K);
-    const size_t need = p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0;
+    const size_t need = w4h::ws_bytes(p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0);
     if (need) {
         if (!workspace) return W4A16_ERR_NULL;
         if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
@@ -693,7 +693,7 @@ int launch_direct(const void* x, int x_dtype, const void* qweight, const void* s
     const int T = pad_n(N) / kTileN;
     const bool bf16 = x_dtype == W4A16_BF16;
     w2x_kernel_t k = bf16 ? pickx<true>(group) : pickx<false>(group);
-    void* out = p.split > 1 ? workspace : y;
+    void* out = p.split > 1 ? w4h::ws_part(workspace) : y;
     const int odt = p.split > 1 ? W4A16_F32 : y_dtype;
     w4h::begin_launches();
     hipLaunchKernelGGL(k, dim3(T, p.split), dim3(64 * p.waves), 0, st, (const uint16_t*)x,
@@ -701,7 +701,7 @@ int launch_direct(const void* x, int x_dtype, const void* qweight, const void* s
     if (p.split > 1) {
         const int MN = M * N;
         hipLaunchKernelGGL(w2_merge_kernel, dim3((MN + 255) / 256), dim3(256), 0, st,
-                           (const float*)workspace, y, y_dtype, MN, p.split);
+                           (const float*)w4h::ws_part(workspace), y, y_dtype, MN, p.split);
     }
     w4h::set_last_variant("w2t_mfma16 %s g%d kernel=w2t_gemv_direct_kernel<%s, %d, 4> tiles=%d "
                           "slices=%d waves=%d",
@@ -782,10 +782,10 @@ extern "C" int w2t_workspace_bytes(int M, int N, int K, int group, size_t* bytes
     if (rc) return rc;
     const Plan2 p = make_plan2(M, N, K, w4h::cu_count());
     if (use_staged(p)) {
-        *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
+        *bytes = w4h::ws_bytes(p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0);
     } else {
         const PlanX px = make_planx(N, K);
-        *bytes = px.split > 1 ? (size_t)px.split * M * N * sizeof(float) : 0;
+        *bytes = w4h::ws_bytes(px.split > 1 ? (size_t)px.split * M * N * sizeof(float) : 0);
     }
     return W4A16_OK;
 }
@@ -806,7 +806,7 @@ extern "C" int w2t_gemv(const void* x, int x_dtype, const void* qweight, const v
     Plan2 p = make_plan2(M, N, K, w4h::cu_count());
     if (!use_staged(p)) return launch_direct(x, x_dtype, qweight, scales, y, y_dtype, M, N, K, group,
                                              workspace, workspace_bytes, stream);
-    const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
+    const size_t need = w4h::ws_bytes(p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0);
     if (need) {
         if (!workspace) return W4A16_ERR_NULL;
         if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
@@ -816,7 +816,7 @@ extern "C" int w2t_gemv(const void* x, int x_dtype, const void* qweight, const v
     hipStream_t st = (hipStream_t)stream;
     const bool bf16 = x_dtype == W4A16_BF16;
     w2_kernel_t k = pick2(bf16, group, p.upw);
-    void* out = p.l.S > 1 ? workspace : y;
+    void* out = p.l.S > 1 ? w4h::ws_part(workspace) : y;
     p.l.out_dtype = p.l.S > 1 ? W4A16_F32 : y_dtype;
     w4h::begin_launches();
     hipLaunchKernelGGL(k, dim3(p.tiles, p.l.S), dim3(64 * p.waves), p.lds, st, (const uint16_t*)x,
@@ -824,7 +824,7 @@ extern "C" int w2t_gemv(const void* x, int x_dtype, const void* qweight, const v
     if (p.l.S > 1) {
         const int MN = M * N;
         hipLaunchKernelGGL(w2_merge_kernel, dim3((MN + 255) / 256), dim3(256), 0, st,
-                           (const float*)workspace, y, y_dtype, MN, p.l.S);
+                           (const float*)w4h::ws_part(workspace), y, y_dtype, MN, p.l.S);
     }
     w4h::set_last_variant("w2t_mfma16 %s g%d kernel=w2t_gemv_kernel<%s, %d, %d> tiles=%d slices=%d "
                           "waves=%d upw=%d lds=%zu",

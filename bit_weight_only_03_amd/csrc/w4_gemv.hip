@@ -56,6 +56,11 @@ using namespace w4k;
 namespace {
 
 constexpr int kMaxWaves = 8;     // waves per workgroup (the kernel's 512-thread launch bound)
+// Balanced plan: 8 waves streaming the workgroup's own tile in chains of 17
+// units, and 8 "extra" waves sharing a piece of a leftover tile in chains of
+// at most 5.
+constexpr int kBalFull = 8, kBalExtra = 8, kBalUpw = 17, kBalExtraUpw = 5, kBalMaxPieces = 4;
+constexpr int kCounterStride = 32;   // unsigneds between arrival counters (one per 128-byte line)
 constexpr int kMaxRows = 16;     // rows per MFMA
 constexpr int kMaxXLoads = 16;   // x load instructions per wave: M * 16 UPW <= 64 * 16
 
@@ -93,6 +98,12 @@ struct GemvLaunch {
     int out_dtype;
     const void* res;   // residual added to y (unsplit calls), or null
     int res_dtype;
+    // Balanced plan (BAL kernels only): bal_full waves of a workgroup own its
+    // whole tile; the others each take a share of one of bal_pieces pieces of
+    // a leftover tile (tiles bal_base and up), merged through the workspace.
+    int bal_full, bal_pieces, bal_base;
+    unsigned* counters;   // arrival counter of leftover tile i at i * kCounterStride, zero between calls
+    float* bal_part;      // [leftover tile][piece][M][16] piece partial sums
 };
 
 // Slots of the register ring for UPW units per wave: all loads are issued
@@ -101,67 +112,34 @@ struct GemvLaunch {
 template <int SPG>
 constexpr int max_slots() { return SPG >= 4 ? 9 : (SPG == 2 ? 7 : 5); }
 
-// One workgroup per (TPW 16-column tiles, K slice); its W waves split the
-// slice's 128-k units into contiguous ranges of at most UPW units.  Each wave
-//   1. starts staging its own range of x (all M rows, zeros past K) in its
-//      own LDS region, loading it straight into LDS -- no other wave's x is
-//      on its critical path;
-//   2. issues the loads of its chain of TPW x UPW units (16 weight bytes,
-//      scale and zero point per lane; unit-major, so one x fragment serves
-//      the TPW tiles back to back) -- all of them up front when the chain
-//      fits the register ring, otherwise with one refill per consumed slot
-//      on a fixed schedule, so the code is straight-line and every wait
-//      covers exactly one slot;
-//   3. dequantizes and multiplies each unit as its slot arrives;
-// then the waves add their partial sums through LDS in wave order and the
-// workgroup stores its tiles (or their fp32 slice partials).
-//
-// A wave whose range is shorter than UPW (or a workgroup with fewer than TPW
-// tiles left) gives its missing units an offset past the buffer resource's
-// size: such loads return zeros without touching memory, and the units are
-// skipped or add exactly zero.
-//
-// Eight waves per SIMD (at most 64 VGPRs) for the short chains, where the
-// register budget allows it without spilling.
-template <int SPG, int UPW>
-constexpr int min_waves() { return (SPG >= 4 && UPW <= 5) || (SPG == 2 && UPW <= 3) ? 8 : 1; }
-
-// MX = true runs MXFP4 weights (mxfp4.hip's device layout) instead: no zero
-// points, one E8M0 scale per 32-k block, which is exactly one MFMA step; the
-// scales fold into the element conversion where a unit's codes allow it and
-// apply step by step otherwise (mx_unit in common.h).  Its slot (5 VGPRs) is
-// the size of a g = 128 slot, so it is instantiated with SPG = 4 for the
-// register plan.
-// PX = true stages x unit by unit instead (up to 4 rows, K a multiple of
-// 128, unconditional arithmetic): each unit's x is one load of [4 rows][256
-// bytes] straight into LDS, issued with the unit's first ring slot, and the
-// wave waits for it just before the unit's products.  The first unit then
-// waits for its own 1 KB of x and not for the wave's whole range.
-template <bool BF16, int SPG, int UPW, int TPW, bool MX = false, bool PX = false>
-__global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4_gemv_kernel(
-    const uint16_t* __restrict__ x, const u32x4_t* __restrict__ qdev,
-    const uint16_t* __restrict__ sdev, const uint32_t* __restrict__ zdev, void* out,
-    GemvLaunch a) {
+// One wave's products: units [w0, w1) of tiles t0 .. t0 + nt - 1 of the
+// current K slice into total[], through a chain of CL units per tile (CL =
+// UPW except for the balanced plan's extra waves, which run a shorter chain).
+// xsb is the wave's LDS region (M rows of UPW units, or PX's per-unit slots).
+// BAR = 1 and 2 are the balanced plan's full and extra waves; an extra
+// wave's region holds M rows of CL units.  One workgroup barrier orders
+// their memory traffic: the extra waves pass it once all of their loads are
+// issued and the full waves before their first, so the extra waves' loads
+// are queued ahead (their shares are merged across workgroups and should
+// finish first).
+template <bool BF16, int SPG, int UPW, int TPW, bool MX, bool PX, int CL, int BAR = 0>
+__device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_t* __restrict__ x,
+                                              const u32x4_t* __restrict__ qdev,
+                                              const uint16_t* __restrict__ sdev,
+                                              const uint32_t* __restrict__ zdev, uint8_t* const xsb, int t0,
+                                              int nt, int w0, int w1, float4_t (&total)[TPW]) {
     constexpr int NG = SPG >= 4 ? 1 : 4 / SPG;          // groups per unit
     constexpr int SPU = SPG >= 4 ? 4 : SPG;             // steps per group inside one unit
-    constexpr int L = UPW * TPW;                         // units in this wave's chain
+    constexpr int L = CL * TPW;                          // units in this wave's chain
     constexpr int DM = TPW > 1 ? 5 : max_slots<SPG>();
     constexpr int D = L < DM ? L : DM;
-    constexpr bool kUncond = SPG >= 4 || (SPG == 2 && UPW <= 6) || UPW <= 2;
+    constexpr bool kUncond = SPG >= 4 || (SPG == 2 && CL <= 6) || CL <= 2;
     constexpr int LPS = MX ? 2 : 1 + 2 * NG;              // loads per ring slot
     using SlotT = typename SlotSel<NG, MX>::type;
-    static_assert(!PX || (kUncond && D <= 9), "per-unit x staging needs a straight-line ring");
     constexpr bool kCvtX = BF16 && !MX;   // bf16 x taken to fp16 in LDS for the 4-bit products
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-
+    constexpr int XU = BAR == 2 ? CL : UPW;   // units per staged row (= xstride / 128 otherwise)
     const int M = a.M, K = a.K, U = a.U;
-    const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int t0 = blockIdx.x * TPW, split = blockIdx.y;
-    const int nt = a.T - t0 < TPW ? a.T - t0 : TPW;                   // tiles of this workgroup
-    const int r0 = split * U / a.S, r1 = (split + 1) * U / a.S;
-    const int w0 = r0 + wave * (r1 - r0) / W, w1 = r0 + (wave + 1) * (r1 - r0) / W;
     const int nu = w1 - w0;                                           // units of this wave
     const int Gp = U * kUnitK / (SPG * 32);
     const int c = lane & 15, kc = lane >> 4;
@@ -179,7 +157,6 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     // up to M = 8 at K = 5120).
     // PX: wave w's region is [UPW units][4 rows][256 bytes] at w UPW 1024
     // bytes, the same chunk swizzle inside each row.
-    uint8_t* const xsb = smem + (PX ? (size_t)wave * UPW * 1024 : (size_t)wave * M * a.xstride * 2);
     const uint32_t xbytes = (uint32_t)M * (uint32_t)K * 2u;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xbytes);
 
@@ -192,12 +169,14 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     //    first memory accesses; where its arithmetic is unconditional the
     //    wave waits for them only after issuing its weight ring (below), so
     //    the two round trips overlap.
+    constexpr int kXL = kMaxXLoads;
+    if constexpr (BAR == 1) __builtin_amdgcn_s_barrier();
     if constexpr (!PX) {
-        constexpr int cpr = UPW * (kUnitK / 8);      // chunks per staged row (xstride = 128 UPW)
+        constexpr int cpr = XU * (kUnitK / 8);       // chunks per staged row
         const int live = nu * (kUnitK / 8);          // positions of a row this wave reads
         const int xch = M * cpr;
 #pragma unroll
-        for (int i = 0; i < kMaxXLoads; ++i) {
+        for (int i = 0; i < kXL; ++i) {
             if (i * 64 < xch) {                    // wave-uniform
                 const int ci = i * 64 + lane;
                 const int m = ci / cpr, pc = ci % cpr;
@@ -280,6 +259,10 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
         load_slot(i, ring[i]);
         __builtin_amdgcn_sched_barrier(0);   // slots issue in ring order
     }
+    if constexpr (BAR == 2) {
+        __builtin_amdgcn_s_barrier();   // no wait: the loads stay in flight
+        __builtin_amdgcn_sched_barrier(0);
+    }
     // Vector memory loads complete in issue order, so once no more than the
     // ring's D * LPS loads are outstanding, every x load issued before
     // them has landed in LDS.  This needs every ring load issued here, after
@@ -292,15 +275,24 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     __builtin_amdgcn_sched_barrier(0);
     // bf16 x: each lane rewrites the chunks its own x loads filled as fp16.
     if constexpr (kCvtX && !PX) {
-        const int cpr = a.xstride / 8, live = nu * (kUnitK / 8), xch = M * cpr;
+        // Four positions per lane at a time: their LDS reads are all issued
+        // before the first conversion waits.
+        constexpr int cpr = XU * (kUnitK / 8);       // as in the staging above
+        const int live = nu * (kUnitK / 8), xch = M * cpr;
 #pragma unroll
-        for (int i = 0; i < kMaxXLoads; ++i) {
-            if (i * 64 < xch) {
-                const int ci = i * 64 + lane;
-                if (ci / cpr < M && ci % cpr < live) {
-                    u32x4_t* const p = (u32x4_t*)(xsb + (uint32_t)ci * 16u);
-                    *p = bf16x8_to_f16x8(*p);
+        for (int i0 = 0; i0 < kXL; i0 += 4) {
+            if (i0 * 64 < xch) {
+                u32x4_t v[4];
+                bool ok[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int ci = (i0 + k) * 64 + lane;
+                    ok[k] = i0 + k < kXL && ci < xch && ci % cpr < live;
+                    if (ok[k]) v[k] = *(const u32x4_t*)(xsb + (uint32_t)ci * 16u);
                 }
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (ok[k]) *(u32x4_t*)(xsb + (uint32_t)((i0 + k) * 64 + lane) * 16u) = bf16x8_to_f16x8(v[k]);
             }
         }
     }
@@ -312,9 +304,8 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
     // Step j of unit i: logical chunk 4 j + kc of row c, at position 4 j + (kc ^ c % 4).
     const uint8_t* xlane =
         xsb + (PX ? (uint32_t)(c * 256 + 16 * (kc ^ (c & 3)))
-                  : (uint32_t)(c * a.xstride + 8 * (kc ^ (c & 3))) * 2u);
+                  : (uint32_t)(c * XU * kUnitK + 8 * (kc ^ (c & 3))) * 2u);
     constexpr uint32_t kXUnit = PX ? 1024u : (uint32_t)kUnitK * 2;   // bytes between units of a row
-    float4_t total[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) total[j] = float4_t{0.f, 0.f, 0.f, 0.f};
     u32x4_t xa[4] = {};
@@ -434,36 +425,216 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 1 : min_waves<SPG, UPW>())) void w4
         __builtin_amdgcn_sched_barrier(0);   // units in order: each waits for its own slot only
     }
 
+}
+
+// One workgroup per (TPW 16-column tiles, K slice); its W waves split the
+// slice's 128-k units into contiguous ranges of at most UPW units.  Each wave
+//   1. starts staging its own range of x (all M rows, zeros past K) in its
+//      own LDS region, loading it straight into LDS -- no other wave's x is
+//      on its critical path;
+//   2. issues the loads of its chain of TPW x UPW units (16 weight bytes,
+//      scale and zero point per lane; unit-major, so one x fragment serves
+//      the TPW tiles back to back) -- all of them up front when the chain
+//      fits the register ring, otherwise with one refill per consumed slot
+//      on a fixed schedule, so the code is straight-line and every wait
+//      covers exactly one slot;
+//   3. dequantizes and multiplies each unit as its slot arrives;
+// then the waves add their partial sums through LDS in wave order and the
+// workgroup stores its tiles (or their fp32 slice partials).
+//
+// A wave whose range is shorter than UPW (or a workgroup with fewer than TPW
+// tiles left) gives its missing units an offset past the buffer resource's
+// size: such loads return zeros without touching memory, and the units are
+// skipped or add exactly zero.
+//
+// Eight waves per SIMD (at most 64 VGPRs) for the short chains, where the
+// register budget allows it without spilling.
+template <int SPG, int UPW>
+constexpr int min_waves() { return (SPG >= 4 && UPW <= 5) || (SPG == 2 && UPW <= 3) ? 8 : 1; }
+
+// MX = true runs MXFP4 weights (mxfp4.hip's device layout) instead: no zero
+// points, one E8M0 scale per 32-k block, which is exactly one MFMA step; the
+// scales fold into the element conversion where a unit's codes allow it and
+// apply step by step otherwise (mx_unit in common.h).  Its slot (5 VGPRs) is
+// the size of a g = 128 slot, so it is instantiated with SPG = 4 for the
+// register plan.
+// PX = true stages x unit by unit instead (up to 4 rows, K a multiple of
+// 128, unconditional arithmetic): each unit's x is one load of [4 rows][256
+// bytes] straight into LDS, issued with the unit's first ring slot, and the
+// wave waits for it just before the unit's products.  The first unit then
+// waits for its own 1 KB of x and not for the wave's whole range.
+// BAL = true runs the balanced plan: one workgroup per CU of 16 waves, 8 of
+// which stream the workgroup's own tile while 8 split one piece of a leftover
+// tile (see the planner); TPW = 1, whole-range x staging, up to 2 rows.
+template <bool BF16, int SPG, int UPW, int TPW, bool MX = false, bool PX = false, bool BAL = false>
+__global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<SPG, UPW>())) void w4_gemv_kernel(
+    const uint16_t* __restrict__ x, const u32x4_t* __restrict__ qdev,
+    const uint16_t* __restrict__ sdev, const uint32_t* __restrict__ zdev, void* out,
+    GemvLaunch a) {
+    constexpr int DM = TPW > 1 ? 5 : max_slots<SPG>();
+    constexpr bool kUncond = SPG >= 4 || (SPG == 2 && UPW <= 6) || UPW <= 2;
+    static_assert(!PX || (kUncond && (UPW * TPW < DM ? UPW * TPW : DM) <= 9),
+                  "per-unit x staging needs a straight-line ring");
+    static_assert(!BAL || (TPW == 1 && !PX && !MX && kUncond && kBalExtraUpw <= UPW),
+                  "the balanced plan runs one tile, whole-range x");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int M = a.M, U = a.U;
+    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    int t0 = blockIdx.x * TPW;
+    const int split = blockIdx.y;
+    int nt = a.T - t0 < TPW ? a.T - t0 : TPW;                         // tiles of this workgroup
+    const int r0 = split * U / a.S, r1 = (split + 1) * U / a.S;
+    int w0 = r0 + wave * (r1 - r0) / W, w1 = r0 + (wave + 1) * (r1 - r0) / W;
+    // Balanced plan: waves 0 .. bal_full - 1 split the workgroup's own tile
+    // over K; each later ("extra") wave takes a share of piece blockIdx.x %
+    // bal_pieces of leftover tile bal_base + blockIdx.x / bal_pieces.
+    const bool extra = BAL && wave >= a.bal_full;
+    // Balanced plan LDS: the full waves' x regions (M rows of UPW units
+    // each), the extra waves' (M rows of kBalExtraUpw units), the full
+    // waves' partial sums [bal_full][M][16], the extra waves'
+    // [kBalExtra][M][16], and the extra waves' arrival count.
+    uint8_t* const xextra = smem + (size_t)a.bal_full * M * a.xstride * 2;
+    float* const fullp = (float*)(xextra + (size_t)kBalExtra * M * kBalExtraUpw * kUnitK * 2);
+    float* const extrap = fullp + (size_t)a.bal_full * M * kTileN;
+    unsigned* const lcount = (unsigned*)(extrap + (size_t)kBalExtra * M * kTileN);
+    if constexpr (BAL) {
+        // The count is zeroed before the chains' barriers (nothing else is
+        // in flight yet).
+        if (threadIdx.x == 0) *lcount = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        const int WF = a.bal_full;
+        if (!extra) {
+            w0 = wave * U / WF;
+            w1 = (wave + 1) * U / WF;
+        } else {
+            const int P = a.bal_pieces, WE = W - WF, pc = blockIdx.x % P, e = wave - WF;
+            const int pa = pc * U / P, pb = (pc + 1) * U / P;
+            t0 = a.bal_base + blockIdx.x / P;
+            w0 = pa + e * (pb - pa) / WE;
+            w1 = pa + (e + 1) * (pb - pa) / WE;
+        }
+        nt = 1;
+    }
+    // LDS: wave w's x range, [M][16 UPW chunks of 16 bytes] at byte
+    // 2 w M xstride; PX: [UPW units][4 rows][256 bytes] at w UPW 1024 bytes
+    // (the layouts are described in w4_wave_chain).
+    uint8_t* const xsb = extra ? xextra + (size_t)(wave - a.bal_full) * M * kBalExtraUpw * kUnitK * 2
+                               : smem + (PX ? (size_t)wave * UPW * 1024 : (size_t)wave * M * a.xstride * 2);
+    const int c = lane & 15, kc = lane >> 4;
+    float4_t total[TPW];
+    if constexpr (BAL) {
+        if (extra)
+            w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, kBalExtraUpw, 2>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0,
+                                                                         w1, total);
+        else
+            w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, UPW, 1>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0, w1, total);
+    } else {
+        w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, UPW>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0, w1, total);
+    }
+
     // 4) Wave partials (lane l holds rows 4*(l/16) + r of column l % 16) ->
     //    [TPW][M][16] floats at the start of the wave's own x region (TPW M
     //    64 <= M UPW 256 bytes; its last x reads were consumed above, and a
     //    wave's LDS accesses complete in order), then M x 16 threads add
-    //    them in wave order and store.
-    float* const red = (float*)xsb;
-    const size_t rstride = PX ? (size_t)UPW * 1024 / 4 : (size_t)M * a.xstride / 2;   // floats between wave regions
+    //    them in wave order and store.  The balanced plan's waves use
+    //    partial areas of their own instead.
+    float* const red = !BAL ? (float*)xsb
+                            : (extra ? extrap + (size_t)(wave - a.bal_full) * M * kTileN
+                                     : fullp + (size_t)wave * M * kTileN);
+    const float* const red0 = BAL ? fullp : (const float*)smem;
+    const size_t rstride = BAL  ? (size_t)M * kTileN
+                           : PX ? (size_t)UPW * 1024 / 4
+                                : (size_t)M * a.xstride / 2;   // floats between wave partials
+    if constexpr (BAL) {
+        if (extra) {
+            // This wave's share of a leftover tile.  The workgroup's extra
+            // waves first add their partial sums through LDS: each writes
+            // them to its own partial area and counts itself in; the last to arrive
+            // adds the kBalExtra partials in wave order, stores that sum
+            // (coherent across the device) as the workgroup's piece of the
+            // tile and counts the piece in the tile's arrival counter; the
+            // last piece to arrive adds the P pieces in piece order and
+            // stores the tile's outputs.  The extra waves' shares are about a
+            // quarter of a full wave's units, so all of this runs while the
+            // full waves still stream.
+            const int P = a.bal_pieces;
+            const int lt = t0 - a.bal_base, pc = blockIdx.x % P;
+            if (kc == 0) {
 #pragma unroll
-    for (int j = 0; j < TPW; ++j)
+                for (int r = 0; r < 4; ++r)
+                    if (r < M) red[r * kTileN + c] = total[0][r];
+            }
+            unsigned wold = 0;
+            if (lane == 0) wold = __hip_atomic_fetch_add(lcount, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+            wold = __builtin_amdgcn_readfirstlane(wold);
+            if (wold == kBalExtra - 1) {
+                float* const piece = a.bal_part + (size_t)lt * P * M * kTileN;
+                if (lane < M * kTileN) {
+                    float pw[kBalExtra];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 4 * kc + r;
-            if (m < M) red[(j * M + m) * kTileN + c] = total[j][r];
+                    for (int e = 0; e < kBalExtra; ++e) pw[e] = extrap[e * M * kTileN + lane];
+                    float v = 0.f;
+#pragma unroll
+                    for (int e = 0; e < kBalExtra; ++e) v += pw[e];
+                    __hip_atomic_store(piece + (size_t)pc * M * kTileN + lane, v, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+                __builtin_amdgcn_s_waitcnt(0);   // the piece's store is done before it is counted
+                unsigned* const counter = a.counters + (size_t)lt * kCounterStride;
+                unsigned old = 0;
+                if (lane == 0) old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                old = __builtin_amdgcn_readfirstlane(old);
+                if (old == (unsigned)(P - 1)) {
+                    if (lane < M * kTileN) {
+                        // Every piece is loaded before the first add; positions
+                        // past P reload the last piece and are not added.
+                        float pv[kBalMaxPieces];
+#pragma unroll
+                        for (int q2 = 0; q2 < kBalMaxPieces; ++q2)
+                            pv[q2] = __hip_atomic_load(piece + (size_t)(q2 < P ? q2 : P - 1) * M * kTileN + lane,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        float v = 0.f;
+#pragma unroll
+                        for (int q2 = 0; q2 < kBalMaxPieces; ++q2) v = q2 < P ? v + pv[q2] : v;
+                        const int m = lane >> 4, n = t0 * kTileN + (lane & 15);
+                        if (n < a.N) {
+                            const size_t o = (size_t)m * a.N + n;
+                            store_out(out, a.out_dtype, o, add_residual(v, a.res, a.res_dtype, o));
+                        }
+                    }
+                    if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
         }
+    }
+    if (!extra) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * kc + r;
+                if (m < M) red[(j * M + m) * kTileN + c] = total[j][r];
+            }
+    }
     __syncthreads();
-    const float* const red0 = (const float*)smem;
     for (int idx = threadIdx.x; idx < TPW * M * kTileN; idx += blockDim.x) {
         const int j = idx / (M * kTileN), rem = idx % (M * kTileN);
         const int m = rem >> 4, cc = rem & 15;
         // All W partials are read before the first add (one LDS round trip),
         // then added in wave order.
         float v = 0.f;
-        if (W == kMaxWaves) {
+        const int WR = BAL ? a.bal_full : W;   // waves holding this tile's partials
+        if (WR == kMaxWaves) {
             float pw[kMaxWaves];
 #pragma unroll
             for (int w = 0; w < kMaxWaves; ++w) pw[w] = red0[w * rstride + (j * M + m) * kTileN + cc];
 #pragma unroll
             for (int w = 0; w < kMaxWaves; ++w) v += pw[w];
         } else {
-            for (int w = 0; w < W; ++w) v += red0[w * rstride + (j * M + m) * kTileN + cc];
+            for (int w = 0; w < WR; ++w) v += red0[w * rstride + (j * M + m) * kTileN + cc];
         }
         const int n = (t0 + j) * kTileN + cc;
         if (j < nt && n < a.N) {
@@ -810,6 +981,54 @@ void allow_full_lds() {
 Plan make_plan(int M, int N, int K, int group, int cus, bool allow_px);
 Plan valu_plan(int M, int N, int K, int group);
 
+// The balanced plan, for calls of up to 3 rows on layers of C + r tiles (C
+// CUs, C a multiple of r) whose K is 8 x 17 units: one workgroup per CU of 8
+// "full" waves, which split the workgroup's own tile over K as the GEMV does,
+// and 8 "extra" waves, which split one of P = C / r pieces of a leftover
+// tile (tile C + b / P, piece b % P).  Every CU then streams the same bytes
+// (the 27B down shape: 1.25 tiles each, where one tile per workgroup gives
+// 64 CUs two tiles and the rest one).  The extra waves' shares are a quarter
+// of a full wave's and their loads are issued first, so their partial sums
+// are merged (in LDS within the workgroup, then across the P workgroups
+// through an arrival counter per leftover tile, the last arrival adding the
+// pieces in a fixed order) while the full waves still stream.  The extra
+// waves run a chain of at most kBalExtraUpw units, a compile-time length, so
+// their code stays straight-line.
+
+struct BalPlan {
+    bool ok = false;
+    int pieces = 0, base = 0;
+    size_t lds = 0, ws = 0;
+};
+
+BalPlan bal_plan(int M, int N, int K, int group, int cus) {
+    BalPlan b;
+    if (w4h::overrides().w4_bal == 0) return b;
+    const int U = (K + kUnitK - 1) / kUnitK, T = pad_n(N) / kTileN;
+    // g = 128 only: at g = 64 a 17-unit chain does not fit the register
+    // budget of unconditional arithmetic, which the x wait's overlap needs.
+    // The full waves hold all of x, kBalUpw units each.  M = 4 does not fit
+    // LDS with the extra waves' x besides.
+    if (M > 3 || group != 128 || K % kUnitK) return b;
+    if (U != kBalFull * kBalUpw) return b;
+    const int r = T - cus;
+    if (r <= 0 || r >= cus || cus % r) return b;
+    const int P = cus / r;
+    if (P > kBalMaxPieces || U / P < kBalExtra) return b;
+    if (((U + P - 1) / P + kBalExtra - 1) / kBalExtra > kBalExtraUpw) return b;   // extra waves' chain
+    // the full and extra waves' x regions, both partial areas, the extra
+    // waves' count
+    b.lds = (size_t)M * kUnitK * 2 * (kBalFull * kBalUpw + kBalExtra * kBalExtraUpw) +
+            (size_t)(kBalFull + kBalExtra) * M * kTileN * 4 + 16;
+    if (b.lds > 160 * 1024) return b;
+    if ((size_t)r * kCounterStride * sizeof(unsigned) > w4h::kWsHead) return b;
+    b.ok = true;
+    b.pieces = P;
+    b.base = cus;
+    b.ws = w4h::ws_bytes((size_t)r * P * M * kTileN * sizeof(float));   // counters, then [tile][piece][M][16]
+    return b;
+}
+
 // Whether the M-tiled kernel (w4_gemm.hip) takes the call: every M above the
 // GEMV's 16, and below that from the measured crossover on.  Measured per
 // call on the 27B-class layers (us, GEMV / tiled):
@@ -835,7 +1054,7 @@ bool use_gemm(int M, int N, int K, int group) {
 }
 
 size_t gemm_workspace(const w4h::GemmPlan& p, int M, int N) {
-    return p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0;
+    return w4h::ws_bytes(p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0);
 }
 
 int check_gemv_args(const void* x, int x_dtype, const void* q, const void* s, const void* z,
@@ -885,8 +1104,8 @@ int launch_gemm(const void* x, int x_dtype, const void* qweight, const void* sca
     const bool bf16 = x_dtype == W4A16_BF16;
     w4h::begin_launches();
     w4h::gemm_launch(p, x, bf16, qweight, scales, zeros, y, y_dtype, res, res_dtype, M, N, K, group,
-                     workspace, st);
-    if (p.split > 1) w4h::launch_merge(workspace, y, y_dtype, res, res_dtype, M, N, p.split, st);
+                     w4h::ws_part(workspace), st);
+    if (p.split > 1) w4h::launch_merge(w4h::ws_part(workspace), y, y_dtype, res, res_dtype, M, N, p.split, st);
     char v[160];
     format_gemm(v, sizeof v, bf16, group, N, p);
     w4h::set_last_variant("%s", v);
@@ -920,7 +1139,11 @@ extern "C" int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* byt
     if (rc) return rc;
     if (overrides().w4_valu == 1 && M <= 8) {
         const Plan p = valu_plan(M, N, K, group);
-        *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
+        *bytes = w4h::ws_bytes(p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0);
+        return W4A16_OK;
+    }
+    if (const BalPlan b = bal_plan(M, N, K, group, w4h::cu_count()); b.ok) {
+        *bytes = b.ws;
         return W4A16_OK;
     }
     if (use_gemm(M, N, K, group)) {
@@ -928,7 +1151,7 @@ extern "C" int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* byt
         return W4A16_OK;
     }
     const Plan p = make_plan(M, N, K, group, w4h::cu_count(), true);
-    *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
+    *bytes = w4h::ws_bytes(p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0);
     return W4A16_OK;
 }
 
@@ -947,7 +1170,7 @@ int launch_valu(const void* x, int x_dtype, const void* qweight, const void* sca
                 size_t workspace_bytes, hipStream_t st) {
     const Plan p = valu_plan(M, N, K, group);
     if (!p.upw || p.l.xstride != p.upw * kUnitK) return W4A16_ERR_UNSUPPORTED;
-    const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
+    const size_t need = w4h::ws_bytes(p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0);
     if (need) {
         if (!workspace) return W4A16_ERR_NULL;
         if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
@@ -955,14 +1178,59 @@ int launch_valu(const void* x, int x_dtype, const void* qweight, const void* sca
     }
     const bool bf16 = x_dtype == W4A16_BF16;
     w4h::begin_launches();
-    int rc = w4h::valu_launch(x, bf16, qweight, scales, zeros, p.l.S > 1 ? workspace : y,
+    int rc = w4h::valu_launch(x, bf16, qweight, scales, zeros, p.l.S > 1 ? w4h::ws_part(workspace) : y,
                               p.l.S > 1 ? W4A16_F32 : y_dtype, M, N, K, group, p.upw, p.l.S, p.lds, st);
     if (rc) return rc;
-    if (p.l.S > 1) w4h::launch_merge(workspace, y, y_dtype, nullptr, W4A16_F32, M, N, p.l.S, st);
+    if (p.l.S > 1) w4h::launch_merge(w4h::ws_part(workspace), y, y_dtype, nullptr, W4A16_F32, M, N, p.l.S, st);
     w4h::set_last_variant("w4_valu %s g%d kernel=w4_gemv_valu_kernel<%s, %d, %d, %d> tiles=%d slices=%d "
                           "waves=8 upw=%d lds=%zu",
                           bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.upw,
                           M == 1 ? 1 : 8, p.tiles, p.l.S, p.upw, p.lds);
+    return w4h::launch_status();
+}
+
+template <bool BF16>
+w4_kernel_t pick_bal() {
+    return w4_gemv_kernel<BF16, 4, kBalUpw, 1, false, false, true>;
+}
+
+void format_bal(char* b, size_t n, bool bf16, int group, int N, const BalPlan& bp) {
+    snprintf(b, n,
+             "w4_bal16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, 1, false, false, true> tiles=%d "
+             "workgroups=%d waves=%d+%d pieces=%d lds=%zu",
+             bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, kBalUpw,
+             pad_n(N) / kTileN, bp.base, kBalFull, kBalExtra, bp.pieces, bp.lds);
+}
+
+int launch_bal(const BalPlan& bp, const void* x, int x_dtype, const void* qweight, const void* scales,
+               const void* zeros, const void* res, int res_dtype, void* y, int y_dtype, int M, int N, int K,
+               int group, void* workspace, size_t workspace_bytes, hipStream_t st) {
+    if (!workspace) return W4A16_ERR_NULL;
+    if (workspace_bytes < bp.ws) return W4A16_ERR_WORKSPACE;
+    if (!w4h::aligned16(workspace)) return W4A16_ERR_ALIGN;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        (void)hipFuncSetAttribute((const void*)pick_bal<false>(), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)kLdsPerCu);
+        (void)hipFuncSetAttribute((const void*)pick_bal<true>(), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)kLdsPerCu);
+        (void)hipGetLastError();
+    });
+    const bool bf16 = x_dtype == W4A16_BF16;
+    const int U = (K + kUnitK - 1) / kUnitK, T = pad_n(N) / kTileN;
+    GemvLaunch l{M, N, K, U, 1, T, kBalUpw * kUnitK, y_dtype, res, res_dtype};
+    l.bal_full = kBalFull;
+    l.bal_pieces = bp.pieces;
+    l.bal_base = bp.base;
+    l.counters = (unsigned*)workspace;
+    l.bal_part = (float*)w4h::ws_part(workspace);
+    w4h::begin_launches();
+    hipLaunchKernelGGL(bf16 ? pick_bal<true>() : pick_bal<false>(), dim3(bp.base),
+                       dim3(64 * (kBalFull + kBalExtra)), bp.lds, st, (const uint16_t*)x,
+                       (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros, y, l);
+    char v[160];
+    format_bal(v, sizeof v, bf16, group, N, bp);
+    w4h::set_last_variant("%s", v);
     return w4h::launch_status();
 }
 
@@ -974,13 +1242,16 @@ int gemv_impl(const void* x, int x_dtype, const void* qweight, const void* scale
     if (overrides().w4_valu == 1 && M <= 8 && !res)
         return launch_valu(x, x_dtype, qweight, scales, zeros, y, y_dtype, M, N, K, group, workspace,
                            workspace_bytes, (hipStream_t)stream);
+    if (const BalPlan bp = bal_plan(M, N, K, group, w4h::cu_count()); bp.ok)
+        return launch_bal(bp, x, x_dtype, qweight, scales, zeros, res, res_dtype, y, y_dtype, M, N, K, group,
+                          workspace, workspace_bytes, (hipStream_t)stream);
     if (use_gemm(M, N, K, group))
         return launch_gemm(x, x_dtype, qweight, scales, zeros, y, y_dtype, res, res_dtype, M, N, K,
                            group, workspace, workspace_bytes, (hipStream_t)stream);
     Plan p = make_plan(M, N, K, group, w4h::cu_count(), true);
     // (The kernels stage x rows of exactly upw units: xstride = 128 upw.)
     if (!p.upw || p.l.xstride != p.upw * kUnitK) return W4A16_ERR_UNSUPPORTED;
-    const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
+    const size_t need = w4h::ws_bytes(p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0);
     if (need) {
         if (!workspace) return W4A16_ERR_NULL;
         if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
@@ -990,7 +1261,7 @@ int gemv_impl(const void* x, int x_dtype, const void* qweight, const void* scale
     hipStream_t st = (hipStream_t)stream;
     const bool bf16 = x_dtype == W4A16_BF16;
     w4_kernel_t k = pick_kernel(bf16, group, p.upw, p.tpw, p.px);
-    void* out = p.l.S > 1 ? workspace : y;
+    void* out = p.l.S > 1 ? w4h::ws_part(workspace) : y;
     p.l.out_dtype = p.l.S > 1 ? W4A16_F32 : y_dtype;
     p.l.res = res;
     p.l.res_dtype = res_dtype;
@@ -999,7 +1270,7 @@ int gemv_impl(const void* x, int x_dtype, const void* qweight, const void* scale
                        (const uint16_t*)x,
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros,
                        out, p.l);
-    if (p.l.S > 1) w4h::launch_merge(workspace, y, y_dtype, res, res_dtype, M, N, p.l.S, st);
+    if (p.l.S > 1) w4h::launch_merge(w4h::ws_part(workspace), y, y_dtype, res, res_dtype, M, N, p.l.S, st);
     char v[160];
     format_gemv(v, sizeof v, bf16, group, p);
     w4h::set_last_variant("%s", v);
@@ -1015,6 +1286,10 @@ extern "C" int w4a16_plan_variant(int M, int N, int K, int group, int x_dtype, c
     if (M < 1 || M > w4h::kMaxRowsGemm || !w4h::x_fits(M, K)) return W4A16_ERR_SHAPE;
     if (int rc = w4h::check_w4_shape(N, K, group)) return rc;
     const bool bf16 = x_dtype == W4A16_BF16;
+    if (const BalPlan bp = bal_plan(M, N, K, group, w4h::cu_count()); bp.ok && overrides().w4_valu != 1) {
+        format_bal(text, text_bytes, bf16, group, N, bp);
+        return W4A16_OK;
+    }
     if (use_gemm(M, N, K, group)) {
         format_gemm(text, text_bytes, bf16, group, N, w4h::gemm_plan(M, N, K, group, w4h::cu_count()));
         return W4A16_OK;
@@ -1139,7 +1414,7 @@ extern "C" int mxfp4_workspace_bytes(int M, int N, int K, size_t* bytes) {
         return W4A16_OK;
     }
     const Plan p = make_plan(M, N, K, kMxPlanGroup, w4h::cu_count(), true);
-    *bytes = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
+    *bytes = w4h::ws_bytes(p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0);
     return W4A16_OK;
 }
 
@@ -1160,8 +1435,8 @@ extern "C" int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const
         hipStream_t st = (hipStream_t)stream;
         w4h::begin_launches();
         w4h::gemm_launch(gp, x, bf16, qweight, scales, nullptr, y, y_dtype, nullptr, W4A16_F32, M, N, K,
-                         kMxPlanGroup, workspace, st, true);
-        if (gp.split > 1) w4h::launch_merge(workspace, y, y_dtype, nullptr, W4A16_F32, M, N, gp.split, st);
+                         kMxPlanGroup, w4h::ws_part(workspace), st, true);
+        if (gp.split > 1) w4h::launch_merge(w4h::ws_part(workspace), y, y_dtype, nullptr, W4A16_F32, M, N, gp.split, st);
         w4h::set_last_variant("mxfp4_gemm16 %s kernel=w4_gemm_kernel<%s, 4, %d, %d, true> tiles=%d "
                               "slices=%d workgroups=%lld",
                               bf16 ? "bf16" : "f16", bf16 ? "true" : "false", gp.rb, gp.tn,
@@ -1170,7 +1445,7 @@ extern "C" int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const
     }
     Plan p = make_plan(M, N, K, kMxPlanGroup, w4h::cu_count(), true);
     if (!p.upw || p.l.xstride != p.upw * kUnitK) return W4A16_ERR_UNSUPPORTED;
-    const size_t need = p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0;
+    const size_t need = w4h::ws_bytes(p.l.S > 1 ? (size_t)p.l.S * M * N * sizeof(float) : 0);
     if (need) {
         if (!workspace) return W4A16_ERR_NULL;
         if (workspace_bytes < need) return W4A16_ERR_WORKSPACE;
@@ -1180,13 +1455,13 @@ extern "C" int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const
     hipStream_t st = (hipStream_t)stream;
     const bool bf16 = x_dtype == W4A16_BF16;
     w4_kernel_t k = pick_mx_kernel(bf16, p.upw, p.tpw, p.px);
-    void* out = p.l.S > 1 ? workspace : y;
+    void* out = p.l.S > 1 ? w4h::ws_part(workspace) : y;
     p.l.out_dtype = p.l.S > 1 ? W4A16_F32 : y_dtype;
     w4h::begin_launches();
     hipLaunchKernelGGL(k, dim3((p.tiles + p.tpw - 1) / p.tpw, p.l.S), dim3(64 * p.waves), p.lds, st,
                        (const uint16_t*)x, (const u32x4_t*)qweight, (const uint16_t*)scales,
                        (const uint32_t*)nullptr, out, p.l);
-    if (p.l.S > 1) w4h::launch_merge(workspace, y, y_dtype, nullptr, W4A16_F32, M, N, p.l.S, st);
+    if (p.l.S > 1) w4h::launch_merge(w4h::ws_part(workspace), y, y_dtype, nullptr, W4A16_F32, M, N, p.l.S, st);
     w4h::set_last_variant("mxfp4_mfma16 %s kernel=w4_gemv_kernel<%s, 4, %d, %d, true%s> tiles=%d "
                           "slices=%d waves=%d upw=%d tpw=%d lds=%zu px=%d",
                           bf16 ? "bf16" : "f16", bf16 ? "true" : "false", p.upw, p.tpw,

@@ -46,6 +46,16 @@
  *     never a silent fallback: a valid but unsupported request returns
  *     W4A16_ERR_UNSUPPORTED.  A launch failure returns W4A16_ERR_HIP.
  *   - Size-query functions (*_packed_sizes, *_workspace_bytes) do no GPU work.
+ *   - Workspaces (sized by the *_workspace_bytes queries; 0 = pass NULL):
+ *     the first W4A16_WORKSPACE_HEAD_BYTES of a workspace hold arrival
+ *     counters.  Zero them once, when the workspace is allocated
+ *     (hipMemset, or a zero-filled allocation); every call leaves them zero
+ *     again.  The rest is scratch that a call writes before it reads it.  So
+ *     one workspace, zeroed once, may serve any sequence of calls of any
+ *     entry point and shape on one stream, graph replays included; calls
+ *     that may overlap in time need distinct workspaces.  A head that is not
+ *     zero gives wrong results (never a fault or a hang: no kernel waits on
+ *     a counter).
  */
 #ifndef W4A16_H
 #define W4A16_H
@@ -58,6 +68,7 @@ extern "C" {
 #endif
 
 struct ihipStream_t;                       /* hipStream_t is struct ihipStream_t* */
+#define W4A16_WORKSPACE_HEAD_BYTES (64u << 10)
 typedef struct ihipStream_t* w4a16_stream_t;
 
 typedef enum {
@@ -107,10 +118,12 @@ int w4a16_unpack(const void* qweight, const void* scales, const void* zeros,
                  int32_t* qweight_canon, uint16_t* scales_canon, int32_t* zeros_canon, int N,
                  int K, int group, w4a16_stream_t stream);
 
-/* Fp32 workspace bytes w4a16_gemv needs for this shape (0 when the shape runs
- * without a K split).  Host only; the answer is fixed for the life of the
- * process, so a workspace sized once may be reused inside a captured graph
- * (NINFER tuning page, section 五: declare workspace capacity up front). */
+/* Workspace bytes w4a16_gemv needs for this shape: 0 when its plan needs
+ * none, else the counter head plus fp32 partial sums (a K split, or the
+ * balanced plan's pieces of leftover tiles).  Host only; the answer is fixed
+ * for the life of the process, so a workspace sized once may be reused
+ * inside a captured graph (NINFER tuning page, section 五: declare workspace
+ * capacity up front). */
 int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* bytes);
 /* (The A/B overrides the planners honour are read from the environment once,
  * at the first size query or call of the process; see w4a16_plan_variant.) */
@@ -120,7 +133,10 @@ int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* bytes);
  * dequantized once for every row).  A few rows run a GEMV kernel whose waves
  * split K; larger M (from a crossover measured per layer shape; always above
  * 16) runs an M-tiled kernel whose waves split N and share x through LDS.
- * w4a16_last_variant() names the kernel that ran.
+ * Layers a little wider than one 16-column tile per CU (C + r tiles on C
+ * CUs, r dividing C) with long K run, up to 3 rows, a balanced GEMV whose
+ * workgroups also split the r leftover tiles over K and merge those pieces
+ * through the workspace.  w4a16_last_variant() names the kernel that ran.
  * x_dtype: W4A16_F16 or W4A16_BF16.  y_dtype: W4A16_F32, W4A16_F16 or
  * W4A16_BF16 (rounded to nearest even from the fp32 result).  q - z is formed
  * exactly before any product (the integer placed in a 16-bit float's mantissa
@@ -133,9 +149,9 @@ int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* bytes);
  * fp16 x holding the same values.  Products and sums are fp32; the result is
  * deterministic: the same inputs give the same bits on every call and every
  * graph replay.  workspace may be NULL when
- * w4a16_workspace_bytes reports 0; otherwise it must hold that many bytes and
- * is scratch owned by the call while it runs (no zeroing needed).  x and y
- * must not overlap the weights or each other. */
+ * w4a16_workspace_bytes reports 0; otherwise it must hold that many bytes,
+ * with a zero head (see the conventions above), and is owned by the call
+ * while it runs.  x and y must not overlap the weights or each other. */
 int w4a16_gemv(const void* x, int x_dtype, const void* qweight, const void* scales,
                const void* zeros, void* y, int y_dtype, int M, int N, int K, int group,
                void* workspace, size_t workspace_bytes, w4a16_stream_t stream);
@@ -161,10 +177,10 @@ int w4a16_gemv_add(const void* x, int x_dtype, const void* qweight, const void* 
  * allocates nothing (no hipMalloc, no library allocation).  Each GPU holds its
  * array from its first use until the process ends; its address is looked up
  * once per device, on the first call that needs it with that device current.
- * The array needs no clearing: every byte a call reads was written earlier
- * in the same call.  All calls on one GPU share that GPU's array, so calls
- * that overlap in time on one GPU (for example on two streams) race and must
- * be serialized by the caller.  Returns W4A16_ERR_WORKSPACE, before any GPU
+ * The array's counter head starts zeroed (static storage) and every call
+ * leaves it zeroed; the rest needs no clearing.  All calls on one GPU share
+ * that GPU's array, so calls that overlap in time on one GPU (for example on
+ * two streams) race and must be serialized by the caller.  Returns W4A16_ERR_WORKSPACE, before any GPU
  * work, when the shape's workspace (w4a16_workspace_bytes) exceeds the array
  * (w4a16_last_error() then says by how much), and the errors of w4a16_gemv
  * otherwise. */

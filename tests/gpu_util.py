@@ -33,11 +33,21 @@ def empty_bytes(n: int) -> torch.Tensor:
     return torch.empty(max(n, 16), dtype=torch.uint8, device=DEV)
 
 
+# Bytes of arrival counters at the start of every workspace: zero before
+# first use, left zero by every call.
+WS_HEAD = L.W4A16_WORKSPACE_HEAD_BYTES
+
+
 def workspace_bytes(n: int) -> torch.Tensor:
-    """A GEMV workspace.  The library needs no zeroing (every byte it reads
-    was written earlier in the same call; the poisoned-workspace tests fill it
-    with NaN to show this), so it is left uninitialised."""
-    return torch.empty(max(n, 16), dtype=torch.uint8, device=DEV)
+    """A workspace of n bytes, zero-filled once as the library requires of
+    its counter head; the rest is scratch each call writes before reading
+    (the poisoned-workspace tests fill it with NaN to show this)."""
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=DEV)
+
+
+def poison(work: torch.Tensor, value: float) -> None:
+    """Fill a workspace past its counter head with value."""
+    work[WS_HEAD:].view(torch.float32)[:] = value
 
 
 class PackedW4:

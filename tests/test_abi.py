@@ -207,19 +207,21 @@ def test_offset_limits_are_rejected_before_launch():
 def test_workspace_queries_follow_the_dispatch():
     # The size queries run the same host planner as the launches (no GPU
     # work; without a device the planner assumes 256 CUs), so they show
-    # which kernel a shape gets.  fp32 partials are S x M x N x 4 bytes.
+    # which kernel a shape gets.  fp32 partials are S x M x N x 4 bytes,
+    # after the 64 KiB counter head.
     # W16A16: few-tile layers run the K-split kernel (no slices); the
     # 17-units-per-wave down shape keeps the tiled kernel in 16 slices.
+    H = lib.W4A16_WORKSPACE_HEAD_BYTES
     assert lib.w16a16_workspace_bytes(1, 7168, 5120) == 0
     assert lib.w16a16_workspace_bytes(8, 5120, 5120) == 0
-    assert lib.w16a16_workspace_bytes(1, 5120, 17408) == 16 * 1 * 5120 * 4
+    assert lib.w16a16_workspace_bytes(1, 5120, 17408) == H + 16 * 1 * 5120 * 4
     # Ternary: the staged kernel unsplit at K = 5120 up to 8 rows, and in 2
     # and 4 slices for the down shape at 4 and 8 rows.
     assert lib.w2t_workspace_bytes(8, 7168, 5120, 128) == 0
-    assert lib.w2t_workspace_bytes(4, 5120, 17408, 128) == 2 * 4 * 5120 * 4
-    assert lib.w2t_workspace_bytes(8, 5120, 17408, 128) == 4 * 8 * 5120 * 4
+    assert lib.w2t_workspace_bytes(4, 5120, 17408, 128) == H + 2 * 4 * 5120 * 4
+    assert lib.w2t_workspace_bytes(8, 5120, 17408, 128) == H + 4 * 8 * 5120 * 4
     # 4-bit: down at M = 4 in 4 slices; M = 8 at K = 5120 unsplit on the GEMV.
-    assert lib.w4a16_workspace_bytes(4, 5120, 17408, 128) == 4 * 4 * 5120 * 4
+    assert lib.w4a16_workspace_bytes(4, 5120, 17408, 128) == H + 4 * 4 * 5120 * 4
     assert lib.w4a16_workspace_bytes(8, 5120, 5120, 128) == 0
 
 
@@ -245,6 +247,23 @@ def test_noalloc_checks_return_before_any_device_work():
     text = open(HEADER).read()
     assert "#define W4A16_NOALLOC_SCRATCH_BYTES (16u << 20)" in text
     assert lib.W4A16_NOALLOC_SCRATCH_BYTES == 16 << 20
+
+
+def test_workspace_head_and_balanced_plan_sizes():
+    # Every workspace begins with the counter head: the split GEMV's size is
+    # the head plus its fp32 partials, and the balanced plan (the 27B-class
+    # down layer, N = 5120, K = 17408, up to 3 rows) the head plus one
+    # [M][16] piece per leftover tile (64 tiles, 4 pieces each).  The
+    # header's head size and the binding's agree.
+    head = lib.W4A16_WORKSPACE_HEAD_BYTES
+    assert "#define W4A16_WORKSPACE_HEAD_BYTES (64u << 10)" in open(HEADER).read()
+    assert head == 64 << 10
+    ws = lib.w4a16_workspace_bytes(4, 512, 17408, 128)
+    assert ws > head and (ws - head) % (4 * 512 * 4) == 0
+    for M in (1, 2, 3):
+        assert lib.w4a16_plan_variant(M, 5120, 17408, 128, "bf16").startswith("w4_bal16")
+        assert lib.w4a16_workspace_bytes(M, 5120, 17408, 128) == head + 64 * 4 * M * 16 * 4
+    assert lib.w4a16_workspace_bytes(1, 4096, 4096, 128) == 0
 
 
 def test_header_compiles_cleanly_as_c_and_cpp(tmp_path):

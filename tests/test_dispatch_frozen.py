@@ -20,6 +20,7 @@ import bit_weight_only_03_amd as L
 def snap():
     return {{
         "w4_ws_down_m1": L.w4a16_workspace_bytes(1, 5120, 17408, 128),
+        "w4_plan_down_m1": L.w4a16_plan_variant(1, 5120, 17408, 128, "f16"),
         "w4_ws_qkv_m1": L.w4a16_workspace_bytes(1, 7168, 5120, 128),
         "w4_plan_qkv_m1": L.w4a16_plan_variant(1, 7168, 5120, 128, "f16"),
         "w4_plan_down_m4": L.w4a16_plan_variant(4, 5120, 17408, 128, "bf16"),
@@ -38,7 +39,7 @@ out["second"] = snap()
 print(json.dumps(out))
 """
 
-OVERRIDES = {"W4A16_SPLIT": "2", "W4A16_TPW": "2", "W4A16_PX": "0", "W4A16_GEMM_SPLIT": "1",
+OVERRIDES = {"W4A16_SPLIT": "2", "W4A16_TPW": "2", "W4A16_PX": "0", "W4A16_BAL": "0", "W4A16_GEMM_SPLIT": "1",
              "W4A16_GEMM_TN": "2", "W16A16_SPLIT": "2", "W16A16_KSPLIT": "0",
              "W2T_STAGED_LDS_MAX": "1"}
 
@@ -62,11 +63,14 @@ def test_overrides_set_before_the_first_call_apply():
     # comparison above is not vacuous.
     plain = _run(before=False)["first"]
     forced = _run(before=True)["first"]
-    assert forced["w4_ws_qkv_m1"] == 2 * 1 * 7168 * 4          # W4A16_SPLIT=2
+    H = 64 << 10                                                 # the workspace's counter head
+    assert forced["w4_ws_qkv_m1"] == H + 2 * 1 * 7168 * 4      # W4A16_SPLIT=2
     assert plain["w4_ws_qkv_m1"] == 0
     assert "px=0" in forced["w4_plan_down_m4"] and "slices=2" in forced["w4_plan_down_m4"]
     assert "px=1" in plain["w4_plan_qkv_m1"]
     assert forced["w4_ws_m64"] == 0 and "slices=1" in forced["w4_plan_m64"]   # W4A16_GEMM_SPLIT=1
     assert "w4_gemm_kernel<false, 4, 4, 2>" in forced["w4_plan_m64"]          # W4A16_GEMM_TN=2
-    assert forced["w16_ws"] == 2 * 1 * 5120 * 4                 # W16A16_SPLIT=2
+    assert forced["w16_ws"] == H + 2 * 1 * 5120 * 4             # W16A16_SPLIT=2
+    assert plain["w4_plan_down_m1"].startswith("w4_bal16")      # W4A16_BAL=0
+    assert forced["w4_plan_down_m1"].startswith("w4_mfma16")
     assert forced["w2t_ws"] != plain["w2t_ws"]                   # direct-x kernel, its own split

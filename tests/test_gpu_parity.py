@@ -20,8 +20,8 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 import bit_weight_only_03_amd as L  # noqa: E402
-from gpu_util import (DEV, PackedMX, PackedW2T, PackedW4, assert_parity, dev, empty_bytes,  # noqa: E402
-                      host_bits, to_f64, workspace_bytes)
+from gpu_util import (DEV, WS_HEAD, PackedMX, PackedW2T, PackedW4, assert_parity, dev,  # noqa: E402
+                      empty_bytes, host_bits, poison, to_f64, workspace_bytes)
 
 
 def say(msg):
@@ -545,6 +545,101 @@ def test_w2t_all_ones_counts_exact():
     assert np.array_equal(y[0], expect.astype(np.float64))
 
 
+# ------------------------------------------------------------ balanced plan ---
+# Layers of 256 + 64 tiles with K = 8 x 17 units (the 27B-class down layer,
+# N = 5120, K = 17408; 5112 gives it a ragged last tile) run the balanced
+# GEMV up to 3 rows: each workgroup's extra waves take a quarter of one of
+# the 64 leftover tiles and the four pieces are merged through the
+# workspace, the last arrival adding them.
+
+BAL_K, BAL_G = 17408, 128
+_BAL = {}
+
+
+def _bal_matrix(N):
+    if N not in _BAL:
+        _BAL.clear()
+        w = synth.gen_w4((150, N), N, BAL_K, BAL_G)
+        _BAL[N] = (w, PackedW4(w, N, BAL_K, BAL_G))
+    return _BAL[N]
+
+
+def _bal_cols(N, seed):
+    """Columns to check on a balanced-plan layer: a sample of the tiles the
+    full waves stream and every column of the leftover tiles (4096 up)."""
+    rng = np.random.default_rng(seed)
+    cols = set(rng.choice(4096, size=96, replace=False).tolist()) | set(range(4096, N)) | {0, 15, 16, 4095}
+    return np.array(sorted(cols), dtype=np.int64)
+
+
+@pytest.mark.parametrize("M,N,xdt", [(1, 5120, "f16"), (1, 5120, "bf16"), (2, 5120, "f16"),
+                                     (3, 5120, "bf16"), (3, 5112, "f16"), (1, 5112, "bf16")])
+def test_balanced_plan_matches_oracle(M, N, xdt):
+    say(f"balanced M={M} N={N} x={xdt}")
+    w, P = _bal_matrix(N)
+    x = synth.gen_x((151, M, N), M, BAL_K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    y = to_f64(P.gemv(dev(x), xdt, M))
+    variant = L.w4a16_last_variant()
+    say("  variant: " + variant)
+    assert variant.startswith("w4_bal16") and "pieces=4" in variant
+    cols = _bal_cols(N, M)
+    ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, BAL_K, BAL_G, cols=cols)
+    assert_parity(y[:, cols], ref, f"balanced M={M} N={N}")
+
+
+def test_balanced_plan_stops_at_four_rows():
+    # Four rows do not fit LDS with the extra waves' x: the split GEMV runs.
+    assert L.w4a16_plan_variant(4, 5120, BAL_K, BAL_G, "f16").startswith("w4_mfma16")
+    assert L.w4a16_plan_variant(3, 5120, BAL_K, BAL_G, "f16").startswith("w4_bal16")
+    assert L.w4a16_plan_variant(1, 5120, BAL_K, 64, "f16").startswith("w4_mfma16")   # g = 64
+
+
+@pytest.mark.parametrize("M,xdt,rdt,ydt,inplace", [(2, "bf16", "bf16", "bf16", True),
+                                                   (1, "f16", "f32", "f16", False)])
+def test_balanced_plan_adds_the_residual(M, xdt, rdt, ydt, inplace):
+    # The leftover tiles' outputs are stored by the last piece to arrive,
+    # which adds the residual there.
+    N = 5120
+    say(f"balanced gemv_add M={M} x={xdt} r={rdt} y={ydt} inplace={inplace}")
+    w, P = _bal_matrix(N)
+    x = synth.gen_x((152, M), M, BAL_K, xdt)
+    r64 = np.random.default_rng(152 + M).standard_normal((M, N)) * 4.0
+    r = torch.from_numpy(r64).to(_TORCH_DT[rdt]).cuda()
+    rref = r.double().cpu().numpy()
+    y = r.clone() if inplace else torch.full((M, N), float("nan"), dtype=_TORCH_DT[ydt], device=DEV)
+    wsb = L.w4a16_workspace_bytes(M, N, BAL_K, BAL_G)
+    ws = workspace_bytes(wsb)
+    L.w4a16_gemv_add(dev(x), xdt, P.q, P.s, P.z, y if inplace else r, rdt, y, ydt, M, N, BAL_K, BAL_G,
+                     ws, wsb)
+    torch.cuda.synchronize()
+    assert L.w4a16_last_variant().startswith("w4_bal16")
+    cols = _bal_cols(N, 7 + M)
+    ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, BAL_K, BAL_G, cols=cols)
+    assert_parity(to_f64(y)[:, cols], ref + rref[:, cols], "balanced gemv_add", extra_rel=_ROUND[ydt])
+
+
+@pytest.mark.parametrize("M,xdt", [(1, "f16"), (3, "bf16")])
+def test_balanced_plan_repeat_calls_and_graph_replays(M, xdt):
+    # Which piece arrives last varies from call to call; the pieces are still
+    # added in a fixed order, so every call and replay gives the same bits,
+    # and every call leaves the arrival counters at zero.
+    N = 5120
+    say(f"balanced determinism M={M} x={xdt}")
+    _, P = _bal_matrix(N)
+    x = dev(synth.gen_x((153, M), M, BAL_K, xdt))
+    wsb = L.w4a16_workspace_bytes(M, N, BAL_K, BAL_G)
+    ws = workspace_bytes(wsb)
+    y0 = P.gemv(x, xdt, M, workspace=ws).clone()
+    for _ in range(20):
+        assert torch.equal(P.gemv(x, xdt, M, workspace=ws), y0)
+    y = torch.empty_like(y0)
+    _graph_replays_match(
+        lambda s: L.w4a16_gemv(x, xdt, P.q, P.s, P.z, y, "f32", M, N, BAL_K, BAL_G, ws, wsb, stream=s),
+        y, y0, lambda: P.gemv(x, xdt, M, workspace=ws))
+    torch.cuda.synchronize()
+    assert int(ws[:WS_HEAD].count_nonzero()) == 0
+
+
 # ------------------------------------------------------- determinism and graphs ---
 
 def test_repeat_calls_and_graph_replay_are_bitwise_identical():
@@ -558,7 +653,7 @@ def test_repeat_calls_and_graph_replay_are_bitwise_identical():
         assert torch.equal(P.gemv(x, "bf16", M), y0)
     y = torch.empty_like(y0)
     wsb = L.w4a16_workspace_bytes(M, N, K, g)
-    ws = empty_bytes(wsb) if wsb else None
+    ws = workspace_bytes(wsb) if wsb else None
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         L.w4a16_gemv(x, "bf16", P.q, P.s, P.z, y, "f32", M, N, K, g, ws, wsb, stream=s)  # warm up
@@ -644,8 +739,8 @@ def test_split_k_narrow_shard_parity_and_poisoned_workspace():
     w = synth.gen_w4((111,), N, K, g)
     x = synth.gen_x((111,), M, K, "bf16", outlier_frac=0.01)
     P = PackedW4(w, N, K, g)
-    work = empty_bytes(ws)
-    work.view(torch.float32)[:] = float("nan")
+    work = workspace_bytes(ws)
+    poison(work, float("nan"))
     y = P.gemv(dev(x), "bf16", M, workspace=work)
     torch.cuda.synchronize()
     variant = L.w4a16_last_variant()
@@ -653,32 +748,39 @@ def test_split_k_narrow_shard_parity_and_poisoned_workspace():
     assert "slices=1 " not in variant
     ref = oracle.w4_gemv(x, "bf16", w["qweight"], w["scales"], w["zeros"], M, N, K, g)
     assert_parity(to_f64(y), ref, "split-K")
-    work.view(torch.float32)[:] = float("inf")
+    poison(work, float("inf"))
     assert torch.equal(P.gemv(dev(x), "bf16", M, workspace=work), y)
+    assert int(work[:WS_HEAD].count_nonzero()) == 0   # the counter head untouched
 
 
 def test_split_k_workspace_reused_across_shapes_and_graph_replays():
-    # One workspace, sized for the largest call and poisoned beforehand,
-    # serves a sequence of split calls of different shapes and slice counts
-    # on one stream, also inside a graph replayed many times with eager calls
-    # through the same workspace in between.  The ternary GEMV's split path
-    # (the direct-x kernel) follows the same contract.
-    cases = [(1, 640, 17408, 128, "f16"), (4, 2048, 8192, 64, "bf16"), (3, 1024, 12288, 128, "f16"),
-             (2, 640, 17408, 128, "bf16")]
+    # One workspace, sized for the largest call and poisoned beforehand past
+    # its counter head, serves a sequence of split calls of different shapes
+    # and slice counts -- and balanced-plan calls, which count arrivals in
+    # the head -- on one stream, also inside a graph replayed many times with
+    # eager calls through the same workspace in between.  The ternary GEMV's
+    # split path (the direct-x kernel) follows the same contract.
+    cases = [(1, 640, 17408, 128, "f16"), (2, 5120, 17408, 128, "bf16"), (4, 2048, 8192, 64, "bf16"),
+             (3, 1024, 12288, 128, "f16"), (1, 5120, 17408, 128, "f16"), (2, 640, 17408, 128, "bf16")]
     packs, xs, refs, sizes = [], [], [], []
     for i, (M, N, K, g, xdt) in enumerate(cases):
         w = synth.gen_w4((115, i), N, K, g)
         x = synth.gen_x((115, i), M, K, xdt)
         packs.append(PackedW4(w, N, K, g))
         xs.append(dev(x))
-        refs.append(oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g))
+        cols = None if N <= 2048 else _bal_cols(N, i)
+        refs.append((cols, oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g,
+                                          cols=cols)))
         sizes.append(L.w4a16_workspace_bytes(M, N, K, g))
+        plan = L.w4a16_plan_variant(M, N, K, g, xdt)
+        assert ("w4_bal16" in plan) == (N == 5120), plan
+        assert "w4_bal16" in plan or "slices=1 " not in plan, plan
     assert all(b > 0 for b in sizes), sizes
     M2, N2, K2, g2 = 8, 640, 17408, 128          # the ternary call at the end
     wsb2 = L.w2t_workspace_bytes(M2, N2, K2, g2)
     assert wsb2 > 0
-    work = empty_bytes(max(sizes + [wsb2]))
-    work.view(torch.float32)[:] = float("nan")
+    work = workspace_bytes(max(sizes + [wsb2]))
+    poison(work, float("nan"))
     ys = [torch.empty((M, N), dtype=torch.float32, device=DEV) for (M, N, _, _, _) in cases]
     s = torch.cuda.Stream()
 
@@ -690,8 +792,9 @@ def test_split_k_workspace_reused_across_shapes_and_graph_replays():
         run_all()
     torch.cuda.synchronize()
     first = [y.clone() for y in ys]
-    for (M, N, K, g, xdt), y, ref in zip(cases, first, refs):
-        assert_parity(to_f64(y), ref, f"shared workspace M={M} N={N} K={K} g={g}")
+    for (M, N, K, g, xdt), y, (cols, ref) in zip(cases, first, refs):
+        got = to_f64(y) if cols is None else to_f64(y)[:, cols]
+        assert_parity(got, ref, f"shared workspace M={M} N={N} K={K} g={g}")
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=s):
         run_all()
@@ -714,6 +817,7 @@ def test_split_k_workspace_reused_across_shapes_and_graph_replays():
     assert "slices=1 " not in L.w4a16_last_variant()
     assert_parity(to_f64(y2), oracle.w2t_gemv(x2, "f16", w2["codes"], w2["scales"], M, N, K, g),
                   "ternary split, shared workspace")
+    assert int(work[:WS_HEAD].count_nonzero()) == 0   # every call left the counters at zero
 
 
 @pytest.mark.parametrize("M,K,g,xdt", [(1, 1152, 128, "f16"), (8, 1152, 128, "bf16"),

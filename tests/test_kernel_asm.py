@@ -66,32 +66,43 @@ def is_vmem_load(line):
     return re.match(r"(buffer|global)_load", line) is not None
 
 
-def check_x_wait(lines):
-    """Returns None if the function's explicit x wait is safe, else a reason."""
+def check_x_wait(lines, expect=1):
+    """Returns None if the function's explicit x waits are safe, else a
+    reason.  A kernel has one such wait per wave chain it compiles: one, or
+    two for the balanced plan (its full and extra waves run chains of
+    different lengths, in separate straight-line blocks)."""
     waits = [i for i, l in enumerate(lines)
              if re.fullmatch(r"s_waitcnt vmcnt\(\d+\)", l) and lines[i - 1].startswith(";;#ASMSTART")]
-    if len(waits) != 1:
+    if len(waits) != expect:
         return f"{len(waits)} explicit vmcnt waits"
-    w = waits[0]
-    n = int(re.search(r"\((\d+)\)", lines[w]).group(1))
-    # Walk back from the wait through straight-line code: the n most recent
-    # vector memory loads on every path into the wait must be ring loads.
-    count = 0
-    for line in reversed(lines[:w]):
-        if count >= n:
-            break
-        if line.startswith(";"):
-            continue
-        if is_vmem_load(line):
-            if " lds" in line:
-                return f"only {count} loads between the last x load and vmcnt({n})"
-            count += 1
-        elif line.endswith(":") or line.startswith(("s_cbranch", "s_branch", "s_setpc")):
-            return f"control flow after only {count} of {n} ring loads ({line})"
-    if count < n:
-        return f"only {count} loads before vmcnt({n})"
-    if any(l.startswith("ds_read") for l in lines[:w]):
-        return "an LDS read precedes the x wait"
+    prev = 0
+    for w in waits:
+        n = int(re.search(r"\((\d+)\)", lines[w]).group(1))
+        # Walk back from the wait through straight-line code: the n most
+        # recent vector memory loads on every path into the wait must be ring
+        # loads.
+        count = 0
+        for line in reversed(lines[:w]):
+            if count >= n:
+                break
+            if line.startswith(";"):
+                continue
+            if is_vmem_load(line):
+                if " lds" in line:
+                    return f"only {count} loads between the last x load and vmcnt({n})"
+                count += 1
+            elif line.endswith(":") or line.startswith(("s_cbranch", "s_branch", "s_setpc")):
+                return f"control flow after only {count} of {n} ring loads ({line})"
+        if count < n:
+            return f"only {count} loads before vmcnt({n})"
+        # No LDS read between the chain's first x load (the first after the
+        # previous wait) and its wait.
+        xs = [i for i in range(prev, w) if is_vmem_load(lines[i]) and " lds" in lines[i]]
+        if not xs:
+            return f"no x load before vmcnt({n})"
+        if any(l.startswith("ds_read") for l in lines[xs[0]:w]):
+            return "an LDS read precedes the x wait"
+        prev = w
     return None
 
 
@@ -134,8 +145,10 @@ def test_x_wait_covers_the_x_loads(asm_files):
             checked += 1
             # The GEMV's per-unit x staging (template argument PX = true)
             # has one wait per x load; every other kernel one wait in all.
-            px = re.search(r"ELb[01]ELb1EEEv", name) is not None   # <..., MX, PX = true>
-            why = check_unit_x_waits(lines) if px else check_x_wait(lines)
+            # <BF16, SPG, UPW, TPW, MX, PX = true, BAL>
+            px = re.search(r"kernelILb[01]ELi\d+ELi\d+ELi\d+ELb[01]ELb1E", name) is not None
+            bal = re.search(r"kernelILb[01]ELi\d+ELi\d+ELi\d+ELb[01]ELb[01]ELb1E", name) is not None
+            why = check_unit_x_waits(lines) if px else check_x_wait(lines, 2 if bal else 1)
             if why:
                 bad.append(f"{src} {name}: {why}")
     # every 4-bit and staged ternary instantiation stages x this way

@@ -3,7 +3,8 @@ workspace is a library-owned static device array instead of a caller buffer
 (for callers that cannot allocate).  Its results must equal w4a16_gemv's bit
 for bit (same plan, same kernels, deterministic sums), call after call, with
 the array still holding the previous call's partials -- the second call of a
-pair is the smaller one -- and on shapes with and without a K split."""
+pair is the smaller one -- and on shapes with and without a K split, and on
+the balanced plan, whose arrival counters live at the head of the array."""
 import numpy as np
 import pytest
 import torch
@@ -30,9 +31,10 @@ def _call_both(P, x, xdt, M):
 
 
 # (M, N, K, group, x dtype): a split GEMV (4 slices), a smaller split GEMV
-# (narrow N), the M-tiled kernel in K slices, then one without a split.
+# (narrow N), the M-tiled kernel in K slices, one without a split, then the
+# balanced plan (leftover tiles merged through the array).
 CASES = [(4, 5120, 17408, 128, "bf16"), (2, 640, 17408, 128, "f16"), (32, 1024, 8192, 64, "f16"),
-         (1, 264, 1024, 128, "f16")]
+         (1, 264, 1024, 128, "f16"), (2, 5120, 17408, 128, "bf16")]
 
 
 def test_noalloc_matches_gemv_bitwise_call_after_call():
@@ -41,8 +43,9 @@ def test_noalloc_matches_gemv_bitwise_call_after_call():
         print(f"noalloc call {i}: M={M} N={N} K={K} g={g} x={xdt}", flush=True)
         ws = L.w4a16_workspace_bytes(M, N, K, g)
         assert ws <= L.W4A16_NOALLOC_SCRATCH_BYTES
-        if i < 3:
+        if i != 3:
             assert ws > 0, "the case must use the workspace"
+        assert ("w4_bal16" in L.w4a16_plan_variant(M, N, K, g, xdt)) == (i == 4)
         if prev_ws is not None and i == 1:
             assert ws < prev_ws, "the second call must be the smaller one"
         prev_ws = ws
@@ -52,7 +55,10 @@ def test_noalloc_matches_gemv_bitwise_call_after_call():
         P = PackedW4(w, N, K, g)
         y, y_ref = _call_both(P, dev(x), xdt, M)
         assert torch.equal(y, y_ref)
-        cols = np.sort(np.random.default_rng(i).choice(N, size=min(N, 96), replace=False))
+        cols = np.random.default_rng(i).choice(N, size=min(N, 96), replace=False)
+        if i == 4:
+            cols = np.concatenate([cols, np.arange(4096, N, 5)])   # the leftover tiles
+        cols = np.unique(cols)
         ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, g,
                              cols=cols.astype(np.int64))
         assert_parity(to_f64(y)[:, cols], ref, f"noalloc call {i}")
