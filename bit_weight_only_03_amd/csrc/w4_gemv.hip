@@ -56,10 +56,12 @@ using namespace w4k;
 namespace {
 
 constexpr int kMaxWaves = 8;     // waves per workgroup (the kernel's 512-thread launch bound)
-// Balanced plan: 8 waves streaming the workgroup's own tile in chains of 17
-// units, and 8 "extra" waves sharing a piece of a leftover tile in chains of
-// at most 5.
-constexpr int kBalFull = 8, kBalExtra = 8, kBalUpw = 17, kBalExtraUpw = 5, kBalMaxPieces = 4;
+// Balanced plan: 8 waves streaming the workgroup's own tile in chains of UPW
+// units, and 8 "extra" waves sharing a piece (of at most 4) of a leftover
+// tile in chains of bal_extra_cl(UPW) units: a quarter of 8 UPW units over 8
+// waves.
+constexpr int kBalFull = 8, kBalExtra = 8, kBalMaxPieces = 4;
+constexpr int bal_extra_cl(int upw) { return (upw + 3) / 4; }
 constexpr int kCounterStride = 32;   // unsigneds between arrival counters (one per 128-byte line)
 constexpr int kMaxRows = 16;     // rows per MFMA
 constexpr int kMaxXLoads = 16;   // x load instructions per wave: M * 16 UPW <= 64 * 16
@@ -475,7 +477,7 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
     constexpr bool kUncond = SPG >= 4 || (SPG == 2 && UPW <= 6) || UPW <= 2;
     static_assert(!PX || (kUncond && (UPW * TPW < DM ? UPW * TPW : DM) <= 9),
                   "per-unit x staging needs a straight-line ring");
-    static_assert(!BAL || (TPW == 1 && !PX && !MX && kUncond && kBalExtraUpw <= UPW),
+    static_assert(!BAL || (TPW == 1 && !PX && !MX && kUncond),
                   "the balanced plan runs one tile, whole-range x");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -493,11 +495,11 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
     // bal_pieces of leftover tile bal_base + blockIdx.x / bal_pieces.
     const bool extra = BAL && wave >= a.bal_full;
     // Balanced plan LDS: the full waves' x regions (M rows of UPW units
-    // each), the extra waves' (M rows of kBalExtraUpw units), the full
+    // each), the extra waves' (M rows of bal_extra_cl(UPW) units), the full
     // waves' partial sums [bal_full][M][16], the extra waves'
     // [kBalExtra][M][16], and the extra waves' arrival count.
     uint8_t* const xextra = smem + (size_t)a.bal_full * M * a.xstride * 2;
-    float* const fullp = (float*)(xextra + (size_t)kBalExtra * M * kBalExtraUpw * kUnitK * 2);
+    float* const fullp = (float*)(xextra + (size_t)kBalExtra * M * bal_extra_cl(UPW) * kUnitK * 2);
     float* const extrap = fullp + (size_t)a.bal_full * M * kTileN;
     unsigned* const lcount = (unsigned*)(extrap + (size_t)kBalExtra * M * kTileN);
     if constexpr (BAL) {
@@ -521,13 +523,13 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
     // LDS: wave w's x range, [M][16 UPW chunks of 16 bytes] at byte
     // 2 w M xstride; PX: [UPW units][4 rows][256 bytes] at w UPW 1024 bytes
     // (the layouts are described in w4_wave_chain).
-    uint8_t* const xsb = extra ? xextra + (size_t)(wave - a.bal_full) * M * kBalExtraUpw * kUnitK * 2
+    uint8_t* const xsb = extra ? xextra + (size_t)(wave - a.bal_full) * M * bal_extra_cl(UPW) * kUnitK * 2
                                : smem + (PX ? (size_t)wave * UPW * 1024 : (size_t)wave * M * a.xstride * 2);
     const int c = lane & 15, kc = lane >> 4;
     float4_t total[TPW];
     if constexpr (BAL) {
         if (extra)
-            w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, kBalExtraUpw, 2>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0,
+            w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, bal_extra_cl(UPW), 2>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0,
                                                                          w1, total);
         else
             w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, UPW, 1>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0, w1, total);
@@ -992,12 +994,15 @@ Plan valu_plan(int M, int N, int K, int group);
 // are merged (in LDS within the workgroup, then across the P workgroups
 // through an arrival counter per leftover tile, the last arrival adding the
 // pieces in a fixed order) while the full waves still stream.  The extra
-// waves run a chain of at most kBalExtraUpw units, a compile-time length, so
-// their code stays straight-line.
+// waves run a chain of at most bal_extra_cl(UPW) units, a compile-time
+// length, so their code stays straight-line.  Instantiated for UPW = 17 (K =
+// 17408, the down layer).  At UPW = 5 (K = 5120, o_proj) it measured slower
+// than one tile per workgroup (6.25 against 5.67 us per call at M = 1, 7.27
+// against 6.67 at M = 4): a 5 us kernel does not hide the merge.
 
 struct BalPlan {
     bool ok = false;
-    int pieces = 0, base = 0;
+    int pieces = 0, base = 0, upw = 0;
     size_t lds = 0, ws = 0;
 };
 
@@ -1007,24 +1012,28 @@ BalPlan bal_plan(int M, int N, int K, int group, int cus) {
     const int U = (K + kUnitK - 1) / kUnitK, T = pad_n(N) / kTileN;
     // g = 128 only: at g = 64 a 17-unit chain does not fit the register
     // budget of unconditional arithmetic, which the x wait's overlap needs.
-    // The full waves hold all of x, kBalUpw units each.  M = 4 does not fit
-    // LDS with the extra waves' x besides.
-    if (M > 3 || group != 128 || K % kUnitK) return b;
-    if (U != kBalFull * kBalUpw) return b;
+    // The full waves hold all of x, upw units each (an instantiated chain
+    // length).  Up to 4 rows (the rows a lane's MFMA sums hold), as far as
+    // LDS allows: 17-unit chains stop at 3.
+    if (M > 4 || group != 128 || K % kUnitK || U % kBalFull) return b;
+    const int upw = U / kBalFull;
+    if (upw != 17) return b;
     const int r = T - cus;
     if (r <= 0 || r >= cus || cus % r) return b;
     const int P = cus / r;
     if (P > kBalMaxPieces || U / P < kBalExtra) return b;
-    if (((U + P - 1) / P + kBalExtra - 1) / kBalExtra > kBalExtraUpw) return b;   // extra waves' chain
+    const int cle = bal_extra_cl(upw);
+    if (((U + P - 1) / P + kBalExtra - 1) / kBalExtra > cle) return b;   // extra waves' chain
     // the full and extra waves' x regions, both partial areas, the extra
     // waves' count
-    b.lds = (size_t)M * kUnitK * 2 * (kBalFull * kBalUpw + kBalExtra * kBalExtraUpw) +
+    b.lds = (size_t)M * kUnitK * 2 * (kBalFull * upw + kBalExtra * cle) +
             (size_t)(kBalFull + kBalExtra) * M * kTileN * 4 + 16;
     if (b.lds > 160 * 1024) return b;
     if ((size_t)r * kCounterStride * sizeof(unsigned) > w4h::kWsHead) return b;
     b.ok = true;
     b.pieces = P;
     b.base = cus;
+    b.upw = upw;
     b.ws = w4h::ws_bytes((size_t)r * P * M * kTileN * sizeof(float));   // counters, then [tile][piece][M][16]
     return b;
 }
@@ -1190,15 +1199,16 @@ int launch_valu(const void* x, int x_dtype, const void* qweight, const void* sca
 }
 
 template <bool BF16>
-w4_kernel_t pick_bal() {
-    return w4_gemv_kernel<BF16, 4, kBalUpw, 1, false, false, true>;
+w4_kernel_t pick_bal(int upw) {
+    (void)upw;   // 17, the planner's only chain length
+    return w4_gemv_kernel<BF16, 4, 17, 1, false, false, true>;
 }
 
 void format_bal(char* b, size_t n, bool bf16, int group, int N, const BalPlan& bp) {
     snprintf(b, n,
              "w4_bal16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, 1, false, false, true> tiles=%d "
              "workgroups=%d waves=%d+%d pieces=%d lds=%zu",
-             bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, kBalUpw,
+             bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, bp.upw,
              pad_n(N) / kTileN, bp.base, kBalFull, kBalExtra, bp.pieces, bp.lds);
 }
 
@@ -1210,22 +1220,24 @@ int launch_bal(const BalPlan& bp, const void* x, int x_dtype, const void* qweigh
     if (!w4h::aligned16(workspace)) return W4A16_ERR_ALIGN;
     static std::once_flag once;
     std::call_once(once, [] {
-        (void)hipFuncSetAttribute((const void*)pick_bal<false>(), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)kLdsPerCu);
-        (void)hipFuncSetAttribute((const void*)pick_bal<true>(), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)kLdsPerCu);
+        for (int u : {17}) {
+            (void)hipFuncSetAttribute((const void*)pick_bal<false>(u),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCu);
+            (void)hipFuncSetAttribute((const void*)pick_bal<true>(u),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCu);
+        }
         (void)hipGetLastError();
     });
     const bool bf16 = x_dtype == W4A16_BF16;
     const int U = (K + kUnitK - 1) / kUnitK, T = pad_n(N) / kTileN;
-    GemvLaunch l{M, N, K, U, 1, T, kBalUpw * kUnitK, y_dtype, res, res_dtype};
+    GemvLaunch l{M, N, K, U, 1, T, bp.upw * kUnitK, y_dtype, res, res_dtype};
     l.bal_full = kBalFull;
     l.bal_pieces = bp.pieces;
     l.bal_base = bp.base;
     l.counters = (unsigned*)workspace;
     l.bal_part = (float*)w4h::ws_part(workspace);
     w4h::begin_launches();
-    hipLaunchKernelGGL(bf16 ? pick_bal<true>() : pick_bal<false>(), dim3(bp.base),
+    hipLaunchKernelGGL(bf16 ? pick_bal<true>(bp.upw) : pick_bal<false>(bp.upw), dim3(bp.base),
                        dim3(64 * (kBalFull + kBalExtra)), bp.lds, st, (const uint16_t*)x,
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros, y, l);
     char v[160];
