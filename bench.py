@@ -89,13 +89,11 @@ def kernel_key(name):
     if not m:
         return None
     k = re.sub(r"\s+", " ", m.group(0))
-    # The 4-bit GEMV's fifth and sixth template arguments (MXFP4 mode,
-    # per-unit x staging) default to false and the variant strings leave
-    # them out; profiler names spell them.
+    # The 4-bit GEMV's template arguments after the fourth (MXFP4 mode,
+    # per-unit x staging, balanced plan) default to false and the variant
+    # strings leave trailing defaults out; profiler names spell them.
     if k.startswith("w4_gemv_kernel<"):
-        if k.count(",") == 5 and k.endswith(", false, false>"):
-            k = k[: -len(", false, false>")] + ">"
-        elif k.count(",") == 4 and k.endswith(", false>"):
+        while k.count(",") > 3 and k.endswith(", false>"):
             k = k[: -len(", false>")] + ">"
     return k
 

@@ -51,6 +51,13 @@ def test_kernel_key_normalises_profiler_and_variant_names():
     assert bench.kernel_key("w16_mfma16 f16 kernel=w16_ksplit_kernel<false> tiles=448") == \
         "w16_ksplit_kernel<false>"
     assert bench.kernel_key("__amd_rocclr_copyBuffer") is None
+    # Trailing default template arguments (MX, PX, balanced plan = false)
+    # are dropped; a set one keeps those before it.
+    assert bench.kernel_key("w4_gemv_kernel<false, 4, 5, 3, false, true, false>") == \
+        "w4_gemv_kernel<false, 4, 5, 3, false, true>"
+    assert bench.kernel_key("w4_gemv_kernel<false, 4, 17, 1, false, false, false>") == "w4_gemv_kernel<false, 4, 17, 1>"
+    bal = "w4_gemv_kernel<false, 4, 17, 1, false, false, true>"
+    assert bench.kernel_key("void (anonymous namespace)::" + bal + "(int)") == bal
 
 
 # gate_up's instantiation at M = 1: three tiles per workgroup, x staged unit by unit.
@@ -65,7 +72,7 @@ def test_committed_traffic_summary_is_consistent():
     assert 0.95 < t["calibration"]["write"]["factor"] < 1.05
     # Each instantiation of the sweep moves about its algorithmic bytes.
     alg = {GATE_UP: bench.alg_bytes(1, 34816, 5120, 128),
-           "w4_gemv_kernel<false, 4, 17, 1>": bench.alg_bytes(1, 5120, 17408, 128)}
+           "w4_gemv_kernel<false, 4, 17, 1, false, false, true>": bench.alg_bytes(1, 5120, 17408, 128)}
     for k, a in alg.items():
         ratio = t["kernels"][k]["bytes_per_dispatch"] / a
         assert 1.0 <= ratio < 1.03, (k, ratio)
