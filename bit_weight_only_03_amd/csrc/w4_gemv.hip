@@ -119,11 +119,11 @@ constexpr int max_slots() { return SPG >= 4 ? 9 : (SPG == 2 ? 7 : 5); }
 // UPW except for the balanced plan's extra waves, which run a shorter chain).
 // xsb is the wave's LDS region (M rows of UPW units, or PX's per-unit slots).
 // BAR = 1 and 2 are the balanced plan's full and extra waves; an extra
-// wave's region holds M rows of CL units.  One workgroup barrier orders
-// their memory traffic: the extra waves pass it once all of their loads are
-// issued and the full waves before their first, so the extra waves' loads
-// are queued ahead (their shares are merged across workgroups and should
-// finish first).
+// wave's region holds M rows of CL units.  Two workgroup barriers order
+// their memory traffic: every wave issues its x loads before the first, the
+// extra waves issue their weight loads between the two and the full waves
+// theirs after the second.  So each wave's x comes first, and the extra
+// waves' shares, which are merged across workgroups, finish early.
 template <bool BF16, int SPG, int UPW, int TPW, bool MX, bool PX, int CL, int BAR = 0>
 __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_t* __restrict__ x,
                                               const u32x4_t* __restrict__ qdev,
@@ -140,6 +140,10 @@ __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_
     using SlotT = typename SlotSel<NG, MX>::type;
     constexpr bool kCvtX = BF16 && !MX;   // bf16 x taken to fp16 in LDS for the 4-bit products
     constexpr int XU = BAR == 2 ? CL : UPW;   // units per staged row (= xstride / 128 otherwise)
+    // PX: x slots in the wave's region.  The balanced plan's waves reuse a
+    // ring of D (unit i in slot i % D: its x load goes out with the refill
+    // after unit i - D's products, whose fragment reads have completed).
+    constexpr int XR = BAR != 0 ? D : UPW;
     const int M = a.M, K = a.K, U = a.U;
     const int lane = threadIdx.x & 63;
     const int nu = w1 - w0;                                           // units of this wave
@@ -172,7 +176,6 @@ __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_
     //    wave waits for them only after issuing its weight ring (below), so
     //    the two round trips overlap.
     constexpr int kXL = kMaxXLoads;
-    if constexpr (BAR == 1) __builtin_amdgcn_s_barrier();
     if constexpr (!PX) {
         constexpr int cpr = XU * (kUnitK / 8);       // chunks per staged row
         const int live = nu * (kUnitK / 8);          // positions of a row this wave reads
@@ -235,7 +238,7 @@ __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_
         if constexpr (PX) {
             if (j == 0) {   // the unit's x: [4 rows][256 bytes] straight into LDS
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    i < nu ? rx : rx0, (__attribute__((address_space(3))) void*)(xsb + i * 1024), 16,
+                    i < nu ? rx : rx0, (__attribute__((address_space(3))) void*)(xsb + (i % XR) * 1024), 16,
                     xlane_off, (uint32_t)u * (kUnitK * 2u), 0, 0);
                 __builtin_amdgcn_sched_barrier(0);   // before the slot's own loads
             }
@@ -255,6 +258,17 @@ __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_
         }
     };
 
+    // Balanced plan: no wait before either barrier, so the loads stay in
+    // flight.
+    if constexpr (BAR == 1) {
+        __builtin_amdgcn_s_barrier();   // every wave's x loads are out
+        __builtin_amdgcn_s_barrier();   // the extra waves' weight loads are out
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (BAR == 2) {
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    }
     SlotT ring[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) {
@@ -262,7 +276,7 @@ __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_
         __builtin_amdgcn_sched_barrier(0);   // slots issue in ring order
     }
     if constexpr (BAR == 2) {
-        __builtin_amdgcn_s_barrier();   // no wait: the loads stay in flight
+        __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     }
     // Vector memory loads complete in issue order, so once no more than the
@@ -332,7 +346,7 @@ __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_
 #undef W4_PX_WAIT
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (kCvtX) {   // the 16 bytes this lane's x load wrote, as fp16
-                    u32x4_t* const p = (u32x4_t*)(xsb + (uint32_t)i * 1024u + (uint32_t)lane * 16u);
+                    u32x4_t* const p = (u32x4_t*)(xsb + (uint32_t)(i % XR) * 1024u + (uint32_t)lane * 16u);
                     *p = bf16x8_to_f16x8(*p);
                 }
             }
@@ -340,7 +354,7 @@ __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_
         if (tj == 0 && i < nu && xrow) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                xa[j] = *(const u32x4_t*)(xlane + (uint32_t)i * kXUnit + 64 * j);
+                xa[j] = *(const u32x4_t*)(xlane + (uint32_t)(PX ? i % XR : i) * kXUnit + 64 * j);
         }
         // Units past this wave's range arrived as zeros (q = z = 0, s = +0) and
         // add exactly 0 with the finite x the lane still holds, so where the
@@ -477,8 +491,7 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
     constexpr bool kUncond = SPG >= 4 || (SPG == 2 && UPW <= 6) || UPW <= 2;
     static_assert(!PX || (kUncond && (UPW * TPW < DM ? UPW * TPW : DM) <= 9),
                   "per-unit x staging needs a straight-line ring");
-    static_assert(!BAL || (TPW == 1 && !PX && !MX && kUncond),
-                  "the balanced plan runs one tile, whole-range x");
+    static_assert(!BAL || (TPW == 1 && !MX && kUncond), "the balanced plan runs one tile");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int M = a.M, U = a.U;
@@ -495,11 +508,16 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
     // bal_pieces of leftover tile bal_base + blockIdx.x / bal_pieces.
     const bool extra = BAL && wave >= a.bal_full;
     // Balanced plan LDS: the full waves' x regions (M rows of UPW units
-    // each), the extra waves' (M rows of bal_extra_cl(UPW) units), the full
-    // waves' partial sums [bal_full][M][16], the extra waves'
-    // [kBalExtra][M][16], and the extra waves' arrival count.
-    uint8_t* const xextra = smem + (size_t)a.bal_full * M * a.xstride * 2;
-    float* const fullp = (float*)(xextra + (size_t)kBalExtra * M * bal_extra_cl(UPW) * kUnitK * 2);
+    // each; PX: a ring of kDF units), the extra waves' (M rows of
+    // bal_extra_cl(UPW) units; PX: kDE units), the full waves' partial sums
+    // [bal_full][M][16], the extra waves' [kBalExtra][M][16], and the extra
+    // waves' arrival count.
+    constexpr int kDF = UPW < max_slots<SPG>() ? UPW : max_slots<SPG>();
+    constexpr int kDE = bal_extra_cl(UPW) < max_slots<SPG>() ? bal_extra_cl(UPW) : max_slots<SPG>();
+    const size_t xfull = PX ? (size_t)kDF * 1024 : (size_t)M * a.xstride * 2;
+    const size_t xext = PX ? (size_t)kDE * 1024 : (size_t)M * bal_extra_cl(UPW) * kUnitK * 2;
+    uint8_t* const xextra = smem + (size_t)a.bal_full * xfull;
+    float* const fullp = (float*)(xextra + (size_t)kBalExtra * xext);
     float* const extrap = fullp + (size_t)a.bal_full * M * kTileN;
     unsigned* const lcount = (unsigned*)(extrap + (size_t)kBalExtra * M * kTileN);
     if constexpr (BAL) {
@@ -523,7 +541,8 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
     // LDS: wave w's x range, [M][16 UPW chunks of 16 bytes] at byte
     // 2 w M xstride; PX: [UPW units][4 rows][256 bytes] at w UPW 1024 bytes
     // (the layouts are described in w4_wave_chain).
-    uint8_t* const xsb = extra ? xextra + (size_t)(wave - a.bal_full) * M * bal_extra_cl(UPW) * kUnitK * 2
+    uint8_t* const xsb = extra ? xextra + (size_t)(wave - a.bal_full) * xext
+                         : BAL ? smem + (size_t)wave * xfull
                                : smem + (PX ? (size_t)wave * UPW * 1024 : (size_t)wave * M * a.xstride * 2);
     const int c = lane & 15, kc = lane >> 4;
     float4_t total[TPW];
@@ -983,7 +1002,7 @@ void allow_full_lds() {
 Plan make_plan(int M, int N, int K, int group, int cus, bool allow_px);
 Plan valu_plan(int M, int N, int K, int group);
 
-// The balanced plan, for calls of up to 3 rows on layers of C + r tiles (C
+// The balanced plan, for calls of up to 4 rows on layers of C + r tiles (C
 // CUs, C a multiple of r) whose K is 8 x 17 units: one workgroup per CU of 8
 // "full" waves, which split the workgroup's own tile over K as the GEMV does,
 // and 8 "extra" waves, which split one of P = C / r pieces of a leftover
@@ -1001,7 +1020,7 @@ Plan valu_plan(int M, int N, int K, int group);
 // against 6.67 at M = 4): a 5 us kernel does not hide the merge.
 
 struct BalPlan {
-    bool ok = false;
+    bool ok = false, px = false;
     int pieces = 0, base = 0, upw = 0;
     size_t lds = 0, ws = 0;
 };
@@ -1013,8 +1032,7 @@ BalPlan bal_plan(int M, int N, int K, int group, int cus) {
     // g = 128 only: at g = 64 a 17-unit chain does not fit the register
     // budget of unconditional arithmetic, which the x wait's overlap needs.
     // The full waves hold all of x, upw units each (an instantiated chain
-    // length).  Up to 4 rows (the rows a lane's MFMA sums hold), as far as
-    // LDS allows: 17-unit chains stop at 3.
+    // length).  Up to 4 rows (the rows a lane's MFMA sums hold).
     if (M > 4 || group != 128 || K % kUnitK || U % kBalFull) return b;
     const int upw = U / kBalFull;
     if (upw != 17) return b;
@@ -1025,9 +1043,12 @@ BalPlan bal_plan(int M, int N, int K, int group, int cus) {
     const int cle = bal_extra_cl(upw);
     if (((U + P - 1) / P + kBalExtra - 1) / kBalExtra > cle) return b;   // extra waves' chain
     // the full and extra waves' x regions, both partial areas, the extra
-    // waves' count
-    b.lds = (size_t)M * kUnitK * 2 * (kBalFull * upw + kBalExtra * cle) +
-            (size_t)(kBalFull + kBalExtra) * M * kTileN * 4 + 16;
+    // waves' count.  Where whole-range staging does not fit (4 rows), x is
+    // staged unit by unit into rings of each chain's slots (9 and 5).
+    const size_t tail = (size_t)(kBalFull + kBalExtra) * M * kTileN * 4 + 16;
+    b.lds = (size_t)M * kUnitK * 2 * (kBalFull * upw + kBalExtra * cle) + tail;
+    b.px = b.lds > 160 * 1024 || w4h::overrides().w4_px == 1;
+    if (b.px) b.lds = (size_t)1024 * (kBalFull * 9 + kBalExtra * (cle < 9 ? cle : 9)) + tail;
     if (b.lds > 160 * 1024) return b;
     if ((size_t)r * kCounterStride * sizeof(unsigned) > w4h::kWsHead) return b;
     b.ok = true;
@@ -1199,17 +1220,17 @@ int launch_valu(const void* x, int x_dtype, const void* qweight, const void* sca
 }
 
 template <bool BF16>
-w4_kernel_t pick_bal(int upw) {
+w4_kernel_t pick_bal(int upw, bool px) {
     (void)upw;   // 17, the planner's only chain length
-    return w4_gemv_kernel<BF16, 4, 17, 1, false, false, true>;
+    return px ? w4_gemv_kernel<BF16, 4, 17, 1, false, true, true> : w4_gemv_kernel<BF16, 4, 17, 1, false, false, true>;
 }
 
 void format_bal(char* b, size_t n, bool bf16, int group, int N, const BalPlan& bp) {
     snprintf(b, n,
-             "w4_bal16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, 1, false, false, true> tiles=%d "
-             "workgroups=%d waves=%d+%d pieces=%d lds=%zu",
-             bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, bp.upw,
-             pad_n(N) / kTileN, bp.base, kBalFull, kBalExtra, bp.pieces, bp.lds);
+             "w4_bal16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, 1, false, %s, true> tiles=%d "
+             "workgroups=%d waves=%d+%d pieces=%d lds=%zu px=%d",
+             bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, bp.upw, bp.px ? "true" : "false",
+             pad_n(N) / kTileN, bp.base, kBalFull, kBalExtra, bp.pieces, bp.lds, (int)bp.px);
 }
 
 int launch_bal(const BalPlan& bp, const void* x, int x_dtype, const void* qweight, const void* scales,
@@ -1220,10 +1241,10 @@ int launch_bal(const BalPlan& bp, const void* x, int x_dtype, const void* qweigh
     if (!w4h::aligned16(workspace)) return W4A16_ERR_ALIGN;
     static std::once_flag once;
     std::call_once(once, [] {
-        for (int u : {17}) {
-            (void)hipFuncSetAttribute((const void*)pick_bal<false>(u),
+        for (bool px : {false, true}) {
+            (void)hipFuncSetAttribute((const void*)pick_bal<false>(17, px),
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCu);
-            (void)hipFuncSetAttribute((const void*)pick_bal<true>(u),
+            (void)hipFuncSetAttribute((const void*)pick_bal<true>(17, px),
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCu);
         }
         (void)hipGetLastError();
@@ -1237,7 +1258,7 @@ int launch_bal(const BalPlan& bp, const void* x, int x_dtype, const void* qweigh
     l.counters = (unsigned*)workspace;
     l.bal_part = (float*)w4h::ws_part(workspace);
     w4h::begin_launches();
-    hipLaunchKernelGGL(bf16 ? pick_bal<true>(bp.upw) : pick_bal<false>(bp.upw), dim3(bp.base),
+    hipLaunchKernelGGL(bf16 ? pick_bal<true>(bp.upw, bp.px) : pick_bal<false>(bp.upw, bp.px), dim3(bp.base),
                        dim3(64 * (kBalFull + kBalExtra)), bp.lds, st, (const uint16_t*)x,
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros, y, l);
     char v[160];

@@ -134,7 +134,7 @@ int w4a16_workspace_bytes(int M, int N, int K, int group, size_t* bytes);
  * split K; larger M (from a crossover measured per layer shape; always above
  * 16) runs an M-tiled kernel whose waves split N and share x through LDS.
  * Layers a little wider than one 16-column tile per CU (C + r tiles on C
- * CUs, r dividing C) with long K run, up to 3 rows, a balanced GEMV whose
+ * CUs, r dividing C) with long K run, up to 4 rows, a balanced GEMV whose
  * workgroups also split the r leftover tiles over K and merge those pieces
  * through the workspace.  w4a16_last_variant() names the kernel that ran.
  * x_dtype: W4A16_F16 or W4A16_BF16.  y_dtype: W4A16_F32, W4A16_F16 or

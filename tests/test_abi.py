@@ -220,8 +220,11 @@ def test_workspace_queries_follow_the_dispatch():
     assert lib.w2t_workspace_bytes(8, 7168, 5120, 128) == 0
     assert lib.w2t_workspace_bytes(4, 5120, 17408, 128) == H + 2 * 4 * 5120 * 4
     assert lib.w2t_workspace_bytes(8, 5120, 17408, 128) == H + 4 * 8 * 5120 * 4
-    # 4-bit: down at M = 4 in 4 slices; M = 8 at K = 5120 unsplit on the GEMV.
-    assert lib.w4a16_workspace_bytes(4, 5120, 17408, 128) == H + 4 * 4 * 5120 * 4
+    # 4-bit: down at M = 4 on the balanced plan (one [4][16] piece per
+    # quarter of its 64 leftover tiles), at M = 5 in 4 slices; M = 8 at
+    # K = 5120 unsplit on the GEMV.
+    assert lib.w4a16_workspace_bytes(4, 5120, 17408, 128) == H + 64 * 4 * 4 * 16 * 4
+    assert lib.w4a16_workspace_bytes(5, 5120, 17408, 128) == H + 4 * 5 * 5120 * 4
     assert lib.w4a16_workspace_bytes(8, 5120, 5120, 128) == 0
 
 
@@ -252,7 +255,7 @@ def test_noalloc_checks_return_before_any_device_work():
 def test_workspace_head_and_balanced_plan_sizes():
     # Every workspace begins with the counter head: the split GEMV's size is
     # the head plus its fp32 partials, and the balanced plan (the 27B-class
-    # down layer, N = 5120, K = 17408, up to 3 rows) the head plus one
+    # down layer, N = 5120, K = 17408, up to 4 rows) the head plus one
     # [M][16] piece per leftover tile (64 tiles, 4 pieces each).  The
     # header's head size and the binding's agree.
     head = lib.W4A16_WORKSPACE_HEAD_BYTES
@@ -260,7 +263,7 @@ def test_workspace_head_and_balanced_plan_sizes():
     assert head == 64 << 10
     ws = lib.w4a16_workspace_bytes(4, 512, 17408, 128)
     assert ws > head and (ws - head) % (4 * 512 * 4) == 0
-    for M in (1, 2, 3):
+    for M in (1, 2, 3, 4):
         assert lib.w4a16_plan_variant(M, 5120, 17408, 128, "bf16").startswith("w4_bal16")
         assert lib.w4a16_workspace_bytes(M, 5120, 17408, 128) == head + 64 * 4 * M * 16 * 4
     assert lib.w4a16_workspace_bytes(1, 4096, 4096, 128) == 0

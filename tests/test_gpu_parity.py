@@ -548,7 +548,7 @@ def test_w2t_all_ones_counts_exact():
 # ------------------------------------------------------------ balanced plan ---
 # Layers of 256 + 64 tiles with K = 8 x 17 units (the 27B-class down layer,
 # N = 5120, K = 17408; 5112 gives it a ragged last tile) run the balanced
-# GEMV up to 3 rows: each workgroup's extra waves take a quarter of one of
+# GEMV up to 4 rows: each workgroup's extra waves take a quarter of one of
 # the 64 leftover tiles and the four pieces are merged through the
 # workspace, the last arrival adding them.
 
@@ -573,7 +573,8 @@ def _bal_cols(N, seed):
 
 
 @pytest.mark.parametrize("M,N,xdt", [(1, 5120, "f16"), (1, 5120, "bf16"), (2, 5120, "f16"),
-                                     (3, 5120, "bf16"), (3, 5112, "f16"), (1, 5112, "bf16")])
+                                     (3, 5120, "bf16"), (3, 5112, "f16"), (1, 5112, "bf16"),
+                                     (4, 5120, "bf16"), (4, 5112, "f16")])
 def test_balanced_plan_matches_oracle(M, N, xdt):
     say(f"balanced M={M} N={N} x={xdt}")
     w, P = _bal_matrix(N)
@@ -587,11 +588,16 @@ def test_balanced_plan_matches_oracle(M, N, xdt):
     assert_parity(y[:, cols], ref, f"balanced M={M} N={N}")
 
 
-def test_balanced_plan_stops_at_four_rows():
-    # Four rows do not fit LDS with the extra waves' x: the split GEMV runs.
-    assert L.w4a16_plan_variant(4, 5120, BAL_K, BAL_G, "f16").startswith("w4_mfma16")
-    assert L.w4a16_plan_variant(3, 5120, BAL_K, BAL_G, "f16").startswith("w4_bal16")
-    assert L.w4a16_plan_variant(1, 5120, BAL_K, 64, "f16").startswith("w4_mfma16")   # g = 64
+def test_balanced_plan_rows_and_group():
+    # Up to 3 rows stage each wave's whole x range; at 4 rows that does not
+    # fit LDS next to the extra waves' x, so x is staged unit by unit into
+    # rings.  Past 4 rows, or at g = 64, the other plans run.
+    for M in (1, 2, 3):
+        v = L.w4a16_plan_variant(M, 5120, BAL_K, BAL_G, "f16")
+        assert v.startswith("w4_bal16") and "px=0" in v, v
+    assert "px=1" in L.w4a16_plan_variant(4, 5120, BAL_K, BAL_G, "bf16")
+    assert L.w4a16_plan_variant(5, 5120, BAL_K, BAL_G, "f16").startswith("w4_mfma16")
+    assert L.w4a16_plan_variant(1, 5120, BAL_K, 64, "f16").startswith("w4_mfma16")
 
 
 @pytest.mark.parametrize("M,xdt,rdt,ydt,inplace", [(2, "bf16", "bf16", "bf16", True),
@@ -618,7 +624,7 @@ def test_balanced_plan_adds_the_residual(M, xdt, rdt, ydt, inplace):
     assert_parity(to_f64(y)[:, cols], ref + rref[:, cols], "balanced gemv_add", extra_rel=_ROUND[ydt])
 
 
-@pytest.mark.parametrize("M,xdt", [(1, "f16"), (3, "bf16")])
+@pytest.mark.parametrize("M,xdt", [(1, "f16"), (3, "bf16"), (4, "bf16")])
 def test_balanced_plan_repeat_calls_and_graph_replays(M, xdt):
     # Which piece arrives last varies from call to call; the pieces are still
     # added in a fixed order, so every call and replay gives the same bits,
@@ -644,7 +650,7 @@ def test_balanced_plan_repeat_calls_and_graph_replays(M, xdt):
 
 def test_repeat_calls_and_graph_replay_are_bitwise_identical():
     say("determinism + graph replay")
-    M, N, K, g = 4, 5120, 17408, 128
+    M, N, K, g = 5, 5120, 17408, 128          # the split GEMV (4 K slices and the merge)
     w = synth.gen_w4((110,), N, K, g)
     P = PackedW4(w, N, K, g)
     x = dev(synth.gen_x((110,), M, K, "bf16", outlier_frac=0.01))

@@ -33,7 +33,7 @@ def _call_both(P, x, xdt, M):
 # (M, N, K, group, x dtype): a split GEMV (4 slices), a smaller split GEMV
 # (narrow N), the M-tiled kernel in K slices, one without a split, then the
 # balanced plan (leftover tiles merged through the array).
-CASES = [(4, 5120, 17408, 128, "bf16"), (2, 640, 17408, 128, "f16"), (32, 1024, 8192, 64, "f16"),
+CASES = [(5, 5120, 17408, 128, "bf16"), (2, 640, 17408, 128, "f16"), (32, 1024, 8192, 64, "f16"),
          (1, 264, 1024, 128, "f16"), (2, 5120, 17408, 128, "bf16")]
 
 
