@@ -267,6 +267,17 @@ def test_workspace_head_and_balanced_plan_sizes():
         assert lib.w4a16_plan_variant(M, 5120, 17408, 128, "bf16").startswith("w4_bal16")
         assert lib.w4a16_workspace_bytes(M, 5120, 17408, 128) == head + 64 * 4 * M * 16 * 4
     assert lib.w4a16_workspace_bytes(1, 4096, 4096, 128) == 0
+    # A balanced call with a short or missing workspace is refused before any
+    # launch (no GPU is touched: stream 0, fake aligned pointers).
+    good = 1 << 20
+    ws = lib.w4a16_workspace_bytes(1, 5120, 17408, 128)
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.w4a16_gemv(good, 0, good, good, good, good, 2, 1, 5120, 17408, 128, workspace=good,
+                       workspace_bytes=ws - 16, stream=0)
+    assert e.value.status == -5
+    with pytest.raises(lib.W4A16Error) as e:
+        lib.w4a16_gemv(good, 0, good, good, good, good, 2, 1, 5120, 17408, 128, stream=0)
+    assert e.value.status == -1
 
 
 def test_header_compiles_cleanly_as_c_and_cpp(tmp_path):
