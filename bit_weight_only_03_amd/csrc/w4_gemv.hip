@@ -491,7 +491,7 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
     constexpr bool kUncond = SPG >= 4 || (SPG == 2 && UPW <= 6) || UPW <= 2;
     static_assert(!PX || (kUncond && (UPW * TPW < DM ? UPW * TPW : DM) <= 9),
                   "per-unit x staging needs a straight-line ring");
-    static_assert(!BAL || (TPW == 1 && !MX && kUncond), "the balanced plan runs one tile");
+    static_assert(!BAL || (TPW == 1 && kUncond), "the balanced plan runs one tile");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int M = a.M, U = a.U;
@@ -1219,34 +1219,43 @@ int launch_valu(const void* x, int x_dtype, const void* qweight, const void* sca
     return w4h::launch_status();
 }
 
-template <bool BF16>
+template <bool BF16, bool MX = false>
 w4_kernel_t pick_bal(int upw, bool px) {
     (void)upw;   // 17, the planner's only chain length
-    return px ? w4_gemv_kernel<BF16, 4, 17, 1, false, true, true> : w4_gemv_kernel<BF16, 4, 17, 1, false, false, true>;
+    return px ? w4_gemv_kernel<BF16, 4, 17, 1, MX, true, true> : w4_gemv_kernel<BF16, 4, 17, 1, MX, false, true>;
 }
 
-void format_bal(char* b, size_t n, bool bf16, int group, int N, const BalPlan& bp) {
-    snprintf(b, n,
-             "w4_bal16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, 1, false, %s, true> tiles=%d "
-             "workgroups=%d waves=%d+%d pieces=%d lds=%zu px=%d",
-             bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, bp.upw, bp.px ? "true" : "false",
-             pad_n(N) / kTileN, bp.base, kBalFull, kBalExtra, bp.pieces, bp.lds, (int)bp.px);
+void format_bal(char* b, size_t n, bool bf16, bool mx, int group, int N, const BalPlan& bp) {
+    if (mx)
+        snprintf(b, n,
+                 "mxfp4_bal16 %s kernel=w4_gemv_kernel<%s, 4, %d, 1, true, %s, true> tiles=%d "
+                 "workgroups=%d waves=%d+%d pieces=%d lds=%zu px=%d",
+                 bf16 ? "bf16" : "f16", bf16 ? "true" : "false", bp.upw, bp.px ? "true" : "false",
+                 pad_n(N) / kTileN, bp.base, kBalFull, kBalExtra, bp.pieces, bp.lds, (int)bp.px);
+    else
+        snprintf(b, n,
+                 "w4_bal16 %s g%d kernel=w4_gemv_kernel<%s, %d, %d, 1, false, %s, true> tiles=%d "
+                 "workgroups=%d waves=%d+%d pieces=%d lds=%zu px=%d",
+                 bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, bp.upw,
+                 bp.px ? "true" : "false", pad_n(N) / kTileN, bp.base, kBalFull, kBalExtra, bp.pieces, bp.lds,
+                 (int)bp.px);
 }
 
+// The balanced plan's launch, for 4-bit weights (zeros given) or MXFP4 (mx:
+// zeros is null, scales are the E8M0 blocks).
 int launch_bal(const BalPlan& bp, const void* x, int x_dtype, const void* qweight, const void* scales,
                const void* zeros, const void* res, int res_dtype, void* y, int y_dtype, int M, int N, int K,
-               int group, void* workspace, size_t workspace_bytes, hipStream_t st) {
+               int group, void* workspace, size_t workspace_bytes, hipStream_t st, bool mx = false) {
     if (!workspace) return W4A16_ERR_NULL;
     if (workspace_bytes < bp.ws) return W4A16_ERR_WORKSPACE;
     if (!w4h::aligned16(workspace)) return W4A16_ERR_ALIGN;
     static std::once_flag once;
     std::call_once(once, [] {
-        for (bool px : {false, true}) {
-            (void)hipFuncSetAttribute((const void*)pick_bal<false>(17, px),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCu);
-            (void)hipFuncSetAttribute((const void*)pick_bal<true>(17, px),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCu);
-        }
+        for (bool px : {false, true})
+            for (const void* k : {(const void*)pick_bal<false>(17, px), (const void*)pick_bal<true>(17, px),
+                                  (const void*)pick_bal<false, true>(17, px),
+                                  (const void*)pick_bal<true, true>(17, px)})
+                (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCu);
         (void)hipGetLastError();
     });
     const bool bf16 = x_dtype == W4A16_BF16;
@@ -1258,11 +1267,12 @@ int launch_bal(const BalPlan& bp, const void* x, int x_dtype, const void* qweigh
     l.counters = (unsigned*)workspace;
     l.bal_part = (float*)w4h::ws_part(workspace);
     w4h::begin_launches();
-    hipLaunchKernelGGL(bf16 ? pick_bal<true>(bp.upw, bp.px) : pick_bal<false>(bp.upw, bp.px), dim3(bp.base),
-                       dim3(64 * (kBalFull + kBalExtra)), bp.lds, st, (const uint16_t*)x,
+    const w4_kernel_t k = mx ? (bf16 ? pick_bal<true, true>(bp.upw, bp.px) : pick_bal<false, true>(bp.upw, bp.px))
+                             : (bf16 ? pick_bal<true>(bp.upw, bp.px) : pick_bal<false>(bp.upw, bp.px));
+    hipLaunchKernelGGL(k, dim3(bp.base), dim3(64 * (kBalFull + kBalExtra)), bp.lds, st, (const uint16_t*)x,
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros, y, l);
-    char v[160];
-    format_bal(v, sizeof v, bf16, group, N, bp);
+    char v[192];
+    format_bal(v, sizeof v, bf16, mx, group, N, bp);
     w4h::set_last_variant("%s", v);
     return w4h::launch_status();
 }
@@ -1320,7 +1330,7 @@ extern "C" int w4a16_plan_variant(int M, int N, int K, int group, int x_dtype, c
     if (int rc = w4h::check_w4_shape(N, K, group)) return rc;
     const bool bf16 = x_dtype == W4A16_BF16;
     if (const BalPlan bp = bal_plan(M, N, K, group, w4h::cu_count()); bp.ok && overrides().w4_valu != 1) {
-        format_bal(text, text_bytes, bf16, group, N, bp);
+        format_bal(text, text_bytes, bf16, false, group, N, bp);
         return W4A16_OK;
     }
     if (use_gemm(M, N, K, group)) {
@@ -1442,6 +1452,10 @@ extern "C" int mxfp4_workspace_bytes(int M, int N, int K, size_t* bytes) {
     if (!bytes) return W4A16_ERR_NULL;
     if (M < 1 || M > w4h::kMaxRowsGemm || !w4h::x_fits(M, K)) return W4A16_ERR_SHAPE;
     if (int rc = w4h::check_mx_shape(N, K)) return rc;
+    if (const BalPlan b = bal_plan(M, N, K, kMxPlanGroup, w4h::cu_count()); b.ok) {
+        *bytes = b.ws;
+        return W4A16_OK;
+    }
     if (use_gemm(M, N, K, kMxPlanGroup)) {
         *bytes = gemm_workspace(w4h::gemm_plan(M, N, K, kMxPlanGroup, w4h::cu_count()), M, N);
         return W4A16_OK;
@@ -1455,6 +1469,9 @@ extern "C" int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const
                           int y_dtype, int M, int N, int K, void* workspace, size_t workspace_bytes,
                           w4a16_stream_t stream) {
     if (int rc = check_mx_args(x, x_dtype, qweight, scales, y, y_dtype, M, N, K)) return rc;
+    if (const BalPlan bp = bal_plan(M, N, K, kMxPlanGroup, w4h::cu_count()); bp.ok)
+        return launch_bal(bp, x, x_dtype, qweight, scales, nullptr, nullptr, W4A16_F32, y, y_dtype, M, N, K,
+                          kMxPlanGroup, workspace, workspace_bytes, (hipStream_t)stream, true);
     if (use_gemm(M, N, K, kMxPlanGroup)) {
         // Rows past the GEMV's crossover: the M-tiled kernel's MXFP4 mode.
         const w4h::GemmPlan gp = w4h::gemm_plan(M, N, K, kMxPlanGroup, w4h::cu_count());

@@ -242,8 +242,9 @@ int mxfp4_unpack(const void* qweight, const void* scales, uint8_t* qweight_canon
  * largest) and the span's fp32 sum takes the remaining power of two; wider
  * spans take the MX specification's block dot product literally, each
  * block's fp32 sum times its own 2^(E - 127).  Deterministic.  Dtypes,
- * alignment, workspace and overlap rules as for w4a16_gemv; workspace size
- * from mxfp4_workspace_bytes. */
+ * alignment, workspace and overlap rules as for w4a16_gemv, whose plans it
+ * shares (the balanced plan included, as at g = 128); workspace size from
+ * mxfp4_workspace_bytes. */
 int mxfp4_workspace_bytes(int M, int N, int K, size_t* bytes);
 int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const void* scales, void* y,
                int y_dtype, int M, int N, int K, void* workspace, size_t workspace_bytes,

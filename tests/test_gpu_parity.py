@@ -646,6 +646,34 @@ def test_balanced_plan_repeat_calls_and_graph_replays(M, xdt):
     assert int(ws[:WS_HEAD].count_nonzero()) == 0
 
 
+_BAL_MX = {}
+
+
+def _bal_mx_matrix(N):
+    if N not in _BAL_MX:
+        _BAL_MX.clear()
+        w = synth.gen_mx((154, N), N, BAL_K)
+        _BAL_MX[N] = (w, PackedMX(w, N, BAL_K))
+    return _BAL_MX[N]
+
+
+@pytest.mark.parametrize("M,N,xdt", [(1, 5120, "f16"), (1, 5112, "bf16"), (2, 5120, "bf16"),
+                                     (3, 5112, "f16"), (4, 5120, "bf16"), (4, 5112, "f16")])
+def test_mxfp4_balanced_plan_matches_oracle(M, N, xdt):
+    # MXFP4 weights on the same layer shapes take the same plan.
+    say(f"mxfp4 balanced M={M} N={N} x={xdt}")
+    w, P = _bal_mx_matrix(N)
+    x = synth.gen_x((155, M, N), M, BAL_K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    y = to_f64(P.gemv(dev(x), xdt, M))
+    variant = L.w4a16_last_variant()
+    say("  variant: " + variant)
+    assert variant.startswith("mxfp4_bal16") and "pieces=4" in variant
+    assert ("px=1" in variant) == (M == 4)
+    cols = _bal_cols(N, 20 + M)
+    ref = oracle.mx_gemv(x, xdt, w["qweight"], w["scales"], M, N, BAL_K, cols=cols)
+    assert_parity(y[:, cols], ref, f"mxfp4 balanced M={M} N={N}")
+
+
 # ------------------------------------------------------- determinism and graphs ---
 
 def test_repeat_calls_and_graph_replay_are_bitwise_identical():
@@ -693,9 +721,12 @@ def _graph_replays_match(call, y, y0, eager):
         assert torch.equal(eager(), y0)          # eager work between replays
 
 
-@pytest.mark.parametrize("M,N,K", [(4, 5120, 17408), (64, 2064, 1280), (1, 4104, 5120)])
+@pytest.mark.parametrize("M,N,K", [(1, 5120, 17408), (4, 5120, 17408), (5, 5120, 17408),
+                                   (64, 2064, 1280), (1, 4104, 5120)])
 def test_mxfp4_repeat_calls_and_graph_replay_are_bitwise_identical(M, N, K):
-    # GEMV with K slices, the M-tiled kernel, and a plain GEMV.
+    # The balanced plan (whole-range and per-unit x staging; it merges four
+    # pieces across workgroups), GEMV with K slices, the M-tiled kernel, and
+    # a plain GEMV.  Every balanced call leaves the arrival counters at zero.
     say(f"mxfp4 determinism M={M} N={N} K={K}")
     w = synth.gen_mx((129, M), N, K)
     P = PackedMX(w, N, K)
@@ -709,6 +740,10 @@ def test_mxfp4_repeat_calls_and_graph_replay_are_bitwise_identical(M, N, K):
     _graph_replays_match(
         lambda s: L.mxfp4_gemv(x, "bf16", P.q, P.s, y, "f32", M, N, K, ws, wsb, stream=s),
         y, y0, lambda: P.gemv(x, "bf16", M))
+    torch.cuda.synchronize()
+    if K == 17408 and M <= 4:
+        assert L.w4a16_last_variant().startswith("mxfp4_bal16")
+        assert int(ws[:WS_HEAD].count_nonzero()) == 0
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 5120, 5120), (24, 1032, 2048)])
