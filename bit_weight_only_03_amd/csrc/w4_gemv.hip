@@ -62,6 +62,16 @@ constexpr int kMaxWaves = 8;     // waves per workgroup (the kernel's 512-thread
 // waves.
 constexpr int kBalFull = 8, kBalExtra = 8, kBalMaxPieces = 4;
 constexpr int bal_extra_cl(int upw) { return (upw + 3) / 4; }
+// Slots in flight per full wave of the balanced plan (4; 3 with per-unit x
+// staging).  Measured on down-shaped layers (graphs of 64 distinct matrices,
+// us per call at 1 / 4 rows): 9 slots 11.8 / 14.0, 6 slots 11.5 / 13.2, 4
+// slots 11.1 / 12.4, 3 slots 11.2 / 12.2, 2 slots 13.1 / 13.4.  A per-wave
+// timeline with 9 slots showed why: each of the grid's 2048 full waves put
+// 9 units in the memory queues at once, so a wave's first unit arrived
+// after about half of that 18 MB burst (4.8 us median), and the waves'
+// dequantization work then bunched up behind it.  Fewer slots per wave keep
+// enough bytes in flight for the read rate while each unit waits less.
+constexpr int bal_full_ring(bool px) { return px ? 3 : 4; }
 constexpr int kCounterStride = 32;   // unsigneds between arrival counters (one per 128-byte line)
 constexpr int kMaxRows = 16;     // rows per MFMA
 constexpr int kMaxXLoads = 16;   // x load instructions per wave: M * 16 UPW <= 64 * 16
@@ -133,7 +143,7 @@ __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_
     constexpr int NG = SPG >= 4 ? 1 : 4 / SPG;          // groups per unit
     constexpr int SPU = SPG >= 4 ? 4 : SPG;             // steps per group inside one unit
     constexpr int L = CL * TPW;                          // units in this wave's chain
-    constexpr int DM = TPW > 1 ? 5 : max_slots<SPG>();
+    constexpr int DM = BAR == 1 ? bal_full_ring(PX) : TPW > 1 ? 5 : max_slots<SPG>();
     constexpr int D = L < DM ? L : DM;
     constexpr bool kUncond = SPG >= 4 || (SPG == 2 && CL <= 6) || CL <= 2;
     constexpr int LPS = MX ? 2 : 1 + 2 * NG;              // loads per ring slot
@@ -512,7 +522,7 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
     // bal_extra_cl(UPW) units; PX: kDE units), the full waves' partial sums
     // [bal_full][M][16], the extra waves' [kBalExtra][M][16], and the extra
     // waves' arrival count.
-    constexpr int kDF = UPW < max_slots<SPG>() ? UPW : max_slots<SPG>();
+    constexpr int kDF = UPW < bal_full_ring(PX) ? UPW : bal_full_ring(PX);
     constexpr int kDE = bal_extra_cl(UPW) < max_slots<SPG>() ? bal_extra_cl(UPW) : max_slots<SPG>();
     const size_t xfull = PX ? (size_t)kDF * 1024 : (size_t)M * a.xstride * 2;
     const size_t xext = PX ? (size_t)kDE * 1024 : (size_t)M * bal_extra_cl(UPW) * kUnitK * 2;
@@ -1044,11 +1054,11 @@ BalPlan bal_plan(int M, int N, int K, int group, int cus) {
     if (((U + P - 1) / P + kBalExtra - 1) / kBalExtra > cle) return b;   // extra waves' chain
     // the full and extra waves' x regions, both partial areas, the extra
     // waves' count.  Where whole-range staging does not fit (4 rows), x is
-    // staged unit by unit into rings of each chain's slots (9 and 5).
+    // staged unit by unit into rings of each chain's slots (3 and 5).
     const size_t tail = (size_t)(kBalFull + kBalExtra) * M * kTileN * 4 + 16;
     b.lds = (size_t)M * kUnitK * 2 * (kBalFull * upw + kBalExtra * cle) + tail;
     b.px = b.lds > 160 * 1024 || w4h::overrides().w4_px == 1;
-    if (b.px) b.lds = (size_t)1024 * (kBalFull * 9 + kBalExtra * (cle < 9 ? cle : 9)) + tail;
+    if (b.px) b.lds = (size_t)1024 * (kBalFull * bal_full_ring(true) + kBalExtra * (cle < 9 ? cle : 9)) + tail;
     if (b.lds > 160 * 1024) return b;
     if ((size_t)r * kCounterStride * sizeof(unsigned) > w4h::kWsHead) return b;
     b.ok = true;
