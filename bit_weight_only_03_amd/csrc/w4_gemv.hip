@@ -129,11 +129,16 @@ constexpr int max_slots() { return SPG >= 4 ? 9 : (SPG == 2 ? 7 : 5); }
 // UPW except for the balanced plan's extra waves, which run a shorter chain).
 // xsb is the wave's LDS region (M rows of UPW units, or PX's per-unit slots).
 // BAR = 1 and 2 are the balanced plan's full and extra waves; an extra
-// wave's region holds M rows of CL units.  Two workgroup barriers order
-// their memory traffic: every wave issues its x loads before the first, the
-// extra waves issue their weight loads between the two and the full waves
-// theirs after the second.  So each wave's x comes first, and the extra
-// waves' shares, which are merged across workgroups, finish early.
+// wave's region holds M rows of CL units.  Workgroup barriers order their
+// memory traffic so that the extra waves' shares, which are merged across
+// workgroups, finish early: the full waves issue their weight loads only
+// after every extra wave has issued its own.  With whole-range x staging
+// that is the only barrier (each wave's x goes out at its start); with
+// per-unit staging a first barrier also waits for every wave to start.
+// Measured on down-shaped layers (us per call, graphs of 32 distinct
+// matrices, f16 x at 1 / 2 / 3 rows): 11.0-11.5 / 11.1 / 11.3-11.5 with the
+// one barrier against 11.5-11.8 / 11.5-11.6 / 11.6 with a second one that
+// first had every wave issue its x, and 12.4-12.7 with no barrier.
 template <bool BF16, int SPG, int UPW, int TPW, bool MX, bool PX, int CL, int BAR = 0>
 __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_t* __restrict__ x,
                                               const u32x4_t* __restrict__ qdev,
@@ -268,14 +273,13 @@ __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_
         }
     };
 
-    // Balanced plan: no wait before either barrier, so the loads stay in
-    // flight.
+    // Balanced plan: no wait before a barrier, so the loads stay in flight.
     if constexpr (BAR == 1) {
-        __builtin_amdgcn_s_barrier();   // every wave's x loads are out
-        __builtin_amdgcn_s_barrier();   // the extra waves' weight loads are out
+        if constexpr (PX) __builtin_amdgcn_s_barrier();   // every wave has started
+        __builtin_amdgcn_s_barrier();                     // the extra waves' weight loads are out
         __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (BAR == 2) {
+    if constexpr (BAR == 2 && PX) {
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     }
