@@ -1272,3 +1272,25 @@ def test_w2t_random_shapes_match_oracle(M, N, K, g, xdt, ydt):
     say("  variant: " + L.w4a16_last_variant())
     ref = oracle.w2t_gemv(x, xdt, w["codes"], w["scales"], M, N, K, g)
     assert_parity(to_f64(y), ref, "w2t random", extra_rel=_ROUND[ydt])
+
+
+# ------------------------------------------------------------ read probe ---
+
+@pytest.mark.parametrize("n16", [4096 * 37 + 3, 1000])
+def test_bw_probe_reads_each_word_once(n16):
+    # Each workgroup folds its own contiguous share of the buffer with XOR;
+    # its sink entry is the low 16 bits of that fold (a ragged last share,
+    # and zero for workgroups whose share is empty).
+    say(f"bw probe n16={n16}")
+    rng = np.random.default_rng(160 + n16)
+    host = rng.integers(0, 2 ** 32, size=n16 * 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to(DEV)
+    nsink = L.w4a16_bw_probe_sink_floats()
+    sink = torch.full((nsink,), -1.0, dtype=torch.float32, device=DEV)
+    L.w4a16_bw_probe(buf, n16 * 16, sink)
+    torch.cuda.synchronize()
+    per = -(-n16 // nsink)
+    padded = np.zeros(nsink * per * 4, dtype=np.uint32)
+    padded[:host.size] = host
+    expect = np.bitwise_xor.reduce(padded.reshape(nsink, per * 4), axis=1) & 0xFFFF
+    assert np.array_equal(sink.cpu().numpy(), expect.astype(np.float32))
