@@ -73,6 +73,15 @@ constexpr int bal_extra_cl(int upw) { return (upw + 3) / 4; }
 // enough bytes in flight for the read rate while each unit waits less.
 constexpr int bal_full_ring(bool px) { return px ? 3 : 4; }
 constexpr int kCounterStride = 32;   // unsigneds between arrival counters (one per 128-byte line)
+// Uneven split of three-tile, 5-unit chains (g = 128, per-unit x staging; see
+// the kernel): waves 0 .. kSkewOld - 1 take 6 units, the later ones 4.
+constexpr int kSkewOld = 4;
+constexpr bool skewed_split(int spg, int upw, int tpw, bool mx, bool px) {
+    return px && !mx && spg >= 4 && upw == 5 && tpw == 3;
+}
+constexpr int skew_units(int w) {   // first unit of wave w's region (= units of waves 0 .. w - 1)
+    return w < kSkewOld ? 6 * w : 6 * kSkewOld + 4 * (w - kSkewOld);
+}
 constexpr int kMaxRows = 16;     // rows per MFMA
 constexpr int kMaxXLoads = 16;   // x load instructions per wave: M * 16 UPW <= 64 * 16
 
@@ -129,7 +138,8 @@ constexpr int max_slots() { return SPG >= 4 ? 9 : (SPG == 2 ? 7 : 5); }
 // UPW except for the balanced plan's extra waves, which run a shorter chain).
 // xsb is the wave's LDS region (M rows of UPW units, or PX's per-unit slots).
 // BAR = 1 and 2 are the balanced plan's full and extra waves; an extra
-// wave's region holds M rows of CL units.  Workgroup barriers order their
+// wave's region holds M rows of CL units.  BAR = 4: a wave of an uneven
+// split (per-unit staging, one x slot per unit of its CL).  Workgroup barriers order their
 // memory traffic so that the extra waves' shares, which are merged across
 // workgroups, finish early: the full waves issue their weight loads only
 // after every extra wave has issued its own.  With whole-range x staging
@@ -158,7 +168,7 @@ __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_
     // PX: x slots in the wave's region.  The balanced plan's waves reuse a
     // ring of D (unit i in slot i % D: its x load goes out with the refill
     // after unit i - D's products, whose fragment reads have completed).
-    constexpr int XR = BAR != 0 ? D : UPW;
+    constexpr int XR = BAR == 4 ? CL : BAR != 0 ? D : UPW;
     const int M = a.M, K = a.K, U = a.U;
     const int lane = threadIdx.x & 63;
     const int nu = w1 - w0;                                           // units of this wave
@@ -517,6 +527,25 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
     int nt = a.T - t0 < TPW ? a.T - t0 : TPW;                         // tiles of this workgroup
     const int r0 = split * U / a.S, r1 = (split + 1) * U / a.S;
     int w0 = r0 + wave * (r1 - r0) / W, w1 = r0 + (wave + 1) * (r1 - r0) / W;
+    // Three-tile chains of 5 units (g = 128, per-unit staging, eight waves):
+    // waves 0-3 take 6 units and waves 4-7 take 4.  A wave's first unit
+    // arrives in the order the grid issued its ring: every CU's first four
+    // waves (the first on each SIMD) before its next four, which on a
+    // 27B-class gate_up received theirs 1.5 us later (median 3.8 against
+    // 2.3 us) and so ended their equal chains 1.4 us later, while the
+    // others waited at the reduction barrier.  Measured (graphs of 64
+    // distinct matrices, us per call): gate_up 19.4 -> 18.9 at M = 4 (bf16),
+    // 17.6 either way at M = 1; 7 and 3 units, 19.2 and 20.6.
+    // With fewer than eight waves (a shorter K) the first four still take 6
+    // units each, which covers the range (6 min(W, 4) + 4 max(W - 4, 0) >=
+    // 5 W for W <= 8); the planner sizes the LDS for these regions.
+    constexpr bool skew = skewed_split(SPG, UPW, TPW, MX, PX) && !BAL;
+    if constexpr (skew) {
+        w0 = r0 + skew_units(wave);
+        w1 = w0 + (wave < kSkewOld ? UPW + 1 : UPW - 1);
+        if (w0 > r1) w0 = r1;
+        if (w1 > r1) w1 = r1;
+    }
     // Balanced plan: waves 0 .. bal_full - 1 split the workgroup's own tile
     // over K; each later ("extra") wave takes a share of piece blockIdx.x %
     // bal_pieces of leftover tile bal_base + blockIdx.x / bal_pieces.
@@ -557,7 +586,9 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
     // (the layouts are described in w4_wave_chain).
     uint8_t* const xsb = extra ? xextra + (size_t)(wave - a.bal_full) * xext
                          : BAL ? smem + (size_t)wave * xfull
-                               : smem + (PX ? (size_t)wave * UPW * 1024 : (size_t)wave * M * a.xstride * 2);
+                               : smem + (skew ? (size_t)skew_units(wave) * 1024
+                                         : PX  ? (size_t)wave * UPW * 1024
+                                               : (size_t)wave * M * a.xstride * 2);
     const int c = lane & 15, kc = lane >> 4;
     float4_t total[TPW];
     if constexpr (BAL) {
@@ -566,6 +597,13 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
                                                                          w1, total);
         else
             w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, UPW, 1>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0, w1, total);
+    } else if constexpr (skew) {
+        if (wave < kSkewOld)
+            w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, UPW + 1, 4>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0, w1,
+                                                                  total);
+        else
+            w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, UPW - 1, 4>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0, w1,
+                                                                  total);
     } else {
         w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, UPW>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0, w1, total);
     }
@@ -665,11 +703,13 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
         if (WR == kMaxWaves) {
             float pw[kMaxWaves];
 #pragma unroll
-            for (int w = 0; w < kMaxWaves; ++w) pw[w] = red0[w * rstride + (j * M + m) * kTileN + cc];
+            for (int w = 0; w < kMaxWaves; ++w)
+                pw[w] = red0[(skew ? (size_t)skew_units(w) * 256 : w * rstride) + (j * M + m) * kTileN + cc];
 #pragma unroll
             for (int w = 0; w < kMaxWaves; ++w) v += pw[w];
         } else {
-            for (int w = 0; w < WR; ++w) v += red0[w * rstride + (j * M + m) * kTileN + cc];
+            for (int w = 0; w < WR; ++w)
+                v += red0[(skew ? (size_t)skew_units(w) * 256 : w * rstride) + (j * M + m) * kTileN + cc];
         }
         const int n = (t0 + j) * kTileN + cc;
         if (j < nt && n < a.N) {
@@ -849,7 +889,9 @@ Plan make_plan(int M, int N, int K, int group, int cus, bool allow_px) {
     // load per unit ran 15.8 against 14.2 us there.
     p.px = allow_px && M <= 4 && K % kUnitK == 0 && px_compiled(group, upw, p.tpw);
     if (tu.w4_px == 0) p.px = false;   // A/B only
-    if (p.px) p.lds = (size_t)W * upw * 1024;
+    // (The uneven split of three-tile 5-unit chains needs its regions' units,
+    // skew_units(W) >= 5 W; MXFP4 runs the even split in the same plan.)
+    if (p.px) p.lds = (size_t)(skewed_split(group / 32, upw, p.tpw, false, true) ? skew_units(W) : W * upw) * 1024;
     p.tiles = T;
     return p;
 }

@@ -216,6 +216,27 @@ def test_w4_gemv_per_unit_x_staging(M, N, K, g, xdt, px):
     assert_parity(y[:, cols], ref, f"per-unit x M={M} K={K}")
 
 
+# Three-tile chains of 5 units (g = 128, per-unit x staging) split K
+# unevenly: the first four waves take 6 units, the rest 4.  With a shorter K
+# the later waves' ranges shrink or vanish (33 units: 6, 6, 6, 6, 4, 4, 1, 0).
+@pytest.mark.parametrize("M,K,xdt", [(1, 4224, "f16"), (4, 4224, "bf16"), (2, 4608, "f16"),
+                                     (3, 5120, "bf16")])
+def test_w4_gemv_uneven_wave_split(M, K, xdt):
+    N = 24592   # 1537 tiles: the last workgroup has one
+    say(f"uneven split M={M} N={N} K={K} x={xdt}")
+    key = (161, M, K)
+    w = synth.gen_w4(key, N, K, 128)
+    x = synth.gen_x(key, M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    P = PackedW4(w, N, K, 128)
+    y = to_f64(P.gemv(dev(x), xdt, M))
+    variant = L.w4a16_last_variant()
+    say("  variant: " + variant)
+    assert "upw=5 tpw=3" in variant and "px=1" in variant and "slices=1 " in variant
+    cols = sample_cols(N, np.random.default_rng(K + M), n=256)
+    ref = oracle.w4_gemv(x, xdt, w["qweight"], w["scales"], w["zeros"], M, N, K, 128, cols=cols)
+    assert_parity(y[:, cols], ref, f"uneven split M={M} K={K}")
+
+
 # M-tiled kernel (more rows than one MFMA block): 2 to 4 row blocks, one or
 # two tiles per wave, every group size, ragged N (a last tile of 8 columns)
 # and ragged K (a last unit of 64 k), with and without K slices.
