@@ -82,6 +82,18 @@ constexpr bool skewed_split(int spg, int upw, int tpw, bool mx, bool px) {
 constexpr int skew_units(int w) {   // first unit of wave w's region (= units of waves 0 .. w - 1)
     return w < kSkewOld ? 6 * w : 6 * kSkewOld + 4 * (w - kSkewOld);
 }
+// The balanced plan's full waves split their tile the same way: the first
+// four take UPW + 1 units, the later four UPW - 1 (8 UPW in all).  On the
+// down-shaped layers (graphs of 32 distinct matrices, us per call, f16 /
+// bf16 x): M = 1 11.2-11.3 / 11.2 -> 11.0 / 10.7-10.9, M = 2 11.0-11.2 /
+// 11.9-12.5 -> 10.7 / 11.3-11.4, M = 3 11.2-11.3 / 12.4-12.5 -> 10.9-11.3 /
+// 12.0-12.2, M = 4 12.0-12.1 / 12.3-12.5 -> 11.7-11.8 / 12.1-12.2; the
+// per-wave timeline had shown waves 4-7 ending 0.9 us (M = 1) and 1.5 us
+// (M = 4) after waves 0-3.  UPW + 2 and UPW - 2 spilled registers.
+template <int UPW>
+constexpr int bal_full_units(int w) {   // first unit of full wave w (w = 8: all of them)
+    return w < kSkewOld ? (UPW + 1) * w : (UPW + 1) * kSkewOld + (UPW - 1) * (w - kSkewOld);
+}
 constexpr int kMaxRows = 16;     // rows per MFMA
 constexpr int kMaxXLoads = 16;   // x load instructions per wave: M * 16 UPW <= 64 * 16
 
@@ -164,7 +176,7 @@ __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_
     constexpr int LPS = MX ? 2 : 1 + 2 * NG;              // loads per ring slot
     using SlotT = typename SlotSel<NG, MX>::type;
     constexpr bool kCvtX = BF16 && !MX;   // bf16 x taken to fp16 in LDS for the 4-bit products
-    constexpr int XU = BAR == 2 ? CL : UPW;   // units per staged row (= xstride / 128 otherwise)
+    constexpr int XU = BAR == 1 || BAR == 2 ? CL : UPW;   // units per staged row (= xstride / 128 otherwise)
     // PX: x slots in the wave's region.  The balanced plan's waves reuse a
     // ring of D (unit i in slot i % D: its x load goes out with the refill
     // after unit i - D's products, whose fragment reads have completed).
@@ -570,8 +582,10 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         const int WF = a.bal_full;
         if (!extra) {
-            w0 = wave * U / WF;
-            w1 = (wave + 1) * U / WF;
+            // The full waves' 8 x UPW units, the first four taking UPW + 1
+            // each and the later four UPW - 1 (see bal_full_units).
+            w0 = bal_full_units<UPW>(wave);
+            w1 = bal_full_units<UPW>(wave + 1);
         } else {
             const int P = a.bal_pieces, WE = W - WF, pc = blockIdx.x % P, e = wave - WF;
             const int pa = pc * U / P, pb = (pc + 1) * U / P;
@@ -585,7 +599,7 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
     // 2 w M xstride; PX: [UPW units][4 rows][256 bytes] at w UPW 1024 bytes
     // (the layouts are described in w4_wave_chain).
     uint8_t* const xsb = extra ? xextra + (size_t)(wave - a.bal_full) * xext
-                         : BAL ? smem + (size_t)wave * xfull
+                         : BAL ? smem + (PX ? (size_t)wave * xfull : (size_t)M * 256 * bal_full_units<UPW>(wave))
                                : smem + (skew ? (size_t)skew_units(wave) * 1024
                                          : PX  ? (size_t)wave * UPW * 1024
                                                : (size_t)wave * M * a.xstride * 2);
@@ -595,8 +609,12 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
         if (extra)
             w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, bal_extra_cl(UPW), 2>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0,
                                                                          w1, total);
+        else if (wave < kSkewOld)
+            w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, UPW + 1, 1>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0, w1,
+                                                                  total);
         else
-            w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, UPW, 1>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0, w1, total);
+            w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, UPW - 1, 1>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0, w1,
+                                                                  total);
     } else if constexpr (skew) {
         if (wave < kSkewOld)
             w4_wave_chain<BF16, SPG, UPW, TPW, MX, PX, UPW + 1, 4>(a, x, qdev, sdev, zdev, xsb, t0, nt, w0, w1,

@@ -69,8 +69,9 @@ def is_vmem_load(line):
 def check_x_wait(lines, expect=1):
     """Returns None if the function's explicit x waits are safe, else a
     reason.  A kernel has one such wait per wave chain it compiles: one, or
-    two for the balanced plan (its full and extra waves run chains of
-    different lengths, in separate straight-line blocks)."""
+    three for the balanced plan (its extra waves and the two halves of its
+    full waves run chains of different lengths, in separate straight-line
+    blocks)."""
     waits = [i for i, l in enumerate(lines)
              if re.fullmatch(r"s_waitcnt vmcnt\(\d+\)", l) and lines[i - 1].startswith(";;#ASMSTART")]
     if len(waits) != expect:
@@ -95,15 +96,41 @@ def check_x_wait(lines, expect=1):
                 return f"control flow after only {count} of {n} ring loads ({line})"
         if count < n:
             return f"only {count} loads before vmcnt({n})"
-        # No LDS read between the chain's first x load (the first after the
-        # previous wait) and its wait.
+        # No LDS read on any path from the chain's first x load (the first
+        # after the previous wait) to its wait.  (Following branches, not the
+        # layout: the compiler may place another chain's blocks in between.)
         xs = [i for i in range(prev, w) if is_vmem_load(lines[i]) and " lds" in lines[i]]
         if not xs:
             return f"no x load before vmcnt({n})"
-        if any(l.startswith("ds_read") for l in lines[xs[0]:w]):
+        if any(lines[i].startswith("ds_read") for i in lines_on_paths(lines, xs[0], w)):
             return "an LDS read precedes the x wait"
         prev = w
     return None
+
+
+def lines_on_paths(lines, a, b):
+    """Indices of the lines on some control-flow path from line a to line b
+    (not past b), following fall-through and branch targets."""
+    labels = {l[:-1]: i for i, l in enumerate(lines) if l.endswith(":") and not l.startswith(";")}
+    seen, stack, out = set(), [a], set()
+    while stack:
+        i = stack.pop()
+        while i < len(lines) and i not in seen:
+            seen.add(i)
+            if i == b:
+                break
+            out.add(i)
+            l = lines[i]
+            if l.startswith(("s_cbranch", "s_branch")):
+                target = l.split()[-1]
+                if target in labels:
+                    stack.append(labels[target])
+                if l.startswith("s_branch"):
+                    break
+            elif l.startswith(("s_endpgm", "s_setpc")):
+                break
+            i += 1
+    return out
 
 
 def check_unit_x_waits(lines):
@@ -148,7 +175,7 @@ def test_x_wait_covers_the_x_loads(asm_files):
             # <BF16, SPG, UPW, TPW, MX, PX = true, BAL>
             px = re.search(r"kernelILb[01]ELi\d+ELi\d+ELi\d+ELb[01]ELb1E", name) is not None
             bal = re.search(r"kernelILb[01]ELi\d+ELi\d+ELi\d+ELb[01]ELb[01]ELb1E", name) is not None
-            why = check_unit_x_waits(lines) if px else check_x_wait(lines, 2 if bal else 1)
+            why = check_unit_x_waits(lines) if px else check_x_wait(lines, 3 if bal else 1)
             if why:
                 bad.append(f"{src} {name}: {why}")
     # every 4-bit and staged ternary instantiation stages x this way
@@ -170,3 +197,24 @@ def test_no_inline_asm_besides_the_x_wait(asm_files):
                     if body and not (len(body) == 1 and re.fullmatch(r"s_waitcnt vmcnt\(\d+\)", body[0])):
                         bad.append(f"{src} {name}: {body}")
     assert not bad, "\n".join(bad[:10])
+
+
+def test_x_wait_checker_on_synthetic_code():
+    # The checker itself, on hand-written sequences: one x load, two ring
+    # loads, the wait for them.
+    head = ["buffer_load_dwordx4 v2, s[0:3], 0 offen lds",
+            "buffer_load_dwordx4 v[4:7], v1, s[4:7], 0 offen",
+            "buffer_load_dword v8, v1, s[8:11], 0 offen"]
+    wait = [";;#ASMSTART", "s_waitcnt vmcnt(2)", ";;#ASMEND"]
+    assert check_x_wait(head + wait) is None
+    # an LDS read on the way to the wait
+    assert "LDS read" in check_x_wait(head[:1] + ["ds_read_b128 v[10:13], v9"] + head[1:] + wait)
+    # a block that is jumped over (another chain's) is not on the path...
+    jumped = head[:1] + ["s_branch .LBB0_2", ".LBB0_1:", "ds_read_b128 v[10:13], v9", ".LBB0_2:"] + head[1:]
+    assert check_x_wait(jumped + wait) is None
+    # ...but one reached by a branch is
+    taken = head[:1] + ["s_cbranch_execz .LBB0_1", "s_branch .LBB0_2", ".LBB0_1:",
+                        "ds_read_b128 v[10:13], v9", ".LBB0_2:"] + head[1:]
+    assert "LDS read" in check_x_wait(taken + wait)
+    # too few ring loads after the x load
+    assert check_x_wait(head[:2] + wait) is not None
