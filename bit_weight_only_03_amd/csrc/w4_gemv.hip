@@ -73,11 +73,12 @@ constexpr int bal_extra_cl(int upw) { return (upw + 3) / 4; }
 // enough bytes in flight for the read rate while each unit waits less.
 constexpr int bal_full_ring(bool px) { return px ? 3 : 4; }
 constexpr int kCounterStride = 32;   // unsigneds between arrival counters (one per 128-byte line)
-// Uneven split of three-tile, 5-unit chains (g = 128, per-unit x staging; see
-// the kernel): waves 0 .. kSkewOld - 1 take 6 units, the later ones 4.
+// Uneven split of three-tile, 5-unit chains (g = 128 or MXFP4, per-unit x
+// staging; see the kernel): waves 0 .. kSkewOld - 1 take 6 units, the later
+// ones 4.
 constexpr int kSkewOld = 4;
-constexpr bool skewed_split(int spg, int upw, int tpw, bool mx, bool px) {
-    return px && !mx && spg >= 4 && upw == 5 && tpw == 3;
+constexpr bool skewed_split(int spg, int upw, int tpw, bool px) {
+    return px && spg >= 4 && upw == 5 && tpw == 3;
 }
 constexpr int skew_units(int w) {   // first unit of wave w's region (= units of waves 0 .. w - 1)
     return w < kSkewOld ? 6 * w : 6 * kSkewOld + 4 * (w - kSkewOld);
@@ -547,11 +548,13 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
     // 2.3 us) and so ended their equal chains 1.4 us later, while the
     // others waited at the reduction barrier.  Measured (graphs of 64
     // distinct matrices, us per call): gate_up 19.4 -> 18.9 at M = 4 (bf16),
-    // 17.6 either way at M = 1; 7 and 3 units, 19.2 and 20.6.
+    // 17.6 either way at M = 1; 7 and 3 units, 19.2 and 20.6.  MXFP4 gate_up
+    // (16 distinct matrices): 19.6-20.4 -> 19.2-19.6 at M = 1, 19.7-21.6 ->
+    // 18.8-20.5 at M = 4.
     // With fewer than eight waves (a shorter K) the first four still take 6
     // units each, which covers the range (6 min(W, 4) + 4 max(W - 4, 0) >=
     // 5 W for W <= 8); the planner sizes the LDS for these regions.
-    constexpr bool skew = skewed_split(SPG, UPW, TPW, MX, PX) && !BAL;
+    constexpr bool skew = skewed_split(SPG, UPW, TPW, PX) && !BAL;
     if constexpr (skew) {
         w0 = r0 + skew_units(wave);
         w1 = w0 + (wave < kSkewOld ? UPW + 1 : UPW - 1);
@@ -908,8 +911,8 @@ Plan make_plan(int M, int N, int K, int group, int cus, bool allow_px) {
     p.px = allow_px && M <= 4 && K % kUnitK == 0 && px_compiled(group, upw, p.tpw);
     if (tu.w4_px == 0) p.px = false;   // A/B only
     // (The uneven split of three-tile 5-unit chains needs its regions' units,
-    // skew_units(W) >= 5 W; MXFP4 runs the even split in the same plan.)
-    if (p.px) p.lds = (size_t)(skewed_split(group / 32, upw, p.tpw, false, true) ? skew_units(W) : W * upw) * 1024;
+    // skew_units(W) >= 5 W.)
+    if (p.px) p.lds = (size_t)(skewed_split(group / 32, upw, p.tpw, true) ? skew_units(W) : W * upw) * 1024;
     p.tiles = T;
     return p;
 }
