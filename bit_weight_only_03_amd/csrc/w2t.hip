@@ -178,13 +178,20 @@ constexpr int min_waves2() { return SPG >= 4 && UPW <= 4 ? 8 : 1; }
 // A wave's missing units load as zeros (code 0 and scale +0): the group sums
 // they feed are multiplied by a zero scale and add exactly 0, so the
 // arithmetic runs unconditionally and each wait covers one slot.
-template <bool BF16, int SPG, int UPW>
-__global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel(
+//
+// TPW > 1 (layers of many tiles): the workgroup takes TPW consecutive tiles
+// and each wave's chain runs unit-major over them, position q = unit q / TPW
+// of tile q % TPW, so the workgroup stages x once for all of them (the
+// 4-bit kernel's three-tile workgroups, for the same reason).
+template <bool BF16, int SPG, int UPW, int TPW = 1>
+__global__ __launch_bounds__(512, (TPW > 1 ? 4 : min_waves2<SPG, UPW>())) void w2t_gemv_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ qdev,
     const uint16_t* __restrict__ sdev, void* __restrict__ out, W2Launch a) {
     constexpr int NG = SPG >= 8 ? 1 : 8 / SPG;   // groups per unit
     constexpr int SPU = SPG >= 8 ? 8 : SPG;      // 32-k steps per group inside one unit
-    constexpr int D = UPW < max_slots2<SPG>() ? UPW : max_slots2<SPG>();
+    static_assert(TPW >= 1 && TPW <= 3, "one to three tiles per workgroup");
+    constexpr int L = UPW * TPW;                 // chain positions
+    constexpr int D = L < max_slots2<SPG>() ? L : max_slots2<SPG>();
     // Unconditional arithmetic where the register budget allows (see below).
     constexpr bool kUncond = SPG >= 4 || UPW <= 2;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -193,7 +200,9 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int t = blockIdx.x, split = blockIdx.y;
+    const int t0 = blockIdx.x * TPW, split = blockIdx.y;
+    const int T = (a.N + kTileN - 1) >> 4;                           // 16-column tiles
+    const int nt = T - t0 < TPW ? T - t0 : TPW;                      // tiles of this workgroup
     const int r0 = split * U / a.S, r1 = (split + 1) * U / a.S;
     const int w0 = r0 + wave * (r1 - r0) / W, w1 = r0 + (wave + 1) * (r1 - r0) / W;
     const int nu = w1 - w0;                                           // units of this wave
@@ -245,21 +254,23 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
     __builtin_amdgcn_sched_barrier(0);
 
     // 2) Weight and scale loads of this wave's units.
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qdev + (size_t)t * U * kLanes, (uint32_t)U * 1024u);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdev + (size_t)t * Gp * kTileN, (uint32_t)Gp * 32u);
+    // The workgroup's nt tiles are contiguous in both arrays.
+    const uint32_t wend = (uint32_t)nt * U * 1024u, send = (uint32_t)nt * Gp * 32u;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qdev + (size_t)t0 * U * kLanes, wend);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sdev + (size_t)t0 * Gp * kTileN, send);
     const uint32_t wlane = (uint32_t)lane * 16u;
     const uint32_t slane = (uint32_t)c * 2u;
-    const uint32_t wend = (uint32_t)U * 1024u, send = (uint32_t)Gp * 32u;
 
-    auto load_slot = [&](int i, Slot2<NG>& r) {   // unit w0 + i
-        const bool valid = i < nu;
+    auto load_slot = [&](int q, Slot2<NG>& r) {   // unit w0 + q / TPW of tile t0 + q % TPW
+        const int i = q / TPW, j = q % TPW;
+        const bool valid = i < nu && j < nt;
         const int u = w0 + i;
         r.w = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
-            rw, valid ? wlane + (uint32_t)u * 1024u : wend, 0, kAuxNT));
+            rw, valid ? wlane + (uint32_t)(j * U + u) * 1024u : wend, 0, kAuxNT));
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi)
             r.s[gi] = __builtin_amdgcn_raw_buffer_load_b16(
-                rs, valid ? slane + (uint32_t)(u * NG + gi) * 32u : send, 0, 0);
+                rs, valid ? slane + (uint32_t)(j * Gp + u * NG + gi) * 32u : send, 0, 0);
     };
 
     Slot2<NG> ring[D];
@@ -279,12 +290,15 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
     const bool xrow = c < M;                                    // lane supplies x row c
     // Step st of unit i: chunk 4 st + kc of row c, at position 4 st + (kc ^ c % 4).
     const uint8_t* xlane = xsb + (uint32_t)(c * xrow_bytes) + 16u * (uint32_t)(kc ^ (c & 3));
-    float4_t total = {0.f, 0.f, 0.f, 0.f};
+    float4_t total[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) total[j] = float4_t{0.f, 0.f, 0.f, 0.f};
     u32x4_t xa[2] = {};
 #pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-        Slot2<NG>& sl = ring[i % D];
-        if (kUncond || i < nu) {
+    for (int q = 0; q < L; ++q) {
+        const int i = q / TPW, tj = q % TPW;
+        Slot2<NG>& sl = ring[q % D];
+        if (kUncond || (i < nu && tj < nt)) {
             float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int dd = 0; dd < 4; ++dd) {
@@ -307,39 +321,49 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
                     }
                     if ((st + 1) % SPU == 0) {    // group complete: scale once, in fp32
                         const float sf = f16_bits_to_f32((uint16_t)sl.s[st / SPU]);
-                        total[0] = __builtin_fmaf(sf, acc[0], total[0]);
-                        total[1] = __builtin_fmaf(sf, acc[1], total[1]);
-                        total[2] = __builtin_fmaf(sf, acc[2], total[2]);
-                        total[3] = __builtin_fmaf(sf, acc[3], total[3]);
+                        total[tj][0] = __builtin_fmaf(sf, acc[0], total[tj][0]);
+                        total[tj][1] = __builtin_fmaf(sf, acc[1], total[tj][1]);
+                        total[tj][2] = __builtin_fmaf(sf, acc[2], total[tj][2]);
+                        total[tj][3] = __builtin_fmaf(sf, acc[3], total[tj][3]);
                         acc = float4_t{0.f, 0.f, 0.f, 0.f};
                     }
                 }
             }
         }
-        if (i + D < UPW) {                 // fixed refill schedule: unit i + D into this slot
+        if (q + D < L) {                   // fixed refill schedule: position q + D into this slot
             __builtin_amdgcn_sched_barrier(0);
-            load_slot(i + D, sl);
+            load_slot(q + D, sl);
         }
         __builtin_amdgcn_sched_barrier(0);   // units in order: each waits for its own slot only
     }
 
-    // 4) Wave partials -> the start of each wave's own x region (its last x
-    //    reads were consumed above, and a wave's LDS accesses complete in
-    //    order), then M x 16 threads add them in wave order.  A wave without
-    //    units has no region; its partial is exactly +0, and skipping it
-    //    leaves the sum unchanged (the sum starts at +0 and so is never -0).
+    // 4) Wave partials [TPW][M][16] -> the start of each wave's own x region
+    //    (TPW M 64 <= M 512 bytes; its last x reads were consumed above, and
+    //    a wave's LDS accesses complete in order), then TPW x M x 16 threads
+    //    add them in wave order.  A wave without units has no region; its
+    //    partial is exactly +0, and skipping it leaves the sum unchanged (the
+    //    sum starts at +0 and so is never -0).
     float* const red = (float*)xsb;
     if (nu > 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 4 * kc + r;
-            if (m < M) red[m * kTileN + c] = total[r];
-        }
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * kc + r;
+                if (m < M) red[(j * M + m) * kTileN + c] = total[j][r];
+            }
     }
     __syncthreads();
     const int sl = r1 - r0;
-    for (int idx = threadIdx.x; idx < M * kTileN; idx += blockDim.x) {
-        const int m = idx >> 4, cc = idx & 15;
+    for (int idx = threadIdx.x; idx < TPW * M * kTileN; idx += blockDim.x) {
+        // idx = (tj M + m) 16 + cc, which is also this output's float in a
+        // wave's partials (no division by M on this path: tj found by
+        // comparison, TPW <= 3).
+        const int cc = idx & 15, tm = idx >> 4;
+        int tj = 0;
+        if constexpr (TPW > 1) tj = (tm >= M) + (tm >= 2 * M);
+        const int m = tm - tj * M;
+        const int po = idx;
         // All partials are read before the first add, then added in wave order.
         float v = 0.f;
         if (W == kWaves2) {
@@ -347,8 +371,7 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
 #pragma unroll
             for (int w = 0; w < kWaves2; ++w) {
                 const int b = w * sl / kWaves2, e = (w + 1) * sl / kWaves2;
-                pw[w] = e > b ? ((const float*)(smem + (size_t)M * (kUnitK2 * 2) * b))[m * kTileN + cc]
-                              : 0.f;
+                pw[w] = e > b ? ((const float*)(smem + (size_t)M * (kUnitK2 * 2) * b))[po] : 0.f;
             }
 #pragma unroll
             for (int w = 0; w < kWaves2; ++w)
@@ -356,11 +379,11 @@ __global__ __launch_bounds__(512, (min_waves2<SPG, UPW>())) void w2t_gemv_kernel
         } else {
             for (int w = 0; w < W; ++w) {
                 const int b = w * sl / W, e = (w + 1) * sl / W;
-                if (e > b) v += ((const float*)(smem + (size_t)M * (kUnitK2 * 2) * b))[m * kTileN + cc];
+                if (e > b) v += ((const float*)(smem + (size_t)M * (kUnitK2 * 2) * b))[po];
             }
         }
-        const int n = t * kTileN + cc;
-        if (n < a.N) {
+        const int n = (t0 + tj) * kTileN + cc;
+        if (tj < nt && n < a.N) {
             const size_t o = (size_t)split * M * a.N + (size_t)m * a.N + n;
             if (a.out_dtype == W4A16_F32)
                 ((float*)out)[o] = v;
@@ -558,7 +581,7 @@ constexpr int kUpwSet2[] = {1, 2, 3, 4, 5, 6, 8, 9, 12, 17};
 
 struct Plan2 {
     W2Launch l;
-    int waves, upw, tiles;
+    int waves, upw, tiles, tpw;
     size_t lds;
 };
 
@@ -599,6 +622,9 @@ Plan2 make_plan2(int M, int N, int K, int cus) {
     p.upw = upw;
     p.tiles = T;
     p.lds = lds;
+    // Three tiles per workgroup when there are many more tiles than the GPU
+    // holds at once (where compiled: the caller checks tpw3_compiled).
+    p.tpw = S == 1 && upw >= 1 && upw <= 4 && T >= 6 * cus ? 3 : 1;
     return p;
 }
 
@@ -634,6 +660,32 @@ w2_kernel_t pick2(bool bf16, int group, int upw) {
     return bf16 ? pick2_group<true>(group, upw) : pick2_group<false>(group, upw);
 }
 
+// Three-tile kernels, compiled where the chain keeps its ring loads in
+// straight-line code (the x wait's condition, checked on the compiled code by
+// a host-side test) and within 128 VGPRs: g = 64 at 3 or 4 units per wave
+// (at 1 or 2 the compiler sinks ring loads into branches), g = 128 at 1 to 3
+// (4 spills), g = 256 at 1 to 4.
+bool tpw3_compiled(int group, int upw) {
+    if (group == 64) return upw == 3 || upw == 4;
+    if (group == 128) return upw >= 1 && upw <= 3;
+    return group == 256 && upw >= 1 && upw <= 4;
+}
+template <bool BF16>
+w2_kernel_t pick2_tpw3_bf(int group, int upw) {
+    if (group == 64) return upw == 3 ? w2t_gemv_kernel<BF16, 2, 3, 3> : w2t_gemv_kernel<BF16, 2, 4, 3>;
+    if (group == 128)
+        return upw == 1 ? w2t_gemv_kernel<BF16, 4, 1, 3>
+             : upw == 2 ? w2t_gemv_kernel<BF16, 4, 2, 3>
+                        : w2t_gemv_kernel<BF16, 4, 3, 3>;
+    return upw == 1 ? w2t_gemv_kernel<BF16, 8, 1, 3>
+         : upw == 2 ? w2t_gemv_kernel<BF16, 8, 2, 3>
+         : upw == 3 ? w2t_gemv_kernel<BF16, 8, 3, 3>
+                    : w2t_gemv_kernel<BF16, 8, 4, 3>;
+}
+w2_kernel_t pick2_tpw3(bool bf16, int group, int upw) {   // tpw3_compiled(group, upw) only
+    return bf16 ? pick2_tpw3_bf<true>(group, upw) : pick2_tpw3_bf<false>(group, upw);
+}
+
 // The staged kernel (split or not) up to 8 rows when its workgroup needs at
 // most half a CU's LDS (two or more workgroups per CU), the direct-x kernel
 // otherwise.  Measured, us per call, staged / direct-x:
@@ -659,11 +711,17 @@ void allow_full_lds2() {
     static std::once_flag once;
     std::call_once(once, [] {
         for (int bf = 0; bf < 2; ++bf)
-            for (int g : {32, 64, 128, 256})
+            for (int g : {32, 64, 128, 256}) {
                 for (int u : kUpwSet2)
                     (void)hipFuncSetAttribute((const void*)pick2(bf, g, u),
                                               hipFuncAttributeMaxDynamicSharedMemorySize,
                                               (int)kLdsPerCu2);
+                for (int u = 1; u <= 4; ++u)
+                    if (tpw3_compiled(g, u))
+                        (void)hipFuncSetAttribute((const void*)pick2_tpw3(bf, g, u),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  (int)kLdsPerCu2);
+            }
         (void)hipGetLastError();
     });
 }
@@ -815,20 +873,27 @@ extern "C" int w2t_gemv(const void* x, int x_dtype, const void* qweight, const v
     allow_full_lds2();
     hipStream_t st = (hipStream_t)stream;
     const bool bf16 = x_dtype == W4A16_BF16;
-    w2_kernel_t k = pick2(bf16, group, p.upw);
+    if (p.tpw > 1 && !tpw3_compiled(group, p.upw)) p.tpw = 1;
+    w2_kernel_t k = p.tpw > 1 ? pick2_tpw3(bf16, group, p.upw) : pick2(bf16, group, p.upw);
     void* out = p.l.S > 1 ? w4h::ws_part(workspace) : y;
     p.l.out_dtype = p.l.S > 1 ? W4A16_F32 : y_dtype;
     w4h::begin_launches();
-    hipLaunchKernelGGL(k, dim3(p.tiles, p.l.S), dim3(64 * p.waves), p.lds, st, (const uint16_t*)x,
-                       (const u32x4_t*)qweight, (const uint16_t*)scales, out, p.l);
+    hipLaunchKernelGGL(k, dim3((p.tiles + p.tpw - 1) / p.tpw, p.l.S), dim3(64 * p.waves), p.lds, st,
+                       (const uint16_t*)x, (const u32x4_t*)qweight, (const uint16_t*)scales, out, p.l);
     if (p.l.S > 1) {
         const int MN = M * N;
         hipLaunchKernelGGL(w2_merge_kernel, dim3((MN + 255) / 256), dim3(256), 0, st,
                            (const float*)w4h::ws_part(workspace), y, y_dtype, MN, p.l.S);
     }
-    w4h::set_last_variant("w2t_mfma16 %s g%d kernel=w2t_gemv_kernel<%s, %d, %d> tiles=%d slices=%d "
-                          "waves=%d upw=%d lds=%zu",
-                          bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.upw,
-                          p.tiles, p.l.S, p.waves, p.upw, p.lds);
+    if (p.tpw > 1)
+        w4h::set_last_variant("w2t_mfma16 %s g%d kernel=w2t_gemv_kernel<%s, %d, %d, %d> tiles=%d slices=%d "
+                              "waves=%d upw=%d tpw=%d lds=%zu",
+                              bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.upw,
+                              p.tpw, p.tiles, p.l.S, p.waves, p.upw, p.tpw, p.lds);
+    else
+        w4h::set_last_variant("w2t_mfma16 %s g%d kernel=w2t_gemv_kernel<%s, %d, %d> tiles=%d slices=%d "
+                              "waves=%d upw=%d lds=%zu",
+                              bf16 ? "bf16" : "f16", group, bf16 ? "true" : "false", group / 32, p.upw,
+                              p.tiles, p.l.S, p.waves, p.upw, p.lds);
     return w4h::launch_status();
 }

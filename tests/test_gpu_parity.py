@@ -1183,6 +1183,27 @@ def test_lm_head_sampled_columns(g, M):
     assert_parity(y[:, cols], ref, f"lm_head g{g} M{M}")
 
 
+# Three tiles per workgroup on layers of many tiles (at least six per CU,
+# no K split, up to 4 units per wave): 1537 tiles leave the last workgroup
+# one; each compiled group size, ragged K (a last unit of 128 k), and waves
+# without units (K = 512: 2 units for 8 waves).
+@pytest.mark.parametrize("M,K,g,xdt", [(1, 2560, 128, "f16"), (4, 4352, 64, "bf16"), (8, 3840, 256, "f16"),
+                                       (3, 2432, 128, "bf16"), (2, 512, 128, "f16")])
+def test_w2t_three_tile_workgroups(M, K, g, xdt):
+    N = 24592
+    say(f"w2t three tiles M={M} K={K} g={g} x={xdt}")
+    key = (162, M, K, g)
+    w = synth.gen_w2t(key, N, K, g)
+    x = synth.gen_x(key, M, K, xdt, outlier_frac=0.01 if xdt == "bf16" else 0.0)
+    y = to_f64(PackedW2T(w, N, K, g).gemv(dev(x), xdt, M))
+    variant = L.w4a16_last_variant()
+    say("  variant: " + variant)
+    assert "tpw=3 " in variant
+    cols = sample_cols(N, np.random.default_rng(K + g), n=256)
+    ref = oracle.w2t_gemv(x, xdt, w["codes"], w["scales"], M, N, K, g, cols=cols)
+    assert_parity(y[:, cols], ref, f"w2t three tiles M={M} K={K} g={g}")
+
+
 @pytest.mark.parametrize("K,N", [(5120, 7168), (5120, 34816), (17408, 5120)])
 @pytest.mark.parametrize("M", [1, 4, 8])
 def test_w2t_full_size_sampled_columns(K, N, M):
