@@ -159,9 +159,12 @@ struct W2Launch {
 };
 
 // Register-ring depth by group size (more groups per unit = more scale words
-// per slot).
+// per slot).  At g >= 128, 4 slots rather than 6: the ternary down shape (K =
+// 17408, N = 5120, 9-unit chains) went from 10.52-10.54 to 10.30-10.32 us at
+// M = 1 (graphs of 16 distinct matrices), the other shapes within noise; 3
+// slots measured no better.
 template <int SPG>
-constexpr int max_slots2() { return SPG >= 4 ? 6 : (SPG == 2 ? 5 : 3); }
+constexpr int max_slots2() { return SPG >= 4 ? 4 : (SPG == 2 ? 5 : 3); }
 
 // Eight waves per SIMD (at most 64 VGPRs) where the chain is short enough.
 template <int SPG, int UPW>
