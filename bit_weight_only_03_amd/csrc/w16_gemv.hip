@@ -9,9 +9,11 @@
 // over its workgroup's K slice, the workgroup streams x through LDS one
 // 128-k unit at a time (double-buffered, shared by its waves), and every
 // 16-byte chunk a lane loads is directly the MFMA B operand.  Layers of a
-// few hundred tiles (up to 16 rows and 8 units per wave) take a second,
-// GEMV-shaped kernel instead: one tile per workgroup, its waves splitting K,
-// so they fill the GPU without K slices and a merge launch.
+// few hundred tiles (up to 16 rows and 8 units per wave) take GEMV-shaped
+// kernels instead: one tile per workgroup, its waves splitting K, so they
+// fill the GPU without K slices and a merge launch.  Up to 4 rows that is a
+// VALU dot-product kernel whose loads read whole lines, above it an MFMA
+// kernel in the layout below.
 //
 // Layout of one unit for one tile: lane l serves column n = 16 t + l % 16;
 // its j-th 16-byte load (j = 0..3) is w[n][128 u + 32 j + 8 (l / 16) .. + 8],
@@ -319,6 +321,186 @@ __global__ __launch_bounds__(512) void w16_ksplit_kernel(const uint16_t* __restr
     }
 }
 
+// Layers of up to 4 rows: dot products on the VALU, which frees the weight
+// loads from the MFMA operand layout.  One workgroup of 8 waves per
+// 16-column tile, the waves splitting its 128-k units as in the K-split
+// kernel, x staged the same way (per-wave regions [M][nu units of 256 bytes],
+// loaded straight into LDS, no swizzle: every lane of a read takes the same
+// row).  Per unit, lane l makes four 16-byte loads j = 0..3 at row
+// 16 t + 4 j + l / 16 and bytes 16 (l % 16) of the unit's 256 in that row:
+// each load instruction reads four rows of 256 contiguous bytes (whole
+// 128-byte lines), with the non-temporal policy.  A read-only copy of this
+// pattern streamed gate_up (N = 34816, K = 5120) in 52.9 us against 60.0 us
+// for the MFMA layout (16 rows of 64 bytes per instruction, default policy),
+// o_proj in 11.7 against 14.3 us.  Against the K-split kernel (bench graphs,
+// fp16, us per call at M = 1 / 2 / 4 / 8): qkv 14.3 / 14.5 / 15.8 / 20.2
+// against 16.1 / 16.0 / 16.5 / 17.7, o_proj 13.0 / 13.3 / 14.6 / 18.4 against
+// 15.1 / 15.2 / 15.7 / 16.7, gate_up 56.8 / 56.9 / 59.6 / 82 against
+// 64.6 / 64.1 / 66.0 / 74.2: at 8 rows the 128 v_dot2 per unit and wave
+// outweigh the better stream, so it stops at 4 rows.  On the down shape
+// (17 units per wave, 320 tiles on 256 CUs) it took 35.3 / 36.4 us at
+// M = 1 / 2 against 35.1 / 35.2 for the tiled kernel in 16 slices, so it
+// also keeps the K-split kernel's limit of 8 units per wave.
+// Each lane keeps, per row of its loads and row of x, an fp32 sum over its
+// 8-k chunks (v_dot2: two exact fp16 or bf16 products added in fp32); at
+// the end the 16 lanes of a row are added in a fixed butterfly, then the
+// waves in wave order through LDS.
+constexpr int kW16DWaves = 8;
+constexpr int kW16DRing = 2;
+constexpr int kW16DMaxRows = 4;
+constexpr int kW16DMaxUnits = 8;        // units per wave
+constexpr int kW16DMaxXLoads = 16;      // x load instructions per wave: M * 16 * units <= 64 * 16
+
+template <bool BF16, int MR>
+__global__ __launch_bounds__(512) void w16_dot_kernel(const uint16_t* __restrict__ x,
+                                                      const uint16_t* __restrict__ w, void* out,
+                                                      W16Launch a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int M = a.M, N = a.N, K = a.K, U = a.U;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kc = lane & 15, r = lane >> 4;
+    const int t = blockIdx.x;
+    const int w0 = wave * U / kW16DWaves, w1 = (wave + 1) * U / kW16DWaves;
+    const int nu = w1 - w0;
+    const int rows = N - 16 * t < 16 ? N - 16 * t : 16;
+    constexpr int kUnitBytes = kUnitK * 2;                  // one row of one unit of x
+    uint8_t* const xsb = smem + (size_t)M * kUnitBytes * w0;
+
+    // 1) x units of this wave -> LDS: 16-byte chunk i of row m's range at
+    //    (m nu 16 + i) 16 bytes (lane l of load p fills chunk 64 p + l).
+    {
+        const int cpr = nu * (kUnitK / 8);
+        const int xch = M * cpr;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+#pragma unroll
+        for (int p = 0; p < kW16DMaxXLoads; ++p) {
+            if (p * 64 < xch) {                      // wave-uniform (false without units)
+                const int ci = p * 64 + lane;
+                const int m = ci / cpr, pc = ci % cpr;
+                const int kg = w0 * kUnitK + pc * 8;
+                if (m < M) {
+                    if (kg < K)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rx, (__attribute__((address_space(3))) void*)(xsb + p * 1024), 16,
+                            (uint32_t)(m * K + kg) * 2u, 0, 0, 0);
+                    else
+                        *(u32x4_t*)(xsb + (uint32_t)ci * 16u) = u32x4_t{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2) The tile's rows as one resource.  Rows past N read zeros; the tail of
+    //    a ragged last unit reads the start of the next row, which meets zero x.
+    const uint32_t wend = (uint32_t)rows * (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)16 * t * K, wend);
+    const uint32_t wlane = (uint32_t)r * (uint32_t)K * 2u + 16u * kc;
+    const uint32_t four_rows = 4u * (uint32_t)K * 2u;
+    auto load_unit = [&](int i, u32x4_t (&q)[4]) {
+        const uint32_t off = i < nu ? wlane + (uint32_t)(w0 + i) * kUnitBytes : wend;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            q[j] = bitcast<u32x4_t>(
+                __builtin_amdgcn_raw_buffer_load_b128(rw, off + four_rows * j, 0, kAuxNT));
+    };
+    constexpr int R = kW16DRing;
+    u32x4_t ring[R][4];
+#pragma unroll
+    for (int d = 0; d < R; ++d) {
+        load_unit(d, ring[d]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // Loads complete in issue order: with the ring's 4 R loads outstanding
+    // the x loads issued before them have landed in LDS (the loop below runs
+    // at least once for every wave, so the ring loads are not sunk into a
+    // branch; a host-side test checks the assembly).
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * R) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3) Products.  Units past the range load zero weights and skip the x
+    //    read, so they add exactly 0 (x is finite).
+    float acc[4][MR];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[j][m] = 0.f;
+    const uint8_t* const xl = xsb + 16u * kc;
+    const int upw = (U + kW16DWaves - 1) / kW16DWaves;   // >= 1, the same for every wave
+    int i = 0;
+    do {
+#pragma unroll
+        for (int d = 0; d < R; ++d) {
+            if (i + d < nu) {
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    if (m < M) {
+                        const u32x4_t xv =
+                            *(const u32x4_t*)(xl + (uint32_t)((m * nu + i + d) * kUnitBytes));
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                if constexpr (BF16)
+                                    acc[j][m] = __builtin_amdgcn_fdot2_f32_bf16(
+                                        bitcast<bf16x2_t>(ring[d][j][e]), bitcast<bf16x2_t>(xv[e]),
+                                        acc[j][m], false);
+                                else
+                                    acc[j][m] = __builtin_amdgcn_fdot2(
+                                        bitcast<half2_t>(ring[d][j][e]), bitcast<half2_t>(xv[e]),
+                                        acc[j][m], false);
+                            }
+                    }
+                }
+            }
+            load_unit(i + d + R, ring[d]);
+        }
+        i += R;
+    } while (i < upw);
+
+    // 4) The 16 lanes of each row (fixed butterfly; lane 16 r keeps the sum),
+    //    then per wave [M][16] partials in the wave's own x region (its last
+    //    reads of it came before, in program order), then the wave-order sum.
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            float v = acc[j][m];
+            v += __shfl_xor(v, 8);
+            v += __shfl_xor(v, 4);
+            v += __shfl_xor(v, 2);
+            v += __shfl_xor(v, 1);
+            acc[j][m] = v;
+        }
+    if (nu > 0 && kc == 0) {
+        float* const red = (float*)xsb;
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+            if (m < M)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) red[m * kTileN + 4 * j + r] = acc[j][m];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < M * kTileN; idx += blockDim.x) {
+        const int m = idx >> 4, cc = idx & 15;
+        float v = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < kW16DWaves; ++wv) {
+            const int b = wv * U / kW16DWaves, e = (wv + 1) * U / kW16DWaves;
+            if (e > b) v += ((const float*)(smem + (size_t)M * kUnitBytes * b))[m * kTileN + cc];
+        }
+        if (cc < rows) store_out(out, a.out_dtype, (size_t)m * N + 16 * t + cc, v);
+    }
+}
+
+template <bool BF16>
+const void* pick_w16_dot(int M) {
+    if (M <= 1) return (const void*)w16_dot_kernel<BF16, 1>;
+    if (M <= 2) return (const void*)w16_dot_kernel<BF16, 2>;
+    return (const void*)w16_dot_kernel<BF16, 4>;
+}
+
 typedef void (*w16_kernel_t)(const uint16_t*, const uint16_t*, void*, W16Launch);
 
 template <bool BF16>
@@ -335,8 +517,9 @@ w16_kernel_t pick_w16_rb(int rb) {
 struct W16Plan {
     int rb, split;
     long long workgroups;
+    bool dot;       // the VALU dot-product kernel (one tile per workgroup)
     bool ksplit;    // the K-split kernel (one tile per workgroup)
-    size_t lds;     // its dynamic LDS bytes
+    size_t lds;     // their dynamic LDS bytes
 };
 
 // K slices double while each keeps at least six units (4 KB of weights per
@@ -355,6 +538,10 @@ W16Plan w16_plan(int M, int N, int K) {
     p.ksplit = M <= 16 && upw <= kW16KMaxUnits && M * upw <= 64 && p.lds <= kW16KLdsMax;
     // Override for A/B measurement only: 0 turns the K-split kernel off.
     if (w4h::overrides().w16_ksplit == 0) p.ksplit = false;
+    // The dot-product kernel up to 4 rows, under the same limits.
+    p.dot = M <= kW16DMaxRows && upw <= kW16DMaxUnits && M * upw <= 64 && p.lds <= kW16KLdsMax;
+    if (w4h::overrides().w16_dot == 0) p.dot = false;
+    if (p.dot) p.ksplit = false;
     p.rb = (M + 15) / 16;
     p.workgroups = (T + kW16Waves - 1) / kW16Waves;
     p.split = 1;
@@ -372,14 +559,17 @@ int check_w16(int M, int N, int K) {
 }
 
 size_t w16_workspace(const W16Plan& p, int M, int N) {
-    return w4h::ws_bytes(!p.ksplit && p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0);
+    return w4h::ws_bytes(!p.dot && !p.ksplit && p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0);
 }
 
 void allow_w16_lds() {
     static std::once_flag once;
     std::call_once(once, [] {
         for (const void* k : {(const void*)w16_ksplit_kernel<false>,
-                              (const void*)w16_ksplit_kernel<true>})
+                              (const void*)w16_ksplit_kernel<true>,
+                              pick_w16_dot<false>(1), pick_w16_dot<false>(2),
+                              pick_w16_dot<false>(4), pick_w16_dot<true>(1),
+                              pick_w16_dot<true>(2), pick_w16_dot<true>(4)})
             (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kW16KLdsMax);
         (void)hipGetLastError();
     });
@@ -415,6 +605,17 @@ extern "C" int w16a16_gemv(const void* x, const void* w, int dtype, void* y, int
     const int T = pad_n(N) / kTileN;
     W16Launch l{M, N, K, U, p.split, T, y_dtype};
     hipStream_t st = (hipStream_t)stream;
+    if (p.dot) {
+        allow_w16_lds();
+        w4h::begin_launches();
+        const void* k = bf16 ? pick_w16_dot<true>(M) : pick_w16_dot<false>(M);
+        const int mr = M <= 1 ? 1 : M <= 2 ? 2 : 4;
+        hipLaunchKernelGGL((w16_kernel_t)k, dim3(T), dim3(64 * kW16DWaves), p.lds, st,
+                           (const uint16_t*)x, (const uint16_t*)w, y, l);
+        w4h::set_last_variant("w16_dot %s kernel=w16_dot_kernel<%s, %d> tiles=%d slices=1 lds=%zu",
+                              bf16 ? "bf16" : "f16", bf16 ? "true" : "false", mr, T, p.lds);
+        return w4h::launch_status();
+    }
     if (p.ksplit) {
         allow_w16_lds();
         w4h::begin_launches();

@@ -209,8 +209,9 @@ def test_workspace_queries_follow_the_dispatch():
     # work; without a device the planner assumes 256 CUs), so they show
     # which kernel a shape gets.  fp32 partials are S x M x N x 4 bytes,
     # after the 64 KiB counter head.
-    # W16A16: few-tile layers run the K-split kernel (no slices); the
-    # 17-units-per-wave down shape keeps the tiled kernel in 16 slices.
+    # W16A16: few-tile layers run the dot-product kernel (up to 4 rows) or
+    # the K-split kernel (up to 16), neither sliced; the 17-units-per-wave
+    # down shape keeps the tiled kernel in 16 slices.
     H = lib.W4A16_WORKSPACE_HEAD_BYTES
     assert lib.w16a16_workspace_bytes(1, 7168, 5120) == 0
     assert lib.w16a16_workspace_bytes(8, 5120, 5120) == 0

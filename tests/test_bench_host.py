@@ -50,6 +50,8 @@ def test_kernel_key_normalises_profiler_and_variant_names():
     assert bench.kernel_key("w16_gemv_kernel<false, 1>") == "w16_gemv_kernel<false, 1>"
     assert bench.kernel_key("w16_mfma16 f16 kernel=w16_ksplit_kernel<false> tiles=448") == \
         "w16_ksplit_kernel<false>"
+    assert bench.kernel_key("w16_dot f16 kernel=w16_dot_kernel<false, 1> tiles=320") == \
+        "w16_dot_kernel<false, 1>"
     assert bench.kernel_key("__amd_rocclr_copyBuffer") is None
     # Trailing default template arguments (MX, PX, balanced plan = false)
     # are dropped; a set one keeps those before it.

@@ -370,24 +370,33 @@ W16_CASES = [
     (24, 40, 8, "bf16"),
     (64, 264, 1536, "f16"),
     (3, 12296, 512, "bf16"),
-    # The K-split kernel at its limits: 16 rows filling half a CU's LDS, a
-    # single unit (seven waves without units), 8 units per wave with a
-    # ragged last one; a shape whose x is too large for it and one with
-    # more units per wave than it takes.
+    # The K-split kernel at its limits: 16 rows filling half a CU's LDS, and
+    # 12 rows with 3 or 4 units per wave and a ragged last one; 7 rows with a
+    # ragged last tile.  The dot-product kernel (up to 4 rows): a single unit
+    # (seven waves without units), 8 units per wave with a ragged last one,
+    # 3 rows of its 4-row block with 5 or 6 units per wave.  Shapes whose x
+    # is too large for both, or with more units per wave than they take.
     (16, 264, 2560, "bf16"),
+    (12, 520, 3240, "f16"),
+    (7, 1000, 3000, "bf16"),
     (2, 40, 8, "f16"),
     (1, 520, 8168, "f16"),
+    (3, 1032, 5760, "f16"),
     (6, 264, 8192, "bf16"),
     (1, 520, 17400, "f16"),
+    (2, 264, 17400, "bf16"),
 ]
 
 
-def w16_expects_ksplit(M, K):
-    # One workgroup per tile up to 8 units per wave, when a wave's x fits 16
-    # loads and the workgroup's x half of a CU's LDS.
+def w16_expected_kernel(M, K):
+    # One workgroup per tile up to 8 units per wave (the dot-product kernel
+    # up to 4 rows, the K-split kernel up to 16) when a wave's x fits 16 loads
+    # and the workgroup's x half of a CU's LDS; otherwise the tiled kernel.
     U = -(-K // 128)
     upw = -(-U // 8)
-    return M <= 16 and upw <= 8 and M * upw <= 64 and M * U * 256 <= 80 * 1024
+    if not (upw <= 8 and M * upw <= 64 and M * U * 256 <= 80 * 1024):
+        return "w16_gemv_kernel"
+    return "w16_dot_kernel" if M <= 4 else "w16_ksplit_kernel" if M <= 16 else "w16_gemv_kernel"
 
 
 @pytest.mark.parametrize("M,N,K,dt", W16_CASES)
@@ -408,8 +417,7 @@ def test_w16a16_gemv_matches_oracle(M, N, K, dt):
         if ydt == "f32":
             variant = L.w4a16_last_variant()
             say("  variant: " + variant)
-            kern = "w16_ksplit_kernel" if w16_expects_ksplit(M, K) else "w16_gemv_kernel"
-            assert kern in variant
+            assert w16_expected_kernel(M, K) + "<" in variant
             y0 = y.clone()
         assert_parity(to_f64(y)[:, cols], ref, f"w16 M={M} N={N} K={K} {dt} y={ydt}", extra_rel=extra)
     y1 = torch.empty_like(y0)
