@@ -56,7 +56,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4_gemv_traffic.json")
 # for the code they were taken on).
 KERNEL_SRCS = [os.path.join(ROOT, "bit_weight_only_03_amd", "csrc", f) for f in ("w4_gemv.hip", "common.h")]
 CALIB_BYTES = 1 << 30       # the plain device copy the counter runs are calibrated with
-KERNEL_RE = re.compile(r"(?:w4_gemv_kernel|w4_gemm_kernel|w16_gemv_kernel|w16_ksplit_kernel|w16_dot_kernel|w2t_gemv_kernel|"
+KERNEL_RE = re.compile(r"(?:w4_gemv_kernel|w4_gemm_kernel|w16_gemv_kernel|w16_ksplit_kernel|w16_dot_kernel|w16_dot_bal_kernel|w2t_gemv_kernel|"
                        r"w2t_gemv_direct_kernel)<[^>]*>")
 
 

@@ -302,6 +302,7 @@ struct Overrides {
     int gemm_split = 0;        // W4A16_GEMM_SPLIT: K slices of the M-tiled kernel
     int w16_ksplit = -1;       // W16A16_KSPLIT: 0 turns the W16 K-split kernel off
     int w16_dot = -1;          // W16A16_DOT: 0 turns the W16 dot-product kernel off
+    int w16_bal = -1;          // W16A16_BAL: 0 / 1 turns the W16 even-share kernel off / on where it fits
     int w16_split = 0;         // W16A16_SPLIT: K slices of the W16 tiled kernel
     long long w2t_staged_lds_max = 0;   // W2T_STAGED_LDS_MAX: LDS limit of the staged ternary kernel
 };

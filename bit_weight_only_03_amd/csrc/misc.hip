@@ -92,6 +92,7 @@ const Overrides& overrides() {
         geti("W4A16_GEMM_SPLIT", o.gemm_split);
         geti("W16A16_KSPLIT", o.w16_ksplit);
         geti("W16A16_DOT", o.w16_dot);
+        geti("W16A16_BAL", o.w16_bal);
         geti("W16A16_SPLIT", o.w16_split);
         if (const char* e = getenv("W2T_STAGED_LDS_MAX")) o.w2t_staged_lds_max = atoll(e);
     });

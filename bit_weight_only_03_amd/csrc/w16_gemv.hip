@@ -494,6 +494,176 @@ __global__ __launch_bounds__(512) void w16_dot_kernel(const uint16_t* __restrict
     }
 }
 
+// The same dot products with one even share of the rows per workgroup, one
+// workgroup per CU, for long-K layers whose 16-column tiles do not spread
+// evenly over the CUs (the down shape's 320 tiles on 256 CUs leave 64 CUs
+// with two) at up to 2 rows.  Workgroup c owns row groups [c G4 / C, (c + 1) G4 / C) of the
+// G4 = ceil(N / 4) groups of 4 rows; an item is one group's 256 bytes per
+// row of one 128-k unit, one 16-byte load per lane (lane l: row l / 16,
+// bytes 16 (l % 16)), and its 16 waves take contiguous item ranges in
+// group-major order, D items in flight.  x is staged whole, once per
+// workgroup ([M][U units of 256 bytes], zeros past K).  A wave adds the
+// items of one group in order and, where its range leaves the group, sums
+// the 16 lanes of each row (a fixed butterfly) into its slot for that
+// group; the slots of the waves that share a group are added in wave order.
+// Measured (bench graphs, fp16, us per call at M = 1 / 2 / 4, against the
+// kernel each shape takes otherwise): down 32.3-32.5 / 33.8-34.3 / 38.9-39.4
+// against 34.8-35.4 / 35.4-35.7 / 36.6-36.8 (tiled, 16 slices); o_proj
+// 13.2-13.4 / 13.8-14.0 / 15.5-15.8 against 13.0 / 13.3 / 14.6, qkv 16.7 /
+// 17.2-17.4 / 19.6 against 14.4 / 14.6 / 16.1 (one tile per workgroup).
+// Only long K at up to 2 rows gains, so only they take it.
+constexpr int kW16BWaves = 16;
+constexpr int kW16BMaxRows = 2;
+constexpr int kW16BMinUnits = 65;               // K > 8192
+constexpr int kW16BRing = 8;
+constexpr size_t kW16BLdsMax = 144 * 1024;      // x and the slots, one workgroup per CU
+constexpr int kW16BMaxXLoads = 9;               // x load instructions per thread (144 KB / 16 KB)
+
+template <bool BF16, int MR>
+__global__ __launch_bounds__(1024) void w16_dot_bal_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ w,
+                                                           void* out, W16Launch a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int M = a.M, N = a.N, K = a.K, U = a.U;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kc = lane & 15, r = lane >> 4;
+    const int G4 = (N + 3) >> 2;
+    const int g0 = (int)((long long)blockIdx.x * G4 / gridDim.x);
+    const int g1 = (int)((long long)(blockIdx.x + 1) * G4 / gridDim.x);
+    const int ng = g1 - g0;
+    if (ng == 0) return;                              // the whole workgroup
+    constexpr int kUnitBytes = kUnitK * 2;
+    const int I = ng * U;                             // items of the workgroup
+    const int a0 = wave * I / kW16BWaves, a1 = (wave + 1) * I / kW16BWaves;
+    const int n = a1 - a0;
+    float* const slots = (float*)(smem + (size_t)M * U * kUnitBytes);   // [ng][waves][M][4]
+
+    // 1) x -> LDS, chunk ci (16 bytes) of the [M][U * 16] chunk grid at ci * 16.
+    {
+        const int cpr = U * (kUnitK / 8);
+        const int xch = M * cpr;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+#pragma unroll
+        for (int p = 0; p < kW16BMaxXLoads; ++p) {
+            if (p * 1024 + wave * 64 < xch) {        // wave-uniform
+                const int ci = p * 1024 + (int)threadIdx.x;
+                const int m = ci / cpr, kg = (ci % cpr) * 8;
+                if (ci < xch) {
+                    if (kg < K)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rx, (__attribute__((address_space(3))) void*)(smem + (size_t)(p * 1024 + wave * 64) * 16), 16,
+                            (uint32_t)(m * K + kg) * 2u, 0, 0, 0);
+                    else
+                        *(u32x4_t*)(smem + (size_t)ci * 16) = u32x4_t{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2) The workgroup's rows as one resource (rows past N read zeros; the
+    //    tail of a ragged last unit reads the next row, which meets zero x).
+    const int rows = (4 * g1 < N ? 4 * g1 : N) - 4 * g0;
+    const uint32_t wend = (uint32_t)rows * (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)4 * g0 * K, wend);
+    const uint32_t row_bytes = (uint32_t)K * 2u;
+    const uint32_t wlane = (uint32_t)r * row_bytes + 16u * kc;
+    int gl = a0 / U, ul = a0 % U;                     // the next item to load
+    auto load_item = [&](bool valid) {
+        // Straight-line code (the ring's loads must reach the x wait below
+        // without a branch): an item past the range sets the offset's top
+        // bit, beyond the resource, so it reads zeros; the counters advance
+        // with selects.
+        const uint32_t off = (wlane + (uint32_t)gl * 4u * row_bytes + (uint32_t)ul * kUnitBytes) |
+                             (valid ? 0u : 0x80000000u);
+        const bool wrap = valid && ul + 1 == U;
+        ul = wrap ? 0 : ul + (valid ? 1 : 0);
+        gl += wrap ? 1 : 0;
+        return bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kAuxNT));
+    };
+    constexpr int D = kW16BRing;
+    u32x4_t ring[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) ring[d] = load_item(d < n);
+    __builtin_amdgcn_sched_barrier(0);
+    // Loads complete in issue order: with the D ring loads outstanding the
+    // x loads this thread issued before them have landed; the barrier then
+    // covers every thread's.
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+
+    // 3) Products, item by item.
+    float acc[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+    int gc = a0 / U, uc = a0 % U;                     // the item being added
+    const uint8_t* const xl = smem + 16u * kc;
+    auto flush = [&]() {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            float v = acc[m];
+            v += __shfl_xor(v, 8);
+            v += __shfl_xor(v, 4);
+            v += __shfl_xor(v, 2);
+            v += __shfl_xor(v, 1);
+            if (m < M && kc == 0) slots[((gc * kW16BWaves + wave) * M + m) * 4 + r] = v;
+            acc[m] = 0.f;
+        }
+    };
+    for (int i = 0; i < n; i += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (i + d < n) {
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    if (m < M) {
+                        const u32x4_t xv =
+                            *(const u32x4_t*)(xl + (uint32_t)((m * U + uc) * kUnitBytes));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if constexpr (BF16)
+                                acc[m] = __builtin_amdgcn_fdot2_f32_bf16(
+                                    bitcast<bf16x2_t>(ring[d][e]), bitcast<bf16x2_t>(xv[e]), acc[m], false);
+                            else
+                                acc[m] = __builtin_amdgcn_fdot2(
+                                    bitcast<half2_t>(ring[d][e]), bitcast<half2_t>(xv[e]), acc[m], false);
+                        }
+                    }
+                }
+                if (++uc == U || i + d + 1 == n) {
+                    flush();
+                    if (uc == U) { uc = 0; ++gc; }
+                }
+            }
+            ring[d] = load_item(i + d + D < n);
+        }
+    }
+
+    // 4) Per row and row of x, the slots of the waves whose ranges meet its
+    //    group, in wave order.
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < M * 4 * ng; idx += blockDim.x) {
+        const int m = idx / (4 * ng), rl = idx - m * 4 * ng;
+        const int g = rl >> 2, rr = rl & 3;
+        float v = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < kW16BWaves; ++wv) {
+            const int b = wv * I / kW16BWaves, e = (wv + 1) * I / kW16BWaves;
+            if (b < (g + 1) * U && e > g * U) v += slots[((g * kW16BWaves + wv) * M + m) * 4 + rr];
+        }
+        const int row = 4 * (g0 + g) + rr;
+        if (row < N) store_out(out, a.out_dtype, (size_t)m * N + row, v);
+    }
+}
+
+template <bool BF16>
+const void* pick_w16_dot_bal(int M) {
+    if (M <= 1) return (const void*)w16_dot_bal_kernel<BF16, 1>;
+    return (const void*)w16_dot_bal_kernel<BF16, 2>;
+}
+
 template <bool BF16>
 const void* pick_w16_dot(int M) {
     if (M <= 1) return (const void*)w16_dot_kernel<BF16, 1>;
@@ -517,6 +687,7 @@ w16_kernel_t pick_w16_rb(int rb) {
 struct W16Plan {
     int rb, split;
     long long workgroups;
+    bool bal;       // the VALU dot-product kernel, one even row share per CU
     bool dot;       // the VALU dot-product kernel (one tile per workgroup)
     bool ksplit;    // the K-split kernel (one tile per workgroup)
     size_t lds;     // their dynamic LDS bytes
@@ -542,6 +713,19 @@ W16Plan w16_plan(int M, int N, int K) {
     p.dot = M <= kW16DMaxRows && upw <= kW16DMaxUnits && M * upw <= 64 && p.lds <= kW16KLdsMax;
     if (w4h::overrides().w16_dot == 0) p.dot = false;
     if (p.dot) p.ksplit = false;
+    // The even row shares up to 2 rows, for layers of between one and two
+    // tiles per CU and more than 64 units (the down shape: 320 tiles on 256
+    // CUs, K = 17408), when x and the slots fit a CU's LDS.
+    const int C = w4h::cu_count();
+    const long long gmax = ((long long)(N + 3) / 4 + C - 1) / C;
+    const size_t bal_lds = (size_t)M * U * kUnitK * 2 + (size_t)gmax * kW16BWaves * M * 4 * sizeof(float);
+    const bool bal_fits = M <= kW16BMaxRows && bal_lds <= kW16BLdsMax && gmax * 4 * K * 2 < (1LL << 31);
+    p.bal = bal_fits && T > C && T < 2 * C && U >= kW16BMinUnits;
+    if (const int o = w4h::overrides().w16_bal; o == 0 || (o == 1 && bal_fits)) p.bal = o == 1;
+    if (p.bal) {
+        p.dot = p.ksplit = false;
+        p.lds = bal_lds;
+    }
     p.rb = (M + 15) / 16;
     p.workgroups = (T + kW16Waves - 1) / kW16Waves;
     p.split = 1;
@@ -559,7 +743,7 @@ int check_w16(int M, int N, int K) {
 }
 
 size_t w16_workspace(const W16Plan& p, int M, int N) {
-    return w4h::ws_bytes(!p.dot && !p.ksplit && p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0);
+    return w4h::ws_bytes(!p.bal && !p.dot && !p.ksplit && p.split > 1 ? (size_t)p.split * M * N * sizeof(float) : 0);
 }
 
 void allow_w16_lds() {
@@ -571,6 +755,9 @@ void allow_w16_lds() {
                               pick_w16_dot<false>(4), pick_w16_dot<true>(1),
                               pick_w16_dot<true>(2), pick_w16_dot<true>(4)})
             (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kW16KLdsMax);
+        for (const void* k : {pick_w16_dot_bal<false>(1), pick_w16_dot_bal<false>(2),
+                              pick_w16_dot_bal<true>(1), pick_w16_dot_bal<true>(2)})
+            (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kW16BLdsMax);
         (void)hipGetLastError();
     });
 }
@@ -605,6 +792,18 @@ extern "C" int w16a16_gemv(const void* x, const void* w, int dtype, void* y, int
     const int T = pad_n(N) / kTileN;
     W16Launch l{M, N, K, U, p.split, T, y_dtype};
     hipStream_t st = (hipStream_t)stream;
+    if (p.bal) {
+        allow_w16_lds();
+        w4h::begin_launches();
+        const void* k = bf16 ? pick_w16_dot_bal<true>(M) : pick_w16_dot_bal<false>(M);
+        const int mr = M <= 1 ? 1 : 2;
+        const int C = w4h::cu_count();
+        hipLaunchKernelGGL((w16_kernel_t)k, dim3(C), dim3(64 * kW16BWaves), p.lds, st,
+                           (const uint16_t*)x, (const uint16_t*)w, y, l);
+        w4h::set_last_variant("w16_dotbal %s kernel=w16_dot_bal_kernel<%s, %d> workgroups=%d slices=1 lds=%zu",
+                              bf16 ? "bf16" : "f16", bf16 ? "true" : "false", mr, C, p.lds);
+        return w4h::launch_status();
+    }
     if (p.dot) {
         allow_w16_lds();
         w4h::begin_launches();

@@ -209,13 +209,16 @@ def test_workspace_queries_follow_the_dispatch():
     # work; without a device the planner assumes 256 CUs), so they show
     # which kernel a shape gets.  fp32 partials are S x M x N x 4 bytes,
     # after the 64 KiB counter head.
-    # W16A16: few-tile layers run the dot-product kernel (up to 4 rows) or
-    # the K-split kernel (up to 16), neither sliced; the 17-units-per-wave
-    # down shape keeps the tiled kernel in 16 slices.
+    # W16A16: the dot-product kernel up to 4 rows and the K-split kernel up
+    # to 16 on few-tile layers, the even-share kernel on the down shape up
+    # to 2 rows; none of them sliced.  The down shape at 4 rows takes the
+    # tiled kernel in 16 slices.
     H = lib.W4A16_WORKSPACE_HEAD_BYTES
     assert lib.w16a16_workspace_bytes(1, 7168, 5120) == 0
     assert lib.w16a16_workspace_bytes(8, 5120, 5120) == 0
-    assert lib.w16a16_workspace_bytes(1, 5120, 17408) == H + 16 * 1 * 5120 * 4
+    assert lib.w16a16_workspace_bytes(1, 5120, 17408) == 0
+    assert lib.w16a16_workspace_bytes(2, 5120, 17408) == 0
+    assert lib.w16a16_workspace_bytes(4, 5120, 17408) == H + 16 * 4 * 5120 * 4
     # Ternary: the staged kernel unsplit at K = 5120 up to 8 rows, and in 2
     # and 4 slices for the down shape at 4 and 8 rows.
     assert lib.w2t_workspace_bytes(8, 7168, 5120, 128) == 0

@@ -27,7 +27,7 @@ def snap():
         "w4_plan_m64": L.w4a16_plan_variant(64, 5120, 5120, 128, "f16"),
         "w4_ws_m64": L.w4a16_workspace_bytes(64, 5120, 5120, 128),
         "w16_ws": L.w16a16_workspace_bytes(1, 5120, 17408),
-        "w16_ws_m4": L.w16a16_workspace_bytes(4, 5120, 17408),
+        "w16_ws_m2": L.w16a16_workspace_bytes(2, 5120, 17408),
         "w2t_ws": L.w2t_workspace_bytes(4, 5120, 17408, 128),
     }}
 
@@ -41,7 +41,7 @@ print(json.dumps(out))
 """
 
 OVERRIDES = {"W4A16_SPLIT": "2", "W4A16_TPW": "2", "W4A16_PX": "0", "W4A16_BAL": "0", "W4A16_GEMM_SPLIT": "1",
-             "W4A16_GEMM_TN": "2", "W16A16_SPLIT": "2", "W16A16_KSPLIT": "0", "W16A16_DOT": "0",
+             "W4A16_GEMM_TN": "2", "W16A16_SPLIT": "2", "W16A16_KSPLIT": "0", "W16A16_DOT": "0", "W16A16_BAL": "0",
              "W2T_STAGED_LDS_MAX": "1"}
 
 
@@ -71,8 +71,9 @@ def test_overrides_set_before_the_first_call_apply():
     assert "px=1" in plain["w4_plan_qkv_m1"]
     assert forced["w4_ws_m64"] == 0 and "slices=1" in forced["w4_plan_m64"]   # W4A16_GEMM_SPLIT=1
     assert "w4_gemm_kernel<false, 4, 4, 2>" in forced["w4_plan_m64"]          # W4A16_GEMM_TN=2
-    assert forced["w16_ws"] == H + 2 * 1 * 5120 * 4             # W16A16_SPLIT=2
-    assert forced["w16_ws_m4"] == H + 2 * 4 * 5120 * 4 and plain["w16_ws_m4"] == H + 16 * 4 * 5120 * 4
+    assert forced["w16_ws"] == H + 2 * 1 * 5120 * 4             # W16A16_BAL=0, W16A16_SPLIT=2
+    assert plain["w16_ws"] == 0 and plain["w16_ws_m2"] == 0      # the even-share kernel
+    assert forced["w16_ws_m2"] == H + 2 * 2 * 5120 * 4
     assert plain["w4_plan_down_m1"].startswith("w4_bal16")      # W4A16_BAL=0
     assert forced["w4_plan_down_m1"].startswith("w4_mfma16")
     assert forced["w2t_ws"] != plain["w2t_ws"]                   # direct-x kernel, its own split

@@ -385,15 +385,29 @@ W16_CASES = [
     (6, 264, 8192, "bf16"),
     (1, 520, 17400, "f16"),
     (2, 264, 17400, "bf16"),
+    # The even-share kernel (between one and two tiles per CU, more than 64
+    # units, up to 2 rows): 4 or 5 groups of 4 rows per workgroup with a
+    # last unit of 8 k, 6 or 7 with the down shape's 136 units (a ragged
+    # last one), 7 or 8 groups.
+    (1, 4104, 8200, "bf16"),
+    (2, 6152, 17400, "f16"),
+    (1, 8176, 9000, "f16"),
 ]
 
 
-def w16_expected_kernel(M, K):
-    # One workgroup per tile up to 8 units per wave (the dot-product kernel
-    # up to 4 rows, the K-split kernel up to 16) when a wave's x fits 16 loads
-    # and the workgroup's x half of a CU's LDS; otherwise the tiled kernel.
+def w16_expected_kernel(M, N, K):
+    # Between one and two tiles per CU, more than 64 units, up to 2 rows:
+    # one even row share per CU when x and the partial slots fit 144 KB.  Else one workgroup per
+    # tile up to 8 units per wave (the dot-product kernel up to 4 rows, the
+    # K-split kernel up to 16) when a wave's x fits 16 loads and the
+    # workgroup's x half of a CU's LDS; otherwise the tiled kernel.
     U = -(-K // 128)
     upw = -(-U // 8)
+    C = torch.cuda.get_device_properties(0).multi_processor_count
+    T = -(-N // 16)
+    gmax = -(-(-(-N // 4)) // C)
+    if M <= 2 and C < T < 2 * C and U > 64 and M * U * 256 + gmax * 16 * M * 16 <= 144 * 1024:
+        return "w16_dot_bal_kernel"
     if not (upw <= 8 and M * upw <= 64 and M * U * 256 <= 80 * 1024):
         return "w16_gemv_kernel"
     return "w16_dot_kernel" if M <= 4 else "w16_ksplit_kernel" if M <= 16 else "w16_gemv_kernel"
@@ -417,7 +431,7 @@ def test_w16a16_gemv_matches_oracle(M, N, K, dt):
         if ydt == "f32":
             variant = L.w4a16_last_variant()
             say("  variant: " + variant)
-            assert w16_expected_kernel(M, K) + "<" in variant
+            assert w16_expected_kernel(M, N, K) + "<" in variant
             y0 = y.clone()
         assert_parity(to_f64(y)[:, cols], ref, f"w16 M={M} N={N} K={K} {dt} y={ydt}", extra_rel=extra)
     y1 = torch.empty_like(y0)
@@ -775,7 +789,7 @@ def test_mxfp4_repeat_calls_and_graph_replay_are_bitwise_identical(M, N, K):
         assert int(ws[:WS_HEAD].count_nonzero()) == 0
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 5120, 5120), (24, 1032, 2048)])
+@pytest.mark.parametrize("M,N,K", [(1, 5120, 5120), (2, 5120, 17408), (24, 1032, 2048)])
 def test_w16a16_and_ternary_graph_replay_are_bitwise_identical(M, N, K):
     say(f"w16 / ternary determinism M={M} N={N} K={K}")
     w = dev(synth.gen_w16((130, M), N, K, "f16"))
