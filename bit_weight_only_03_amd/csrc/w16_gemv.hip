@@ -322,7 +322,7 @@ __global__ __launch_bounds__(512) void w16_ksplit_kernel(const uint16_t* __restr
 }
 
 // Layers of up to 4 rows: dot products on the VALU, which frees the weight
-// loads from the MFMA operand layout.  One workgroup of 8 waves per
+// loads from the MFMA operand layout.  One workgroup of 4 waves per
 // 16-column tile, the waves splitting its 128-k units as in the K-split
 // kernel, x staged the same way (per-wave regions [M][nu units of 256 bytes],
 // loaded straight into LDS, no swizzle: every lane of a read takes the same
@@ -337,22 +337,27 @@ __global__ __launch_bounds__(512) void w16_ksplit_kernel(const uint16_t* __restr
 // against 16.1 / 16.0 / 16.5 / 17.7, o_proj 13.0 / 13.3 / 14.6 / 18.4 against
 // 15.1 / 15.2 / 15.7 / 16.7, gate_up 56.8 / 56.9 / 59.6 / 82 against
 // 64.6 / 64.1 / 66.0 / 74.2: at 8 rows the 128 v_dot2 per unit and wave
-// outweigh the better stream, so it stops at 4 rows.  On the down shape
-// (17 units per wave, 320 tiles on 256 CUs) it took 35.3 / 36.4 us at
-// M = 1 / 2 against 35.1 / 35.2 for the tiled kernel in 16 slices, so it
-// also keeps the K-split kernel's limit of 8 units per wave.
+// outweigh the better stream, so it stops at 4 rows.  (Those figures are
+// for 8 waves per tile.)  On the down shape (136 units, 320 tiles on 256
+// CUs) it took 35.3 / 36.4 us at M = 1 / 2 against 35.1 / 35.2 for the
+// tiled kernel in 16 slices, so it keeps to the K-split kernel's 64 units.
+// Four waves per tile (10 units each on these shapes) against eight: qkv
+// 13.8 against 14.3 us, o_proj 12.3 against 13.0, gate_up even at M = 1
+// (M = 4: o_proj 13.9 against 14.6); two waves: o_proj 11.8 but qkv 13.9,
+// gate_up 58.9, and every shape 1.3-10 us slower at M = 4; 3 or 4 units
+// in flight per wave instead of 2: 0.2-0.6 us slower.
 // Each lane keeps, per row of its loads and row of x, an fp32 sum over its
 // 8-k chunks (v_dot2: two exact fp16 or bf16 products added in fp32); at
 // the end the 16 lanes of a row are added in a fixed butterfly, then the
 // waves in wave order through LDS.
-constexpr int kW16DWaves = 8;
+constexpr int kW16DWaves = 4;
 constexpr int kW16DRing = 2;
 constexpr int kW16DMaxRows = 4;
-constexpr int kW16DMaxUnits = 8;        // units per wave
+constexpr int kW16DMaxUnits = 16;       // units per wave
 constexpr int kW16DMaxXLoads = 16;      // x load instructions per wave: M * 16 * units <= 64 * 16
 
 template <bool BF16, int MR>
-__global__ __launch_bounds__(512) void w16_dot_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(64 * kW16DWaves) void w16_dot_kernel(const uint16_t* __restrict__ x,
                                                       const uint16_t* __restrict__ w, void* out,
                                                       W16Launch a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -709,8 +714,11 @@ W16Plan w16_plan(int M, int N, int K) {
     p.ksplit = M <= 16 && upw <= kW16KMaxUnits && M * upw <= 64 && p.lds <= kW16KLdsMax;
     // Override for A/B measurement only: 0 turns the K-split kernel off.
     if (w4h::overrides().w16_ksplit == 0) p.ksplit = false;
-    // The dot-product kernel up to 4 rows, under the same limits.
-    p.dot = M <= kW16DMaxRows && upw <= kW16DMaxUnits && M * upw <= 64 && p.lds <= kW16KLdsMax;
+    // The dot-product kernel up to 4 rows, under the same limits (x load
+    // instructions per wave: M * 16 * units / 64).
+    const int upw_d = (U + kW16DWaves - 1) / kW16DWaves;
+    p.dot = M <= kW16DMaxRows && upw_d <= kW16DMaxUnits && M * upw_d * 16 <= 64 * kW16DMaxXLoads &&
+            p.lds <= kW16KLdsMax;
     if (w4h::overrides().w16_dot == 0) p.dot = false;
     if (p.dot) p.ksplit = false;
     // The even row shares up to 2 rows, for layers of between one and two

@@ -373,8 +373,8 @@ W16_CASES = [
     # The K-split kernel at its limits: 16 rows filling half a CU's LDS, and
     # 12 rows with 3 or 4 units per wave and a ragged last one; 7 rows with a
     # ragged last tile.  The dot-product kernel (up to 4 rows): a single unit
-    # (seven waves without units), 8 units per wave with a ragged last one,
-    # 3 rows of its 4-row block with 5 or 6 units per wave.  Shapes whose x
+    # (three waves without units), 16 units per wave with a ragged last one,
+    # 3 rows of its 4-row block with 11 or 12 units per wave.  Shapes whose x
     # is too large for both, or with more units per wave than they take.
     (16, 264, 2560, "bf16"),
     (12, 520, 3240, "f16"),
