@@ -440,6 +440,31 @@ def test_w16a16_gemv_matches_oracle(M, N, K, dt):
     assert torch.equal(y0, y1)                           # deterministic
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 264, 1000), (1, 4104, 8200), (8, 264, 2560), (24, 40, 2048)])
+@pytest.mark.parametrize("sub", ["x", "w"])
+def test_w16a16_fp16_subnormal_operands(M, N, K, sub):
+    # Every product has one fp16 subnormal factor (2^-20, bits 0x0010) and
+    # one 1.0: y = K * 2^-20 exactly in fp32 for every column.  An operand
+    # flushed to zero anywhere on the path (the dot-product kernels' v_dot2,
+    # the MFMA kernels) would give 0.  One shape per kernel: dot product,
+    # even shares, K-split, tiled.
+    say(f"w16 subnormal {sub} M={M} N={N} K={K}")
+    one, tiny = np.uint16(0x3C00), np.uint16(0x0010)
+    x = np.full((M, K), tiny if sub == "x" else one, dtype=np.uint16)
+    w = np.full((N, K), tiny if sub == "w" else one, dtype=np.uint16)
+    wsb = L.w16a16_workspace_bytes(M, N, K)
+    ws = workspace_bytes(wsb) if wsb else None
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    L.w16a16_gemv(dev(x), dev(w), "f16", y, "f32", M, N, K, ws, wsb)
+    torch.cuda.synchronize()
+    say("  variant: " + L.w4a16_last_variant())
+    cols = np.array([0, 1, N // 2, N - 1], dtype=np.int64)
+    ref = oracle.w16_gemv(x, "f16", w, M, N, K, cols=cols)
+    assert np.all(ref == K * 2.0 ** -20)
+    assert np.array_equal(to_f64(y)[:, cols], ref)
+    assert torch.all(y == K * 2.0 ** -20)
+
+
 W2_GEMV_CASES = [
     (1, 7, 32, 32, "f16"),
     (4, 40, 768, 128, "f16"),
