@@ -21,6 +21,16 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 
+# Per-source device flags.  The 4-bit GEMV kernel takes the arguments every
+# wave needs first as leading scalars and pointers (ten arguments, 14
+# dwords); this option compiles them as preloaded into SGPRs at wave launch,
+# which saves each wave a scalar load before its first memory access
+# (measured 0.25-0.3 us per call on the qkv and o_proj shapes).  The code
+# object keeps a prologue that loads them itself where the firmware does not
+# preload.
+SOURCE_FLAGS = {"w4_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
@@ -29,6 +39,7 @@ def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(HERE, "_build", os.path.basename(src) + ".o")
     cmd = [HIPCC, "-c", "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           *SOURCE_FLAGS.get(os.path.basename(src), []),
            "-Wall", "-Wno-unused-function", "-o", obj, src]
     if verbose:
         print(" ".join(cmd), flush=True)

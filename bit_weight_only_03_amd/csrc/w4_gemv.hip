@@ -521,9 +521,31 @@ constexpr int min_waves() { return (SPG >= 4 && UPW <= 5) || (SPG == 2 && UPW <=
 // tile (see the planner); TPW = 1, whole-range x staging, up to 2 rows.
 template <bool BF16, int SPG, int UPW, int TPW, bool MX = false, bool PX = false, bool BAL = false>
 __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<SPG, UPW>())) void w4_gemv_kernel(
+    int M_, int K_, int U_, int T_, int plan0, int plan1,
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ qdev,
     const uint16_t* __restrict__ sdev, const uint32_t* __restrict__ zdev, void* out,
-    GemvLaunch a) {
+    GemvLaunch a_in) {
+    // The first ten arguments (14 dwords) are everything a wave needs before
+    // its first load; this file is compiled to have the hardware preload
+    // them into SGPRs at wave launch, so no wave starts with a scalar load
+    // of its kernel arguments.  The launch's other fields stay in a_in,
+    // loaded where they are used.  plan0 / plan1 are the K slice count and
+    // the wave count, or for the balanced plan (one slice, kBalFull +
+    // kBalExtra waves) the leftover tiles' piece count and first tile.
+    GemvLaunch a = a_in;
+    a.M = M_;
+    a.K = K_;
+    a.U = U_;
+    a.T = T_;
+    a.xstride = UPW * kUnitK;   // every launch stages rows of exactly UPW units
+    if constexpr (BAL) {
+        a.S = 1;
+        a.bal_full = kBalFull;
+        a.bal_pieces = plan0;
+        a.bal_base = plan1;
+    } else {
+        a.S = plan0;
+    }
     constexpr int DM = TPW > 1 ? 5 : max_slots<SPG>();
     constexpr bool kUncond = SPG >= 4 || (SPG == 2 && UPW <= 6) || UPW <= 2;
     static_assert(!PX || (kUncond && (UPW * TPW < DM ? UPW * TPW : DM) <= 9),
@@ -532,7 +554,7 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int M = a.M, U = a.U;
-    const int W = blockDim.x >> 6;
+    const int W = BAL ? kBalFull + kBalExtra : plan1;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     int t0 = blockIdx.x * TPW;
@@ -917,8 +939,8 @@ Plan make_plan(int M, int N, int K, int group, int cus, bool allow_px) {
     return p;
 }
 
-typedef void (*w4_kernel_t)(const uint16_t*, const u32x4_t*, const uint16_t*, const uint32_t*,
-                            void*, GemvLaunch);
+typedef void (*w4_kernel_t)(int, int, int, int, int, int, const uint16_t*, const u32x4_t*,
+                            const uint16_t*, const uint32_t*, void*, GemvLaunch);
 
 template <bool BF16, int SPG, int TPW>
 w4_kernel_t pick_small_upw(int upw) {
@@ -1346,7 +1368,8 @@ int launch_bal(const BalPlan& bp, const void* x, int x_dtype, const void* qweigh
     w4h::begin_launches();
     const w4_kernel_t k = mx ? (bf16 ? pick_bal<true, true>(bp.upw, bp.px) : pick_bal<false, true>(bp.upw, bp.px))
                              : (bf16 ? pick_bal<true>(bp.upw, bp.px) : pick_bal<false>(bp.upw, bp.px));
-    hipLaunchKernelGGL(k, dim3(bp.base), dim3(64 * (kBalFull + kBalExtra)), bp.lds, st, (const uint16_t*)x,
+    hipLaunchKernelGGL(k, dim3(bp.base), dim3(64 * (kBalFull + kBalExtra)), bp.lds, st, l.M, l.K, l.U, l.T,
+                       l.bal_pieces, l.bal_base, (const uint16_t*)x,
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros, y, l);
     char v[192];
     format_bal(v, sizeof v, bf16, mx, group, N, bp);
@@ -1387,6 +1410,7 @@ int gemv_impl(const void* x, int x_dtype, const void* qweight, const void* scale
     p.l.res_dtype = res_dtype;
     w4h::begin_launches();
     hipLaunchKernelGGL(k, dim3((p.tiles + p.tpw - 1) / p.tpw, p.l.S), dim3(64 * p.waves), p.lds, st,
+                       p.l.M, p.l.K, p.l.U, p.l.T, p.l.S, p.waves,
                        (const uint16_t*)x,
                        (const u32x4_t*)qweight, (const uint16_t*)scales, (const uint32_t*)zeros,
                        out, p.l);
@@ -1586,6 +1610,7 @@ extern "C" int mxfp4_gemv(const void* x, int x_dtype, const void* qweight, const
     p.l.out_dtype = p.l.S > 1 ? W4A16_F32 : y_dtype;
     w4h::begin_launches();
     hipLaunchKernelGGL(k, dim3((p.tiles + p.tpw - 1) / p.tpw, p.l.S), dim3(64 * p.waves), p.lds, st,
+                       p.l.M, p.l.K, p.l.U, p.l.T, p.l.S, p.waves,
                        (const uint16_t*)x, (const u32x4_t*)qweight, (const uint16_t*)scales,
                        (const uint32_t*)nullptr, out, p.l);
     if (p.l.S > 1) w4h::launch_merge(w4h::ws_part(workspace), y, y_dtype, nullptr, W4A16_F32, M, N, p.l.S, st);

@@ -35,8 +35,10 @@ pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not ins
 
 
 def compile_asm(src, out):
+    # The library's own per-source flags, so the assembly checked is the one built.
+    from bit_weight_only_03_amd.build import SOURCE_FLAGS
     cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *SOURCE_FLAGS.get(src, []),
            f"-I{CSRC}", "-o", out, os.path.join(CSRC, src)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
