@@ -23,12 +23,15 @@ ARCH = "gfx950"
 
 # Per-source device flags.  The 4-bit GEMV kernel takes the arguments every
 # wave needs first as leading scalars and pointers (ten arguments, 14
-# dwords); this option compiles them as preloaded into SGPRs at wave launch,
+# dwords; the W16A16 and ternary kernels likewise); this option compiles them as
+# preloaded into SGPRs at wave launch,
 # which saves each wave a scalar load before its first memory access
 # (measured 0.25-0.3 us per call on the qkv and o_proj shapes).  The code
 # object keeps a prologue that loads them itself where the firmware does not
 # preload.
-SOURCE_FLAGS = {"w4_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
+SOURCE_FLAGS = {"w4_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"],
+                "w16_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"],
+                "w2t.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
 
 
 def sources():

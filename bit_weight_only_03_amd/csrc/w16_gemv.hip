@@ -49,6 +49,18 @@ struct W16Launch {
     int out_dtype;
 };
 
+// Every kernel here takes the launch fields a wave needs first as seven
+// leading scalars (the last, G_, the launch's workgroups along x, which the
+// even-share kernel divides its rows by) ahead of its three pointers (ten
+// arguments, 13 dwords),
+// which the build compiles as preloaded into SGPRs at wave launch, so no
+// wave starts with a scalar load of its arguments; out_dtype, used only by
+// the stores, stays in the struct.
+__device__ __forceinline__ W16Launch lead_launch(int M, int N, int K, int U, int S, int T,
+                                                 const W16Launch& rest) {
+    return W16Launch{M, N, K, U, S, T, rest.out_dtype};
+}
+
 // One workgroup per (4 tiles, K slice); per unit of the slice: x of the unit
 // staged in LDS buffer u % 2 by all threads (zeros past K and in rows >= M,
 // whose outputs are never stored), every wave multiplies its tile's unit
@@ -58,9 +70,11 @@ struct W16Launch {
 // them) into the other buffer; one barrier per unit.  Units past the
 // slice and rows past N load as zeros, so the loop body is uniform.
 template <bool BF16, int RB>
-__global__ __launch_bounds__(256) void w16_gemv_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256) void w16_gemv_kernel(int M_, int N_, int K_, int U_, int S_, int T_, int G_,
+        const uint16_t* __restrict__ x,
                                                        const uint16_t* __restrict__ w, void* out,
-                                                       W16Launch a) {
+                                                       W16Launch a_in) {
+    const W16Launch a = lead_launch(M_, N_, K_, U_, S_, T_, a_in);
     constexpr int ROWS = 16 * RB;
     constexpr int XCH = ROWS * (kUnitK / 8);   // 16-byte chunks of one staged unit
     constexpr int XPT = XCH / 256;             // chunks per thread (= RB)
@@ -195,9 +209,11 @@ constexpr int kW16KMaxUnits = 8;
 constexpr int kW16KMaxXLoads = 16;   // x load instructions per wave: M * 16 * units <= 64 * 16
 
 template <bool BF16>
-__global__ __launch_bounds__(512) void w16_ksplit_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(512) void w16_ksplit_kernel(int M_, int N_, int K_, int U_, int S_, int T_, int G_,
+        const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ w, void* out,
-                                                         W16Launch a) {
+                                                         W16Launch a_in) {
+    const W16Launch a = lead_launch(M_, N_, K_, U_, S_, T_, a_in);
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int M = a.M, N = a.N, K = a.K, U = a.U;
     const int lane = threadIdx.x & 63;
@@ -357,9 +373,11 @@ constexpr int kW16DMaxUnits = 16;       // units per wave
 constexpr int kW16DMaxXLoads = 16;      // x load instructions per wave: M * 16 * units <= 64 * 16
 
 template <bool BF16, int MR>
-__global__ __launch_bounds__(64 * kW16DWaves) void w16_dot_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(64 * kW16DWaves) void w16_dot_kernel(int M_, int N_, int K_, int U_, int S_, int T_, int G_,
+        const uint16_t* __restrict__ x,
                                                       const uint16_t* __restrict__ w, void* out,
-                                                      W16Launch a) {
+                                                      W16Launch a_in) {
+    const W16Launch a = lead_launch(M_, N_, K_, U_, S_, T_, a_in);
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int M = a.M, N = a.N, K = a.K, U = a.U;
     const int lane = threadIdx.x & 63;
@@ -525,17 +543,19 @@ constexpr size_t kW16BLdsMax = 144 * 1024;      // x and the slots, one workgrou
 constexpr int kW16BMaxXLoads = 9;               // x load instructions per thread (144 KB / 16 KB)
 
 template <bool BF16, int MR>
-__global__ __launch_bounds__(1024) void w16_dot_bal_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(1024) void w16_dot_bal_kernel(int M_, int N_, int K_, int U_, int S_, int T_, int G_,
+        const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ w,
-                                                           void* out, W16Launch a) {
+                                                           void* out, W16Launch a_in) {
+    const W16Launch a = lead_launch(M_, N_, K_, U_, S_, T_, a_in);
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int M = a.M, N = a.N, K = a.K, U = a.U;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int kc = lane & 15, r = lane >> 4;
     const int G4 = (N + 3) >> 2;
-    const int g0 = (int)((long long)blockIdx.x * G4 / gridDim.x);
-    const int g1 = (int)((long long)(blockIdx.x + 1) * G4 / gridDim.x);
+    const int g0 = (int)((long long)blockIdx.x * G4 / G_);
+    const int g1 = (int)((long long)(blockIdx.x + 1) * G4 / G_);
     const int ng = g1 - g0;
     if (ng == 0) return;                              // the whole workgroup
     constexpr int kUnitBytes = kUnitK * 2;
@@ -676,7 +696,8 @@ const void* pick_w16_dot(int M) {
     return (const void*)w16_dot_kernel<BF16, 4>;
 }
 
-typedef void (*w16_kernel_t)(const uint16_t*, const uint16_t*, void*, W16Launch);
+typedef void (*w16_kernel_t)(int, int, int, int, int, int, int, const uint16_t*, const uint16_t*,
+                             void*, W16Launch);
 
 template <bool BF16>
 w16_kernel_t pick_w16_rb(int rb) {
@@ -806,8 +827,8 @@ extern "C" int w16a16_gemv(const void* x, const void* w, int dtype, void* y, int
         const void* k = bf16 ? pick_w16_dot_bal<true>(M) : pick_w16_dot_bal<false>(M);
         const int mr = M <= 1 ? 1 : 2;
         const int C = w4h::cu_count();
-        hipLaunchKernelGGL((w16_kernel_t)k, dim3(C), dim3(64 * kW16BWaves), p.lds, st,
-                           (const uint16_t*)x, (const uint16_t*)w, y, l);
+        hipLaunchKernelGGL((w16_kernel_t)k, dim3(C), dim3(64 * kW16BWaves), p.lds, st, l.M, l.N, l.K,
+                           l.U, l.S, l.T, C, (const uint16_t*)x, (const uint16_t*)w, y, l);
         w4h::set_last_variant("w16_dotbal %s kernel=w16_dot_bal_kernel<%s, %d> workgroups=%d slices=1 lds=%zu",
                               bf16 ? "bf16" : "f16", bf16 ? "true" : "false", mr, C, p.lds);
         return w4h::launch_status();
@@ -817,8 +838,8 @@ extern "C" int w16a16_gemv(const void* x, const void* w, int dtype, void* y, int
         w4h::begin_launches();
         const void* k = bf16 ? pick_w16_dot<true>(M) : pick_w16_dot<false>(M);
         const int mr = M <= 1 ? 1 : M <= 2 ? 2 : 4;
-        hipLaunchKernelGGL((w16_kernel_t)k, dim3(T), dim3(64 * kW16DWaves), p.lds, st,
-                           (const uint16_t*)x, (const uint16_t*)w, y, l);
+        hipLaunchKernelGGL((w16_kernel_t)k, dim3(T), dim3(64 * kW16DWaves), p.lds, st, l.M, l.N, l.K,
+                           l.U, l.S, l.T, T, (const uint16_t*)x, (const uint16_t*)w, y, l);
         w4h::set_last_variant("w16_dot %s kernel=w16_dot_kernel<%s, %d> tiles=%d slices=1 lds=%zu",
                               bf16 ? "bf16" : "f16", bf16 ? "true" : "false", mr, T, p.lds);
         return w4h::launch_status();
@@ -827,8 +848,8 @@ extern "C" int w16a16_gemv(const void* x, const void* w, int dtype, void* y, int
         allow_w16_lds();
         w4h::begin_launches();
         hipLaunchKernelGGL(bf16 ? w16_ksplit_kernel<true> : w16_ksplit_kernel<false>, dim3(T),
-                           dim3(64 * kW16KWaves), p.lds, st, (const uint16_t*)x, (const uint16_t*)w,
-                           y, l);
+                           dim3(64 * kW16KWaves), p.lds, st, l.M, l.N, l.K, l.U, l.S, l.T, T,
+                           (const uint16_t*)x, (const uint16_t*)w, y, l);
         w4h::set_last_variant("w16_mfma16 %s kernel=w16_ksplit_kernel<%s> tiles=%d slices=1 lds=%zu",
                               bf16 ? "bf16" : "f16", bf16 ? "true" : "false", T, p.lds);
         return w4h::launch_status();
@@ -836,7 +857,8 @@ extern "C" int w16a16_gemv(const void* x, const void* w, int dtype, void* y, int
     w4h::begin_launches();
     hipLaunchKernelGGL(bf16 ? pick_w16_rb<true>(p.rb) : pick_w16_rb<false>(p.rb),
                        dim3((unsigned)p.workgroups, p.split), dim3(64 * kW16Waves), 0, st,
-                       (const uint16_t*)x, (const uint16_t*)w, p.split > 1 ? w4h::ws_part(workspace) : y, l);
+                       l.M, l.N, l.K, l.U, l.S, l.T, (int)p.workgroups, (const uint16_t*)x,
+                       (const uint16_t*)w, p.split > 1 ? w4h::ws_part(workspace) : y, l);
     if (p.split > 1) w4h::launch_merge(w4h::ws_part(workspace), y, y_dtype, nullptr, W4A16_F32, M, N, p.split, st);
     w4h::set_last_variant("w16_mfma16 %s kernel=w16_gemv_kernel<%s, %d> tiles=%d slices=%d "
                           "workgroups=%lld",

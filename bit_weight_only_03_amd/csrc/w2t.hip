@@ -188,8 +188,13 @@ constexpr int min_waves2() { return SPG >= 4 && UPW <= 4 ? 8 : 1; }
 // 4-bit kernel's three-tile workgroups, for the same reason).
 template <bool BF16, int SPG, int UPW, int TPW = 1>
 __global__ __launch_bounds__(512, (TPW > 1 ? 4 : min_waves2<SPG, UPW>())) void w2t_gemv_kernel(
+    int M_, int N_, int K_, int U_, int S_, int W_,
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ qdev,
-    const uint16_t* __restrict__ sdev, void* __restrict__ out, W2Launch a) {
+    const uint16_t* __restrict__ sdev, void* __restrict__ out, W2Launch a_in) {
+    // The fields a wave needs first arrive as leading scalars (with the
+    // pointers: ten arguments, 14 dwords), which the build compiles as
+    // preloaded into SGPRs at wave launch; out_dtype stays in the struct.
+    const W2Launch a{M_, N_, K_, U_, S_, a_in.out_dtype};
     constexpr int NG = SPG >= 8 ? 1 : 8 / SPG;   // groups per unit
     constexpr int SPU = SPG >= 8 ? 8 : SPG;      // 32-k steps per group inside one unit
     static_assert(TPW >= 1 && TPW <= 3, "one to three tiles per workgroup");
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 4 : min_waves2<SPG, UPW>())) void w
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int M = a.M, K = a.K, U = a.U;
-    const int W = blockDim.x >> 6;
+    const int W = W_;                                                  // waves per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int t0 = blockIdx.x * TPW, split = blockIdx.y;
@@ -430,17 +435,17 @@ struct SlotX {
 
 // SPG = group / 32 steps per group; a unit has 8 steps (256 k).
 template <bool BF16, int SPG, int D>
-__global__ __launch_bounds__(512) void w2t_gemv_direct_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(512) void w2t_gemv_direct_kernel(int M, int N, int K, int S, int nw,
+                                                       const uint16_t* __restrict__ x,
                                                        const u32x4_t* __restrict__ qdev,
                                                        const uint16_t* __restrict__ sdev,
-                                                       void* __restrict__ out, int out_dtype, int M,
-                                                       int N, int K, int S) {
+                                                       void* __restrict__ out, int out_dtype) {
     static_assert(D % 2 == 0, "x double buffer alternates with the ring index");
     constexpr int NG = SPG >= 8 ? 1 : 8 / SPG;   // groups per unit
     constexpr int SPU = SPG >= 8 ? 8 : SPG;      // steps per group inside one unit
     __shared__ float red[kMaxWavesX][kMaxRows][kTileN];
 
-    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63;   // nw: waves per workgroup (an argument, preloaded)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int t = blockIdx.x, split = blockIdx.y;
     const int U = (K + kUnitK2 - 1) / kUnitK2;
@@ -562,8 +567,8 @@ PlanX make_planx(int N, int K) {
     return p;
 }
 
-typedef void (*w2x_kernel_t)(const uint16_t*, const u32x4_t*, const uint16_t*, void*, int, int, int,
-                             int, int);
+typedef void (*w2x_kernel_t)(int, int, int, int, int, const uint16_t*, const u32x4_t*,
+                             const uint16_t*, void*, int);
 
 template <bool BF16>
 w2x_kernel_t pickx(int group) {
@@ -631,7 +636,8 @@ Plan2 make_plan2(int M, int N, int K, int cus) {
     return p;
 }
 
-typedef void (*w2_kernel_t)(const uint16_t*, const u32x4_t*, const uint16_t*, void*, W2Launch);
+typedef void (*w2_kernel_t)(int, int, int, int, int, int, const uint16_t*, const u32x4_t*,
+                            const uint16_t*, void*, W2Launch);
 
 template <bool BF16, int SPG>
 w2_kernel_t pick_upw2_kernel(int upw) {
@@ -757,8 +763,8 @@ int launch_direct(const void* x, int x_dtype, const void* qweight, const void* s
     void* out = p.split > 1 ? w4h::ws_part(workspace) : y;
     const int odt = p.split > 1 ? W4A16_F32 : y_dtype;
     w4h::begin_launches();
-    hipLaunchKernelGGL(k, dim3(T, p.split), dim3(64 * p.waves), 0, st, (const uint16_t*)x,
-                       (const u32x4_t*)qweight, (const uint16_t*)scales, out, odt, M, N, K, p.split);
+    hipLaunchKernelGGL(k, dim3(T, p.split), dim3(64 * p.waves), 0, st, M, N, K, p.split, p.waves,
+                       (const uint16_t*)x, (const u32x4_t*)qweight, (const uint16_t*)scales, out, odt);
     if (p.split > 1) {
         const int MN = M * N;
         hipLaunchKernelGGL(w2_merge_kernel, dim3((MN + 255) / 256), dim3(256), 0, st,
@@ -882,7 +888,8 @@ extern "C" int w2t_gemv(const void* x, int x_dtype, const void* qweight, const v
     p.l.out_dtype = p.l.S > 1 ? W4A16_F32 : y_dtype;
     w4h::begin_launches();
     hipLaunchKernelGGL(k, dim3((p.tiles + p.tpw - 1) / p.tpw, p.l.S), dim3(64 * p.waves), p.lds, st,
-                       (const uint16_t*)x, (const u32x4_t*)qweight, (const uint16_t*)scales, out, p.l);
+                       p.l.M, p.l.N, p.l.K, p.l.U, p.l.S, p.waves, (const uint16_t*)x,
+                       (const u32x4_t*)qweight, (const uint16_t*)scales, out, p.l);
     if (p.l.S > 1) {
         const int MN = M * N;
         hipLaunchKernelGGL(w2_merge_kernel, dim3((MN + 255) / 256), dim3(256), 0, st,
