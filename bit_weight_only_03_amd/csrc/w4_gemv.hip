@@ -560,8 +560,23 @@ __global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<S
     int t0 = blockIdx.x * TPW;
     const int split = blockIdx.y;
     int nt = a.T - t0 < TPW ? a.T - t0 : TPW;                         // tiles of this workgroup
-    const int r0 = split * U / a.S, r1 = (split + 1) * U / a.S;
-    int w0 = r0 + wave * (r1 - r0) / W, w1 = r0 + (wave + 1) * (r1 - r0) / W;
+    // A wave's share of its slice's units.  Unsplit launches of eight waves
+    // (every hot layer) take it without the two runtime divisions, which
+    // sit between a wave's start and its first load; the balanced plan (one
+    // slice) replaces the shares below.
+    static_assert(kMaxWaves == 8, "the unsplit range below divides by 8 with a shift");
+    int r0, r1, w0, w1;
+    if (BAL || (a.S == 1 && W == kMaxWaves)) {
+        r0 = 0;
+        r1 = U;
+        w0 = (wave * U) >> 3;
+        w1 = ((wave + 1) * U) >> 3;
+    } else {
+        r0 = split * U / a.S;
+        r1 = (split + 1) * U / a.S;
+        w0 = r0 + wave * (r1 - r0) / W;
+        w1 = r0 + (wave + 1) * (r1 - r0) / W;
+    }
     // Three-tile chains of 5 units (g = 128, per-unit staging, eight waves):
     // waves 0-3 take 6 units and waves 4-7 take 4.  A wave's first unit
     // arrives in the order the grid issued its ring: every CU's first four
