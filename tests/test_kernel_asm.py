@@ -220,3 +220,39 @@ def test_x_wait_checker_on_synthetic_code():
     assert "LDS read" in check_x_wait(taken + wait)
     # too few ring loads after the x load
     assert check_x_wait(head[:2] + wait) is not None
+
+
+def test_gemv_kernel_arguments_are_preloaded(asm_files):
+    # The GEMV kernels take the fields every wave needs before its first
+    # load as leading arguments, compiled as preloaded into SGPRs (the
+    # build's per-source flags): the kernel descriptor must say so, and the
+    # hot instantiations must reach their first buffer load from the
+    # preloaded entry without waiting for a scalar load (later fields may be
+    # loaded on the way, as long as nothing waits for them).
+    want = {"w4_gemv.hip": ("w4_gemv_kernel", 14), "w16_gemv.hip": ("w16_", 14),
+            "w2t.hip": ("w2t_gemv", 10)}
+    bad = []
+    for src, (stem, min_len) in want.items():
+        text = asm_files[src]
+        descs = re.findall(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", text, re.S)
+        hits = [(n, b) for n, b in descs if stem in n]
+        assert hits, src
+        for name, body in hits:
+            m = re.search(r"\.amdhsa_user_sgpr_kernarg_preload_length (\d+)", body)
+            if not m or int(m.group(1)) < min_len:
+                bad.append(f"{src} {name}: preload {m.group(1) if m else None}")
+    # the hot 4-bit instantiations (qkv / o_proj, gate_up, down)
+    for name, lines in functions(asm_files["w4_gemv.hip"]):
+        if not re.search(r"w4_gemv_kernelILb0ELi4ELi5ELi[13]ELb0ELb1ELb0E|w4_gemv_kernelILb0ELi4ELi17ELi1ELb0ELb0ELb1E", name):
+            continue
+        # the preloaded entry is the first label after the compatibility block
+        entry = next(i for i, l in enumerate(lines) if i > 0 and re.fullmatch(r"\.LBB\d+_0:", l))
+        first = next(i for i in range(entry, len(lines)) if is_vmem_load(lines[i]))
+        pending = False
+        for l in lines[entry:first]:
+            if l.startswith("s_load"):
+                pending = True
+            elif pending and l.startswith("s_waitcnt") and "lgkmcnt" in l:
+                bad.append(f"{name}: waits for a scalar load before its first buffer load")
+                break
+    assert not bad, "\n".join(bad[:10])
