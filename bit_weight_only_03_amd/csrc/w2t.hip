@@ -188,11 +188,11 @@ constexpr int min_waves2() { return SPG >= 4 && UPW <= 4 ? 8 : 1; }
 // 4-bit kernel's three-tile workgroups, for the same reason).
 template <bool BF16, int SPG, int UPW, int TPW = 1>
 __global__ __launch_bounds__(512, (TPW > 1 ? 4 : min_waves2<SPG, UPW>())) void w2t_gemv_kernel(
-    int M_, int N_, int K_, int U_, int S_, int W_,
+    int M_, int N_, int K_, int U_, int S_,
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ qdev,
     const uint16_t* __restrict__ sdev, void* __restrict__ out, W2Launch a_in) {
     // The fields a wave needs first arrive as leading scalars (with the
-    // pointers: ten arguments, 14 dwords), which the build compiles as
+    // pointers: nine arguments, 14 dwords), which the build compiles as
     // preloaded into SGPRs at wave launch; out_dtype stays in the struct.
     const W2Launch a{M_, N_, K_, U_, S_, a_in.out_dtype};
     constexpr int NG = SPG >= 8 ? 1 : 8 / SPG;   // groups per unit
@@ -205,13 +205,19 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 4 : min_waves2<SPG, UPW>())) void w
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int M = a.M, K = a.K, U = a.U;
-    const int W = W_;                                                  // waves per workgroup
+    constexpr int W = kWaves2;                                         // waves per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int t0 = blockIdx.x * TPW, split = blockIdx.y;
     const int T = (a.N + kTileN - 1) >> 4;                           // 16-column tiles
     const int nt = T - t0 < TPW ? T - t0 : TPW;                      // tiles of this workgroup
-    const int r0 = split * U / a.S, r1 = (split + 1) * U / a.S;
+    // Unsplit launches take the slice without a runtime division (it sits
+    // between a wave's start and its first load).
+    int r0 = 0, r1 = U;
+    if (a.S != 1) {
+        r0 = split * U / a.S;
+        r1 = (split + 1) * U / a.S;
+    }
     const int w0 = r0 + wave * (r1 - r0) / W, w1 = r0 + (wave + 1) * (r1 - r0) / W;
     const int nu = w1 - w0;                                           // units of this wave
     const int Gp = U * kUnitK2 / (SPG * 32);
@@ -636,7 +642,7 @@ Plan2 make_plan2(int M, int N, int K, int cus) {
     return p;
 }
 
-typedef void (*w2_kernel_t)(int, int, int, int, int, int, const uint16_t*, const u32x4_t*,
+typedef void (*w2_kernel_t)(int, int, int, int, int, const uint16_t*, const u32x4_t*,
                             const uint16_t*, void*, W2Launch);
 
 template <bool BF16, int SPG>
@@ -888,7 +894,7 @@ extern "C" int w2t_gemv(const void* x, int x_dtype, const void* qweight, const v
     p.l.out_dtype = p.l.S > 1 ? W4A16_F32 : y_dtype;
     w4h::begin_launches();
     hipLaunchKernelGGL(k, dim3((p.tiles + p.tpw - 1) / p.tpw, p.l.S), dim3(64 * p.waves), p.lds, st,
-                       p.l.M, p.l.N, p.l.K, p.l.U, p.l.S, p.waves, (const uint16_t*)x,
+                       p.l.M, p.l.N, p.l.K, p.l.U, p.l.S, (const uint16_t*)x,
                        (const u32x4_t*)qweight, (const uint16_t*)scales, out, p.l);
     if (p.l.S > 1) {
         const int MN = M * N;
