@@ -246,23 +246,31 @@ __global__ __launch_bounds__(512, (TPW > 1 ? 4 : min_waves2<SPG, UPW>())) void w
         const int xch = M * cpr;
         const uint32_t xbytes = (uint32_t)M * (uint32_t)K * 2u;
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, xbytes);
+        // ci -> (row, position): one row needs no division (a division sits
+        // on the way to the wave's first load).
+        auto stage = [&](auto row_of) {
 #pragma unroll
-        for (int i = 0; i < kMaxXLoads2; ++i) {
-            if (i * 64 < xch) {                    // wave-uniform (false for a wave without units)
-                const int ci = i * 64 + lane;
-                const int m = ci / cpr, pc = ci % cpr;
-                const int lc = pc ^ (m & 3);       // same unit and step as pc
-                const int kg = w0 * kUnitK2 + lc * 8;
-                if (m < M) {
-                    if (kg < K)
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                            rx, (__attribute__((address_space(3))) void*)(xsb + i * 1024), 16,
-                            (uint32_t)(m * K + kg) * 2u, 0, 0, 0);
-                    else
-                        *(u32x4_t*)(xsb + (uint32_t)ci * 16u) = u32x4_t{0u, 0u, 0u, 0u};
+            for (int i = 0; i < kMaxXLoads2; ++i) {
+                if (i * 64 < xch) {                    // wave-uniform (false for a wave without units)
+                    const int ci = i * 64 + lane;
+                    const int m = row_of(ci), pc = ci - m * cpr;
+                    const int lc = pc ^ (m & 3);       // same unit and step as pc
+                    const int kg = w0 * kUnitK2 + lc * 8;
+                    if (m < M) {
+                        if (kg < K)
+                            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                                rx, (__attribute__((address_space(3))) void*)(xsb + i * 1024), 16,
+                                (uint32_t)(m * K + kg) * 2u, 0, 0, 0);
+                        else
+                            *(u32x4_t*)(xsb + (uint32_t)ci * 16u) = u32x4_t{0u, 0u, 0u, 0u};
+                    }
                 }
             }
-        }
+        };
+        if (M == 1)
+            stage([](int) { return 0; });
+        else
+            stage([&](int ci) { return ci / cpr; });
         if constexpr (!kUncond) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __builtin_amdgcn_sched_barrier(0);
