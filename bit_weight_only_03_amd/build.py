@@ -23,7 +23,7 @@ ARCH = "gfx950"
 
 # Per-source device flags.  The 4-bit GEMV kernel takes the arguments every
 # wave needs first as leading scalars and pointers (ten arguments, 14
-# dwords; the W16A16 and ternary kernels likewise); this option compiles them as
+# dwords; the W16A16, ternary and M-tiled kernels likewise); this option compiles them as
 # preloaded into SGPRs at wave launch,
 # which saves each wave a scalar load before its first memory access
 # (measured 0.25-0.3 us per call on the qkv and o_proj shapes).  The code
@@ -31,7 +31,8 @@ ARCH = "gfx950"
 # preload.
 SOURCE_FLAGS = {"w4_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"],
                 "w16_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"],
-                "w2t.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
+                "w2t.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"],
+                "w4_gemm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
 
 
 def sources():

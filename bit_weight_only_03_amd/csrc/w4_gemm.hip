@@ -87,11 +87,22 @@ struct GSlotSel<NG, true> {
 // SPG = 4): no zero points, each unit's four block scales folded into the
 // element conversion or applied step by step (mx_unit in common.h).
 template <bool BF16, int SPG, int RB, int TN, bool MX = false>
-__global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256) void w4_gemm_kernel(int M_, int N_, int K_, int U_, int S_, int T_,
+                                                      const uint16_t* __restrict__ x,
                                                       const u32x4_t* __restrict__ qdev,
                                                       const uint16_t* __restrict__ sdev,
                                                       const uint32_t* __restrict__ zdev,
-                                                      void* out, GemmLaunch a) {
+                                                      void* out, GemmLaunch a_in) {
+    // The fields a wave needs first arrive as leading scalars (with the four
+    // input pointers: ten arguments, 14 dwords), which the build compiles as
+    // preloaded into SGPRs at wave launch; the rest stays in the struct.
+    GemmLaunch a = a_in;
+    a.M = M_;
+    a.N = N_;
+    a.K = K_;
+    a.U = U_;
+    a.S = S_;
+    a.T = T_;
     constexpr int NG = SPG >= 4 ? 1 : 4 / SPG;    // groups per unit
     constexpr int SPU = SPG >= 4 ? 4 : SPG;       // 32-k steps per group inside one unit
     constexpr int ROWS = 16 * RB;
@@ -105,7 +116,11 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int c = lane & 15, kc = lane >> 4;
     const int split = blockIdx.y;
-    const int r0 = split * U / a.S, r1 = (split + 1) * U / a.S;          // the slice's units
+    int r0 = 0, r1 = U;                                                   // the slice's units
+    if (a.S != 1) {   // (no division on the way to an unsplit launch's first load)
+        r0 = split * U / a.S;
+        r1 = (split + 1) * U / a.S;
+    }
     const int nu = r1 - r0;
     const int tw = (blockIdx.x * kGemmWaves + wave) * TN;                // the wave's first tile
     const int nt = T - tw < 0 ? 0 : (T - tw < TN ? T - tw : TN);         // its tiles inside N
@@ -352,8 +367,8 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
     }
 }
 
-typedef void (*gemm_kernel_t)(const uint16_t*, const u32x4_t*, const uint16_t*, const uint32_t*,
-                              void*, GemmLaunch);
+typedef void (*gemm_kernel_t)(int, int, int, int, int, int, const uint16_t*, const u32x4_t*,
+                              const uint16_t*, const uint32_t*, void*, GemmLaunch);
 
 template <bool BF16, int SPG, int TN, bool MX = false>
 gemm_kernel_t pick_rb(int rb) {
@@ -418,7 +433,7 @@ int gemm_launch(const GemmPlan& p, const void* x, bool bf16, const void* qweight
     GemmLaunch l{M, N, K, U, p.split, T, y_dtype, res, res_dtype};
     gemm_kernel_t k = mx ? pick_gemm_mx(bf16, p.rb, p.tn) : pick_gemm(bf16, group, p.rb, p.tn);
     hipLaunchKernelGGL(k, dim3((unsigned)p.workgroups, p.split), dim3(64 * kGemmWaves), 0, st,
-                       (const uint16_t*)x, (const u32x4_t*)qweight, (const uint16_t*)scales,
+                       l.M, l.N, l.K, l.U, l.S, l.T, (const uint16_t*)x, (const u32x4_t*)qweight, (const uint16_t*)scales,
                        (const uint32_t*)zeros, p.split > 1 ? workspace : y, l);
     return W4A16_OK;
 }

@@ -230,7 +230,7 @@ def test_gemv_kernel_arguments_are_preloaded(asm_files):
     # preloaded entry without waiting for a scalar load (later fields may be
     # loaded on the way, as long as nothing waits for them).
     want = {"w4_gemv.hip": ("w4_gemv_kernel", 14), "w16_gemv.hip": ("w16_", 14),
-            "w2t.hip": ("w2t_gemv", 10)}
+            "w2t.hip": ("w2t_gemv", 10), "w4_gemm.hip": ("w4_gemm_kernel", 14)}
     bad = []
     for src, (stem, min_len) in want.items():
         text = asm_files[src]
