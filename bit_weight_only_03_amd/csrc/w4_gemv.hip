@@ -177,6 +177,13 @@ __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_
     constexpr int LPS = MX ? 2 : 1 + 2 * NG;              // loads per ring slot
     using SlotT = typename SlotSel<NG, MX>::type;
     constexpr bool kCvtX = BF16 && !MX;   // bf16 x taken to fp16 in LDS for the 4-bit products
+    // One-tile per-unit chains with bf16 x load each unit's x into registers
+    // and store it to LDS converted: one LDS round trip per unit instead of
+    // two (an LDS-direct load, then a read, convert and write back).
+    // Measured at M = 4 (bf16 x): qkv 6.68-6.78 -> 6.47-6.53 us, o_proj
+    // 6.26-6.29 -> 6.06-6.08 us.  Multi-tile chains stay at 128 VGPRs
+    // without the room for it.
+    constexpr bool kRegX = kCvtX && PX && BAR == 0 && TPW == 1;
     constexpr int XU = BAR == 1 || BAR == 2 ? CL : UPW;   // units per staged row (= xstride / 128 otherwise)
     // PX: x slots in the wave's region.  The balanced plan's waves reuse a
     // ring of D (unit i in slot i % D: its x load goes out with the refill
@@ -269,15 +276,20 @@ __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_
 
     // Chain position q = unit i (of this wave's range) x tile j, unit-major,
     // so one x fragment serves the workgroup's TPW tiles back to back.
+    u32x4_t xreg[kRegX ? XR : 1];
     auto load_slot = [&](int q, SlotT& r) {
         const int i = q / TPW, j = q % TPW;
         const bool valid = i < nu && j < nt;
         const int u = w0 + i;
         if constexpr (PX) {
             if (j == 0) {   // the unit's x: [4 rows][256 bytes] straight into LDS
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    i < nu ? rx : rx0, (__attribute__((address_space(3))) void*)(xsb + (i % XR) * 1024), 16,
-                    xlane_off, (uint32_t)u * (kUnitK * 2u), 0, 0);
+                if constexpr (kRegX)
+                    xreg[i % XR] = bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(
+                        i < nu ? rx : rx0, xlane_off, (uint32_t)u * (kUnitK * 2u), 0));
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        i < nu ? rx : rx0, (__attribute__((address_space(3))) void*)(xsb + (i % XR) * 1024), 16,
+                        xlane_off, (uint32_t)u * (kUnitK * 2u), 0, 0);
                 __builtin_amdgcn_sched_barrier(0);   // before the slot's own loads
             }
         }
@@ -366,7 +378,12 @@ __device__ __forceinline__ void w4_wave_chain(const GemvLaunch& a, const uint16_
     for (int q = 0; q < L; ++q) {
         const int i = q / TPW, tj = q % TPW;
         SlotT& sl = ring[q % D];
-        if constexpr (PX) {
+        if constexpr (kRegX) {
+            if (tj == 0) {   // this unit's x, converted, into its LDS slot (the compiler waits for it)
+                *(u32x4_t*)(xsb + (uint32_t)(i % XR) * 1024u + (uint32_t)lane * 16u) =
+                    bf16x8_to_f16x8(xreg[i % XR]);
+            }
+        } else if constexpr (PX) {
             if (tj == 0) {
                 // Wait for this unit's x: loads complete in issue order, and
                 // after it went out came its slot's LPS loads and, for each
@@ -520,7 +537,11 @@ constexpr int min_waves() { return (SPG >= 4 && UPW <= 5) || (SPG == 2 && UPW <=
 // which stream the workgroup's own tile while 8 split one piece of a leftover
 // tile (see the planner); TPW = 1, whole-range x staging, up to 2 rows.
 template <bool BF16, int SPG, int UPW, int TPW, bool MX = false, bool PX = false, bool BAL = false>
-__global__ __launch_bounds__(BAL ? 1024 : 512, (TPW > 1 || BAL ? 1 : min_waves<SPG, UPW>())) void w4_gemv_kernel(
+// (One-tile per-unit chains with bf16 x hold each unit's x in registers
+// until it is stored converted, so they run under a four-waves-per-SIMD
+// bound: their layers put at most two workgroups on a CU.)
+__global__ __launch_bounds__(BAL ? 1024 : 512,
+                             (TPW > 1 || BAL ? 1 : (BF16 && PX && !MX) ? 4 : min_waves<SPG, UPW>())) void w4_gemv_kernel(
     int M_, int K_, int U_, int T_, int plan0, int plan1,
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ qdev,
     const uint16_t* __restrict__ sdev, const uint32_t* __restrict__ zdev, void* out,
