@@ -530,16 +530,17 @@ constexpr int min_waves() { return (SPG >= 4 && UPW <= 5) || (SPG == 2 && UPW <=
 // register plan.
 // PX = true stages x unit by unit instead (up to 4 rows, K a multiple of
 // 128, unconditional arithmetic): each unit's x is one load of [4 rows][256
-// bytes] straight into LDS, issued with the unit's first ring slot, and the
+// bytes] straight into LDS (one-tile chains with bf16 x: into registers,
+// stored to LDS converted), issued with the unit's first ring slot, and the
 // wave waits for it just before the unit's products.  The first unit then
 // waits for its own 1 KB of x and not for the wave's whole range.
 // BAL = true runs the balanced plan: one workgroup per CU of 16 waves, 8 of
 // which stream the workgroup's own tile while 8 split one piece of a leftover
 // tile (see the planner); TPW = 1, whole-range x staging, up to 2 rows.
-template <bool BF16, int SPG, int UPW, int TPW, bool MX = false, bool PX = false, bool BAL = false>
-// (One-tile per-unit chains with bf16 x hold each unit's x in registers
+// One-tile per-unit chains with bf16 x hold each unit's x in registers
 // until it is stored converted, so they run under a four-waves-per-SIMD
-// bound: their layers put at most two workgroups on a CU.)
+// bound (their layers put at most two workgroups on a CU).
+template <bool BF16, int SPG, int UPW, int TPW, bool MX = false, bool PX = false, bool BAL = false>
 __global__ __launch_bounds__(BAL ? 1024 : 512,
                              (TPW > 1 || BAL ? 1 : (BF16 && PX && !MX) ? 4 : min_waves<SPG, UPW>())) void w4_gemv_kernel(
     int M_, int K_, int U_, int T_, int plan0, int plan1,
